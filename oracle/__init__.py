@@ -1,0 +1,190 @@
+"""fp64 CPU oracle for the Mamba-2 selective state-space layer.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import this package.  The product
+path (``libssd.so`` and ``selective_state_space_08_amd``) never imports it and
+shares no code with it.
+
+The arithmetic lives in ``ssd_oracle.c`` (plain C, double precision, token by
+token, OpenMP over (batch, head)); this module only builds that library and
+marshals numpy arrays into it.  Every function is pinned by the CPU tests in
+``tests/test_oracle_pins.py`` against forms that do not share its code: the
+quadratic (materialised-matrix) SSD form, an independent chunked form,
+closed forms (geometric series, prefix sums, conv impulse response, steady
+state), special cases (dt = 0, A = 0) and invariants (linearity, group
+sharing, split-carry, decode = prefill).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssd_oracle.c")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def compile_source(src: str, out: str) -> str:
+    """gcc a copy of the oracle source into a shared library (no fast-math, no
+    FMA contraction: plain IEEE double arithmetic)."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+           "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wextra",
+           src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile ssd_oracle.c into liboracle.so."""
+    if not force and os.path.exists(LIB_PATH):
+        return LIB_PATH
+    return compile_source(_SRC, LIB_PATH)
+
+
+def _bind(lib):
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    I64 = ctypes.c_int64
+    lib.oracle_causal_conv1d.argtypes = [P, I64, P, P, P, I, P, P, I, I, I, I]
+    lib.oracle_causal_conv1d.restype = I
+    lib.oracle_mamba2_fwd.argtypes = [P, I64, P, P, I, P, P, P, P, P, I, P, P, P, P, P,
+                                      I, I, I, I, I, I]
+    lib.oracle_mamba2_fwd.restype = I
+    lib.oracle_mamba2_decode_step.argtypes = [P, P, P, P, P, I, P, P, P, P, I, P, P,
+                                              I, I, I, I, I]
+    lib.oracle_mamba2_decode_step.restype = I
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = I
+    return lib
+
+
+def load_library(path: str):
+    """Load and bind an oracle library built from ssd_oracle.c at ``path``."""
+    return _bind(ctypes.CDLL(path))
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        build()
+    _lib = load_library(LIB_PATH)
+    return _lib
+
+
+def _f32(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _f64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    return _load().oracle_num_threads()
+
+
+def causal_conv1d(xbc, w, bias=None, conv_state_in=None, apply_silu=True):
+    """Depthwise causal conv over xbc [B, L, Cdim] with weights w [Cdim, K].
+
+    Returns (out [B, L, Cdim] float64, conv_state_out [B, K-1, Cdim] float64).
+    """
+    lib = _load()
+    x = _f32(xbc)
+    B, L, C = x.shape
+    w = _f32(w)
+    K = w.shape[1]
+    bias = _f32(bias)
+    hist = _f32(conv_state_in)
+    out = np.empty((B, L, C), np.float64)
+    hist_out = np.empty((B, K - 1, C), np.float64)
+    rc = lib.oracle_causal_conv1d(_ptr(x), C, _ptr(w), _ptr(bias), _ptr(hist),
+                                  int(bool(apply_silu)), _ptr(out), _ptr(hist_out),
+                                  B, L, C, K)
+    if rc != 0:
+        raise ValueError("oracle_causal_conv1d: bad argument")
+    return out, hist_out
+
+
+def mamba2_fwd(xbc, dt, A, *, nheads, headdim, ngroups, dstate, conv_w=None,
+               conv_b=None, conv_state_in=None, D=None, dt_bias=None,
+               dt_softplus=True, z=None, h0=None):
+    """The layer, token by token in fp64.
+
+    xbc [B, L, Cdim] raw x|B|C (post-conv when conv_w is None); dt [B, L, H];
+    A [H]; z [B, L, H, P] or None; h0 [B, H, P, N] or None.
+    Returns (y [B, L, H, P], h_final [B, H, P, N], conv_state_out or None),
+    all float64.
+    """
+    lib = _load()
+    x = _f32(xbc)
+    B, L, C = x.shape
+    H, P, G, N = nheads, headdim, ngroups, dstate
+    if C != H * P + 2 * G * N:
+        raise ValueError("xbc channel count %d != H*P + 2*G*N" % C)
+    dt = _f32(dt).reshape(B, L, H)
+    A = _f32(A)
+    conv_w = _f32(conv_w)
+    K = 0 if conv_w is None else conv_w.shape[1]
+    conv_b = _f32(conv_b)
+    hist = _f32(conv_state_in)
+    D = _f32(D)
+    dt_bias = _f32(dt_bias)
+    z = None if z is None else _f32(z).reshape(B, L, H, P)
+    h0 = None if h0 is None else _f64(h0).reshape(B, H, P, N)
+    y = np.empty((B, L, H, P), np.float64)
+    hT = np.empty((B, H, P, N), np.float64)
+    hist_out = np.empty((B, K - 1, C), np.float64) if conv_w is not None else None
+    rc = lib.oracle_mamba2_fwd(_ptr(x), C, _ptr(conv_w), _ptr(conv_b), K, _ptr(hist),
+                               _ptr(dt), _ptr(A), _ptr(D), _ptr(dt_bias),
+                               int(bool(dt_softplus)), _ptr(z), _ptr(h0), _ptr(y),
+                               _ptr(hT), _ptr(hist_out), B, L, H, P, G, N)
+    if rc != 0:
+        raise ValueError("oracle_mamba2_fwd: bad argument")
+    return y, hT, hist_out
+
+
+class DecodeState:
+    """fp64 decode carry: the SSM state [B, H, P, N] and the conv ring
+    [B, K-1, Cdim] (oldest row first)."""
+
+    def __init__(self, state, ring):
+        self.state = _f64(state).copy()
+        self.ring = None if ring is None else _f64(ring).copy()
+
+
+def mamba2_decode_step(carry: DecodeState, xbc, dt, A, *, nheads, headdim, ngroups,
+                       dstate, conv_w=None, conv_b=None, D=None, dt_bias=None,
+                       dt_softplus=True, z=None):
+    """One decode step; updates ``carry`` in place and returns y [B, H*P] float64."""
+    lib = _load()
+    x = _f32(xbc)
+    B, C = x.shape
+    H, P, G, N = nheads, headdim, ngroups, dstate
+    conv_w = _f32(conv_w)
+    K = 0 if conv_w is None else conv_w.shape[1]
+    y = np.empty((B, H * P), np.float64)
+    rc = lib.oracle_mamba2_decode_step(
+        _ptr(carry.state), _ptr(x), _ptr(carry.ring), _ptr(conv_w), _ptr(_f32(conv_b)), K,
+        _ptr(_f32(dt).reshape(B, H)), _ptr(_f32(A)), _ptr(_f32(D)), _ptr(_f32(dt_bias)),
+        int(bool(dt_softplus)), _ptr(None if z is None else _f32(z).reshape(B, H * P)),
+        _ptr(y), B, H, P, G, N)
+    if rc != 0:
+        raise ValueError("oracle_mamba2_decode_step: bad argument")
+    return y
