@@ -1,0 +1,302 @@
+#!/usr/bin/env python3
+"""Benchmark of the Mamba-2 SSD layer on one MI355X.
+
+One step = one prefill of the Nemotron-H-8B-shaped Mamba-2 layer (batch 4 x
+8192 tokens, 128 heads x 64, d_state 128, 8 groups, chunk 128, conv 4 + SiLU,
+SiLU(z) gate; bf16 activations, fp32 state and output) through libssd: the
+causal conv, the chunked scan and the gated epilogue.  `value` is prefill
+tokens/s with every input already resident in HBM.  The same run times the
+decode workload (256 sequences x 1000 chained one-token ssd_state_update
+steps, fp32 state) and reports it under "decode".
+
+Kernel durations come from HIP events recorded on the stream the kernels are
+launched on (torch's current stream, which the binding passes to libssd).
+The CPU baseline is the fp64 oracle timed on a bounded sample of the same
+workload on this host's cores.
+
+Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "selective_state_space_08_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def prefill_alg_bytes_per_token(wl, fused: bool) -> float:
+    """Minimum HBM traffic of the layer per token: raw x|B|C, z and dt read once
+    (bf16), y written once (fp32).  The unfused path adds the fp32 conv
+    intermediate's write and re-read."""
+    e, o = 2, 4
+    b = e * wl.cdim + e * wl.d_inner + e * wl.nheads + o * wl.d_inner
+    if not fused:
+        b += 2 * 4 * wl.cdim
+    return float(b)
+
+
+def prefill_alg_flops_per_token(wl) -> float:
+    """Matrix-product work of the chunked form per token, counting the causal
+    lower triangles: 4 H N P (chunk state + inter-chunk read-out) +
+    (Q+1) (G N + H P) (C B^T per group and M X per head)."""
+    H, N, P, G, Q = wl.nheads, wl.dstate, wl.headdim, wl.ngroups, wl.chunk
+    return 4.0 * H * N * P + (Q + 1) * (G * N + H * P)
+
+
+def decode_alg_bytes_per_step(wl) -> float:
+    B, H, P, N, K = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.width
+    state = 2 * 4 * B * H * P * N                 # fp32 state read + write
+    ring = 2 * 2 * B * (K - 1) * wl.cdim          # bf16 ring rows read + written
+    io = 2 * B * wl.cdim + 2 * B * wl.d_inner + 2 * B * H + 4 * B * wl.d_inner
+    return float(state + ring + io)
+
+
+def traffic_record(kernel_key: str, current_hash: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path)).get(kernel_key)
+    except Exception:
+        return None
+    if not rec or rec.get("source_hash") != current_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_prefill(args, wl, torch, layer, synth, dev, dev32):
+    log("prefill %s: generating inputs" % wl.name)
+    t0 = time.time()
+    inp = synth.make_prefill(wl)
+    log("  generated in %.1fs; uploading" % (time.time() - t0))
+    from selective_state_space_08_amd import ssd
+    xbc = dev(inp.xbc, wl.dtype)
+    dt = dev(inp.dt, wl.dtype)
+    z = dev(inp.z, wl.dtype)
+    p = layer.LayerParams(nheads=wl.nheads, ngroups=wl.ngroups, conv_w=dev32(inp.conv_w),
+                          A=dev32(inp.A), dt_bias=dev32(inp.dt_bias), D=dev32(inp.D),
+                          chunk=wl.chunk)
+    h0 = dev32(inp.h0)
+    hT = torch.empty((wl.batch, wl.nheads, wl.headdim, wl.dstate), device="cuda")
+    y = torch.empty((wl.batch, wl.seqlen, wl.nheads, wl.headdim), device="cuda")
+    fused = not args.unfused
+    conv_out = None if fused else torch.empty((wl.batch, wl.seqlen, wl.cdim), device="cuda")
+    need = ssd.ssd_chunk_scan_workspace_bytes(wl.batch, wl.seqlen, wl.nheads,
+                                              ngroups=wl.ngroups)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    del inp
+
+    def step():
+        layer.prefill(xbc, dt, z, p, fused=fused, math="bf16", initial_state=h0,
+                      final_state=hT, conv_out=conv_out, y=y, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(stop)
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    step_ms = total_ms / args.steps
+    log("prefill: %.3f ms/step (events), median step %.3f ms, wall %.3f s" %
+        (step_ms, per[len(per) // 2], t_wall))
+    return dict(step_ms=step_ms, median_ms=per[len(per) // 2], fused=fused,
+                nseg_workspace=need)
+
+
+def time_decode(args, wl, torch, layer, synth, dev, dev32):
+    T = args.decode_steps
+    log("decode %s: generating %d steps of inputs" % (wl.name, T))
+    inp = synth.make_decode(wl)
+    xbc = torch.empty((T, wl.batch, wl.cdim), dtype=torch.bfloat16, device="cuda")
+    z = torch.empty((T, wl.batch, wl.d_inner), dtype=torch.bfloat16, device="cuda")
+    dt = torch.empty((T, wl.batch, wl.nheads), dtype=torch.bfloat16, device="cuda")
+    BLK = 100
+    for s0 in range(0, T, BLK):
+        s1 = min(T, s0 + BLK)
+        a, b, c = inp.steps(s0, s1)
+        xbc[s0:s1] = dev(a, "bf16")
+        z[s0:s1] = dev(b, "bf16")
+        dt[s0:s1] = dev(c, "bf16")
+    p = layer.LayerParams(nheads=wl.nheads, ngroups=wl.ngroups, conv_w=dev32(inp.conv_w),
+                          A=dev32(inp.A), dt_bias=dev32(inp.dt_bias), D=dev32(inp.D))
+    st0 = dev32(inp.state)
+    ring0 = dev(inp.ring, "bf16")
+    st, ring = st0.clone(), ring0.clone()
+    y = torch.empty((T, wl.batch, wl.d_inner), device="cuda")
+    log("decode: inputs resident (%.1f GB)" % ((xbc.numel() + z.numel()) * 2 / 1e9))
+
+    def chain(n):
+        for t in range(n):
+            layer.decode_step(st, xbc[t], dt[t], z[t], ring, p, y=y[t])
+
+    chain(min(T, 20))
+    torch.cuda.synchronize()
+    st.copy_(st0)
+    ring.copy_(ring0)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(T + 1)]
+    marks[0].record(stream)
+    for t in range(T):
+        layer.decode_step(st, xbc[t], dt[t], z[t], ring, p, y=y[t])
+        marks[t + 1].record(stream)
+    torch.cuda.synchronize()
+    total_ms = marks[0].elapsed_time(marks[T])
+    steps = [marks[t].elapsed_time(marks[t + 1]) for t in range(T)]
+    first = sum(steps[:10]) / 10
+    last = sum(steps[-10:]) / 10
+    log("decode: %.3f ms per step; first 10 %.3f ms, last 10 %.3f ms" % (total_ms / T, first, last))
+    return dict(chain_ms=total_ms, step_ms=total_ms / T, first10_ms=first, last10_ms=last)
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The fp64 oracle on a bounded sample of the prefill workload: whole
+    sequences of sampled (sequence, head) pairs, conv included."""
+    import numpy as np
+    import oracle
+    from selective_state_space_08_amd import synth
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from harness import oracle_pairs
+    inp = synth.make_prefill(wl)
+    everything = [(b, h) for b in range(wl.batch) for h in range(wl.nheads)]
+    order = np.random.default_rng(100).permutation(len(everything))
+    n, done, elapsed = 16, 0, 0.0
+    while done < len(everything):
+        pairs = [everything[i] for i in order[done:done + n]]
+        t0 = time.perf_counter()
+        oracle_pairs(inp, pairs)
+        elapsed += time.perf_counter() - t0
+        done += len(pairs)
+        if elapsed >= budget_s:
+            break
+        n = max(16, int(done * (budget_s - elapsed) / max(elapsed, 1e-3)))
+    frac = done / len(everything)
+    tok_s = wl.tokens * frac / elapsed
+    return dict(value=tok_s, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample="%d of %d (sequence, head) pairs of %s, each over all %d tokens with its "
+                       "conv channels; %.1f s of oracle time, scaled by the sampled fraction" %
+                       (done, len(everything), wl.name, wl.seqlen, elapsed))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--unfused", action="store_true",
+                    help="conv kernel + scan kernel instead of the fused scan")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(asked for --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from selective_state_space_08_amd import layer, ssd, synth
+    from selective_state_space_08_amd.workloads import DECODE_MAIN, PREFILL_MAIN, WORKLOADS
+    from selective_state_space_08_amd.devio import dev, dev32
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ssd.load()
+    wl = WORKLOADS[PREFILL_MAIN]
+    pre = time_prefill(args, wl, torch, layer, synth, dev, dev32)
+    tok_s = wl.tokens / (pre["step_ms"] / 1e3)
+    bpt = prefill_alg_bytes_per_token(wl, pre["fused"])
+    fpt = prefill_alg_flops_per_token(wl)
+    kernel_ms = pre["median_ms"]
+    achieved = bpt * wl.tokens / (kernel_ms / 1e3) / 1e9
+    kfile = ("scan_bf16.hip",) if pre["fused"] else ("scan_bf16.hip", "conv1d.hip")
+    key = "prefill_fused_scan" if pre["fused"] else "prefill_unfused"
+    traffic = traffic_record(key, src_hash(*kfile))
+    out = {
+        "metric": "Mamba-2 SSD prefill tokens/s + decode steps/s; % of MFMA / HBM peak",
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre["step_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; shapes and distributions of the Nemotron-H-8B Mamba-2 layer)",
+        "config": {"workload": wl.name, "batch": wl.batch, "seqlen": wl.seqlen,
+                   "nheads": wl.nheads, "headdim": wl.headdim, "dstate": wl.dstate,
+                   "ngroups": wl.ngroups, "chunk": wl.chunk, "conv_width": wl.width,
+                   "activations": "bf16", "state_and_output": "fp32",
+                   "path": "fused conv+scan" if pre["fused"] else "conv kernel + scan kernel",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": key, "alg_bytes_per_token": bpt,
+                     "launch_ms": kernel_ms},
+        "mfma": {"alg_flops_per_token": fpt,
+                 "achieved_tflops": fpt * wl.tokens / (kernel_ms / 1e3) / 1e12,
+                 "peak_tflops": BF16_PEAK_TFLOPS,
+                 "frac": fpt * wl.tokens / (kernel_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS},
+    }
+    if not args.no_decode:
+        dwl = WORKLOADS[DECODE_MAIN].with_(decode_steps=args.decode_steps)
+        dec = time_decode(args, dwl, torch, layer, synth, dev, dev32)
+        dbytes = decode_alg_bytes_per_step(dwl)
+        dach = dbytes / (dec["step_ms"] / 1e3) / 1e9
+        out["decode"] = {"workload": dwl.name, "steps_per_s": 1e3 / dec["step_ms"],
+                         "tokens_per_s": dwl.batch * 1e3 / dec["step_ms"],
+                         "ms_per_step": dec["step_ms"], "first10_ms": dec["first10_ms"],
+                         "last10_ms": dec["last10_ms"],
+                         "roofline": {"bound": "hbm", "achieved": dach, "peak": HBM_PEAK_GBS,
+                                      "unit": "GB/s", "frac": dach / HBM_PEAK_GBS,
+                                      "alg_bytes_per_step": dbytes}}
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+        log("cpu baseline: %.1f tokens/s on %d threads" % (out["cpu_baseline"]["value"],
+                                                           out["cpu_baseline"]["cores"]))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,193 @@
+/*
+ * ssd.h -- C ABI of libssd.so, a Mamba-2 selective state-space (SSD) layer
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What the layer computes (page title, then section):
+ *  - The recurrence h_t = Abar_t h_{t-1} + Bbar_t x_t with read-out
+ *    y_t = C_t h_t + D x_t, whose parameters depend on the input:
+ *    "Hybrid Architectures for Language Models: Systematic Analysis and Design
+ *    Insights" (Korean summary), section 2 Background.  The same section notes
+ *    that Mamba-2's state space duality recasts this as matrix multiplies;
+ *    ssd_chunk_scan_fwd computes it in that chunked form.
+ *  - A depthwise causal conv (kernel 4) with SiLU in front of the scan, over
+ *    the x|B|C channels: "Nemotron-H style Hybrid Mamba-Transformer 3B
+ *    feasibility study", tables 1.4 and 1.5 (conv_kernel 4, activation SiLU);
+ *    the conv's channel span follows the Mamba cache size
+ *    2*N_L*(d_ssm*d_state + N_conv*(2*d_state + d_ssm)) in "Hybrid
+ *    Architectures ..." summary, Appendix C.
+ *  - Shapes: head_dim P = 64, d_state N = 128, n_groups G, chunk 128
+ *    (feasibility study, table 1.4).
+ *  - The decode state is of fixed size, independent of the position
+ *    ("Nemotron-H paper explainer", Transformer-vs-Mamba table: O(1) compute
+ *    and memory per token).
+ *
+ * Readings where the pages are silent:
+ *  - delta_t = softplus(dt_t + dt_bias_h) if dt_softplus, else dt_t (+ dt_bias_h);
+ *    Abar_t = exp(delta_t * A_h) (one scalar per token and head, A_h < 0);
+ *    Bbar_t = delta_t * B_t.
+ *  - y_t reads the state after x_t has been added.
+ *  - out = (y + D_h x) * z * sigmoid(z) when z is given (SiLU gate), else y + D_h x.
+ *  - Head h reads group g = floor(h * G / H) of B and C.
+ *  - Conv: u[t,c] = bias[c] + sum_{k<K} w[c][k] * xin[t-(K-1)+k, c] (the last tap
+ *    meets the current token); xin before the first token comes from the conv
+ *    state (oldest row first) or is zero; the activation is SiLU.
+ *
+ * Conventions for every entry point:
+ *  - All tensors are device pointers owned by the caller; the library
+ *    allocates no device memory and keeps no state but a thread-local error
+ *    string.  Scratch comes from the caller's workspace.
+ *  - Activations are token-major: row t of sequence b of a tensor X with
+ *    token stride S (in elements) starts at X + (b*L + t)*S; within a row the
+ *    innermost index is contiguous.  x, B and C may therefore be views into
+ *    one [B, L, Cdim] buffer with channel order x (H*P) | B (G*N) | C (G*N).
+ *  - Parameters (conv weights and bias, A, D, dt_bias) are fp32.  SSM states
+ *    are fp32 [B, H, P, N], N contiguous.  Conv states are [B, K-1, Cdim] in
+ *    the dtype of the raw x|B|C input, oldest row first.
+ *  - Every call validates all arguments on the host before anything is
+ *    enqueued, so an error status means nothing was written.  Work is
+ *    enqueued on `stream` and the call returns without synchronising; a
+ *    kernel fault surfaces at the caller's next synchronisation.
+ *  - Results are deterministic: no floating-point atomics and a fixed
+ *    reduction order, so identical inputs give identical bytes.
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef SSD_H_
+#define SSD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype_t;
+
+/* Arithmetic of the scan's matrix products.
+ * SSD_MATH_F32: every product and sum in fp32 (vector ALU).
+ * SSD_MATH_BF16: the intra-chunk and state products take bf16 operands on the
+ *   matrix cores with fp32 accumulation; decays, the state carry between
+ *   chunks, the D skip and the gate stay fp32. */
+typedef enum ssd_math { SSD_MATH_F32 = 0, SSD_MATH_BF16 = 1 } ssd_math_t;
+
+enum ssd_status {
+  SSD_OK = 0,
+  SSD_ERR_INVALID_ARG = -1, /* NULL required pointer, bad size/stride/alignment, overlap */
+  SSD_ERR_UNSUPPORTED = -2, /* valid, but no compiled kernel for it (e.g. P != 64)     */
+  SSD_ERR_WORKSPACE = -3,   /* workspace missing or smaller than the query said        */
+  SSD_ERR_HIP = -4          /* a HIP runtime call failed; ssd_last_error() has detail  */
+};
+
+/*
+ * Depthwise causal conv1d (+ SiLU) over [B, L, Cdim].
+ *
+ *   x               [B, L, Cdim] x_dtype, token stride x_tok_stride >= cdim
+ *   weight          [Cdim, K] fp32;  bias [Cdim] fp32 or NULL
+ *   conv_state_in   [B, K-1, Cdim] x_dtype or NULL (zero history)
+ *   conv_state_out  [B, K-1, Cdim] x_dtype or NULL: the last K-1 raw inputs
+ *                   of each sequence (reaching into conv_state_in when L < K-1);
+ *                   must not overlap conv_state_in
+ *   out             [B, L, Cdim] out_dtype, token stride out_tok_stride >= cdim;
+ *                   must not overlap x
+ *   width K in [1, 4]; apply_silu 0/1.
+ * batch == 0 or seqlen == 0 is a valid call that only writes conv_state_out.
+ */
+int ssd_causal_conv1d_fwd(const void* x, int64_t x_tok_stride, ssd_dtype_t x_dtype,
+                          const float* weight, const float* bias,
+                          const void* conv_state_in, void* conv_state_out, void* out,
+                          int64_t out_tok_stride, ssd_dtype_t out_dtype, int batch,
+                          int seqlen, int cdim, int width, int apply_silu,
+                          hipStream_t stream);
+
+/* Bytes of device workspace ssd_chunk_scan_fwd needs for this shape (it may be
+ * 0).  The same arguments must be passed to ssd_chunk_scan_fwd. */
+size_t ssd_chunk_scan_workspace_bytes(int batch, int seqlen, int nheads, int headdim,
+                                      int ngroups, int dstate, int chunk,
+                                      ssd_math_t math);
+
+/*
+ * Chunked selective scan of one Mamba-2 layer (prefill), from x, B, C, dt and z
+ * to the gated output, with optional initial and final SSM state.
+ *
+ *   x   [B, L, H, P]  xbc_dtype, token stride x_tok_stride
+ *   Bm  [B, L, G, N]  xbc_dtype, token stride b_tok_stride
+ *   Cm  [B, L, G, N]  xbc_dtype, token stride c_tok_stride
+ *       post-conv values when conv_w is NULL; raw conv inputs otherwise.
+ *   conv_w [Cdim, K] fp32, conv_b [Cdim] fp32 or NULL, conv_width K in [1,4]:
+ *       when conv_w is non-NULL the depthwise causal conv + SiLU of
+ *       ssd_causal_conv1d_fwd is applied to x, B and C inside the scan
+ *       (channel c of x, B, C is row c of conv_w, in the order x | B | C);
+ *       conv_state_in / conv_state_out [B, K-1, Cdim] xbc_dtype or NULL as in
+ *       ssd_causal_conv1d_fwd.  Both must be NULL when conv_w is NULL.
+ *   dt  [B, L, H]     act_dtype, token stride dt_tok_stride (raw, before bias)
+ *   z   [B, L, H, P]  act_dtype, token stride z_tok_stride, or NULL (no gate)
+ *   A [H] fp32 (< 0 for a decaying state); D [H] fp32 or NULL (no skip);
+ *   dt_bias [H] fp32 or NULL; dt_softplus 0/1.
+ *   initial_state [B, H, P, N] fp32 or NULL (zero); final_state [B, H, P, N]
+ *       fp32 or NULL.  They may be the same buffer.
+ *   y   [B, L, H, P]  y_dtype, token stride y_tok_stride; must not overlap any
+ *       input.
+ *   Supported: P = 64, N = 128, H % G == 0; chunk 128 for SSD_MATH_BF16 and
+ *   chunk in {32, 64, 128, 256} for SSD_MATH_F32; seqlen >= 0 (0 only copies
+ *   the states); innermost rows 16-byte aligned.
+ *   workspace: at least ssd_chunk_scan_workspace_bytes(...) bytes, 256-byte
+ *   aligned (NULL allowed when that is 0).
+ */
+int ssd_chunk_scan_fwd(const void* x, int64_t x_tok_stride, const void* Bm,
+                       int64_t b_tok_stride, const void* Cm, int64_t c_tok_stride,
+                       ssd_dtype_t xbc_dtype, const float* conv_w, const float* conv_b,
+                       int conv_width, const void* conv_state_in, void* conv_state_out,
+                       const void* dt, int64_t dt_tok_stride, const void* z,
+                       int64_t z_tok_stride, ssd_dtype_t act_dtype, const float* A,
+                       const float* D, const float* dt_bias, int dt_softplus,
+                       const float* initial_state, float* final_state, void* y,
+                       int64_t y_tok_stride, ssd_dtype_t y_dtype, int batch, int seqlen,
+                       int nheads, int headdim, int ngroups, int dstate, int chunk,
+                       ssd_math_t math, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/*
+ * One-token decode step for a batch of sequences: the conv step on the ring of
+ * the last K-1 raw inputs, then h <- exp(delta A) h + delta x B^T and
+ * y = h C + D x, gated.  The state and the ring are updated in place.
+ *
+ *   state      [B, H, P, N] fp32, in/out
+ *   xbc        [B, Cdim] xbc_dtype: the new token's raw x|B|C when conv_w is
+ *              non-NULL, its post-conv values when conv_w is NULL
+ *   conv_state [B, K-1, Cdim] xbc_dtype, in/out (required iff conv_w != NULL)
+ *   conv_w [Cdim, K] fp32 or NULL, conv_b [Cdim] fp32 or NULL, conv_width K in [1,4]
+ *   dt [B, H] act_dtype;  z [B, H*P] act_dtype or NULL
+ *   A, D, dt_bias, dt_softplus as in ssd_chunk_scan_fwd
+ *   y [B, H*P] y_dtype; must not overlap any input
+ *   Supported: P = 64, N = 128, H % G == 0.
+ */
+int ssd_state_update(float* state, const void* xbc, ssd_dtype_t xbc_dtype,
+                     void* conv_state, const float* conv_w, const float* conv_b,
+                     int conv_width, const void* dt, const void* z, ssd_dtype_t act_dtype,
+                     const float* A, const float* D, const float* dt_bias, int dt_softplus,
+                     void* y, ssd_dtype_t y_dtype, int batch, int nheads, int headdim,
+                     int ngroups, int dstate, hipStream_t stream);
+
+/* Bytes of decode cache per sequence and layer: the fp32 SSM state
+ * (4*H*P*N) plus the conv ring ((K-1) * Cdim elements of conv_dtype).
+ * This is the fixed-size Mamba cache of "Hybrid Architectures ..." summary,
+ * Appendix C, with an fp32 state and K-1 stored conv rows.  0 on bad input. */
+size_t ssd_decode_cache_bytes(int nheads, int headdim, int ngroups, int dstate, int width,
+                              ssd_dtype_t conv_dtype);
+
+/* Static text for a status code. */
+const char* ssd_status_string(int status);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char* ssd_last_error(void);
+
+/* Library version string. */
+const char* ssd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H_ */

@@ -1,0 +1,190 @@
+// Depthwise causal conv1d + SiLU over [B, L, Cdim] (the conv in front of the
+// Mamba-2 scan: kernel 4, SiLU; "Nemotron-H style Hybrid Mamba-Transformer 3B
+// feasibility study", table 1.4).
+//
+// HBM-bound: each input element is read once and each output written once.
+// A thread owns VEC adjacent channels (16-byte loads: 8 bf16 or 4 fp32) and
+// walks TOK consecutive tokens, keeping the last three inputs in registers,
+// so neighbouring threads read neighbouring 16-byte pieces of one token row
+// (fully coalesced) and the 3-token halo is re-read only once per TOK tokens.
+#include "ssd_common.h"
+
+namespace ssd {
+namespace {
+
+constexpr int TOK = 32;       // tokens per thread
+constexpr int THREADS = 256;
+
+template <typename T, int VEC> struct Vec;
+template <> struct Vec<bf16, 8> {
+  static __device__ __forceinline__ void load(const bf16* p, float* v) {
+    uint4 r = *reinterpret_cast<const uint4*>(p);
+    uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+template <> struct Vec<float, 4> {
+  static __device__ __forceinline__ void load(const float* p, float* v) {
+    float4 r = *reinterpret_cast<const float4*>(p);
+    v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
+  }
+};
+template <typename T> struct Vec<T, 1> {
+  static __device__ __forceinline__ void load(const T* p, float* v) { v[0] = to_f32(*p); }
+};
+
+template <typename T, int VEC>
+__device__ __forceinline__ void store_vec(T* p, const float* v) {
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) p[i] = from_f32<T>(v[i]);
+}
+template <>
+__device__ __forceinline__ void store_vec<float, 8>(float* p, const float* v) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+template <>
+__device__ __forceinline__ void store_vec<float, 4>(float* p, const float* v) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16 a = (bf16)lo, b = (bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+template <>
+__device__ __forceinline__ void store_vec<bf16, 8>(bf16* p, const float* v) {
+  *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                            pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+}
+
+// raw input of channels [c, c+VEC) at position tau of sequence b (tau may be
+// negative: then the history row (K-1)+tau, or zero)
+template <typename Tin, int VEC>
+__device__ __forceinline__ void load_raw(const Tin* x, int64_t x_stride, const Tin* hist,
+                                         int b, int L, int C, int K, int tau, int c,
+                                         float* v) {
+  if (tau >= 0) {
+    Vec<Tin, VEC>::load(x + ((int64_t)b * L + tau) * x_stride + c, v);
+  } else if (hist != nullptr && tau >= -(K - 1)) {
+    Vec<Tin, VEC>::load(hist + ((int64_t)b * (K - 1) + (K - 1) + tau) * C + c, v);
+  } else {
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) v[i] = 0.f;
+  }
+}
+
+template <typename Tin, typename Tout, int VEC>
+__global__ __launch_bounds__(THREADS) void causal_conv1d_kernel(
+    const Tin* __restrict__ x, int64_t x_stride, const float* __restrict__ w,
+    const float* __restrict__ bias, const Tin* __restrict__ hist_in,
+    Tin* __restrict__ hist_out, Tout* __restrict__ out, int64_t out_stride, int L, int C,
+    int K, int apply_silu) {
+  const int nv = C / VEC;
+  const int cv = blockIdx.x * THREADS + threadIdx.x;
+  if (cv >= nv) return;
+  const int c = cv * VEC;
+  const int b = blockIdx.z;
+  const int t0 = blockIdx.y * TOK;
+
+  // taps right-aligned to the current token: w4[3] meets x[t], w4[3-j] meets x[t-j]
+  float w4[4][VEC], bv[VEC];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) {
+    bv[i] = bias ? bias[c + i] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = j - (4 - K);
+      w4[j][i] = k >= 0 ? w[(int64_t)(c + i) * K + k] : 0.f;
+    }
+  }
+
+  if (t0 < L) {
+    float win[3][VEC];  // x[t-3], x[t-2], x[t-1]
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      load_raw<Tin, VEC>(x, x_stride, hist_in, b, L, C, K, t0 - 3 + j, c, win[j]);
+    const int t1 = min(L, t0 + TOK);
+    for (int t = t0; t < t1; ++t) {
+      float cur[VEC], o[VEC];
+      Vec<Tin, VEC>::load(x + ((int64_t)b * L + t) * x_stride + c, cur);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        float u = bv[i] + w4[0][i] * win[0][i] + w4[1][i] * win[1][i] +
+                  w4[2][i] * win[2][i] + w4[3][i] * cur[i];
+        o[i] = apply_silu ? silu_f32(u) : u;
+        win[0][i] = win[1][i];
+        win[1][i] = win[2][i];
+        win[2][i] = cur[i];
+      }
+      store_vec<Tout, VEC>(out + ((int64_t)b * L + t) * out_stride + c, o);
+    }
+  }
+
+  // the last token tile hands the last K-1 raw inputs on
+  if (hist_out != nullptr && blockIdx.y == gridDim.y - 1) {
+    for (int j = 0; j < K - 1; ++j) {
+      float v[VEC];
+      load_raw<Tin, VEC>(x, x_stride, hist_in, b, L, C, K, L - (K - 1) + j, c, v);
+      store_vec<Tin, VEC>(hist_out + ((int64_t)b * (K - 1) + j) * C + c, v);
+    }
+  }
+}
+
+template <typename Tin, typename Tout, int VEC>
+hipError_t launch_typed(const void* x, int64_t x_stride, const float* w, const float* bias,
+                        const void* hist_in, void* hist_out, void* out, int64_t out_stride,
+                        int B, int L, int C, int K, int apply_silu, hipStream_t stream) {
+  const int nv = C / VEC;
+  dim3 grid((nv + THREADS - 1) / THREADS, L > 0 ? (L + TOK - 1) / TOK : 1, B);
+  hipLaunchKernelGGL((causal_conv1d_kernel<Tin, Tout, VEC>), grid, dim3(THREADS), 0, stream,
+                     static_cast<const Tin*>(x), x_stride, w, bias,
+                     static_cast<const Tin*>(hist_in), static_cast<Tin*>(hist_out),
+                     static_cast<Tout*>(out), out_stride, L, C, K, apply_silu);
+  return hipGetLastError();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+template <typename Tin, typename Tout>
+hipError_t dispatch_vec(const void* x, int64_t x_stride, const float* w, const float* bias,
+                        const void* hist_in, void* hist_out, void* out, int64_t out_stride,
+                        int B, int L, int C, int K, int apply_silu, hipStream_t stream) {
+  constexpr int V = sizeof(Tin) == 2 ? 8 : 4;
+  const bool vec_ok = C % V == 0 && x_stride % V == 0 && out_stride % V == 0 && aligned16(x) &&
+                      (hist_in == nullptr || aligned16(hist_in)) &&
+                      (hist_out == nullptr || aligned16(hist_out)) &&
+                      (sizeof(Tout) == 2 ? aligned16(out) && out_stride % 8 == 0
+                                         : aligned16(out));
+  if (vec_ok)
+    return launch_typed<Tin, Tout, V>(x, x_stride, w, bias, hist_in, hist_out, out, out_stride,
+                                      B, L, C, K, apply_silu, stream);
+  return launch_typed<Tin, Tout, 1>(x, x_stride, w, bias, hist_in, hist_out, out, out_stride,
+                                    B, L, C, K, apply_silu, stream);
+}
+
+}  // namespace
+
+hipError_t launch_causal_conv1d(const void* x, int64_t x_stride, ssd_dtype_t x_dtype,
+                                const float* w, const float* bias, const void* hist_in,
+                                void* hist_out, void* out, int64_t out_stride,
+                                ssd_dtype_t out_dtype, int B, int L, int C, int K,
+                                int apply_silu, hipStream_t stream) {
+  if (x_dtype == SSD_BF16 && out_dtype == SSD_F32)
+    return dispatch_vec<bf16, float>(x, x_stride, w, bias, hist_in, hist_out, out, out_stride,
+                                     B, L, C, K, apply_silu, stream);
+  if (x_dtype == SSD_BF16 && out_dtype == SSD_BF16)
+    return dispatch_vec<bf16, bf16>(x, x_stride, w, bias, hist_in, hist_out, out, out_stride,
+                                    B, L, C, K, apply_silu, stream);
+  if (x_dtype == SSD_F32 && out_dtype == SSD_F32)
+    return dispatch_vec<float, float>(x, x_stride, w, bias, hist_in, hist_out, out, out_stride,
+                                      B, L, C, K, apply_silu, stream);
+  return dispatch_vec<float, bf16>(x, x_stride, w, bias, hist_in, hist_out, out, out_stride, B,
+                                   L, C, K, apply_silu, stream);
+}
+
+}  // namespace ssd

@@ -1,0 +1,588 @@
+// Chunked selective scan on the gfx950 matrix cores (SSD_MATH_BF16).
+//
+// The recurrence h_t = exp(delta_t A) h_{t-1} + delta_t x_t B_t^T,
+// y_t = C_t h_t + D x_t ("Hybrid Architectures for Language Models" summary,
+// section 2 Background) is evaluated in its chunked matrix form (the same
+// section: SSD recasts the state-space computation as matrix multiplies).
+// For a chunk of Q = 128 tokens with cumulative log decay Lam_t:
+//   Y      = (C B^T o exp(Lam_t - Lam_s) delta_s [s <= t]) X + diag(exp Lam) C H^T
+//   H_next = exp(Lam_last) H + (X o w)^T B,  w_s = exp(Lam_last - Lam_s) delta_s
+//   out    = (Y + D x) * silu(z)
+// All products are 32x32x16 bf16 MFMAs with fp32 accumulation.  The chunk
+// state product, whose result is carried across the whole sequence, splits
+// both operands into bf16 hi + lo parts and sums hi*hi + hi*lo + lo*hi, so
+// the carried state keeps ~16 mantissa bits instead of 8.
+//
+// One workgroup ("walker", 4 waves) owns one (sequence, head) -- or one
+// segment of it, see below -- and walks its chunks in order, carrying the
+// fp32 state H [64 x 128] in MFMA accumulator registers, so no state goes to
+// HBM between chunks.  Wave w owns output rows [32w, 32w+32) of the chunk and
+// the state tile rows p in [32(w/2), +32), columns n in [64(w%2), +64).
+//
+// LDS per walker (~151 KiB of gfx950's 160 KiB): B and x of the chunk in
+// fp32 (the bf16 operands and their hi/lo parts are formed on the fly), C and
+// the bf16 copy of H for the read-out, and the per-token decays.
+//
+// The decayed C B^T tile never touches LDS: it is produced as the transpose
+// (B C^T, rows s, columns t) so that each lane's accumulator column is one
+// output row t; after masking and decay the 16 values a lane holds are
+// exactly its A-operand for two K=16 steps of M X, with the K index permuted
+// the same way on the X side.
+//
+// Low (batch x heads) counts are split along the sequence: pass 1 runs the
+// state-only walker on segments 0..S-2 from a zero state, a small combine
+// kernel chains the segment states (H_in[k] = exp(sum of log decay of
+// segment k-1) H_in[k-1] + H_loc[k-1]), and pass 2 walks every segment from
+// its own incoming state.
+//
+// Walker order is XCD-aware: workgroups are dealt to the 8 XCDs round-robin,
+// so consecutive walker indices are remapped to put the heads that read the
+// same group's B and C (same sequence, group and segment) on one XCD, where
+// they share its L2.
+#include "ssd_common.h"
+
+namespace ssd {
+namespace {
+
+constexpr int Q = 128;
+constexpr int P = 64;
+constexpr int N = 128;
+constexpr int THREADS = 256;
+constexpr int NXCD = 8;
+constexpr int LDB = N + 8;     // bf16 row stride of sC, sH (272 B: 16-B row reads conflict-free)
+constexpr int LDB32 = N + 4;   // fp32 row stride of sB32 (528 B)
+constexpr int LDX32 = Q + 4;   // fp32 row stride of sX32 [p][t] (528 B)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 lds8(const bf16* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(float4 a, float4 b) {
+  bf16x8 r;
+  r[0] = (bf16)a.x; r[1] = (bf16)a.y; r[2] = (bf16)a.z; r[3] = (bf16)a.w;
+  r[4] = (bf16)b.x; r[5] = (bf16)b.y; r[6] = (bf16)b.z; r[7] = (bf16)b.w;
+  return r;
+}
+
+// v = hi + lo with hi = bf16(v), lo = bf16(v - hi)
+__device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const bf16 h = (bf16)v[e];
+    hi[e] = h;
+    lo[e] = (bf16)(v[e] - (float)h);
+  }
+}
+
+// 8 consecutive raw elements of a token row -> fp32 (16-B aligned source)
+template <typename T> struct Load8;
+template <> struct Load8<bf16> {
+  static __device__ __forceinline__ void get(const bf16* p, float* v) {
+    const uint4 r = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+template <> struct Load8<float> {
+  static __device__ __forceinline__ void get(const float* p, float* v) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
+// 8 values -> LDS row, as fp32 or bf16
+__device__ __forceinline__ void put8(float* dst, const float* v) {
+  reinterpret_cast<float4*>(dst)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  reinterpret_cast<float4*>(dst)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+__device__ __forceinline__ void put8(bf16* dst, const float* v) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (bf16)v[e];
+  *reinterpret_cast<bf16x8*>(dst) = r;
+}
+
+// Stage rows [0, Q) x columns [0, 128) of a token-major post-conv tensor into
+// an LDS tile (row stride LD), zero rows >= nvalid.  16 threads cover a row.
+template <typename Tx, typename Td, int LD>
+__device__ __forceinline__ void stage_rows(Td* dst, const Tx* src, int64_t stride, int64_t row0,
+                                           int nvalid) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < (Q * N / 8) / THREADS; ++k) {
+    const int i = tid + THREADS * k;
+    const int r = i >> 4, cv = i & 15;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (r < nvalid) Load8<Tx>::get(src + (row0 + r) * stride + 8 * cv, v);
+    put8(dst + r * LD + 8 * cv, v);
+  }
+}
+
+// Fused conv staging of B or C (128 channels starting at conv channel c0,
+// column jcol0 of the raw tensor): each thread walks 8 consecutive tokens of 8
+// channels with a sliding window of the last 3 raw inputs.
+template <typename Tx, typename Td, int LD>
+__device__ __forceinline__ void stage_rows_conv(const ScanArgs& a, Td* dst, const Tx* src,
+                                                int64_t stride, int b, int t0, int nvalid,
+                                                int jcol0, int c0, int cdim) {
+  const int tid = threadIdx.x;
+  const int cv = tid & 15, rg = tid >> 4;  // 16 channel vectors x 16 row groups of 8
+  const int K = a.conv_k;
+  const int L = a.seqlen;
+  float w4[4][8], bv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int c = c0 + 8 * cv + e;
+    bv[e] = a.conv_b ? a.conv_b[c] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = j - (4 - K);
+      w4[j][e] = k >= 0 ? a.conv_w[(int64_t)c * K + k] : 0.f;
+    }
+  }
+  // raw input at position tau: the sequence itself, else (tau < 0) the history
+  auto raw = [&](int tau, float* v) {
+    if (tau >= 0 && tau < L) {
+      Load8<Tx>::get(src + ((int64_t)b * L + tau) * stride + jcol0 + 8 * cv, v);
+    } else if (tau < 0 && tau >= -(K - 1) && a.conv_state_in != nullptr) {
+      Load8<Tx>::get(static_cast<const Tx*>(a.conv_state_in) +
+                         ((int64_t)b * (K - 1) + (K - 1) + tau) * cdim + c0 + 8 * cv,
+                     v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    }
+  };
+  float win[3][8];
+  const int r0 = rg * 8;
+  raw(t0 + r0 - 3, win[0]);
+  raw(t0 + r0 - 2, win[1]);
+  raw(t0 + r0 - 1, win[2]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = r0 + i;
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (r < nvalid) {
+      float cur[8];
+      raw(t0 + r, cur);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float u = bv[e] + w4[0][e] * win[0][e] + w4[1][e] * win[1][e] +
+                        w4[2][e] * win[2][e] + w4[3][e] * cur[e];
+        o[e] = silu_f32(u);
+        win[0][e] = win[1][e];
+        win[1][e] = win[2][e];
+        win[2][e] = cur[e];
+      }
+    }
+    put8(dst + r * LD + 8 * cv, o);
+  }
+}
+
+// Post-conv value of one x element for the fused conv.
+template <typename Tx>
+__device__ __forceinline__ float conv_point(const ScanArgs& a, const Tx* base, int64_t stride,
+                                            int b, int t, int c, int cdim) {
+  const int K = a.conv_k;
+  float u = a.conv_b ? a.conv_b[c] : 0.f;
+  for (int k = 0; k < K; ++k) {
+    const int tau = t - (K - 1) + k;  // tau <= t < seqlen
+    float v = 0.f;
+    if (tau >= 0)
+      v = to_f32(base[((int64_t)b * a.seqlen + tau) * stride + c]);
+    else if (a.conv_state_in != nullptr)
+      v = to_f32(static_cast<const Tx*>(
+          a.conv_state_in)[((int64_t)b * (K - 1) + (K - 1) + tau) * cdim + c]);
+    u += a.conv_w[(int64_t)c * K + k] * v;
+  }
+  return silu_f32(u);
+}
+
+template <typename T>
+__device__ __forceinline__ float ld1(const void* p, int64_t i) {
+  return to_f32(static_cast<const T*>(p)[i]);
+}
+
+// In-place inclusive prefix sum of s[0..Q) by waves 0 and 1 (fixed order).
+__device__ __forceinline__ void scan_lam(float* s, float* red) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  float v = 0.f;
+  if (tid < Q) {
+    v = s[tid];
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const float o = __shfl_up(v, d, 64);
+      if (lane >= d) v += o;
+    }
+    if (lane == 63) red[w] = v;
+  }
+  __syncthreads();
+  if (tid >= 64 && tid < Q) s[tid] = v + red[0];
+  if (tid < 64) s[tid] = v;
+  __syncthreads();
+}
+
+// Walker index of this workgroup: (sequence b, head h, segment seg), with
+// the heads of one (b, group, segment) contiguous and dealt to one XCD.
+struct Walker {
+  int b, h, seg;
+};
+__device__ __forceinline__ Walker walker_of(int lin, int total, int H, int G, int nsegs) {
+  // item order: ((b * nsegs + seg) * G + g) * hpg + hh; lin -> item puts
+  // item ranges of length total/8 on one XCD (lin % 8)
+  const int per = total / NXCD;
+  int item = lin;
+  if (lin < per * NXCD) item = (lin % NXCD) * per + lin / NXCD;
+  const int hpg = H / G;
+  const int hh = item % hpg;
+  int rest = item / hpg;
+  const int g = rest % G;
+  rest /= G;
+  const int seg = rest % nsegs;
+  const int b = rest / nsegs;
+  return Walker{b, g * hpg + hh, seg};
+}
+
+template <typename Tx, typename Ta, typename Ty, bool CONV, bool STATE_ONLY>
+__global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
+  __shared__ __attribute__((aligned(16))) float sB32[Q * LDB32];
+  __shared__ __attribute__((aligned(16))) float sX32[P * LDX32];
+  __shared__ __attribute__((aligned(16))) bf16 sC[STATE_ONLY ? 8 : Q * LDB];
+  __shared__ __attribute__((aligned(16))) bf16 sH[STATE_ONLY ? 8 : P * LDB];
+  __shared__ __attribute__((aligned(16))) float sLam[Q];
+  __shared__ __attribute__((aligned(16))) float sDel[Q];
+  __shared__ __attribute__((aligned(16))) float sW[Q];
+  __shared__ float sRed[4];
+
+  const int H = a.nheads, G = a.ngroups, L = a.seqlen;
+  // pass 1 (state-only) walks segments 0..nseg-2, pass 2 all segments
+  const int nsegs = STATE_ONLY ? a.nseg - 1 : a.nseg;
+  const Walker wk = walker_of(blockIdx.x, gridDim.x, H, G, nsegs);
+  const int b = wk.b, h = wk.h, seg = wk.seg;
+  const int bh = b * H + h;
+  const int hpg = H / G, g = h / hpg;
+  const int HP = H * P, GN = G * N, cdim = HP + 2 * GN;
+  const int nc = (L + Q - 1) / Q;
+  const int cbeg = seg * a.seg_chunks;
+  const int cend = min(nc, cbeg + a.seg_chunks);
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int pt = w >> 1, nt0 = 2 * (w & 1);
+  const float Ah = a.A[h];
+  const float Dh = a.D ? a.D[h] : 0.f;
+
+  const Tx* xg = static_cast<const Tx*>(a.x);
+  const Tx* Bg = static_cast<const Tx*>(a.Bm);
+  const Tx* Cg = static_cast<const Tx*>(a.Cm);
+
+  // ---- incoming state: accumulator element r of tile j is
+  //      (p = 32 pt + 8 (r/4) + 4 hf + r%4, n = 32 (nt0 + j) + l32)
+  const float* h_in = nullptr;
+  if (!STATE_ONLY) {
+    if (a.nseg > 1)
+      h_in = a.seg_state + ((int64_t)bh * a.nseg + seg) * P * N;
+    else
+      h_in = a.initial_state ? a.initial_state + (int64_t)bh * P * N : nullptr;
+  }
+  f32x16 hacc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int p = 32 * pt + 8 * (r >> 2) + 4 * hf + (r & 3);
+      const int n = 32 * (nt0 + j) + l32;
+      hacc[j][r] = h_in ? h_in[p * N + n] : 0.f;
+    }
+  if (!STATE_ONLY) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int p = 32 * pt + 8 * (r >> 2) + 4 * hf + (r & 3);
+        sH[p * LDB + 32 * (nt0 + j) + l32] = (bf16)hacc[j][r];
+      }
+  }
+  float log_decay = 0.f;  // sum of delta*A over the segment (state-only pass)
+
+  for (int c = cbeg; c < cend; ++c) {
+    const int t0 = c * Q;
+    const int Lc = min(Q, L - t0);
+    const int64_t row0 = (int64_t)b * L + t0;
+    __syncthreads();  // the previous chunk is done with every LDS buffer
+
+    if (tid < Q) {
+      const float d = tid < Lc ? make_delta(ld1<Ta>(a.dt, (row0 + tid) * a.dt_stride + h),
+                                            a.dt_bias, h, a.dt_softplus)
+                               : 0.f;
+      sDel[tid] = d;
+      sLam[tid] = d * Ah;
+    }
+    if (CONV) {
+      stage_rows_conv<Tx, float, LDB32>(a, sB32, Bg, a.b_stride, b, t0, Lc, g * N, HP + g * N,
+                                         cdim);
+      if (!STATE_ONLY)
+        stage_rows_conv<Tx, bf16, LDB>(a, sC, Cg, a.c_stride, b, t0, Lc, g * N,
+                                       HP + GN + g * N, cdim);
+    } else {
+      stage_rows<Tx, float, LDB32>(sB32, Bg + g * N, a.b_stride, row0, Lc);
+      if (!STATE_ONLY) stage_rows<Tx, bf16, LDB>(sC, Cg + g * N, a.c_stride, row0, Lc);
+    }
+    // x rows of this wave, fp32, transposed into sX32[p][t]; z into registers
+    // in the accumulator layout: element (j, r) is
+    // (t = 32 w + 8 (r/4) + 4 hf + r%4, p = 32 j + l32)
+    float zr[2][16];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int p = 32 * j + l32;
+        const int tb = 32 * w + 8 * q + 4 * hf;
+        float xv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = tb + e;
+          float v = 0.f, zv = 0.f;
+          if (t < Lc) {
+            if (CONV)
+              v = conv_point<Tx>(a, xg, a.x_stride, b, t0 + t, h * P + p, cdim);
+            else
+              v = to_f32(xg[(row0 + t) * a.x_stride + h * P + p]);
+            if (!STATE_ONLY && a.z != nullptr)
+              zv = ld1<Ta>(a.z, (row0 + t) * a.z_stride + h * P + p);
+          }
+          xv[e] = v;
+          zr[j][4 * q + e] = zv;
+        }
+        *reinterpret_cast<float4*>(sX32 + p * LDX32 + tb) = make_float4(xv[0], xv[1], xv[2], xv[3]);
+      }
+    __syncthreads();
+    scan_lam(sLam, sRed);
+    const float lam_last = sLam[Q - 1];
+    if (STATE_ONLY) log_decay += lam_last;
+    if (tid < Q) sW[tid] = __expf(lam_last - sLam[tid]) * sDel[tid];
+    __syncthreads();
+
+    if (!STATE_ONLY) {
+      // ---- inter-chunk read-out: Y = diag(exp Lam) C H^T
+      f32x16 yacc[2] = {};
+      const bf16* crow = sC + (32 * w + l32) * LDB + 8 * hf;
+#pragma unroll
+      for (int kk = 0; kk < N / 16; ++kk) {
+        const bf16x8 af = lds8(crow + 16 * kk);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          yacc[j] = mfma(af, lds8(sH + (32 * j + l32) * LDB + 16 * kk + 8 * hf), yacc[j]);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = __expf(sLam[32 * w + 8 * (r >> 2) + 4 * hf + (r & 3)]);
+        yacc[0][r] *= e;
+        yacc[1][r] *= e;
+      }
+
+      // ---- intra-chunk: Y += (C B^T o decay mask) X, tile by tile below the diagonal
+      const int tcol = 32 * w + l32;
+      const float lam_t = sLam[tcol];
+      for (int u = 0; u <= w; ++u) {
+        f32x16 cb = {};
+        const float* brow = sB32 + (32 * u + l32) * LDB32 + 8 * hf;
+#pragma unroll
+        for (int kk = 0; kk < N / 16; ++kk) {
+          const float4* bp = reinterpret_cast<const float4*>(brow + 16 * kk);
+          cb = mfma(to_bf16x8(bp[0], bp[1]), lds8(crow + 16 * kk), cb);
+        }
+        // cb[r] = (B C^T)[s][t], s = 32u + 8(r/4) + 4hf + r%4, t = tcol
+        bf16x8 mf[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int s = 32 * u + 8 * (r >> 2) + 4 * hf + (r & 3);
+          const float m = s <= tcol ? cb[r] * __expf(lam_t - sLam[s]) * sDel[s] : 0.f;
+          mf[r >> 3][r & 7] = (bf16)m;
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int sb = 32 * u + 16 * k2 + 4 * hf;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const float* xp = sX32 + (32 * j + l32) * LDX32 + sb;
+            const bf16x8 xf = to_bf16x8(*reinterpret_cast<const float4*>(xp),
+                                        *reinterpret_cast<const float4*>(xp + 8));
+            yacc[j] = mfma(mf[k2], xf, yacc[j]);
+          }
+        }
+      }
+
+      // ---- epilogue: skip, gate, store
+      Ty* yg = static_cast<Ty*>(a.y);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int tb = 32 * w + 8 * q + 4 * hf;
+          const float4 xq = *reinterpret_cast<const float4*>(sX32 + (32 * j + l32) * LDX32 + tb);
+          const float xs[4] = {xq.x, xq.y, xq.z, xq.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = tb + e, r = 4 * q + e;
+            if (t < Lc) {
+              float yv = yacc[j][r] + Dh * xs[e];
+              if (a.z != nullptr) yv *= silu_f32(zr[j][r]);
+              yg[(row0 + t) * a.y_stride + h * P + 32 * j + l32] = from_f32<Ty>(yv);
+            }
+          }
+        }
+      __syncthreads();  // every wave is done reading sH
+    }
+
+    // ---- state: H <- exp(Lam_last) H + (X o w)^T B, operands split hi + lo
+    const float gamma = __expf(lam_last);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) hacc[j] *= gamma;
+    const float* xrow = sX32 + (32 * pt + l32) * LDX32;
+#pragma unroll 2
+    for (int kk = 0; kk < Q / 16; ++kk) {
+      const int s0 = 16 * kk + 8 * hf;
+      float xw[8];
+      {
+        const float4 x0 = *reinterpret_cast<const float4*>(xrow + s0);
+        const float4 x1 = *reinterpret_cast<const float4*>(xrow + s0 + 4);
+        const float4 w0 = *reinterpret_cast<const float4*>(sW + s0);
+        const float4 w1 = *reinterpret_cast<const float4*>(sW + s0 + 4);
+        xw[0] = x0.x * w0.x; xw[1] = x0.y * w0.y; xw[2] = x0.z * w0.z; xw[3] = x0.w * w0.w;
+        xw[4] = x1.x * w1.x; xw[5] = x1.y * w1.y; xw[6] = x1.z * w1.z; xw[7] = x1.w * w1.w;
+      }
+      bf16x8 ah, al;
+      split8(xw, ah, al);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float* bc = sB32 + s0 * LDB32 + 32 * (nt0 + j) + l32;
+        float bv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bv[e] = bc[e * LDB32];
+        bf16x8 bhi, blo;
+        split8(bv, bhi, blo);
+        hacc[j] = mfma(ah, bhi, hacc[j]);
+        hacc[j] = mfma(ah, blo, hacc[j]);
+        hacc[j] = mfma(al, bhi, hacc[j]);
+      }
+    }
+    if (!STATE_ONLY) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int p = 32 * pt + 8 * (r >> 2) + 4 * hf + (r & 3);
+          sH[p * LDB + 32 * (nt0 + j) + l32] = (bf16)hacc[j][r];
+        }
+    }
+  }
+
+  // ---- outgoing state
+  float* h_out = nullptr;
+  if (STATE_ONLY)
+    h_out = a.seg_state + ((int64_t)bh * a.nseg + seg + 1) * P * N;
+  else if (seg == a.nseg - 1)
+    h_out = a.final_state ? a.final_state + (int64_t)bh * P * N : nullptr;
+  if (h_out != nullptr) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int p = 32 * pt + 8 * (r >> 2) + 4 * hf + (r & 3);
+        h_out[p * N + 32 * (nt0 + j) + l32] = hacc[j][r];
+      }
+  }
+  if (STATE_ONLY && tid == 0) a.seg_logdecay[(int64_t)bh * a.nseg + seg] = log_decay;
+
+  // ---- conv history hand-over (last segment)
+  if (CONV && !STATE_ONLY && seg == a.nseg - 1 && a.conv_state_out != nullptr) {
+    const int K = a.conv_k;
+    Tx* out = static_cast<Tx*>(a.conv_state_out);
+    const Tx* hin = static_cast<const Tx*>(a.conv_state_in);
+    auto raw = [&](const Tx* base, int64_t stride, int tau, int j, int c) -> Tx {
+      if (tau >= 0) return base[((int64_t)b * L + tau) * stride + j];  // tau < L here
+      if (hin != nullptr && tau >= -(K - 1))
+        return hin[((int64_t)b * (K - 1) + (K - 1) + tau) * cdim + c];
+      return from_f32<Tx>(0.f);
+    };
+    for (int i = tid; i < (K - 1) * P; i += THREADS) {
+      const int j = i / P, p = i % P, c = h * P + p;
+      out[((int64_t)b * (K - 1) + j) * cdim + c] = raw(xg, a.x_stride, L - (K - 1) + j, c, c);
+    }
+    if (h % hpg == 0)
+      for (int i = tid; i < (K - 1) * 2 * N; i += THREADS) {
+        const int j = i / (2 * N), e = i % (2 * N);
+        const bool isB = e < N;
+        const int n = isB ? e : e - N;
+        const int c = (isB ? HP : HP + GN) + g * N + n;
+        out[((int64_t)b * (K - 1) + j) * cdim + c] =
+            isB ? raw(Bg, a.b_stride, L - (K - 1) + j, g * N + n, c)
+                : raw(Cg, a.c_stride, L - (K - 1) + j, g * N + n, c);
+      }
+  }
+}
+
+// H_in[0] = h0; H_in[k] = exp(log_decay[k-1]) H_in[k-1] + H_loc[k-1], in place:
+// slot k holds H_loc[k-1] on entry and H_in[k] on exit.
+__global__ __launch_bounds__(THREADS) void combine_segments_kernel(ScanArgs a) {
+  const int bh = blockIdx.x;
+  float* slots = a.seg_state + (int64_t)bh * a.nseg * P * N;
+  const float* ld = a.seg_logdecay + (int64_t)bh * a.nseg;
+  for (int i = threadIdx.x; i < P * N; i += THREADS) {
+    float carry = a.initial_state ? a.initial_state[(int64_t)bh * P * N + i] : 0.f;
+    slots[i] = carry;
+    for (int k = 1; k < a.nseg; ++k) {
+      carry = __expf(ld[k - 1]) * carry + slots[(int64_t)k * P * N + i];
+      slots[(int64_t)k * P * N + i] = carry;
+    }
+  }
+}
+
+template <typename Tx, typename Ta, typename Ty, bool CONV>
+hipError_t launch_conv(const ScanArgs& a, hipStream_t stream) {
+  const int BH = a.batch * a.nheads;
+  if (a.nseg > 1) {
+    hipLaunchKernelGGL((scan_bf16_kernel<Tx, Ta, Ty, CONV, true>), dim3(BH * (a.nseg - 1)),
+                       dim3(THREADS), 0, stream, a);
+    hipLaunchKernelGGL(combine_segments_kernel, dim3(BH), dim3(THREADS), 0, stream, a);
+  }
+  hipLaunchKernelGGL((scan_bf16_kernel<Tx, Ta, Ty, CONV, false>), dim3(BH * a.nseg),
+                     dim3(THREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename Tx, typename Ta, typename Ty>
+hipError_t launch_typed(const ScanArgs& a, hipStream_t s) {
+  return a.conv_w ? launch_conv<Tx, Ta, Ty, true>(a, s) : launch_conv<Tx, Ta, Ty, false>(a, s);
+}
+
+template <typename Tx, typename Ta>
+hipError_t pick_y(const ScanArgs& a, ssd_dtype_t yd, hipStream_t s) {
+  return yd == SSD_F32 ? launch_typed<Tx, Ta, float>(a, s) : launch_typed<Tx, Ta, bf16>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_scan_bf16(const ScanArgs& a, ssd_dtype_t xd, ssd_dtype_t ad, ssd_dtype_t yd,
+                            hipStream_t s) {
+  if (xd == SSD_BF16 && ad == SSD_BF16) return pick_y<bf16, bf16>(a, yd, s);
+  if (xd == SSD_BF16) return pick_y<bf16, float>(a, yd, s);
+  if (ad == SSD_BF16) return pick_y<float, bf16>(a, yd, s);
+  return pick_y<float, float>(a, yd, s);
+}
+
+}  // namespace ssd

@@ -1,0 +1,85 @@
+// Shared device helpers and kernel-launch declarations for libssd.so.
+// gfx950 (CDNA4) only: wave64, bf16 MFMA, 160 KiB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ssd.h"
+
+namespace ssd {
+
+using bf16 = __bf16;
+
+// ------------------------------------------------------------------ numerics
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+// round to nearest even (gfx950 converts in hardware)
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
+
+// softplus(v) = log(1 + e^v) in the form that neither overflows nor cancels.
+__device__ __forceinline__ float softplus_f32(float v) {
+  return fmaxf(v, 0.f) + log1pf(__expf(-fabsf(v)));
+}
+
+__device__ __forceinline__ float silu_f32(float u) { return u / (1.f + __expf(-u)); }
+
+// delta = softplus(dt + bias) | dt + bias
+__device__ __forceinline__ float make_delta(float dt, const float* dt_bias, int h,
+                                            int softplus) {
+  float v = dt + (dt_bias ? dt_bias[h] : 0.f);
+  return softplus ? softplus_f32(v) : v;
+}
+
+// ------------------------------------------------------------------ arguments
+
+// Everything a scan kernel needs; passed by value as the kernel argument.
+struct ScanArgs {
+  const void* x;  int64_t x_stride;
+  const void* Bm; int64_t b_stride;
+  const void* Cm; int64_t c_stride;
+  const float* conv_w; const float* conv_b; int conv_k;   // conv_w == nullptr: post-conv
+  const void* conv_state_in; void* conv_state_out;
+  const void* dt; int64_t dt_stride;
+  const void* z;  int64_t z_stride;
+  const float* A; const float* D; const float* dt_bias; int dt_softplus;
+  const float* initial_state; float* final_state;
+  void* y; int64_t y_stride;
+  int batch, seqlen, nheads, ngroups, chunk;
+  // sequence split: each (b, h) is walked as `nseg` segments of `seg_chunks` chunks
+  int nseg, seg_chunks;
+  float* seg_state;      // [B, H, nseg, P, N] workspace (nseg > 1)
+  float* seg_logdecay;   // [B, H, nseg]       workspace (nseg > 1)
+};
+
+// ------------------------------------------------------------------ launchers
+// Each returns hipSuccess or the launch error; shapes are validated by the caller.
+
+hipError_t launch_causal_conv1d(const void* x, int64_t x_stride, ssd_dtype_t x_dtype,
+                                const float* w, const float* bias, const void* hist_in,
+                                void* hist_out, void* out, int64_t out_stride,
+                                ssd_dtype_t out_dtype, int batch, int seqlen, int cdim,
+                                int width, int apply_silu, hipStream_t stream);
+
+hipError_t launch_scan_f32(const ScanArgs& a, ssd_dtype_t xbc_dtype, ssd_dtype_t act_dtype,
+                           ssd_dtype_t y_dtype, hipStream_t stream);
+
+hipError_t launch_scan_bf16(const ScanArgs& a, ssd_dtype_t xbc_dtype, ssd_dtype_t act_dtype,
+                            ssd_dtype_t y_dtype, hipStream_t stream);
+
+hipError_t launch_state_update(float* state, const void* xbc, ssd_dtype_t xbc_dtype,
+                               void* ring, const float* conv_w, const float* conv_b, int K,
+                               const void* dt, const void* z, ssd_dtype_t act_dtype,
+                               const float* A, const float* D, const float* dt_bias,
+                               int softplus, void* y, ssd_dtype_t y_dtype, int batch,
+                               int nheads, int ngroups, hipStream_t stream);
+
+// Copies (or zero-fills when src is null) n floats / n elements: used for the
+// state hand-through of empty sequences.  A kernel, not hipMemsetAsync.
+hipError_t launch_copy_or_zero(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+}  // namespace ssd

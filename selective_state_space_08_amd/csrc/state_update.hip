@@ -1,0 +1,157 @@
+// One-token decode step of the Mamba-2 layer: conv step on the ring of the
+// last K-1 raw inputs, then h <- exp(delta A) h + delta x B^T, y = h C + D x,
+// gated by SiLU(z).  The state is of fixed size per sequence (the
+// O(1)-per-token decode of the "Nemotron-H paper explainer", Transformer-vs-
+// Mamba table; the fixed Mamba cache of "Hybrid Architectures ..." summary,
+// Appendix C).
+//
+// HBM-bound: the fp32 state (32 KiB per head) is read and written once per
+// step and is ~98% of the bytes.  One workgroup owns one (sequence, group):
+// it convolves the group's channels once (x of its H/G heads, B and C of the
+// group), so the ring rows it shifts are touched by no other workgroup, then
+// streams the heads' states with 16-byte coalesced accesses, prefetching the
+// next head's state while it updates the current one.
+#include "ssd_common.h"
+
+namespace ssd {
+namespace {
+
+constexpr int P = 64;
+constexpr int N = 128;
+constexpr int THREADS = 256;
+constexpr int ROWS_PER_PASS = THREADS / (N / 4);  // 8 state rows per pass
+constexpr int PASSES = P / ROWS_PER_PASS;         // 8 float4 per thread per head
+
+template <typename Tx, typename Ta, typename Ty>
+__global__ __launch_bounds__(THREADS) void state_update_kernel(
+    float* __restrict__ state, const Tx* __restrict__ xbc, Tx* __restrict__ ring,
+    const float* __restrict__ conv_w, const float* __restrict__ conv_b, int K,
+    const Ta* __restrict__ dt, const Ta* __restrict__ z, const float* __restrict__ A,
+    const float* __restrict__ D, const float* __restrict__ dt_bias, int softplus,
+    Ty* __restrict__ y, int H, int G) {
+  extern __shared__ float sxc[];  // post-conv: x of the group's heads | B | C
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int hpg = H / G;
+  const int HP = H * P, GN = G * N, C = HP + 2 * GN;
+  const int nx = hpg * P, nch = nx + 2 * N;
+  const int tid = threadIdx.x;
+
+  // conv step for the group's channels; each channel's ring column is owned
+  // by this workgroup alone
+  for (int i = tid; i < nch; i += THREADS) {
+    const int c = i < nx ? g * nx + i
+                         : (i < nx + N ? HP + g * N + (i - nx) : HP + GN + g * N + (i - nx - N));
+    const Tx raw = xbc[(int64_t)b * C + c];
+    float v = to_f32(raw);
+    if (conv_w != nullptr) {
+      Tx* r = ring + (int64_t)b * (K - 1) * C + c;  // r[k*C]: row k, oldest first
+      float u = conv_b ? conv_b[c] : 0.f;
+      for (int k = 0; k < K - 1; ++k) u += conv_w[(int64_t)c * K + k] * to_f32(r[(int64_t)k * C]);
+      u += conv_w[(int64_t)c * K + K - 1] * v;
+      for (int k = 0; k + 1 < K - 1; ++k) r[(int64_t)k * C] = r[(int64_t)(k + 1) * C];
+      if (K > 1) r[(int64_t)(K - 2) * C] = raw;
+      v = silu_f32(u);
+    }
+    sxc[i] = v;
+  }
+  __syncthreads();
+
+  // thread -> float4 column n4 = tid % 32 (fixed), rows p = tid / 32 + 8 j
+  const int col = tid & 31;
+  const int row0 = tid >> 5;
+  const float4 Bv = reinterpret_cast<const float4*>(sxc + nx)[col];
+  const float4 Cv = reinterpret_cast<const float4*>(sxc + nx + N)[col];
+
+  const int h0 = g * hpg;
+  float4* st = reinterpret_cast<float4*>(state + ((int64_t)b * H + h0) * P * N);
+  float4 cur[PASSES];
+#pragma unroll
+  for (int j = 0; j < PASSES; ++j) cur[j] = st[tid + THREADS * j];
+
+  for (int hh = 0; hh < hpg; ++hh) {
+    const int h = h0 + hh;
+    float4 nxt[PASSES];
+    if (hh + 1 < hpg) {
+      const float4* sn = st + (int64_t)(hh + 1) * (P * N / 4);
+#pragma unroll
+      for (int j = 0; j < PASSES; ++j) nxt[j] = sn[tid + THREADS * j];
+    }
+    const float delta = make_delta(to_f32(dt[(int64_t)b * H + h]), dt_bias, h, softplus);
+    const float a = __expf(delta * A[h]);
+    const float Dh = D ? D[h] : 0.f;
+    float4* sh = st + (int64_t)hh * (P * N / 4);
+#pragma unroll
+    for (int j = 0; j < PASSES; ++j) {
+      const int p = row0 + ROWS_PER_PASS * j;
+      const float xp = sxc[hh * P + p];
+      const float dx = delta * xp;
+      float4 s = cur[j];
+      s.x = a * s.x + dx * Bv.x;
+      s.y = a * s.y + dx * Bv.y;
+      s.z = a * s.z + dx * Bv.z;
+      s.w = a * s.w + dx * Bv.w;
+      sh[tid + THREADS * j] = s;
+      float acc = s.x * Cv.x + s.y * Cv.y + s.z * Cv.z + s.w * Cv.w;
+      // sum over the 32 lanes holding row p (fixed butterfly order: deterministic)
+#pragma unroll
+      for (int m = 16; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 32);
+      if (col == 0) {
+        float yv = acc + Dh * xp;
+        const int64_t o = (int64_t)b * HP + h * P + p;
+        if (z != nullptr) yv *= silu_f32(to_f32(z[o]));
+        y[o] = from_f32<Ty>(yv);
+      }
+    }
+    if (hh + 1 < hpg) {
+#pragma unroll
+      for (int j = 0; j < PASSES; ++j) cur[j] = nxt[j];
+    }
+  }
+}
+
+template <typename Tx, typename Ta, typename Ty>
+hipError_t launch_typed(float* state, const void* xbc, void* ring, const float* conv_w,
+                        const float* conv_b, int K, const void* dt, const void* z,
+                        const float* A, const float* D, const float* dt_bias, int softplus,
+                        void* y, int B, int H, int G, hipStream_t stream) {
+  const size_t lds = sizeof(float) * (size_t)((H / G) * P + 2 * N);
+  hipLaunchKernelGGL((state_update_kernel<Tx, Ta, Ty>), dim3(G, B), dim3(THREADS), lds, stream,
+                     state, static_cast<const Tx*>(xbc), static_cast<Tx*>(ring), conv_w, conv_b,
+                     K, static_cast<const Ta*>(dt), static_cast<const Ta*>(z), A, D, dt_bias,
+                     softplus, static_cast<Ty*>(y), H, G);
+  return hipGetLastError();
+}
+
+template <typename Tx, typename Ta>
+hipError_t pick_y(ssd_dtype_t yd, float* state, const void* xbc, void* ring, const float* w,
+                  const float* cb, int K, const void* dt, const void* z, const float* A,
+                  const float* D, const float* dtb, int sp, void* y, int B, int H, int G,
+                  hipStream_t s) {
+  if (yd == SSD_F32)
+    return launch_typed<Tx, Ta, float>(state, xbc, ring, w, cb, K, dt, z, A, D, dtb, sp, y, B, H,
+                                       G, s);
+  return launch_typed<Tx, Ta, bf16>(state, xbc, ring, w, cb, K, dt, z, A, D, dtb, sp, y, B, H, G,
+                                    s);
+}
+
+}  // namespace
+
+hipError_t launch_state_update(float* state, const void* xbc, ssd_dtype_t xd, void* ring,
+                               const float* conv_w, const float* conv_b, int K, const void* dt,
+                               const void* z, ssd_dtype_t ad, const float* A, const float* D,
+                               const float* dt_bias, int softplus, void* y, ssd_dtype_t yd,
+                               int B, int H, int G, hipStream_t s) {
+  if (xd == SSD_BF16 && ad == SSD_BF16)
+    return pick_y<bf16, bf16>(yd, state, xbc, ring, conv_w, conv_b, K, dt, z, A, D, dt_bias,
+                              softplus, y, B, H, G, s);
+  if (xd == SSD_BF16)
+    return pick_y<bf16, float>(yd, state, xbc, ring, conv_w, conv_b, K, dt, z, A, D, dt_bias,
+                               softplus, y, B, H, G, s);
+  if (ad == SSD_BF16)
+    return pick_y<float, bf16>(yd, state, xbc, ring, conv_w, conv_b, K, dt, z, A, D, dt_bias,
+                               softplus, y, B, H, G, s);
+  return pick_y<float, float>(yd, state, xbc, ring, conv_w, conv_b, K, dt, z, A, D, dt_bias,
+                              softplus, y, B, H, G, s);
+}
+
+}  // namespace ssd

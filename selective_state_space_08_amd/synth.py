@@ -116,6 +116,15 @@ def _fill_tokens(rng, wl: Workload, xbc, z=None, dt=None):
                 round_bf16_(a)
 
 
+def raw_history(wl: Workload, seed: int) -> np.ndarray:
+    """A conv history [B, K-1, Cdim] of raw x|B|C values drawn like the tokens
+    (its own generator, block -1 of the seed)."""
+    h = np.empty((wl.batch, wl.width - 1, wl.cdim), np.float32)
+    _fill_tokens(np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 2**31 - 1]))),
+                 wl, h)
+    return h
+
+
 @dataclass
 class PrefillInputs:
     wl: Workload
