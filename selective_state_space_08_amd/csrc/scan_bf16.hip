@@ -81,12 +81,13 @@ __device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
   }
 }
 
-// 8 consecutive raw elements of a token row -> fp32 (16-B aligned source)
-template <typename T> struct Load8;
-template <> struct Load8<bf16> {
-  static __device__ __forceinline__ void get(const bf16* p, float* v) {
-    const uint4 r = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+// 8 raw elements of one token row, kept packed between load and use
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16> {
+  uint4 u;
+  __device__ __forceinline__ void load(const bf16* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void get(float* v) const {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       v[2 * i] = __uint_as_float(w[i] << 16);
@@ -94,14 +95,22 @@ template <> struct Load8<bf16> {
     }
   }
 };
-template <> struct Load8<float> {
-  static __device__ __forceinline__ void get(const float* p, float* v) {
-    const float4 a = reinterpret_cast<const float4*>(p)[0];
-    const float4 b = reinterpret_cast<const float4*>(p)[1];
+template <> struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ void get(float* v) const {
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   }
 };
+
+template <typename T>
+__device__ __forceinline__ float ld1(const void* p, int64_t i) {
+  return to_f32(static_cast<const T*>(p)[i]);
+}
 
 // 8 values -> LDS row, as fp32 or bf16
 __device__ __forceinline__ void put8(float* dst, const float* v) {
@@ -115,106 +124,159 @@ __device__ __forceinline__ void put8(bf16* dst, const float* v) {
   *reinterpret_cast<bf16x8*>(dst) = r;
 }
 
-// Stage rows [0, Q) x columns [0, 128) of a token-major post-conv tensor into
-// an LDS tile (row stride LD), zero rows >= nvalid.  16 threads cover a row.
-template <typename Tx, typename Td, int LD>
-__device__ __forceinline__ void stage_rows(Td* dst, const Tx* src, int64_t stride, int64_t row0,
-                                           int nvalid) {
-  const int tid = threadIdx.x;
+// The rows of one 8-channel column piece a thread stages: positions
+// tstart + i, i < R + HALO (HALO = 3 rows of conv history in front when the
+// conv is fused).  Every load is unconditional: its address is chosen first
+// -- positions before the sequence read the conv history, positions past
+// its end re-read the last row -- and values outside the sequence and its
+// history are zeroed when read back, so all loads of a chunk are in flight
+// together.
+template <typename Tx, int NR>
+struct RowLoad {
+  Raw8<Tx> v[NR];
+  __device__ __forceinline__ void load(const ScanArgs& a, const Tx* src, int64_t stride, int col,
+                                       int c0, int cdim, int b, int tstart) {
+    const int L = a.seqlen, K = a.conv_k;
+    const Tx* hist = static_cast<const Tx*>(a.conv_state_in);
 #pragma unroll
-  for (int k = 0; k < (Q * N / 8) / THREADS; ++k) {
-    const int i = tid + THREADS * k;
-    const int r = i >> 4, cv = i & 15;
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (r < nvalid) Load8<Tx>::get(src + (row0 + r) * stride + 8 * cv, v);
-    put8(dst + r * LD + 8 * cv, v);
+    for (int i = 0; i < NR; ++i) {
+      const int tau = tstart + i;
+      const Tx* p;
+      if (tau < 0 && hist != nullptr && tau >= -(K - 1))
+        p = hist + ((int64_t)b * (K - 1) + (K - 1) + tau) * cdim + c0;
+      else
+        p = src + ((int64_t)b * L + min(max(tau, 0), L - 1)) * stride + col;
+      v[i].load(p);
+    }
   }
-}
+  __device__ __forceinline__ void get(const ScanArgs& a, int tstart, int i, float* out) const {
+    const int tau = tstart + i;
+    const bool ok = tau < a.seqlen &&
+                    (tau >= 0 || (a.conv_state_in != nullptr && tau >= -(a.conv_k - 1)));
+    v[i].get(out);
+    if (!ok) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = 0.f;
+    }
+  }
+};
 
-// Fused conv staging of B or C (128 channels starting at conv channel c0,
-// column jcol0 of the raw tensor): each thread walks 8 consecutive tokens of 8
-// channels with a sliding window of the last 3 raw inputs.
-template <typename Tx, typename Td, int LD>
-__device__ __forceinline__ void stage_rows_conv(const ScanArgs& a, Td* dst, const Tx* src,
-                                                int64_t stride, int b, int t0, int nvalid,
-                                                int jcol0, int c0, int cdim) {
-  const int tid = threadIdx.x;
-  const int cv = tid & 15, rg = tid >> 4;  // 16 channel vectors x 16 row groups of 8
+// Depthwise conv + SiLU of R consecutive rows of 8 channels from R + 3 raw
+// rows (the first 3 are the history in front); row i goes to dst + i * ld
+// (stride ld, or a transposed float4 column when TRANSPOSE), zero for rows
+// >= nvalid.
+template <typename Tx, int R, typename Td>
+__device__ __forceinline__ void conv_rows_to(const ScanArgs& a, const RowLoad<Tx, R + 3>& rl,
+                                             int tstart, int c0, int rfirst, int nvalid,
+                                             Td* dst, int ld) {
   const int K = a.conv_k;
-  const int L = a.seqlen;
   float w4[4][8], bv[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int c = c0 + 8 * cv + e;
-    bv[e] = a.conv_b ? a.conv_b[c] : 0.f;
+    bv[e] = a.conv_b ? a.conv_b[c0 + e] : 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int k = j - (4 - K);
-      w4[j][e] = k >= 0 ? a.conv_w[(int64_t)c * K + k] : 0.f;
+      w4[j][e] = k >= 0 ? a.conv_w[(int64_t)(c0 + e) * K + k] : 0.f;
     }
   }
-  // raw input at position tau: the sequence itself, else (tau < 0) the history
-  auto raw = [&](int tau, float* v) {
-    if (tau >= 0 && tau < L) {
-      Load8<Tx>::get(src + ((int64_t)b * L + tau) * stride + jcol0 + 8 * cv, v);
-    } else if (tau < 0 && tau >= -(K - 1) && a.conv_state_in != nullptr) {
-      Load8<Tx>::get(static_cast<const Tx*>(a.conv_state_in) +
-                         ((int64_t)b * (K - 1) + (K - 1) + tau) * cdim + c0 + 8 * cv,
-                     v);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = 0.f;
-    }
-  };
   float win[3][8];
-  const int r0 = rg * 8;
-  raw(t0 + r0 - 3, win[0]);
-  raw(t0 + r0 - 2, win[1]);
-  raw(t0 + r0 - 1, win[2]);
+  rl.get(a, tstart, 0, win[0]);
+  rl.get(a, tstart, 1, win[1]);
+  rl.get(a, tstart, 2, win[2]);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = r0 + i;
-    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (r < nvalid) {
-      float cur[8];
-      raw(t0 + r, cur);
+  for (int i = 0; i < R; ++i) {
+    float cur[8], o[8];
+    rl.get(a, tstart, i + 3, cur);
+    const bool ok = rfirst + i < nvalid;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float u = bv[e] + w4[0][e] * win[0][e] + w4[1][e] * win[1][e] +
-                        w4[2][e] * win[2][e] + w4[3][e] * cur[e];
-        o[e] = silu_f32(u);
-        win[0][e] = win[1][e];
-        win[1][e] = win[2][e];
-        win[2][e] = cur[e];
-      }
+    for (int e = 0; e < 8; ++e) {
+      const float u = bv[e] + w4[0][e] * win[0][e] + w4[1][e] * win[1][e] +
+                      w4[2][e] * win[2][e] + w4[3][e] * cur[e];
+      o[e] = ok ? silu_f32(u) : 0.f;
+      win[0][e] = win[1][e];
+      win[1][e] = win[2][e];
+      win[2][e] = cur[e];
     }
-    put8(dst + r * LD + 8 * cv, o);
+    put8(dst + i * ld, o);
   }
 }
 
-// Post-conv value of one x element for the fused conv.
-template <typename Tx>
-__device__ __forceinline__ float conv_point(const ScanArgs& a, const Tx* base, int64_t stride,
-                                            int b, int t, int c, int cdim) {
-  const int K = a.conv_k;
-  float u = a.conv_b ? a.conv_b[c] : 0.f;
-  for (int k = 0; k < K; ++k) {
-    const int tau = t - (K - 1) + k;  // tau <= t < seqlen
-    float v = 0.f;
-    if (tau >= 0)
-      v = to_f32(base[((int64_t)b * a.seqlen + tau) * stride + c]);
-    else if (a.conv_state_in != nullptr)
-      v = to_f32(static_cast<const Tx*>(
-          a.conv_state_in)[((int64_t)b * (K - 1) + (K - 1) + tau) * cdim + c]);
-    u += a.conv_w[(int64_t)c * K + k] * v;
+// Rows as they are (post-conv input), zero for rows >= nvalid.
+template <typename Tx, int R, typename Td>
+__device__ __forceinline__ void copy_rows_to(const ScanArgs& a, const RowLoad<Tx, R>& rl,
+                                             int tstart, int rfirst, int nvalid, Td* dst, int ld) {
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    float o[8];
+    rl.get(a, tstart, i, o);
+    if (rfirst + i >= nvalid)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = 0.f;
+    put8(dst + i * ld, o);
   }
-  return silu_f32(u);
 }
 
-template <typename T>
-__device__ __forceinline__ float ld1(const void* p, int64_t i) {
-  return to_f32(static_cast<const T*>(p)[i]);
-}
+// One chunk's B, C and x for the whole workgroup: thread (cv = tid % 16,
+// rg = tid / 16) owns rows [8 rg, 8 rg + 8) x channels [8 cv, 8 cv + 8) of B
+// and of C; thread (xv = tid % 8, xg = tid / 8) owns rows [4 xg, 4 xg + 4) x
+// channels [8 xv, 8 xv + 8) of x.
+template <typename Tx, bool CONV, bool WITH_C>
+struct ChunkStage {
+  static constexpr int HB = CONV ? 3 : 0;
+  RowLoad<Tx, 8 + HB> rb;
+  RowLoad<Tx, WITH_C ? 8 + HB : 1> rc;
+  RowLoad<Tx, 4 + HB> rx;
+
+  __device__ __forceinline__ void load(const ScanArgs& a, int b, int h, int g, int t0) {
+    const int tid = threadIdx.x;
+    const int cv = tid & 15, rg = tid >> 4, xv = tid & 7, xr = tid >> 3;
+    const int HP = a.nheads * P, GN = a.ngroups * N, cdim = HP + 2 * GN;
+    rb.load(a, static_cast<const Tx*>(a.Bm), a.b_stride, g * N + 8 * cv, HP + g * N + 8 * cv, cdim,
+            b, t0 + 8 * rg - HB);
+    if constexpr (WITH_C)
+      rc.load(a, static_cast<const Tx*>(a.Cm), a.c_stride, g * N + 8 * cv,
+              HP + GN + g * N + 8 * cv, cdim, b, t0 + 8 * rg - HB);
+    rx.load(a, static_cast<const Tx*>(a.x), a.x_stride, h * P + 8 * xv, h * P + 8 * xv, cdim, b,
+            t0 + 4 * xr - HB);
+  }
+
+  __device__ __forceinline__ void store(const ScanArgs& a, int h, int g, int t0, int Lc,
+                                        float* sB32, bf16* sC, float* sX32) const {
+    const int tid = threadIdx.x;
+    const int cv = tid & 15, rg = tid >> 4, xv = tid & 7, xr = tid >> 3;
+    const int HP = a.nheads * P, GN = a.ngroups * N;
+    if constexpr (CONV) {
+      conv_rows_to<Tx, 8>(a, rb, t0 + 8 * rg - 3, HP + g * N + 8 * cv, 8 * rg, Lc,
+                          sB32 + (8 * rg) * LDB32 + 8 * cv, LDB32);
+      if constexpr (WITH_C)
+        conv_rows_to<Tx, 8>(a, rc, t0 + 8 * rg - 3, HP + GN + g * N + 8 * cv, 8 * rg, Lc,
+                            sC + (8 * rg) * LDB + 8 * cv, LDB);
+    } else {
+      copy_rows_to<Tx, 8>(a, rb, t0 + 8 * rg, 8 * rg, Lc, sB32 + (8 * rg) * LDB32 + 8 * cv, LDB32);
+      if constexpr (WITH_C)
+        copy_rows_to<Tx, 8>(a, rc, t0 + 8 * rg, 8 * rg, Lc, sC + (8 * rg) * LDB + 8 * cv, LDB);
+    }
+    // x: 4 rows x 8 channels, transposed into sX32[p][t] through a small
+    // row-major scratch in registers
+    float o[4][8];
+    {
+      float tmp[4 * 8];
+      if constexpr (CONV)
+        conv_rows_to<Tx, 4>(a, rx, t0 + 4 * xr - 3, h * P + 8 * xv, 4 * xr, Lc, tmp, 8);
+      else
+        copy_rows_to<Tx, 4>(a, rx, t0 + 4 * xr, 4 * xr, Lc, tmp, 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[i][e] = tmp[8 * i + e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      *reinterpret_cast<float4*>(sX32 + (8 * xv + e) * LDX32 + 4 * xr) =
+          make_float4(o[0][e], o[1][e], o[2][e], o[3][e]);
+  }
+};
 
 // In-place inclusive prefix sum of s[0..Q) by waves 0 and 1 (fixed order).
 __device__ __forceinline__ void scan_lam(float* s, float* red) {
@@ -322,52 +384,30 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     const int t0 = c * Q;
     const int Lc = min(Q, L - t0);
     const int64_t row0 = (int64_t)b * L + t0;
+    // every global load of the chunk is issued before anything waits on one
+    ChunkStage<Tx, CONV, !STATE_ONLY> stage;
+    stage.load(a, b, h, g, t0);
+    float dtv = 0.f;
+    if (tid < Q) dtv = ld1<Ta>(a.dt, (row0 + min(tid, Lc - 1)) * a.dt_stride + h);
     __syncthreads();  // the previous chunk is done with every LDS buffer
-
     if (tid < Q) {
-      const float d = tid < Lc ? make_delta(ld1<Ta>(a.dt, (row0 + tid) * a.dt_stride + h),
-                                            a.dt_bias, h, a.dt_softplus)
-                               : 0.f;
+      const float d = tid < Lc ? make_delta(dtv, a.dt_bias, h, a.dt_softplus) : 0.f;
       sDel[tid] = d;
       sLam[tid] = d * Ah;
     }
-    if (CONV) {
-      stage_rows_conv<Tx, float, LDB32>(a, sB32, Bg, a.b_stride, b, t0, Lc, g * N, HP + g * N,
-                                         cdim);
-      if (!STATE_ONLY)
-        stage_rows_conv<Tx, bf16, LDB>(a, sC, Cg, a.c_stride, b, t0, Lc, g * N,
-                                       HP + GN + g * N, cdim);
-    } else {
-      stage_rows<Tx, float, LDB32>(sB32, Bg + g * N, a.b_stride, row0, Lc);
-      if (!STATE_ONLY) stage_rows<Tx, bf16, LDB>(sC, Cg + g * N, a.c_stride, row0, Lc);
-    }
-    // x rows of this wave, fp32, transposed into sX32[p][t]; z into registers
-    // in the accumulator layout: element (j, r) is
-    // (t = 32 w + 8 (r/4) + 4 hf + r%4, p = 32 j + l32)
+    stage.store(a, h, g, t0, Lc, sB32, sC, sX32);
+    // z in the accumulator layout: element (j, r) is
+    // (t = 32 w + 8 (r/4) + 4 hf + r%4, p = 32 j + l32); rows past the end
+    // re-read the last row and are never stored
     float zr[2][16];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int p = 32 * j + l32;
-        const int tb = 32 * w + 8 * q + 4 * hf;
-        float xv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = tb + e;
-          float v = 0.f, zv = 0.f;
-          if (t < Lc) {
-            if (CONV)
-              v = conv_point<Tx>(a, xg, a.x_stride, b, t0 + t, h * P + p, cdim);
-            else
-              v = to_f32(xg[(row0 + t) * a.x_stride + h * P + p]);
-            if (!STATE_ONLY && a.z != nullptr)
-              zv = ld1<Ta>(a.z, (row0 + t) * a.z_stride + h * P + p);
-          }
-          xv[e] = v;
-          zr[j][4 * q + e] = zv;
-        }
-        *reinterpret_cast<float4*>(sX32 + p * LDX32 + tb) = make_float4(xv[0], xv[1], xv[2], xv[3]);
+      for (int r = 0; r < 16; ++r) {
+        const int t = min(32 * w + 8 * (r >> 2) + 4 * hf + (r & 3), Lc - 1);
+        zr[j][r] = (!STATE_ONLY && a.z != nullptr)
+                       ? ld1<Ta>(a.z, (row0 + t) * a.z_stride + h * P + 32 * j + l32)
+                       : 0.f;
       }
     __syncthreads();
     scan_lam(sLam, sRed);

@@ -99,6 +99,8 @@ def _tok(t: Optional[torch.Tensor], B: int, L: int, width: int, name: str) -> in
     if tuple(t.shape[:2]) != (B, L) or inner != width:
         raise ValueError("%s has shape %s, want [%d, %d, (%d elements)]"
                          % (name, tuple(t.shape), B, L, width))
+    if B == 0 or L == 0:
+        return width  # empty: nothing is read or written
     row = t.view(B, L, width)  # raises rather than copies if rows are not contiguous
     if width > 1 and row.stride(2) != 1:
         raise ValueError("%s: per-token rows must be contiguous" % name)
