@@ -103,7 +103,7 @@ def time_prefill(args, wl, torch, layer, synth, dev, dev32):
     fused = not args.unfused
     conv_out = None if fused else torch.empty((wl.batch, wl.seqlen, wl.cdim), device="cuda")
     need = ssd.ssd_chunk_scan_workspace_bytes(wl.batch, wl.seqlen, wl.nheads,
-                                              ngroups=wl.ngroups)
+                                              ngroups=wl.ngroups, fused_conv=fused)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     del inp
 

@@ -102,10 +102,13 @@ int ssd_causal_conv1d_fwd(const void* x, int64_t x_tok_stride, ssd_dtype_t x_dty
                           hipStream_t stream);
 
 /* Bytes of device workspace ssd_chunk_scan_fwd needs for this shape (it may be
- * 0).  The same arguments must be passed to ssd_chunk_scan_fwd. */
+ * 0); fused_conv is 1 when conv_w will be passed.  The matrix-core path uses
+ * it for per-segment states when it splits a long sequence over more
+ * workgroups, and, with the conv fused, for the post-conv fp32 B and C
+ * (convolved once per group rather than once per head). */
 size_t ssd_chunk_scan_workspace_bytes(int batch, int seqlen, int nheads, int headdim,
                                       int ngroups, int dstate, int chunk,
-                                      ssd_math_t math);
+                                      ssd_math_t math, int fused_conv);
 
 /*
  * Chunked selective scan of one Mamba-2 layer (prefill), from x, B, C, dt and z
@@ -133,7 +136,7 @@ size_t ssd_chunk_scan_workspace_bytes(int batch, int seqlen, int nheads, int hea
  *   chunk in {32, 64, 128, 256} for SSD_MATH_F32; seqlen >= 0 (0 only copies
  *   the states); innermost rows 16-byte aligned.
  *   workspace: at least ssd_chunk_scan_workspace_bytes(...) bytes, 256-byte
- *   aligned (NULL allowed when that is 0).
+ *   aligned, overlapping no tensor (NULL allowed when that is 0).
  */
 int ssd_chunk_scan_fwd(const void* x, int64_t x_tok_stride, const void* Bm,
                        int64_t b_tok_stride, const void* Cm, int64_t c_tok_stride,

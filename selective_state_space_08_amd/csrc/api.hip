@@ -90,11 +90,25 @@ int plan_segments(int batch, int seqlen, int nheads) {
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-size_t scan_workspace(int batch, int seqlen, int nheads, int nseg) {
-  if (nseg <= 1) return 0;
+// Workspace of the matrix-core scan: per-segment states and log decays when
+// the sequence is split, and the post-conv fp32 B|C of the whole input when
+// the conv is fused (B and C are convolved once per group there, rather than
+// once per head inside every walker).
+struct WsLayout {
+  size_t seg_state = 0, seg_ld = 0, bc = 0, total = 0;
+};
+WsLayout ws_layout(int batch, int seqlen, int nheads, int ngroups, int nseg, bool fused_conv) {
+  WsLayout w;
   const size_t bh = (size_t)batch * nheads;
-  return round_up(bh * nseg * kP * kN * sizeof(float), 256) +
-         round_up(bh * nseg * sizeof(float), 256);
+  size_t off = 0;
+  w.seg_state = off;
+  if (nseg > 1) off += round_up(bh * nseg * kP * kN * sizeof(float), 256);
+  w.seg_ld = off;
+  if (nseg > 1) off += round_up(bh * nseg * sizeof(float), 256);
+  w.bc = off;
+  if (fused_conv) off += round_up((size_t)batch * seqlen * 2 * ngroups * kN * sizeof(float), 256);
+  w.total = off;
+  return w;
 }
 
 }  // namespace
@@ -164,17 +178,20 @@ int ssd_causal_conv1d_fwd(const void* x, int64_t x_tok_stride, ssd_dtype_t x_dty
   if (batch == 0) return SSD_OK;
   if (rows == 0 && conv_state_out == nullptr) return SSD_OK;
   hipError_t e = launch_causal_conv1d(x, x_tok_stride, x_dtype, weight, bias, conv_state_in,
-                                      conv_state_out, out, out_tok_stride, out_dtype, batch,
+                                      conv_state_out, cdim, out, out_tok_stride, out_dtype, batch,
                                       seqlen, cdim, width, apply_silu, stream);
   return e == hipSuccess ? SSD_OK : hip_fail(e, "conv1d launch");
 }
 
 size_t ssd_chunk_scan_workspace_bytes(int batch, int seqlen, int nheads, int headdim,
-                                      int ngroups, int dstate, int chunk, ssd_math_t math) {
-  (void)headdim; (void)ngroups; (void)dstate; (void)chunk;
-  if (batch <= 0 || seqlen <= 0 || nheads <= 0) return 0;
+                                      int ngroups, int dstate, int chunk, ssd_math_t math,
+                                      int fused_conv) {
+  (void)headdim; (void)dstate; (void)chunk;
+  if (batch <= 0 || seqlen <= 0 || nheads <= 0 || ngroups <= 0) return 0;
   if (math != SSD_MATH_BF16) return 0;
-  return scan_workspace(batch, seqlen, nheads, plan_segments(batch, seqlen, nheads));
+  return ws_layout(batch, seqlen, nheads, ngroups, plan_segments(batch, seqlen, nheads),
+                   fused_conv != 0)
+      .total;
 }
 
 int ssd_chunk_scan_fwd(const void* x, int64_t x_tok_stride, const void* Bm,
@@ -263,14 +280,22 @@ int ssd_chunk_scan_fwd(const void* x, int64_t x_tok_stride, const void* Bm,
     if (overlap(rfs, ins[i]))
       return fail(SSD_ERR_INVALID_ARG, "scan: final_state overlaps an activation");
   // ---- workspace
-  const int nseg = math == SSD_MATH_BF16 && rows > 0 ? plan_segments(batch, seqlen, nheads) : 1;
-  const size_t ws_need = math == SSD_MATH_BF16 && rows > 0 ? scan_workspace(batch, seqlen, nheads, nseg) : 0;
+  const bool mc = math == SSD_MATH_BF16 && rows > 0;
+  const int nseg = mc ? plan_segments(batch, seqlen, nheads) : 1;
+  const WsLayout wl = mc ? ws_layout(batch, seqlen, nheads, ngroups, nseg, conv_w != nullptr)
+                         : WsLayout{};
+  const size_t ws_need = wl.total;
   if (ws_need > 0) {
     if (workspace == nullptr || workspace_bytes < ws_need)
       return fail(SSD_ERR_WORKSPACE, "scan: workspace needs %zu bytes, got %zu", ws_need,
                   workspace == nullptr ? (size_t)0 : workspace_bytes);
     if (!aligned(workspace, 256))
       return fail(SSD_ERR_INVALID_ARG, "scan: workspace is not 256-byte aligned");
+    const Range rws = dense_range(workspace, (int64_t)ws_need, 1);
+    if (overlap(rws, ry) || overlap(rws, rso) || overlap(rws, rfs))
+      return fail(SSD_ERR_INVALID_ARG, "scan: workspace overlaps a tensor");
+    for (const Range& r : ins)
+      if (overlap(rws, r)) return fail(SSD_ERR_INVALID_ARG, "scan: workspace overlaps a tensor");
   }
 
   if (batch == 0) return SSD_OK;
@@ -300,11 +325,34 @@ int ssd_chunk_scan_fwd(const void* x, int64_t x_tok_stride, const void* Bm,
   a.nseg = nseg;
   a.seg_chunks = (nc + nseg - 1) / nseg;
   a.nseg = (nc + a.seg_chunks - 1) / a.seg_chunks;  // no empty trailing segment
+  char* ws = static_cast<char*>(workspace);
   if (nseg > 1) {
-    const size_t bh = (size_t)batch * nheads;
-    a.seg_state = static_cast<float*>(workspace);
-    a.seg_logdecay = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                              round_up(bh * nseg * kP * kN * sizeof(float), 256));
+    a.seg_state = reinterpret_cast<float*>(ws + wl.seg_state);
+    a.seg_logdecay = reinterpret_cast<float*>(ws + wl.seg_ld);
+  }
+  if (math == SSD_MATH_BF16 && conv_w != nullptr) {
+    // B and C: conv + SiLU once per group into fp32 [B, L, 2*G*N]; the scan
+    // convolves only the x channels itself
+    float* bc = reinterpret_cast<float*>(ws + wl.bc);
+    const int GNi = (int)GN;
+    const size_t hoff = (size_t)HP * xe;
+    e = launch_causal_conv1d(Bm, b_tok_stride, xbc_dtype, conv_w + HP * conv_width,
+                             conv_b ? conv_b + HP : nullptr,
+                             conv_state_in ? static_cast<const char*>(conv_state_in) + hoff : nullptr,
+                             conv_state_out ? static_cast<char*>(conv_state_out) + hoff : nullptr,
+                             cdim, bc, 2 * GN, SSD_F32, batch, seqlen, GNi, conv_width, 1, stream);
+    if (e == hipSuccess)
+      e = launch_causal_conv1d(
+          Cm, c_tok_stride, xbc_dtype, conv_w + (HP + GN) * conv_width,
+          conv_b ? conv_b + HP + GN : nullptr,
+          conv_state_in ? static_cast<const char*>(conv_state_in) + hoff + GN * xe : nullptr,
+          conv_state_out ? static_cast<char*>(conv_state_out) + hoff + GN * xe : nullptr, cdim,
+          bc + GN, 2 * GN, SSD_F32, batch, seqlen, GNi, conv_width, 1, stream);
+    if (e != hipSuccess) return hip_fail(e, "scan: B/C conv launch");
+    a.Bm = bc;
+    a.b_stride = 2 * GN;
+    a.Cm = bc + GN;
+    a.c_stride = 2 * GN;
   }
   e = math == SSD_MATH_BF16 ? launch_scan_bf16(a, xbc_dtype, act_dtype, y_dtype, stream)
                             : launch_scan_f32(a, xbc_dtype, act_dtype, y_dtype, stream);

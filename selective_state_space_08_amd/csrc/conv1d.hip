@@ -66,12 +66,12 @@ __device__ __forceinline__ void store_vec<bf16, 8>(bf16* p, const float* v) {
 // negative: then the history row (K-1)+tau, or zero)
 template <typename Tin, int VEC>
 __device__ __forceinline__ void load_raw(const Tin* x, int64_t x_stride, const Tin* hist,
-                                         int b, int L, int C, int K, int tau, int c,
+                                         int64_t hs, int b, int L, int K, int tau, int c,
                                          float* v) {
   if (tau >= 0) {
     Vec<Tin, VEC>::load(x + ((int64_t)b * L + tau) * x_stride + c, v);
   } else if (hist != nullptr && tau >= -(K - 1)) {
-    Vec<Tin, VEC>::load(hist + ((int64_t)b * (K - 1) + (K - 1) + tau) * C + c, v);
+    Vec<Tin, VEC>::load(hist + ((int64_t)b * (K - 1) + (K - 1) + tau) * hs + c, v);
   } else {
 #pragma unroll
     for (int i = 0; i < VEC; ++i) v[i] = 0.f;
@@ -82,8 +82,8 @@ template <typename Tin, typename Tout, int VEC>
 __global__ __launch_bounds__(THREADS) void causal_conv1d_kernel(
     const Tin* __restrict__ x, int64_t x_stride, const float* __restrict__ w,
     const float* __restrict__ bias, const Tin* __restrict__ hist_in,
-    Tin* __restrict__ hist_out, Tout* __restrict__ out, int64_t out_stride, int L, int C,
-    int K, int apply_silu) {
+    Tin* __restrict__ hist_out, int64_t hs, Tout* __restrict__ out, int64_t out_stride, int L,
+    int C, int K, int apply_silu) {
   const int nv = C / VEC;
   const int cv = blockIdx.x * THREADS + threadIdx.x;
   if (cv >= nv) return;
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(THREADS) void causal_conv1d_kernel(
     float win[3][VEC];  // x[t-3], x[t-2], x[t-1]
 #pragma unroll
     for (int j = 0; j < 3; ++j)
-      load_raw<Tin, VEC>(x, x_stride, hist_in, b, L, C, K, t0 - 3 + j, c, win[j]);
+      load_raw<Tin, VEC>(x, x_stride, hist_in, hs, b, L, K, t0 - 3 + j, c, win[j]);
     const int t1 = min(L, t0 + TOK);
     for (int t = t0; t < t1; ++t) {
       float cur[VEC], o[VEC];
@@ -129,21 +129,22 @@ __global__ __launch_bounds__(THREADS) void causal_conv1d_kernel(
   if (hist_out != nullptr && blockIdx.y == gridDim.y - 1) {
     for (int j = 0; j < K - 1; ++j) {
       float v[VEC];
-      load_raw<Tin, VEC>(x, x_stride, hist_in, b, L, C, K, L - (K - 1) + j, c, v);
-      store_vec<Tin, VEC>(hist_out + ((int64_t)b * (K - 1) + j) * C + c, v);
+      load_raw<Tin, VEC>(x, x_stride, hist_in, hs, b, L, K, L - (K - 1) + j, c, v);
+      store_vec<Tin, VEC>(hist_out + ((int64_t)b * (K - 1) + j) * hs + c, v);
     }
   }
 }
 
 template <typename Tin, typename Tout, int VEC>
 hipError_t launch_typed(const void* x, int64_t x_stride, const float* w, const float* bias,
-                        const void* hist_in, void* hist_out, void* out, int64_t out_stride,
-                        int B, int L, int C, int K, int apply_silu, hipStream_t stream) {
+                        const void* hist_in, void* hist_out, int64_t hs, void* out,
+                        int64_t out_stride, int B, int L, int C, int K, int apply_silu,
+                        hipStream_t stream) {
   const int nv = C / VEC;
   dim3 grid((nv + THREADS - 1) / THREADS, L > 0 ? (L + TOK - 1) / TOK : 1, B);
   hipLaunchKernelGGL((causal_conv1d_kernel<Tin, Tout, VEC>), grid, dim3(THREADS), 0, stream,
                      static_cast<const Tin*>(x), x_stride, w, bias,
-                     static_cast<const Tin*>(hist_in), static_cast<Tin*>(hist_out),
+                     static_cast<const Tin*>(hist_in), static_cast<Tin*>(hist_out), hs,
                      static_cast<Tout*>(out), out_stride, L, C, K, apply_silu);
   return hipGetLastError();
 }
@@ -152,38 +153,40 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 template <typename Tin, typename Tout>
 hipError_t dispatch_vec(const void* x, int64_t x_stride, const float* w, const float* bias,
-                        const void* hist_in, void* hist_out, void* out, int64_t out_stride,
-                        int B, int L, int C, int K, int apply_silu, hipStream_t stream) {
+                        const void* hist_in, void* hist_out, int64_t hs, void* out,
+                        int64_t out_stride, int B, int L, int C, int K, int apply_silu,
+                        hipStream_t stream) {
   constexpr int V = sizeof(Tin) == 2 ? 8 : 4;
-  const bool vec_ok = C % V == 0 && x_stride % V == 0 && out_stride % V == 0 && aligned16(x) &&
+  const bool vec_ok = C % V == 0 && x_stride % V == 0 && out_stride % V == 0 && hs % V == 0 &&
+                      aligned16(x) &&
                       (hist_in == nullptr || aligned16(hist_in)) &&
                       (hist_out == nullptr || aligned16(hist_out)) &&
                       (sizeof(Tout) == 2 ? aligned16(out) && out_stride % 8 == 0
                                          : aligned16(out));
   if (vec_ok)
-    return launch_typed<Tin, Tout, V>(x, x_stride, w, bias, hist_in, hist_out, out, out_stride,
-                                      B, L, C, K, apply_silu, stream);
-  return launch_typed<Tin, Tout, 1>(x, x_stride, w, bias, hist_in, hist_out, out, out_stride,
-                                    B, L, C, K, apply_silu, stream);
+    return launch_typed<Tin, Tout, V>(x, x_stride, w, bias, hist_in, hist_out, hs, out,
+                                      out_stride, B, L, C, K, apply_silu, stream);
+  return launch_typed<Tin, Tout, 1>(x, x_stride, w, bias, hist_in, hist_out, hs, out,
+                                    out_stride, B, L, C, K, apply_silu, stream);
 }
 
 }  // namespace
 
 hipError_t launch_causal_conv1d(const void* x, int64_t x_stride, ssd_dtype_t x_dtype,
                                 const float* w, const float* bias, const void* hist_in,
-                                void* hist_out, void* out, int64_t out_stride,
+                                void* hist_out, int64_t hs, void* out, int64_t out_stride,
                                 ssd_dtype_t out_dtype, int B, int L, int C, int K,
                                 int apply_silu, hipStream_t stream) {
   if (x_dtype == SSD_BF16 && out_dtype == SSD_F32)
-    return dispatch_vec<bf16, float>(x, x_stride, w, bias, hist_in, hist_out, out, out_stride,
+    return dispatch_vec<bf16, float>(x, x_stride, w, bias, hist_in, hist_out, hs, out, out_stride,
                                      B, L, C, K, apply_silu, stream);
   if (x_dtype == SSD_BF16 && out_dtype == SSD_BF16)
-    return dispatch_vec<bf16, bf16>(x, x_stride, w, bias, hist_in, hist_out, out, out_stride,
+    return dispatch_vec<bf16, bf16>(x, x_stride, w, bias, hist_in, hist_out, hs, out, out_stride,
                                     B, L, C, K, apply_silu, stream);
   if (x_dtype == SSD_F32 && out_dtype == SSD_F32)
-    return dispatch_vec<float, float>(x, x_stride, w, bias, hist_in, hist_out, out, out_stride,
+    return dispatch_vec<float, float>(x, x_stride, w, bias, hist_in, hist_out, hs, out, out_stride,
                                       B, L, C, K, apply_silu, stream);
-  return dispatch_vec<float, bf16>(x, x_stride, w, bias, hist_in, hist_out, out, out_stride, B,
+  return dispatch_vec<float, bf16>(x, x_stride, w, bias, hist_in, hist_out, hs, out, out_stride, B,
                                    L, C, K, apply_silu, stream);
 }
 

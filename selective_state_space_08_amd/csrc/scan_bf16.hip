@@ -219,62 +219,46 @@ __device__ __forceinline__ void copy_rows_to(const ScanArgs& a, const RowLoad<Tx
 
 // One chunk's B, C and x for the whole workgroup: thread (cv = tid % 16,
 // rg = tid / 16) owns rows [8 rg, 8 rg + 8) x channels [8 cv, 8 cv + 8) of B
-// and of C; thread (xv = tid % 8, xg = tid / 8) owns rows [4 xg, 4 xg + 4) x
-// channels [8 xv, 8 xv + 8) of x.
-template <typename Tx, bool CONV, bool WITH_C>
+// and of C (post-conv values of type Tbc); thread (xv = tid % 8, xr = tid / 8)
+// owns rows [4 xr, 4 xr + 4) x channels [8 xv, 8 xv + 8) of x (raw values of
+// type Tx with 3 rows of history in front when XCONV, post-conv otherwise).
+template <typename Tx, typename Tbc, bool XCONV, bool WITH_C>
 struct ChunkStage {
-  static constexpr int HB = CONV ? 3 : 0;
-  RowLoad<Tx, 8 + HB> rb;
-  RowLoad<Tx, WITH_C ? 8 + HB : 1> rc;
-  RowLoad<Tx, 4 + HB> rx;
+  static constexpr int HX = XCONV ? 3 : 0;
+  RowLoad<Tbc, 8> rb;
+  RowLoad<Tbc, WITH_C ? 8 : 1> rc;
+  RowLoad<Tx, 4 + HX> rx;
 
   __device__ __forceinline__ void load(const ScanArgs& a, int b, int h, int g, int t0) {
     const int tid = threadIdx.x;
     const int cv = tid & 15, rg = tid >> 4, xv = tid & 7, xr = tid >> 3;
-    const int HP = a.nheads * P, GN = a.ngroups * N, cdim = HP + 2 * GN;
-    rb.load(a, static_cast<const Tx*>(a.Bm), a.b_stride, g * N + 8 * cv, HP + g * N + 8 * cv, cdim,
-            b, t0 + 8 * rg - HB);
+    const int cdim = a.nheads * P + 2 * a.ngroups * N;
+    rb.load(a, static_cast<const Tbc*>(a.Bm), a.b_stride, g * N + 8 * cv, 0, cdim, b,
+            t0 + 8 * rg);
     if constexpr (WITH_C)
-      rc.load(a, static_cast<const Tx*>(a.Cm), a.c_stride, g * N + 8 * cv,
-              HP + GN + g * N + 8 * cv, cdim, b, t0 + 8 * rg - HB);
+      rc.load(a, static_cast<const Tbc*>(a.Cm), a.c_stride, g * N + 8 * cv, 0, cdim, b,
+              t0 + 8 * rg);
     rx.load(a, static_cast<const Tx*>(a.x), a.x_stride, h * P + 8 * xv, h * P + 8 * xv, cdim, b,
-            t0 + 4 * xr - HB);
+            t0 + 4 * xr - HX);
   }
 
-  __device__ __forceinline__ void store(const ScanArgs& a, int h, int g, int t0, int Lc,
-                                        float* sB32, bf16* sC, float* sX32) const {
+  __device__ __forceinline__ void store(const ScanArgs& a, int h, int t0, int Lc, float* sB32,
+                                        bf16* sC, float* sX32) const {
     const int tid = threadIdx.x;
     const int cv = tid & 15, rg = tid >> 4, xv = tid & 7, xr = tid >> 3;
-    const int HP = a.nheads * P, GN = a.ngroups * N;
-    if constexpr (CONV) {
-      conv_rows_to<Tx, 8>(a, rb, t0 + 8 * rg - 3, HP + g * N + 8 * cv, 8 * rg, Lc,
-                          sB32 + (8 * rg) * LDB32 + 8 * cv, LDB32);
-      if constexpr (WITH_C)
-        conv_rows_to<Tx, 8>(a, rc, t0 + 8 * rg - 3, HP + GN + g * N + 8 * cv, 8 * rg, Lc,
-                            sC + (8 * rg) * LDB + 8 * cv, LDB);
-    } else {
-      copy_rows_to<Tx, 8>(a, rb, t0 + 8 * rg, 8 * rg, Lc, sB32 + (8 * rg) * LDB32 + 8 * cv, LDB32);
-      if constexpr (WITH_C)
-        copy_rows_to<Tx, 8>(a, rc, t0 + 8 * rg, 8 * rg, Lc, sC + (8 * rg) * LDB + 8 * cv, LDB);
-    }
-    // x: 4 rows x 8 channels, transposed into sX32[p][t] through a small
-    // row-major scratch in registers
-    float o[4][8];
-    {
-      float tmp[4 * 8];
-      if constexpr (CONV)
-        conv_rows_to<Tx, 4>(a, rx, t0 + 4 * xr - 3, h * P + 8 * xv, 4 * xr, Lc, tmp, 8);
-      else
-        copy_rows_to<Tx, 4>(a, rx, t0 + 4 * xr, 4 * xr, Lc, tmp, 8);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[i][e] = tmp[8 * i + e];
-    }
+    copy_rows_to<Tbc, 8>(a, rb, t0 + 8 * rg, 8 * rg, Lc, sB32 + (8 * rg) * LDB32 + 8 * cv, LDB32);
+    if constexpr (WITH_C)
+      copy_rows_to<Tbc, 8>(a, rc, t0 + 8 * rg, 8 * rg, Lc, sC + (8 * rg) * LDB + 8 * cv, LDB);
+    // x: 4 rows x 8 channels, transposed into sX32[p][t]
+    float tmp[4 * 8];
+    if constexpr (XCONV)
+      conv_rows_to<Tx, 4>(a, rx, t0 + 4 * xr - 3, h * P + 8 * xv, 4 * xr, Lc, tmp, 8);
+    else
+      copy_rows_to<Tx, 4>(a, rx, t0 + 4 * xr, 4 * xr, Lc, tmp, 8);
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       *reinterpret_cast<float4*>(sX32 + (8 * xv + e) * LDX32 + 4 * xr) =
-          make_float4(o[0][e], o[1][e], o[2][e], o[3][e]);
+          make_float4(tmp[e], tmp[8 + e], tmp[16 + e], tmp[24 + e]);
   }
 };
 
@@ -318,7 +302,7 @@ __device__ __forceinline__ Walker walker_of(int lin, int total, int H, int G, in
   return Walker{b, g * hpg + hh, seg};
 }
 
-template <typename Tx, typename Ta, typename Ty, bool CONV, bool STATE_ONLY>
+template <typename Tx, typename Tbc, typename Ta, typename Ty, bool XCONV, bool STATE_ONLY>
 __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) float sB32[Q * LDB32];
   __shared__ __attribute__((aligned(16))) float sX32[P * LDX32];
@@ -348,8 +332,6 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
   const float Dh = a.D ? a.D[h] : 0.f;
 
   const Tx* xg = static_cast<const Tx*>(a.x);
-  const Tx* Bg = static_cast<const Tx*>(a.Bm);
-  const Tx* Cg = static_cast<const Tx*>(a.Cm);
 
   // ---- incoming state: accumulator element r of tile j is
   //      (p = 32 pt + 8 (r/4) + 4 hf + r%4, n = 32 (nt0 + j) + l32)
@@ -385,7 +367,7 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     const int Lc = min(Q, L - t0);
     const int64_t row0 = (int64_t)b * L + t0;
     // every global load of the chunk is issued before anything waits on one
-    ChunkStage<Tx, CONV, !STATE_ONLY> stage;
+    ChunkStage<Tx, Tbc, XCONV, !STATE_ONLY> stage;
     stage.load(a, b, h, g, t0);
     float dtv = 0.f;
     if (tid < Q) dtv = ld1<Ta>(a.dt, (row0 + min(tid, Lc - 1)) * a.dt_stride + h);
@@ -395,7 +377,7 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
       sDel[tid] = d;
       sLam[tid] = d * Ah;
     }
-    stage.store(a, h, g, t0, Lc, sB32, sC, sX32);
+    stage.store(a, h, t0, Lc, sB32, sC, sX32);
     // z in the accumulator layout: element (j, r) is
     // (t = 32 w + 8 (r/4) + 4 hf + r%4, p = 32 j + l32); rows past the end
     // re-read the last row and are never stored
@@ -548,31 +530,22 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
   }
   if (STATE_ONLY && tid == 0) a.seg_logdecay[(int64_t)bh * a.nseg + seg] = log_decay;
 
-  // ---- conv history hand-over (last segment)
-  if (CONV && !STATE_ONLY && seg == a.nseg - 1 && a.conv_state_out != nullptr) {
+  // ---- conv history hand-over of this head's x channels (last segment; the
+  //      B and C channels are handed over by their conv pass)
+  if (XCONV && !STATE_ONLY && seg == a.nseg - 1 && a.conv_state_out != nullptr) {
     const int K = a.conv_k;
     Tx* out = static_cast<Tx*>(a.conv_state_out);
     const Tx* hin = static_cast<const Tx*>(a.conv_state_in);
-    auto raw = [&](const Tx* base, int64_t stride, int tau, int j, int c) -> Tx {
-      if (tau >= 0) return base[((int64_t)b * L + tau) * stride + j];  // tau < L here
-      if (hin != nullptr && tau >= -(K - 1))
-        return hin[((int64_t)b * (K - 1) + (K - 1) + tau) * cdim + c];
-      return from_f32<Tx>(0.f);
-    };
     for (int i = tid; i < (K - 1) * P; i += THREADS) {
-      const int j = i / P, p = i % P, c = h * P + p;
-      out[((int64_t)b * (K - 1) + j) * cdim + c] = raw(xg, a.x_stride, L - (K - 1) + j, c, c);
+      const int j = i / P, c = h * P + i % P;
+      const int tau = L - (K - 1) + j;  // < L
+      Tx v = from_f32<Tx>(0.f);
+      if (tau >= 0)
+        v = xg[((int64_t)b * L + tau) * a.x_stride + c];
+      else if (hin != nullptr)
+        v = hin[((int64_t)b * (K - 1) + (K - 1) + tau) * cdim + c];
+      out[((int64_t)b * (K - 1) + j) * cdim + c] = v;
     }
-    if (h % hpg == 0)
-      for (int i = tid; i < (K - 1) * 2 * N; i += THREADS) {
-        const int j = i / (2 * N), e = i % (2 * N);
-        const bool isB = e < N;
-        const int n = isB ? e : e - N;
-        const int c = (isB ? HP : HP + GN) + g * N + n;
-        out[((int64_t)b * (K - 1) + j) * cdim + c] =
-            isB ? raw(Bg, a.b_stride, L - (K - 1) + j, g * N + n, c)
-                : raw(Cg, a.c_stride, L - (K - 1) + j, g * N + n, c);
-      }
   }
 }
 
@@ -592,37 +565,35 @@ __global__ __launch_bounds__(THREADS) void combine_segments_kernel(ScanArgs a) {
   }
 }
 
-template <typename Tx, typename Ta, typename Ty, bool CONV>
-hipError_t launch_conv(const ScanArgs& a, hipStream_t stream) {
+template <typename Tx, typename Tbc, typename Ta, typename Ty, bool XCONV>
+hipError_t launch_walkers(const ScanArgs& a, hipStream_t stream) {
   const int BH = a.batch * a.nheads;
   if (a.nseg > 1) {
-    hipLaunchKernelGGL((scan_bf16_kernel<Tx, Ta, Ty, CONV, true>), dim3(BH * (a.nseg - 1)),
+    hipLaunchKernelGGL((scan_bf16_kernel<Tx, Tbc, Ta, Ty, XCONV, true>), dim3(BH * (a.nseg - 1)),
                        dim3(THREADS), 0, stream, a);
     hipLaunchKernelGGL(combine_segments_kernel, dim3(BH), dim3(THREADS), 0, stream, a);
   }
-  hipLaunchKernelGGL((scan_bf16_kernel<Tx, Ta, Ty, CONV, false>), dim3(BH * a.nseg),
+  hipLaunchKernelGGL((scan_bf16_kernel<Tx, Tbc, Ta, Ty, XCONV, false>), dim3(BH * a.nseg),
                      dim3(THREADS), 0, stream, a);
   return hipGetLastError();
 }
 
-template <typename Tx, typename Ta, typename Ty>
-hipError_t launch_typed(const ScanArgs& a, hipStream_t s) {
-  return a.conv_w ? launch_conv<Tx, Ta, Ty, true>(a, s) : launch_conv<Tx, Ta, Ty, false>(a, s);
-}
-
-template <typename Tx, typename Ta>
-hipError_t pick_y(const ScanArgs& a, ssd_dtype_t yd, hipStream_t s) {
-  return yd == SSD_F32 ? launch_typed<Tx, Ta, float>(a, s) : launch_typed<Tx, Ta, bf16>(a, s);
+template <typename Ta, typename Ty>
+hipError_t pick_x(const ScanArgs& a, ssd_dtype_t xd, hipStream_t s) {
+  if (a.conv_w != nullptr)  // raw x, post-conv fp32 B and C from the conv pass
+    return xd == SSD_BF16 ? launch_walkers<bf16, float, Ta, Ty, true>(a, s)
+                          : launch_walkers<float, float, Ta, Ty, true>(a, s);
+  return xd == SSD_BF16 ? launch_walkers<bf16, bf16, Ta, Ty, false>(a, s)
+                        : launch_walkers<float, float, Ta, Ty, false>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_scan_bf16(const ScanArgs& a, ssd_dtype_t xd, ssd_dtype_t ad, ssd_dtype_t yd,
                             hipStream_t s) {
-  if (xd == SSD_BF16 && ad == SSD_BF16) return pick_y<bf16, bf16>(a, yd, s);
-  if (xd == SSD_BF16) return pick_y<bf16, float>(a, yd, s);
-  if (ad == SSD_BF16) return pick_y<float, bf16>(a, yd, s);
-  return pick_y<float, float>(a, yd, s);
+  if (ad == SSD_BF16)
+    return yd == SSD_F32 ? pick_x<bf16, float>(a, xd, s) : pick_x<bf16, bf16>(a, xd, s);
+  return yd == SSD_F32 ? pick_x<float, float>(a, xd, s) : pick_x<float, bf16>(a, xd, s);
 }
 
 }  // namespace ssd

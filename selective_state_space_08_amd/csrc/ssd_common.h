@@ -26,7 +26,11 @@ __device__ __forceinline__ float softplus_f32(float v) {
   return fmaxf(v, 0.f) + log1pf(__expf(-fabsf(v)));
 }
 
-__device__ __forceinline__ float silu_f32(float u) { return u / (1.f + __expf(-u)); }
+// SiLU(u) = u * sigmoid(u), with the hardware reciprocal (1 ulp) in place of
+// an IEEE division
+__device__ __forceinline__ float silu_f32(float u) {
+  return u * __builtin_amdgcn_rcpf(1.f + __expf(-u));
+}
 
 // delta = softplus(dt + bias) | dt + bias
 __device__ __forceinline__ float make_delta(float dt, const float* dt_bias, int h,
@@ -59,11 +63,13 @@ struct ScanArgs {
 // ------------------------------------------------------------------ launchers
 // Each returns hipSuccess or the launch error; shapes are validated by the caller.
 
+// hist_stride: elements between consecutive history rows (cdim for a dense
+// [B, K-1, cdim] history; larger when the channels are a slice of one)
 hipError_t launch_causal_conv1d(const void* x, int64_t x_stride, ssd_dtype_t x_dtype,
                                 const float* w, const float* bias, const void* hist_in,
-                                void* hist_out, void* out, int64_t out_stride,
-                                ssd_dtype_t out_dtype, int batch, int seqlen, int cdim,
-                                int width, int apply_silu, hipStream_t stream);
+                                void* hist_out, int64_t hist_stride, void* out,
+                                int64_t out_stride, ssd_dtype_t out_dtype, int batch, int seqlen,
+                                int cdim, int width, int apply_silu, hipStream_t stream);
 
 hipError_t launch_scan_f32(const ScanArgs& a, ssd_dtype_t xbc_dtype, ssd_dtype_t act_dtype,
                            ssd_dtype_t y_dtype, hipStream_t stream);

@@ -26,7 +26,7 @@ _V, _I, _I64, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size
 SIGNATURES = {
     "ssd_causal_conv1d_fwd": (_I, [_V, _I64, _I, _V, _V, _V, _V, _V, _I64, _I, _I, _I, _I, _I,
                                    _I, _V]),
-    "ssd_chunk_scan_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
+    "ssd_chunk_scan_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I, _I]),
     "ssd_chunk_scan_fwd": (_I, [_V, _I64, _V, _I64, _V, _I64, _I, _V, _V, _I, _V, _V, _V, _I64,
                                 _V, _I64, _I, _V, _V, _V, _I, _V, _V, _V, _I64, _I, _I, _I, _I,
                                 _I, _I, _I, _I, _I, _V, _SZ, _V]),
@@ -128,10 +128,10 @@ def ssd_decode_cache_bytes(nheads, headdim, ngroups, dstate, width, conv_dtype=t
 
 
 def ssd_chunk_scan_workspace_bytes(batch, seqlen, nheads, headdim=64, ngroups=8, dstate=128,
-                                   chunk=128, math="bf16"):
+                                   chunk=128, math="bf16", fused_conv=False):
     return load().ssd_chunk_scan_workspace_bytes(
         batch, seqlen, nheads, headdim, ngroups, dstate, chunk,
-        SSD_MATH_BF16 if math == "bf16" else SSD_MATH_F32)
+        SSD_MATH_BF16 if math == "bf16" else SSD_MATH_F32, int(bool(fused_conv)))
 
 
 def ssd_causal_conv1d_fwd(x, weight, bias=None, conv_state_in=None, conv_state_out=None,
@@ -186,7 +186,7 @@ def ssd_chunk_scan_fwd(x, Bm, Cm, dt, A, *, D=None, z=None, dt_bias=None, dt_sof
         y = torch.empty((B, L, H, P), dtype=y_dtype, device=x.device)
     ys = _tok(y, B, L, H * P, "y")
     m = SSD_MATH_BF16 if math == "bf16" else SSD_MATH_F32
-    need = lib.ssd_chunk_scan_workspace_bytes(B, L, H, P, G, N, chunk, m)
+    need = lib.ssd_chunk_scan_workspace_bytes(B, L, H, P, G, N, chunk, m, int(conv_w is not None))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -63,13 +63,17 @@ def test_decode_cache_bytes_rejects_bad_input():
 def test_workspace_query():
     lib = ssd.load()
     # fp32 path and short sequences never need a workspace
-    assert lib.ssd_chunk_scan_workspace_bytes(1, 131072, 80, 64, 8, 128, 128, 0) == 0
-    assert lib.ssd_chunk_scan_workspace_bytes(4, 128, 128, 64, 8, 128, 128, 1) == 0
-    assert lib.ssd_chunk_scan_workspace_bytes(4, 8192, 128, 64, 8, 128, 128, 1) == 0
+    for fused in (0, 1):
+        assert lib.ssd_chunk_scan_workspace_bytes(1, 131072, 80, 64, 8, 128, 128, 0, fused) == 0
+    assert lib.ssd_chunk_scan_workspace_bytes(4, 128, 128, 64, 8, 128, 128, 1, 0) == 0
+    assert lib.ssd_chunk_scan_workspace_bytes(4, 8192, 128, 64, 8, 128, 128, 1, 0) == 0
+    # fused conv: the post-conv fp32 B|C of every token
+    assert lib.ssd_chunk_scan_workspace_bytes(4, 8192, 128, 64, 8, 128, 128, 1, 1) == \
+        4 * 8192 * 2 * 8 * 128 * 4
     # one long sequence with few heads is split into segments: per-segment states
-    ws = lib.ssd_chunk_scan_workspace_bytes(1, 131072, 80, 64, 8, 128, 128, 1)
+    ws = lib.ssd_chunk_scan_workspace_bytes(1, 131072, 80, 64, 8, 128, 128, 1, 0)
     assert ws >= 80 * 2 * 64 * 128 * 4
-    assert lib.ssd_chunk_scan_workspace_bytes(0, 128, 8, 64, 8, 128, 128, 1) == 0
+    assert lib.ssd_chunk_scan_workspace_bytes(0, 128, 8, 64, 8, 128, 128, 1, 0) == 0
 
 
 # ------------------------------------------------------------------ validation
@@ -148,6 +152,15 @@ def test_scan_rejects_y_overlapping_state():
     assert call_scan(a) == INVALID
 
 
+def test_scan_rejects_workspace_overlapping_y():
+    lib = ssd.load()
+    need = lib.ssd_chunk_scan_workspace_bytes(1, 65536, 8, 64, 2, 128, 128, 1, 0)
+    a = scan_args(B=1, L=65536)
+    a["ws"] = ctypes.c_void_p(a["y"].value)
+    a["wsb"] = need
+    assert call_scan(a) == INVALID
+
+
 def test_scan_rejects_conv_state_out_on_conv_state_in():
     a = scan_args(conv_w=ctypes.c_void_p(1 << 45), K=4)
     a["csi"] = ctypes.c_void_p(1 << 46)
@@ -159,7 +172,7 @@ def test_scan_workspace_required():
     """One long sequence with few heads needs a workspace for the sequence
     split; without it (or with too little) the call fails with SSD_ERR_WORKSPACE."""
     lib = ssd.load()
-    need = lib.ssd_chunk_scan_workspace_bytes(1, 65536, 8, 64, 2, 128, 128, 1)
+    need = lib.ssd_chunk_scan_workspace_bytes(1, 65536, 8, 64, 2, 128, 128, 1, 0)
     assert need > 0
     assert call_scan(scan_args(B=1, L=65536)) == WORKSPACE
     assert call_scan(scan_args(B=1, L=65536, ws=ctypes.c_void_p(1 << 47), wsb=need - 1)) == WORKSPACE

@@ -175,7 +175,7 @@ def test_sequence_split_segments(fused):
     into segments (state-only pass, segment combine, full pass)."""
     inp = small(1, 128 * 40 + 17, 4, 2, "bf16", seed=11)
     wl = inp.wl
-    need = ssd.ssd_chunk_scan_workspace_bytes(1, wl.seqlen, 4, ngroups=2)
+    need = ssd.ssd_chunk_scan_workspace_bytes(1, wl.seqlen, 4, ngroups=2, fused_conv=fused)
     assert need > 0, "this shape should be split"
     say("segments fused=%s ws=%d" % (fused, need))
     for probe in (False, True):
