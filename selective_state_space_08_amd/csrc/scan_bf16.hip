@@ -8,16 +8,19 @@
 //   Y      = (C B^T o exp(Lam_t - Lam_s) delta_s [s <= t]) X + diag(exp Lam) C H^T
 //   H_next = exp(Lam_last) H + (X o w)^T B,  w_s = exp(Lam_last - Lam_s) delta_s
 //   out    = (Y + D x) * silu(z)
-// All products are 32x32x16 bf16 MFMAs with fp32 accumulation.  The chunk
+// All products are 16x16x32 bf16 MFMAs with fp32 accumulation.  The chunk
 // state product, whose result is carried across the whole sequence, splits
 // both operands into bf16 hi + lo parts and sums hi*hi + hi*lo + lo*hi, so
 // the carried state keeps ~16 mantissa bits instead of 8.
 //
-// One workgroup ("walker", 4 waves) owns one (sequence, head) -- or one
-// segment of it, see below -- and walks its chunks in order, carrying the
-// fp32 state H [64 x 128] in MFMA accumulator registers, so no state goes to
-// HBM between chunks.  Wave w owns output rows [32w, 32w+32) of the chunk and
-// the state tile rows p in [32(w/2), +32), columns n in [64(w%2), +64).
+// One workgroup ("walker", 8 waves, two per SIMD so that each hides the
+// other's LDS, matrix-core and memory latency) owns one (sequence, head) --
+// or one segment of it, see below -- and walks its chunks in order, carrying
+// the fp32 state H [64 x 128] in MFMA accumulator registers, so no state goes
+// to HBM between chunks.  Wave w owns the 16 output rows of row tile
+// rt(w) = w < 4 ? w : 11 - w (the two waves of a SIMD together own tiles
+// i and 7 - i, which balances the causal triangle of C B^T) and the 16 state
+// columns n in [16 w, 16 w + 16).
 //
 // LDS per walker (~151 KiB of gfx950's 160 KiB): B and x of the chunk in
 // fp32 (the bf16 operands and their hi/lo parts are formed on the fly), C and
@@ -25,9 +28,9 @@
 //
 // The decayed C B^T tile never touches LDS: it is produced as the transpose
 // (B C^T, rows s, columns t) so that each lane's accumulator column is one
-// output row t; after masking and decay the 16 values a lane holds are
-// exactly its A-operand for two K=16 steps of M X, with the K index permuted
-// the same way on the X side.
+// output row t; after masking and decay, the 4 values a lane holds from each
+// of two neighbouring 16-token tiles are exactly its 8 A-operand values for
+// one K=32 step of M X, with the K index permuted the same way on the X side.
 //
 // Low (batch x heads) counts are split along the sequence: pass 1 runs the
 // state-only walker on segments 0..S-2 from a zero state, a small combine
@@ -47,17 +50,19 @@ namespace {
 constexpr int Q = 128;
 constexpr int P = 64;
 constexpr int N = 128;
-constexpr int THREADS = 256;
+constexpr int THREADS = 512;  // 8 waves
 constexpr int NXCD = 8;
 constexpr int LDB = N + 8;     // bf16 row stride of sC, sH (272 B: 16-B row reads conflict-free)
 constexpr int LDB32 = N + 4;   // fp32 row stride of sB32 (528 B)
 constexpr int LDX32 = Q + 4;   // fp32 row stride of sX32 [p][t] (528 B)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+// D = A B + C for a 16x16 tile, K = 32.  Lane l = i + 16 q holds A[i][8q..8q+7],
+// B[8q..8q+7][j = l % 16] and D[4q..4q+3][j = l % 16].
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8 lds8(const bf16* p) {
@@ -218,47 +223,47 @@ __device__ __forceinline__ void copy_rows_to(const ScanArgs& a, const RowLoad<Tx
 }
 
 // One chunk's B, C and x for the whole workgroup: thread (cv = tid % 16,
-// rg = tid / 16) owns rows [8 rg, 8 rg + 8) x channels [8 cv, 8 cv + 8) of B
+// rg = tid / 16) owns rows [4 rg, 4 rg + 4) x channels [8 cv, 8 cv + 8) of B
 // and of C (post-conv values of type Tbc); thread (xv = tid % 8, xr = tid / 8)
-// owns rows [4 xr, 4 xr + 4) x channels [8 xv, 8 xv + 8) of x (raw values of
+// owns rows [2 xr, 2 xr + 2) x channels [8 xv, 8 xv + 8) of x (raw values of
 // type Tx with 3 rows of history in front when XCONV, post-conv otherwise).
 template <typename Tx, typename Tbc, bool XCONV, bool WITH_C>
 struct ChunkStage {
   static constexpr int HX = XCONV ? 3 : 0;
-  RowLoad<Tbc, 8> rb;
-  RowLoad<Tbc, WITH_C ? 8 : 1> rc;
-  RowLoad<Tx, 4 + HX> rx;
+  RowLoad<Tbc, 4> rb;
+  RowLoad<Tbc, WITH_C ? 4 : 1> rc;
+  RowLoad<Tx, 2 + HX> rx;
 
   __device__ __forceinline__ void load(const ScanArgs& a, int b, int h, int g, int t0) {
     const int tid = threadIdx.x;
     const int cv = tid & 15, rg = tid >> 4, xv = tid & 7, xr = tid >> 3;
     const int cdim = a.nheads * P + 2 * a.ngroups * N;
     rb.load(a, static_cast<const Tbc*>(a.Bm), a.b_stride, g * N + 8 * cv, 0, cdim, b,
-            t0 + 8 * rg);
+            t0 + 4 * rg);
     if constexpr (WITH_C)
       rc.load(a, static_cast<const Tbc*>(a.Cm), a.c_stride, g * N + 8 * cv, 0, cdim, b,
-              t0 + 8 * rg);
+              t0 + 4 * rg);
     rx.load(a, static_cast<const Tx*>(a.x), a.x_stride, h * P + 8 * xv, h * P + 8 * xv, cdim, b,
-            t0 + 4 * xr - HX);
+            t0 + 2 * xr - HX);
   }
 
   __device__ __forceinline__ void store(const ScanArgs& a, int h, int t0, int Lc, float* sB32,
                                         bf16* sC, float* sX32) const {
     const int tid = threadIdx.x;
     const int cv = tid & 15, rg = tid >> 4, xv = tid & 7, xr = tid >> 3;
-    copy_rows_to<Tbc, 8>(a, rb, t0 + 8 * rg, 8 * rg, Lc, sB32 + (8 * rg) * LDB32 + 8 * cv, LDB32);
+    copy_rows_to<Tbc, 4>(a, rb, t0 + 4 * rg, 4 * rg, Lc, sB32 + (4 * rg) * LDB32 + 8 * cv, LDB32);
     if constexpr (WITH_C)
-      copy_rows_to<Tbc, 8>(a, rc, t0 + 8 * rg, 8 * rg, Lc, sC + (8 * rg) * LDB + 8 * cv, LDB);
-    // x: 4 rows x 8 channels, transposed into sX32[p][t]
-    float tmp[4 * 8];
+      copy_rows_to<Tbc, 4>(a, rc, t0 + 4 * rg, 4 * rg, Lc, sC + (4 * rg) * LDB + 8 * cv, LDB);
+    // x: 2 rows x 8 channels, transposed into sX32[p][t]
+    float tmp[2 * 8];
     if constexpr (XCONV)
-      conv_rows_to<Tx, 4>(a, rx, t0 + 4 * xr - 3, h * P + 8 * xv, 4 * xr, Lc, tmp, 8);
+      conv_rows_to<Tx, 2>(a, rx, t0 + 2 * xr - 3, h * P + 8 * xv, 2 * xr, Lc, tmp, 8);
     else
-      copy_rows_to<Tx, 4>(a, rx, t0 + 4 * xr, 4 * xr, Lc, tmp, 8);
+      copy_rows_to<Tx, 2>(a, rx, t0 + 2 * xr, 2 * xr, Lc, tmp, 8);
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      *reinterpret_cast<float4*>(sX32 + (8 * xv + e) * LDX32 + 4 * xr) =
-          make_float4(tmp[e], tmp[8 + e], tmp[16 + e], tmp[24 + e]);
+      *reinterpret_cast<float2*>(sX32 + (8 * xv + e) * LDX32 + 2 * xr) =
+          make_float2(tmp[e], tmp[8 + e]);
   }
 };
 
@@ -326,15 +331,14 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
   const int cend = min(nc, cbeg + a.seg_chunks);
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
-  const int pt = w >> 1, nt0 = 2 * (w & 1);
+  const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, q = lane >> 4;
+  const int rt = w < 4 ? w : 11 - w;  // output row tile: rows [16 rt, 16 rt + 16)
+  const int ncol = 16 * w + l16;      // state column n of this lane
   const float Ah = a.A[h];
   const float Dh = a.D ? a.D[h] : 0.f;
-
   const Tx* xg = static_cast<const Tx*>(a.x);
 
-  // ---- incoming state: accumulator element r of tile j is
-  //      (p = 32 pt + 8 (r/4) + 4 hf + r%4, n = 32 (nt0 + j) + l32)
+  // ---- incoming state: element r of hacc[pt] is (p = 16 pt + 4 q + r, n = ncol)
   const float* h_in = nullptr;
   if (!STATE_ONLY) {
     if (a.nseg > 1)
@@ -342,24 +346,15 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     else
       h_in = a.initial_state ? a.initial_state + (int64_t)bh * P * N : nullptr;
   }
-  f32x16 hacc[2];
+  f32x4 hacc[4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int p = 32 * pt + 8 * (r >> 2) + 4 * hf + (r & 3);
-      const int n = 32 * (nt0 + j) + l32;
-      hacc[j][r] = h_in ? h_in[p * N + n] : 0.f;
+    for (int r = 0; r < 4; ++r) {
+      const int p = 16 * pt + 4 * q + r;
+      hacc[pt][r] = h_in ? h_in[p * N + ncol] : 0.f;
+      if (!STATE_ONLY) sH[p * LDB + ncol] = (bf16)hacc[pt][r];
     }
-  if (!STATE_ONLY) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int p = 32 * pt + 8 * (r >> 2) + 4 * hf + (r & 3);
-        sH[p * LDB + 32 * (nt0 + j) + l32] = (bf16)hacc[j][r];
-      }
-  }
   float log_decay = 0.f;  // sum of delta*A over the segment (state-only pass)
 
   for (int c = cbeg; c < cend; ++c) {
@@ -378,18 +373,17 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
       sLam[tid] = d * Ah;
     }
     stage.store(a, h, t0, Lc, sB32, sC, sX32);
-    // z in the accumulator layout: element (j, r) is
-    // (t = 32 w + 8 (r/4) + 4 hf + r%4, p = 32 j + l32); rows past the end
-    // re-read the last row and are never stored
-    float zr[2][16];
+    // z in the accumulator layout: zr[pj][r] is (t = 16 rt + 4 q + r,
+    // p = 16 pj + l16); rows past the end re-read the last row, never stored
+    float zr[4][4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int pj = 0; pj < 4; ++pj)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = min(32 * w + 8 * (r >> 2) + 4 * hf + (r & 3), Lc - 1);
-        zr[j][r] = (!STATE_ONLY && a.z != nullptr)
-                       ? ld1<Ta>(a.z, (row0 + t) * a.z_stride + h * P + 32 * j + l32)
-                       : 0.f;
+      for (int r = 0; r < 4; ++r) {
+        const int t = min(16 * rt + 4 * q + r, Lc - 1);
+        zr[pj][r] = (!STATE_ONLY && a.z != nullptr)
+                        ? ld1<Ta>(a.z, (row0 + t) * a.z_stride + h * P + 16 * pj + l16)
+                        : 0.f;
       }
     __syncthreads();
     scan_lam(sLam, sRed);
@@ -399,117 +393,113 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     __syncthreads();
 
     if (!STATE_ONLY) {
-      // ---- inter-chunk read-out: Y = diag(exp Lam) C H^T
-      f32x16 yacc[2] = {};
-      const bf16* crow = sC + (32 * w + l32) * LDB + 8 * hf;
+      // ---- inter-chunk read-out: Y = diag(exp Lam) C H^T;
+      //      element r of yacc[pj] is (t = 16 rt + 4 q + r, p = 16 pj + l16)
+      f32x4 yacc[4] = {};
+      const bf16* crow = sC + (16 * rt + l16) * LDB + 8 * q;
 #pragma unroll
-      for (int kk = 0; kk < N / 16; ++kk) {
-        const bf16x8 af = lds8(crow + 16 * kk);
+      for (int kk = 0; kk < N / 32; ++kk) {
+        const bf16x8 af = lds8(crow + 32 * kk);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          yacc[j] = mfma(af, lds8(sH + (32 * j + l32) * LDB + 16 * kk + 8 * hf), yacc[j]);
+        for (int pj = 0; pj < 4; ++pj)
+          yacc[pj] = mfma(af, lds8(sH + (16 * pj + l16) * LDB + 32 * kk + 8 * q), yacc[pj]);
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __expf(sLam[32 * w + 8 * (r >> 2) + 4 * hf + (r & 3)]);
-        yacc[0][r] *= e;
-        yacc[1][r] *= e;
+      for (int r = 0; r < 4; ++r) {
+        const float e = __expf(sLam[16 * rt + 4 * q + r]);
+#pragma unroll
+        for (int pj = 0; pj < 4; ++pj) yacc[pj][r] *= e;
       }
 
-      // ---- intra-chunk: Y += (C B^T o decay mask) X, tile by tile below the diagonal
-      const int tcol = 32 * w + l32;
+      // ---- intra-chunk: Y += (C B^T o decay mask) X over the source tiles
+      //      u <= rt, two 16-token tiles per K=32 step
+      const int tcol = 16 * rt + l16;
       const float lam_t = sLam[tcol];
-      for (int u = 0; u <= w; ++u) {
-        f32x16 cb = {};
-        const float* brow = sB32 + (32 * u + l32) * LDB32 + 8 * hf;
+      for (int u0 = 0; u0 <= rt; u0 += 2) {
+        bf16x8 mf;
 #pragma unroll
-        for (int kk = 0; kk < N / 16; ++kk) {
-          const float4* bp = reinterpret_cast<const float4*>(brow + 16 * kk);
-          cb = mfma(to_bf16x8(bp[0], bp[1]), lds8(crow + 16 * kk), cb);
-        }
-        // cb[r] = (B C^T)[s][t], s = 32u + 8(r/4) + 4hf + r%4, t = tcol
-        bf16x8 mf[2];
+        for (int half = 0; half < 2; ++half) {
+          const int u = u0 + half;
+          f32x4 cb = {};
+          if (u <= rt) {
+            const float* brow = sB32 + (16 * u + l16) * LDB32 + 8 * q;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int s = 32 * u + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const float m = s <= tcol ? cb[r] * __expf(lam_t - sLam[s]) * sDel[s] : 0.f;
-          mf[r >> 3][r & 7] = (bf16)m;
-        }
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const int sb = 32 * u + 16 * k2 + 4 * hf;
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const float* xp = sX32 + (32 * j + l32) * LDX32 + sb;
-            const bf16x8 xf = to_bf16x8(*reinterpret_cast<const float4*>(xp),
-                                        *reinterpret_cast<const float4*>(xp + 8));
-            yacc[j] = mfma(mf[k2], xf, yacc[j]);
+            for (int kk = 0; kk < N / 32; ++kk) {
+              const float4* bp = reinterpret_cast<const float4*>(brow + 32 * kk);
+              cb = mfma(to_bf16x8(bp[0], bp[1]), lds8(crow + 32 * kk), cb);
+            }
           }
+          // cb[r] = (B C^T)[s = 16 u + 4 q + r][t = tcol]
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int s = 16 * u + 4 * q + r;
+            const float m = (u <= rt && s <= tcol) ? cb[r] * __expf(lam_t - sLam[s]) * sDel[s] : 0.f;
+            mf[4 * half + r] = (bf16)m;
+          }
+        }
+#pragma unroll
+        for (int pj = 0; pj < 4; ++pj) {
+          const float* xp = sX32 + (16 * pj + l16) * LDX32 + 4 * q;
+          const bf16x8 xf = to_bf16x8(*reinterpret_cast<const float4*>(xp + 16 * u0),
+                                      *reinterpret_cast<const float4*>(xp + 16 * u0 + 16));
+          yacc[pj] = mfma(mf, xf, yacc[pj]);
         }
       }
 
       // ---- epilogue: skip, gate, store
       Ty* yg = static_cast<Ty*>(a.y);
+      const int tb = 16 * rt + 4 * q;
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int pj = 0; pj < 4; ++pj) {
+        const float4 xq = *reinterpret_cast<const float4*>(sX32 + (16 * pj + l16) * LDX32 + tb);
+        const float xs[4] = {xq.x, xq.y, xq.z, xq.w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int tb = 32 * w + 8 * q + 4 * hf;
-          const float4 xq = *reinterpret_cast<const float4*>(sX32 + (32 * j + l32) * LDX32 + tb);
-          const float xs[4] = {xq.x, xq.y, xq.z, xq.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int t = tb + e, r = 4 * q + e;
-            if (t < Lc) {
-              float yv = yacc[j][r] + Dh * xs[e];
-              if (a.z != nullptr) yv *= silu_f32(zr[j][r]);
-              yg[(row0 + t) * a.y_stride + h * P + 32 * j + l32] = from_f32<Ty>(yv);
-            }
+        for (int r = 0; r < 4; ++r) {
+          if (tb + r < Lc) {
+            float yv = yacc[pj][r] + Dh * xs[r];
+            if (a.z != nullptr) yv *= silu_f32(zr[pj][r]);
+            yg[(row0 + tb + r) * a.y_stride + h * P + 16 * pj + l16] = from_f32<Ty>(yv);
           }
         }
+      }
       __syncthreads();  // every wave is done reading sH
     }
 
-    // ---- state: H <- exp(Lam_last) H + (X o w)^T B, operands split hi + lo
+    // ---- state: H <- exp(Lam_last) H + (X o w)^T B, operands split hi + lo;
+    //      this wave's columns n = 16 w + l16, all 64 rows p
     const float gamma = __expf(lam_last);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) hacc[j] *= gamma;
-    const float* xrow = sX32 + (32 * pt + l32) * LDX32;
-#pragma unroll 2
-    for (int kk = 0; kk < Q / 16; ++kk) {
-      const int s0 = 16 * kk + 8 * hf;
-      float xw[8];
-      {
-        const float4 x0 = *reinterpret_cast<const float4*>(xrow + s0);
-        const float4 x1 = *reinterpret_cast<const float4*>(xrow + s0 + 4);
-        const float4 w0 = *reinterpret_cast<const float4*>(sW + s0);
-        const float4 w1 = *reinterpret_cast<const float4*>(sW + s0 + 4);
-        xw[0] = x0.x * w0.x; xw[1] = x0.y * w0.y; xw[2] = x0.z * w0.z; xw[3] = x0.w * w0.w;
-        xw[4] = x1.x * w1.x; xw[5] = x1.y * w1.y; xw[6] = x1.z * w1.z; xw[7] = x1.w * w1.w;
-      }
-      bf16x8 ah, al;
-      split8(xw, ah, al);
+    for (int pt = 0; pt < 4; ++pt) hacc[pt] *= gamma;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const float* bc = sB32 + s0 * LDB32 + 32 * (nt0 + j) + l32;
-        float bv[8];
+    for (int kk = 0; kk < Q / 32; ++kk) {
+      const int s0 = 32 * kk + 8 * q;
+      float bv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) bv[e] = bc[e * LDB32];
-        bf16x8 bhi, blo;
-        split8(bv, bhi, blo);
-        hacc[j] = mfma(ah, bhi, hacc[j]);
-        hacc[j] = mfma(ah, blo, hacc[j]);
-        hacc[j] = mfma(al, bhi, hacc[j]);
+      for (int e = 0; e < 8; ++e) bv[e] = sB32[(s0 + e) * LDB32 + ncol];
+      bf16x8 bhi, blo;
+      split8(bv, bhi, blo);
+      const float4 w0 = *reinterpret_cast<const float4*>(sW + s0);
+      const float4 w1 = *reinterpret_cast<const float4*>(sW + s0 + 4);
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        const float* xr = sX32 + (16 * pt + l16) * LDX32 + s0;
+        const float4 x0 = *reinterpret_cast<const float4*>(xr);
+        const float4 x1 = *reinterpret_cast<const float4*>(xr + 4);
+        const float xw[8] = {x0.x * w0.x, x0.y * w0.y, x0.z * w0.z, x0.w * w0.w,
+                             x1.x * w1.x, x1.y * w1.y, x1.z * w1.z, x1.w * w1.w};
+        bf16x8 ahi, alo;
+        split8(xw, ahi, alo);
+        hacc[pt] = mfma(ahi, bhi, hacc[pt]);
+        hacc[pt] = mfma(ahi, blo, hacc[pt]);
+        hacc[pt] = mfma(alo, bhi, hacc[pt]);
       }
     }
     if (!STATE_ONLY) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int p = 32 * pt + 8 * (r >> 2) + 4 * hf + (r & 3);
-          sH[p * LDB + 32 * (nt0 + j) + l32] = (bf16)hacc[j][r];
-        }
+        for (int r = 0; r < 4; ++r)
+          sH[(16 * pt + 4 * q + r) * LDB + ncol] = (bf16)hacc[pt][r];
     }
   }
 
@@ -521,12 +511,9 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     h_out = a.final_state ? a.final_state + (int64_t)bh * P * N : nullptr;
   if (h_out != nullptr) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int p = 32 * pt + 8 * (r >> 2) + 4 * hf + (r & 3);
-        h_out[p * N + 32 * (nt0 + j) + l32] = hacc[j][r];
-      }
+      for (int r = 0; r < 4; ++r) h_out[(16 * pt + 4 * q + r) * N + ncol] = hacc[pt][r];
   }
   if (STATE_ONLY && tid == 0) a.seg_logdecay[(int64_t)bh * a.nseg + seg] = log_decay;
 
