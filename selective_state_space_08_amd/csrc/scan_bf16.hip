@@ -167,23 +167,23 @@ struct RowLoad {
 };
 
 // Depthwise conv + SiLU of R consecutive rows of 8 channels from R + 3 raw
-// rows (the first 3 are the history in front); row i goes to dst + i * ld
-// (stride ld, or a transposed float4 column when TRANSPOSE), zero for rows
-// >= nvalid.
+// rows (the first 3 are the history in front); row i goes to dst + i * ld,
+// zero for rows >= nvalid.  cw is the conv of the workgroup's channels in
+// LDS: tap j of local channel c at cw[j * P + c] (taps right-aligned, zero in
+// front when the width is below 4), the bias at cw[4 * P + c]; cl is the
+// local channel of the first of the 8.
 template <typename Tx, int R, typename Td>
 __device__ __forceinline__ void conv_rows_to(const ScanArgs& a, const RowLoad<Tx, R + 3>& rl,
-                                             int tstart, int c0, int rfirst, int nvalid,
-                                             Td* dst, int ld) {
-  const int K = a.conv_k;
+                                             int tstart, const float* cw, int cl, int rfirst,
+                                             int nvalid, Td* dst, int ld) {
   float w4[4][8], bv[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    bv[e] = a.conv_b ? a.conv_b[c0 + e] : 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = j - (4 - K);
-      w4[j][e] = k >= 0 ? a.conv_w[(int64_t)(c0 + e) * K + k] : 0.f;
-    }
+  for (int j = 0; j < 5; ++j) {
+    const float4 lo = *reinterpret_cast<const float4*>(cw + j * P + cl);
+    const float4 hi = *reinterpret_cast<const float4*>(cw + j * P + cl + 4);
+    float* d = j < 4 ? w4[j] : bv;
+    d[0] = lo.x; d[1] = lo.y; d[2] = lo.z; d[3] = lo.w;
+    d[4] = hi.x; d[5] = hi.y; d[6] = hi.z; d[7] = hi.w;
   }
   float win[3][8];
   rl.get(a, tstart, 0, win[0]);
@@ -222,42 +222,59 @@ __device__ __forceinline__ void copy_rows_to(const ScanArgs& a, const RowLoad<Tx
   }
 }
 
-// One chunk's B, C and x for the whole workgroup: thread (cv = tid % 16,
+// One chunk's B and C for the whole workgroup: thread (cv = tid % 16,
 // rg = tid / 16) owns rows [4 rg, 4 rg + 4) x channels [8 cv, 8 cv + 8) of B
-// and of C (post-conv values of type Tbc); thread (xv = tid % 8, xr = tid / 8)
-// owns rows [2 xr, 2 xr + 2) x channels [8 xv, 8 xv + 8) of x (raw values of
-// type Tx with 3 rows of history in front when XCONV, post-conv otherwise).
-template <typename Tx, typename Tbc, bool XCONV, bool WITH_C>
-struct ChunkStage {
-  static constexpr int HX = XCONV ? 3 : 0;
+// and of C (post-conv values of type Tbc).
+template <typename Tbc, bool WITH_C>
+struct StageBC {
   RowLoad<Tbc, 4> rb;
   RowLoad<Tbc, WITH_C ? 4 : 1> rc;
-  RowLoad<Tx, 2 + HX> rx;
 
-  __device__ __forceinline__ void load(const ScanArgs& a, int b, int h, int g, int t0) {
+  __device__ __forceinline__ void load(const ScanArgs& a, int b, int g, int t0) {
     const int tid = threadIdx.x;
-    const int cv = tid & 15, rg = tid >> 4, xv = tid & 7, xr = tid >> 3;
+    const int cv = tid & 15, rg = tid >> 4;
     const int cdim = a.nheads * P + 2 * a.ngroups * N;
     rb.load(a, static_cast<const Tbc*>(a.Bm), a.b_stride, g * N + 8 * cv, 0, cdim, b,
             t0 + 4 * rg);
     if constexpr (WITH_C)
       rc.load(a, static_cast<const Tbc*>(a.Cm), a.c_stride, g * N + 8 * cv, 0, cdim, b,
               t0 + 4 * rg);
+  }
+
+  __device__ __forceinline__ void store(const ScanArgs& a, int t0, int Lc, float* sB32,
+                                        bf16* sC) const {
+    const int tid = threadIdx.x;
+    const int cv = tid & 15, rg = tid >> 4;
+    copy_rows_to<Tbc, 4>(a, rb, t0 + 4 * rg, 4 * rg, Lc, sB32 + (4 * rg) * LDB32 + 8 * cv, LDB32);
+    if constexpr (WITH_C)
+      copy_rows_to<Tbc, 4>(a, rc, t0 + 4 * rg, 4 * rg, Lc, sC + (4 * rg) * LDB + 8 * cv, LDB);
+  }
+};
+
+// One chunk's x for the whole workgroup: thread (xv = tid % 8, xr = tid / 8)
+// owns rows [2 xr, 2 xr + 2) x channels [8 xv, 8 xv + 8) (raw values of type
+// Tx with 3 rows of history in front when XCONV, post-conv otherwise).
+template <typename Tx, bool XCONV>
+struct StageX {
+  static constexpr int HX = XCONV ? 3 : 0;
+  RowLoad<Tx, 2 + HX> rx;
+
+  __device__ __forceinline__ void load(const ScanArgs& a, int b, int h, int t0) {
+    const int tid = threadIdx.x;
+    const int xv = tid & 7, xr = tid >> 3;
+    const int cdim = a.nheads * P + 2 * a.ngroups * N;
     rx.load(a, static_cast<const Tx*>(a.x), a.x_stride, h * P + 8 * xv, h * P + 8 * xv, cdim, b,
             t0 + 2 * xr - HX);
   }
 
-  __device__ __forceinline__ void store(const ScanArgs& a, int h, int t0, int Lc, float* sB32,
-                                        bf16* sC, float* sX32) const {
+  // 2 rows x 8 channels, transposed into sX32[p][t]
+  __device__ __forceinline__ void store(const ScanArgs& a, const float* cw, int t0, int Lc,
+                                        float* sX32) const {
     const int tid = threadIdx.x;
-    const int cv = tid & 15, rg = tid >> 4, xv = tid & 7, xr = tid >> 3;
-    copy_rows_to<Tbc, 4>(a, rb, t0 + 4 * rg, 4 * rg, Lc, sB32 + (4 * rg) * LDB32 + 8 * cv, LDB32);
-    if constexpr (WITH_C)
-      copy_rows_to<Tbc, 4>(a, rc, t0 + 4 * rg, 4 * rg, Lc, sC + (4 * rg) * LDB + 8 * cv, LDB);
-    // x: 2 rows x 8 channels, transposed into sX32[p][t]
+    const int xv = tid & 7, xr = tid >> 3;
     float tmp[2 * 8];
     if constexpr (XCONV)
-      conv_rows_to<Tx, 2>(a, rx, t0 + 2 * xr - 3, h * P + 8 * xv, 2 * xr, Lc, tmp, 8);
+      conv_rows_to<Tx, 2>(a, rx, t0 + 2 * xr - 3, cw, 8 * xv, 2 * xr, Lc, tmp, 8);
     else
       copy_rows_to<Tx, 2>(a, rx, t0 + 2 * xr, 2 * xr, Lc, tmp, 8);
 #pragma unroll
@@ -317,6 +334,7 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) float sDel[Q];
   __shared__ __attribute__((aligned(16))) float sW[Q];
   __shared__ float sRed[4];
+  __shared__ __attribute__((aligned(16))) float sCw[XCONV ? 5 * P : 4];  // x-channel conv
 
   const int H = a.nheads, G = a.ngroups, L = a.seqlen;
   // pass 1 (state-only) walks segments 0..nseg-2, pass 2 all segments
@@ -356,23 +374,48 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
       if (!STATE_ONLY) sH[p * LDB + ncol] = (bf16)hacc[pt][r];
     }
   float log_decay = 0.f;  // sum of delta*A over the segment (state-only pass)
+  if (XCONV && tid < P) {
+    // the conv of this head's x channels: read at every chunk from LDS (the
+    // first read follows the barrier at the top of the chunk loop)
+    const int K = a.conv_k;
+    const int64_t ch = (int64_t)h * P + tid;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = j - (4 - K);
+      sCw[j * P + tid] = k >= 0 ? a.conv_w[ch * K + k] : 0.f;
+    }
+    sCw[4 * P + tid] = a.conv_b ? a.conv_b[ch] : 0.f;
+  }
+
+  // Chunk c+1's x and dt are loaded as soon as chunk c is in LDS, so they are
+  // in flight while chunk c is computed.  B and C, which the heads of a group
+  // share through L2, are loaded at the top of their own chunk, and z after
+  // the staging, ahead of its use in the epilogue.
+  StageX<Tx, XCONV> sx;
+  float dtv = 0.f;
+  auto prefetch = [&](int cc) {
+    const int tt0 = cc * Q;
+    sx.load(a, b, h, tt0);
+    if (tid < Q)
+      dtv = ld1<Ta>(a.dt, ((int64_t)b * L + min(tt0 + tid, L - 1)) * a.dt_stride + h);
+  };
+  if (cbeg < cend) prefetch(cbeg);
 
   for (int c = cbeg; c < cend; ++c) {
     const int t0 = c * Q;
     const int Lc = min(Q, L - t0);
     const int64_t row0 = (int64_t)b * L + t0;
-    // every global load of the chunk is issued before anything waits on one
-    ChunkStage<Tx, Tbc, XCONV, !STATE_ONLY> stage;
-    stage.load(a, b, h, g, t0);
-    float dtv = 0.f;
-    if (tid < Q) dtv = ld1<Ta>(a.dt, (row0 + min(tid, Lc - 1)) * a.dt_stride + h);
+    StageBC<Tbc, !STATE_ONLY> sbc;
+    sbc.load(a, b, g, t0);
     __syncthreads();  // the previous chunk is done with every LDS buffer
     if (tid < Q) {
       const float d = tid < Lc ? make_delta(dtv, a.dt_bias, h, a.dt_softplus) : 0.f;
       sDel[tid] = d;
       sLam[tid] = d * Ah;
     }
-    stage.store(a, h, t0, Lc, sB32, sC, sX32);
+    sx.store(a, sCw, t0, Lc, sX32);
+    sbc.store(a, t0, Lc, sB32, sC);
+    if (c + 1 < cend) prefetch(c + 1);
     // z in the accumulator layout: zr[pj][r] is (t = 16 rt + 4 q + r,
     // p = 16 pj + l16); rows past the end re-read the last row, never stored
     float zr[4][4];
