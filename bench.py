@@ -183,6 +183,25 @@ def time_decode(args, wl, torch, layer, synth, dev, dev32):
     return dict(chain_ms=total_ms, step_ms=total_ms / T, first10_ms=first, last10_ms=last)
 
 
+def calibrate_copy(torch, ssd, reps: int = 3):
+    """A plain copy kernel of known size for scaling the HBM byte counters:
+    ssd_chunk_scan_fwd on an empty sequence copies initial_state to
+    final_state (the library's copy_or_zero_kernel) and does nothing else."""
+    B, H, P, N = 256, 128, 64, 128
+    nbytes = B * H * P * N * 4
+    h0 = torch.randn((B, H, P, N), device="cuda")
+    hT = torch.empty_like(h0)
+    x = torch.empty((B, 0, H, P), dtype=torch.bfloat16, device="cuda")
+    bc = torch.empty((B, 0, 1, N), dtype=torch.bfloat16, device="cuda")
+    dt = torch.empty((B, 0, H), dtype=torch.bfloat16, device="cuda")
+    A = -torch.ones(H, device="cuda")
+    for _ in range(reps):
+        ssd.ssd_chunk_scan_fwd(x, bc, bc, dt, A, initial_state=h0, final_state=hT)
+    torch.cuda.synchronize()
+    assert torch.equal(hT, h0)
+    return nbytes
+
+
 def cpu_baseline(wl, budget_s: float):
     """The fp64 oracle on a bounded sample of the prefill workload: whole
     sequences of sampled (sequence, head) pairs, conv included."""
@@ -223,6 +242,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--unfused", action="store_true",
                     help="conv kernel + scan kernel instead of the fused scan")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain copy kernel of known size (for scaling the HBM "
+                         "byte counters of a rocprofv3 --pmc run) and print its size")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -240,6 +262,11 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     ssd.load()
+    if args.calibrate_copy:
+        nbytes = calibrate_copy(torch, ssd)
+        print(json.dumps({"calibration": "copy_or_zero_kernel", "bytes_read": nbytes,
+                          "bytes_written": nbytes}), flush=True)
+        return
     wl = WORKLOADS[PREFILL_MAIN]
     pre = time_prefill(args, wl, torch, layer, synth, dev, dev32)
     tok_s = wl.tokens / (pre["step_ms"] / 1e3)
@@ -247,8 +274,12 @@ def main():
     fpt = prefill_alg_flops_per_token(wl)
     kernel_ms = pre["median_ms"]
     achieved = bpt * wl.tokens / (kernel_ms / 1e3) / 1e9
-    kfile = ("scan_bf16.hip",) if pre["fused"] else ("scan_bf16.hip", "conv1d.hip")
-    key = "prefill_fused_scan" if pre["fused"] else "prefill_unfused"
+    # The measured unit is one ssd_chunk_scan_fwd call: with the conv fused it
+    # launches causal_conv1d twice (B and C of each group into the fp32
+    # workspace) and then the scan walker; unfused, the step is the conv
+    # kernel over x|B|C followed by the scan walker.
+    kfile = ("scan_bf16.hip", "conv1d.hip", "api.hip")
+    key = "prefill_fused_call" if pre["fused"] else "prefill_unfused_step"
     traffic = traffic_record(key, src_hash(*kfile))
     out = {
         "metric": "Mamba-2 SSD prefill tokens/s + decode steps/s; % of MFMA / HBM peak",
@@ -271,7 +302,11 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": key, "alg_bytes_per_token": bpt,
+                     "kernel": key,
+                     "launches": (["causal_conv1d_kernel (B)", "causal_conv1d_kernel (C)",
+                                   "scan_bf16_kernel"] if pre["fused"] else
+                                  ["causal_conv1d_kernel (x|B|C)", "scan_bf16_kernel"]),
+                     "alg_bytes_per_token": bpt, "tokens_per_launch": wl.tokens,
                      "launch_ms": kernel_ms},
         "mfma": {"alg_flops_per_token": fpt,
                  "achieved_tflops": fpt * wl.tokens / (kernel_ms / 1e3) / 1e12,
@@ -289,6 +324,10 @@ def main():
                          "last10_ms": dec["last10_ms"],
                          "roofline": {"bound": "hbm", "achieved": dach, "peak": HBM_PEAK_GBS,
                                       "unit": "GB/s", "frac": dach / HBM_PEAK_GBS,
+                                      "traffic": traffic_record(
+                                          "decode_state_update",
+                                          src_hash("state_update.hip", "api.hip")),
+                                      "kernel": "state_update_kernel",
                                       "alg_bytes_per_step": dbytes}}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
