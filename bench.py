@@ -184,9 +184,11 @@ def time_decode(args, wl, torch, layer, synth, dev, dev32):
 
 
 def calibrate_copy(torch, ssd, reps: int = 3):
-    """A plain copy kernel of known size for scaling the HBM byte counters:
-    ssd_chunk_scan_fwd on an empty sequence copies initial_state to
-    final_state (the library's copy_or_zero_kernel) and does nothing else."""
+    """A plain copy kernel of known size: ssd_chunk_scan_fwd on an empty
+    sequence copies initial_state to final_state (the library's
+    copy_or_zero_kernel) and does nothing else.  Used for scaling the HBM
+    byte counters, and timed as the measured HBM bandwidth of this GPU.
+    Returns (bytes copied per call, median GB/s of read + write)."""
     B, H, P, N = 256, 128, 64, 128
     nbytes = B * H * P * N * 4
     h0 = torch.randn((B, H, P, N), device="cuda")
@@ -195,11 +197,29 @@ def calibrate_copy(torch, ssd, reps: int = 3):
     bc = torch.empty((B, 0, 1, N), dtype=torch.bfloat16, device="cuda")
     dt = torch.empty((B, 0, H), dtype=torch.bfloat16, device="cuda")
     A = -torch.ones(H, device="cuda")
+    stream = torch.cuda.current_stream()
+    times = []
     for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
         ssd.ssd_chunk_scan_fwd(x, bc, bc, dt, A, initial_state=h0, final_state=hT)
-    torch.cuda.synchronize()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
     assert torch.equal(hT, h0)
-    return nbytes
+    del h0, hT
+    ms = sorted(times)[len(times) // 2]
+    return nbytes, 2 * nbytes / (ms / 1e3) / 1e9
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(wl, budget_s: float):
@@ -226,6 +246,7 @@ def cpu_baseline(wl, budget_s: float):
     frac = done / len(everything)
     tok_s = wl.tokens * frac / elapsed
     return dict(value=tok_s, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                cpu=cpu_model(), host_cpus=os.cpu_count(),
                 sample="%d of %d (sequence, head) pairs of %s, each over all %d tokens with its "
                        "conv channels; %.1f s of oracle time, scaled by the sampled fraction" %
                        (done, len(everything), wl.name, wl.seqlen, elapsed))
@@ -263,10 +284,12 @@ def main():
         sys.exit(1)
     ssd.load()
     if args.calibrate_copy:
-        nbytes = calibrate_copy(torch, ssd)
+        nbytes, gbs = calibrate_copy(torch, ssd)
         print(json.dumps({"calibration": "copy_or_zero_kernel", "bytes_read": nbytes,
-                          "bytes_written": nbytes}), flush=True)
+                          "bytes_written": nbytes, "GB/s": gbs}), flush=True)
         return
+    _, copy_gbs = calibrate_copy(torch, ssd, reps=5)
+    log("copy kernel: %.0f GB/s (read + write)" % copy_gbs)
     wl = WORKLOADS[PREFILL_MAIN]
     pre = time_prefill(args, wl, torch, layer, synth, dev, dev32)
     tok_s = wl.tokens / (pre["step_ms"] / 1e3)
@@ -307,7 +330,8 @@ def main():
                                    "scan_bf16_kernel"] if pre["fused"] else
                                   ["causal_conv1d_kernel (x|B|C)", "scan_bf16_kernel"]),
                      "alg_bytes_per_token": bpt, "tokens_per_launch": wl.tokens,
-                     "launch_ms": kernel_ms},
+                     "launch_ms": kernel_ms, "measured_peak": copy_gbs,
+                     "frac_of_measured": achieved / copy_gbs},
         "mfma": {"alg_flops_per_token": fpt,
                  "achieved_tflops": fpt * wl.tokens / (kernel_ms / 1e3) / 1e12,
                  "peak_tflops": BF16_PEAK_TFLOPS,
@@ -328,6 +352,8 @@ def main():
                                           "decode_state_update",
                                           src_hash("state_update.hip", "api.hip")),
                                       "kernel": "state_update_kernel",
+                                      "measured_peak": copy_gbs,
+                                      "frac_of_measured": dach / copy_gbs,
                                       "alg_bytes_per_step": dbytes}}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
