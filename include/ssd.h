@@ -101,11 +101,14 @@ int ssd_causal_conv1d_fwd(const void* x, int64_t x_tok_stride, ssd_dtype_t x_dty
                           int seqlen, int cdim, int width, int apply_silu,
                           hipStream_t stream);
 
-/* Bytes of device workspace ssd_chunk_scan_fwd needs for this shape (it may be
- * 0); fused_conv is 1 when conv_w will be passed.  The matrix-core path uses
- * it for per-segment states when it splits a long sequence over more
- * workgroups, and, with the conv fused, for the post-conv fp32 B and C
- * (convolved once per group rather than once per head). */
+/* Bytes of device workspace ssd_chunk_scan_fwd needs for this shape (0 for
+ * SSD_MATH_F32 and for empty inputs); fused_conv is 1 when conv_w will be
+ * passed (the size does not depend on it in this version).  The matrix-core
+ * path uses the workspace for B and C of every chunk and group, post-conv, in
+ * the bf16 layouts its products read (8 bytes per token, group and state
+ * column; B and C are convolved and converted once per group rather than once
+ * per head), and for per-segment states when it splits a long sequence over
+ * more workgroups. */
 size_t ssd_chunk_scan_workspace_bytes(int batch, int seqlen, int nheads, int headdim,
                                       int ngroups, int dstate, int chunk,
                                       ssd_math_t math, int fused_conv);

@@ -91,13 +91,12 @@ int plan_segments(int batch, int seqlen, int nheads) {
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Workspace of the matrix-core scan: per-segment states and log decays when
-// the sequence is split, and the post-conv fp32 B|C of the whole input when
-// the conv is fused (B and C are convolved once per group there, rather than
-// once per head inside every walker).
+// the sequence is split, and the B|C pack (B and C of every chunk and group,
+// post-conv, in the bf16 layouts the matrix-core products read).
 struct WsLayout {
   size_t seg_state = 0, seg_ld = 0, bc = 0, total = 0;
 };
-WsLayout ws_layout(int batch, int seqlen, int nheads, int ngroups, int nseg, bool fused_conv) {
+WsLayout ws_layout(int batch, int seqlen, int nheads, int ngroups, int nseg) {
   WsLayout w;
   const size_t bh = (size_t)batch * nheads;
   size_t off = 0;
@@ -106,7 +105,7 @@ WsLayout ws_layout(int batch, int seqlen, int nheads, int ngroups, int nseg, boo
   w.seg_ld = off;
   if (nseg > 1) off += round_up(bh * nseg * sizeof(float), 256);
   w.bc = off;
-  if (fused_conv) off += round_up((size_t)batch * seqlen * 2 * ngroups * kN * sizeof(float), 256);
+  off += round_up(scan_bf16_pack_bytes(batch, seqlen, ngroups), 256);
   w.total = off;
   return w;
 }
@@ -186,12 +185,10 @@ int ssd_causal_conv1d_fwd(const void* x, int64_t x_tok_stride, ssd_dtype_t x_dty
 size_t ssd_chunk_scan_workspace_bytes(int batch, int seqlen, int nheads, int headdim,
                                       int ngroups, int dstate, int chunk, ssd_math_t math,
                                       int fused_conv) {
-  (void)headdim; (void)dstate; (void)chunk;
+  (void)headdim; (void)dstate; (void)chunk; (void)fused_conv;
   if (batch <= 0 || seqlen <= 0 || nheads <= 0 || ngroups <= 0) return 0;
   if (math != SSD_MATH_BF16) return 0;
-  return ws_layout(batch, seqlen, nheads, ngroups, plan_segments(batch, seqlen, nheads),
-                   fused_conv != 0)
-      .total;
+  return ws_layout(batch, seqlen, nheads, ngroups, plan_segments(batch, seqlen, nheads)).total;
 }
 
 int ssd_chunk_scan_fwd(const void* x, int64_t x_tok_stride, const void* Bm,
@@ -282,8 +279,7 @@ int ssd_chunk_scan_fwd(const void* x, int64_t x_tok_stride, const void* Bm,
   // ---- workspace
   const bool mc = math == SSD_MATH_BF16 && rows > 0;
   const int nseg = mc ? plan_segments(batch, seqlen, nheads) : 1;
-  const WsLayout wl = mc ? ws_layout(batch, seqlen, nheads, ngroups, nseg, conv_w != nullptr)
-                         : WsLayout{};
+  const WsLayout wl = mc ? ws_layout(batch, seqlen, nheads, ngroups, nseg) : WsLayout{};
   const size_t ws_need = wl.total;
   if (ws_need > 0) {
     if (workspace == nullptr || workspace_bytes < ws_need)
@@ -330,30 +326,7 @@ int ssd_chunk_scan_fwd(const void* x, int64_t x_tok_stride, const void* Bm,
     a.seg_state = reinterpret_cast<float*>(ws + wl.seg_state);
     a.seg_logdecay = reinterpret_cast<float*>(ws + wl.seg_ld);
   }
-  if (math == SSD_MATH_BF16 && conv_w != nullptr) {
-    // B and C: conv + SiLU once per group into fp32 [B, L, 2*G*N]; the scan
-    // convolves only the x channels itself
-    float* bc = reinterpret_cast<float*>(ws + wl.bc);
-    const int GNi = (int)GN;
-    const size_t hoff = (size_t)HP * xe;
-    e = launch_causal_conv1d(Bm, b_tok_stride, xbc_dtype, conv_w + HP * conv_width,
-                             conv_b ? conv_b + HP : nullptr,
-                             conv_state_in ? static_cast<const char*>(conv_state_in) + hoff : nullptr,
-                             conv_state_out ? static_cast<char*>(conv_state_out) + hoff : nullptr,
-                             cdim, bc, 2 * GN, SSD_F32, batch, seqlen, GNi, conv_width, 1, stream);
-    if (e == hipSuccess)
-      e = launch_causal_conv1d(
-          Cm, c_tok_stride, xbc_dtype, conv_w + (HP + GN) * conv_width,
-          conv_b ? conv_b + HP + GN : nullptr,
-          conv_state_in ? static_cast<const char*>(conv_state_in) + hoff + GN * xe : nullptr,
-          conv_state_out ? static_cast<char*>(conv_state_out) + hoff + GN * xe : nullptr, cdim,
-          bc + GN, 2 * GN, SSD_F32, batch, seqlen, GNi, conv_width, 1, stream);
-    if (e != hipSuccess) return hip_fail(e, "scan: B/C conv launch");
-    a.Bm = bc;
-    a.b_stride = 2 * GN;
-    a.Cm = bc + GN;
-    a.c_stride = 2 * GN;
-  }
+  if (math == SSD_MATH_BF16) a.bc_pack = ws + wl.bc;
   e = math == SSD_MATH_BF16 ? launch_scan_bf16(a, xbc_dtype, act_dtype, y_dtype, stream)
                             : launch_scan_f32(a, xbc_dtype, act_dtype, y_dtype, stream);
   return e == hipSuccess ? SSD_OK : hip_fail(e, "scan launch");

@@ -13,24 +13,31 @@
 // both operands into bf16 hi + lo parts and sums hi*hi + hi*lo + lo*hi, so
 // the carried state keeps ~16 mantissa bits instead of 8.
 //
-// One workgroup ("walker", 8 waves, two per SIMD so that each hides the
-// other's LDS, matrix-core and memory latency) owns one (sequence, head) --
-// or one segment of it, see below -- and walks its chunks in order, carrying
-// the fp32 state H [64 x 128] in MFMA accumulator registers, so no state goes
-// to HBM between chunks.  Wave w owns the 16 output rows of row tile
-// rt(w) = w < 4 ? w : 11 - w (the two waves of a SIMD together own tiles
+// Two kernels:
+//
+// bc_pack_kernel, one workgroup per (sequence, group, chunk), applies the
+// conv + SiLU to B and C once per group (or takes them post-conv) and writes
+// them in the forms the matrix cores read, per chunk: C and B as bf16 [t][n],
+// and B as bf16 hi and lo parts transposed, [n][s].  The heads of a group
+// then read their B and C from this pack (through L2) with 16-byte loads and
+// no conversion work.
+//
+// scan_bf16_kernel ("walker", 8 waves, two per SIMD) owns one (sequence,
+// head) -- or one segment of it, see below -- and walks its chunks in order,
+// carrying the fp32 state H [64 x 128] in MFMA accumulator registers, so no
+// state goes to HBM between chunks.  Wave w owns the 16 output tokens of row
+// tile rt(w) = w < 4 ? w : 11 - w (the two waves of a SIMD together own tiles
 // i and 7 - i, which balances the causal triangle of C B^T) and the 16 state
-// columns n in [16 w, 16 w + 16).
+// columns n in [16 w, 16 w + 16).  Each wave loads the C rows of its tokens
+// and the B columns of its state columns straight into registers; B (as bf16
+// [s][n]), x and H, which every wave reads whole, go through LDS.
 //
-// LDS per walker (~151 KiB of gfx950's 160 KiB): B and x of the chunk in
-// fp32 (the bf16 operands and their hi/lo parts are formed on the fly), C and
-// the bf16 copy of H for the read-out, and the per-token decays.
-//
-// The decayed C B^T tile never touches LDS: it is produced as the transpose
-// (B C^T, rows s, columns t) so that each lane's accumulator column is one
-// output row t; after masking and decay, the 4 values a lane holds from each
-// of two neighbouring 16-token tiles are exactly its 8 A-operand values for
-// one K=32 step of M X, with the K index permuted the same way on the X side.
+// Outputs are produced transposed (Y^T = H C^T + X^T (M)^T, rows p, columns
+// t), so that each lane ends with 4 consecutive channels p of one token: z is
+// read and y written as 4-element vectors.  The masked C B^T tile never
+// touches LDS: it is produced as B C^T (rows s, columns t), whose accumulator
+// layout, after masking and decay, is the B-operand layout of the next
+// product for a K index permuted the same way on the X^T side.
 //
 // Low (batch x heads) counts are split along the sequence: pass 1 runs the
 // state-only walker on segments 0..S-2 from a zero state, a small combine
@@ -45,18 +52,29 @@
 #include "ssd_common.h"
 
 namespace ssd {
+
 namespace {
 
 constexpr int Q = 128;
 constexpr int P = 64;
 constexpr int N = 128;
-constexpr int THREADS = 512;  // 8 waves
+constexpr int THREADS = 512;     // walker: 8 waves
+constexpr int PACK_THREADS = 256;
 constexpr int NXCD = 8;
-constexpr int LDB = N + 8;     // bf16 row stride of sC, sH (272 B: 16-B row reads conflict-free)
-constexpr int LDB32 = N + 4;   // fp32 row stride of sB32 (528 B)
-constexpr int LDX32 = Q + 4;   // fp32 row stride of sX32 [p][t] (528 B)
+constexpr int LDB = N + 8;       // bf16 row stride of [.][n] tiles (272 B)
+constexpr int LDT = Q + 8;       // bf16 row stride of [p][s] tiles (272 B)
+constexpr int LDX = P + 4;       // fp32 row stride of x [t][p] (272 B)
+
+// One (sequence, group, chunk) of the B|C pack, in bf16 elements
+constexpr int PK_C = 0;            // C  [t][n]
+constexpr int PK_BN = Q * N;       // B  [s][n] (hi part)
+constexpr int PK_BTH = 2 * Q * N;  // B  [n][s] hi
+constexpr int PK_BTL = 3 * Q * N;  // B  [n][s] lo
+constexpr int PACK = 4 * Q * N;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // D = A B + C for a 16x16 tile, K = 32.  Lane l = i + 16 q holds A[i][8q..8q+7],
@@ -69,21 +87,14 @@ __device__ __forceinline__ bf16x8 lds8(const bf16* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
-__device__ __forceinline__ bf16x8 to_bf16x8(float4 a, float4 b) {
-  bf16x8 r;
-  r[0] = (bf16)a.x; r[1] = (bf16)a.y; r[2] = (bf16)a.z; r[3] = (bf16)a.w;
-  r[4] = (bf16)b.x; r[5] = (bf16)b.y; r[6] = (bf16)b.z; r[7] = (bf16)b.w;
-  return r;
+__device__ __forceinline__ bf16x8 ldg8(const bf16* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
 }
 
-// v = hi + lo with hi = bf16(v), lo = bf16(v - hi)
-__device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const bf16 h = (bf16)v[e];
-    hi[e] = h;
-    lo[e] = (bf16)(v[e] - (float)h);
-  }
+// hi = bf16(v), lo = bf16(v - hi)
+__device__ __forceinline__ void split1(float v, bf16& hi, bf16& lo) {
+  hi = (bf16)v;
+  lo = (bf16)(v - (float)hi);
 }
 
 // 8 raw elements of one token row, kept packed between load and use
@@ -169,18 +180,19 @@ struct RowLoad {
 // Depthwise conv + SiLU of R consecutive rows of 8 channels from R + 3 raw
 // rows (the first 3 are the history in front); row i goes to dst + i * ld,
 // zero for rows >= nvalid.  cw is the conv of the workgroup's channels in
-// LDS: tap j of local channel c at cw[j * P + c] (taps right-aligned, zero in
-// front when the width is below 4), the bias at cw[4 * P + c]; cl is the
-// local channel of the first of the 8.
+// LDS: tap j of local channel c at cw[j * cws + c] (taps right-aligned, zero
+// in front when the width is below 4), the bias at cw[4 * cws + c]; cl is the
+// local channel of the first of the 8; cws is the stride between taps (the
+// number of channels staged).
 template <typename Tx, int R, typename Td>
 __device__ __forceinline__ void conv_rows_to(const ScanArgs& a, const RowLoad<Tx, R + 3>& rl,
-                                             int tstart, const float* cw, int cl, int rfirst,
-                                             int nvalid, Td* dst, int ld) {
+                                             int tstart, const float* cw, int cws, int cl,
+                                             int rfirst, int nvalid, Td* dst, int ld) {
   float w4[4][8], bv[8];
 #pragma unroll
   for (int j = 0; j < 5; ++j) {
-    const float4 lo = *reinterpret_cast<const float4*>(cw + j * P + cl);
-    const float4 hi = *reinterpret_cast<const float4*>(cw + j * P + cl + 4);
+    const float4 lo = *reinterpret_cast<const float4*>(cw + j * cws + cl);
+    const float4 hi = *reinterpret_cast<const float4*>(cw + j * cws + cl + 4);
     float* d = j < 4 ? w4[j] : bv;
     d[0] = lo.x; d[1] = lo.y; d[2] = lo.z; d[3] = lo.w;
     d[4] = hi.x; d[5] = hi.y; d[6] = hi.z; d[7] = hi.w;
@@ -222,38 +234,137 @@ __device__ __forceinline__ void copy_rows_to(const ScanArgs& a, const RowLoad<Tx
   }
 }
 
-// One chunk's B and C for the whole workgroup: thread (cv = tid % 16,
-// rg = tid / 16) owns rows [4 rg, 4 rg + 4) x channels [8 cv, 8 cv + 8) of B
-// and of C (post-conv values of type Tbc).
-template <typename Tbc, bool WITH_C>
-struct StageBC {
-  RowLoad<Tbc, 4> rb;
-  RowLoad<Tbc, WITH_C ? 4 : 1> rc;
 
-  __device__ __forceinline__ void load(const ScanArgs& a, int b, int g, int t0) {
-    const int tid = threadIdx.x;
-    const int cv = tid & 15, rg = tid >> 4;
-    const int cdim = a.nheads * P + 2 * a.ngroups * N;
-    rb.load(a, static_cast<const Tbc*>(a.Bm), a.b_stride, g * N + 8 * cv, 0, cdim, b,
-            t0 + 4 * rg);
-    if constexpr (WITH_C)
-      rc.load(a, static_cast<const Tbc*>(a.Cm), a.c_stride, g * N + 8 * cv, 0, cdim, b,
-              t0 + 4 * rg);
+// 4 consecutive elements of an activation row, kept packed between load and
+// use (z in the epilogue)
+template <typename T> struct Raw4;
+template <> struct Raw4<bf16> {
+  uint2 u;
+  __device__ __forceinline__ void load(const bf16* p) { u = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ void get(float* v) const {
+    v[0] = __uint_as_float(u.x << 16);
+    v[1] = __uint_as_float(u.x & 0xffff0000u);
+    v[2] = __uint_as_float(u.y << 16);
+    v[3] = __uint_as_float(u.y & 0xffff0000u);
   }
-
-  __device__ __forceinline__ void store(const ScanArgs& a, int t0, int Lc, float* sB32,
-                                        bf16* sC) const {
-    const int tid = threadIdx.x;
-    const int cv = tid & 15, rg = tid >> 4;
-    copy_rows_to<Tbc, 4>(a, rb, t0 + 4 * rg, 4 * rg, Lc, sB32 + (4 * rg) * LDB32 + 8 * cv, LDB32);
-    if constexpr (WITH_C)
-      copy_rows_to<Tbc, 4>(a, rc, t0 + 4 * rg, 4 * rg, Lc, sC + (4 * rg) * LDB + 8 * cv, LDB);
+};
+template <> struct Raw4<float> {
+  float4 f;
+  __device__ __forceinline__ void load(const float* p) { f = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ void get(float* v) const {
+    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
   }
 };
 
+// 4 consecutive outputs of one token
+__device__ __forceinline__ void store4(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store4(bf16* p, const float* v) {
+  bf16x4 r;
+  r[0] = (bf16)v[0]; r[1] = (bf16)v[1]; r[2] = (bf16)v[2]; r[3] = (bf16)v[3];
+  *reinterpret_cast<bf16x4*>(p) = r;
+}
+
+// ------------------------------------------------------------ B|C pack
+
+// One workgroup per (chunk c, group g, sequence b).  Thread (cv = tid % 16,
+// rg = tid / 16) owns channels [8 cv, 8 cv + 8) and tokens [8 rg, 8 rg + 8)
+// of the chunk for B and for C.  Tokens past the end of the sequence are
+// written as zeros.  With the conv, the workgroup of the last chunk also hands
+// the last K-1 raw B and C rows of the group over to conv_state_out.
+template <typename Tin, bool CONV>
+__global__ __launch_bounds__(PACK_THREADS) void bc_pack_kernel(ScanArgs a, bf16* pack) {
+  __shared__ __attribute__((aligned(16))) float sCw[CONV ? 5 * 2 * N : 4];
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int L = a.seqlen, nc = (L + Q - 1) / Q, G = a.ngroups;
+  const int t0 = c * Q, Lc = min(Q, L - t0);
+  const int tid = threadIdx.x, cv = tid & 15, rg = tid >> 4;
+  const int HP = a.nheads * P, GN = G * N, cdim = HP + 2 * GN;
+  bf16* pk = pack + ((int64_t)(b * G + g) * nc + c) * PACK;
+  constexpr int HALO = CONV ? 3 : 0;
+
+  if constexpr (CONV) {
+    // taps of the group's B channels (local 0..N-1) and C channels (N..2N-1)
+    const int K = a.conv_k;
+    const int ch = tid < N ? HP + g * N + tid : HP + GN + g * N + (tid - N);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = j - (4 - K);
+      sCw[j * 2 * N + tid] = k >= 0 ? a.conv_w[(int64_t)ch * K + k] : 0.f;
+    }
+    sCw[4 * 2 * N + tid] = a.conv_b ? a.conv_b[ch] : 0.f;
+    __syncthreads();
+  }
+
+  const int tstart = t0 + 8 * rg - HALO;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {  // m = 0: B, m = 1: C
+    const Tin* src = static_cast<const Tin*>(m == 0 ? a.Bm : a.Cm);
+    const int64_t stride = m == 0 ? a.b_stride : a.c_stride;
+    const int hcol = HP + m * GN + g * N + 8 * cv;  // channel in the conv state rows
+    RowLoad<Tin, 8 + HALO> rl;
+    rl.load(a, src, stride, g * N + 8 * cv, hcol, cdim, b, tstart);
+    float v[8][8];
+    if constexpr (CONV)
+      conv_rows_to<Tin, 8>(a, rl, tstart, sCw, 2 * N, m * N + 8 * cv, 8 * rg, Lc, &v[0][0], 8);
+    else
+      copy_rows_to<Tin, 8>(a, rl, tstart, 8 * rg, Lc, &v[0][0], 8);
+    // natural [t][n]: C, or the hi part of B
+    bf16* nat = pk + (m == 0 ? PK_BN : PK_C) + (8 * rg) * N + 8 * cv;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      bf16x8 r;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r[e] = (bf16)v[i][e];
+      *reinterpret_cast<bf16x8*>(nat + i * N) = r;
+    }
+    if (m == 0) {
+      // B transposed [n][s], hi and lo
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bf16x8 hi, lo;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          bf16 hh, ll;
+          split1(v[i][e], hh, ll);
+          hi[i] = hh;
+          lo[i] = ll;
+        }
+        const int64_t o = (int64_t)(8 * cv + e) * Q + 8 * rg;
+        *reinterpret_cast<bf16x8*>(pk + PK_BTH + o) = hi;
+        *reinterpret_cast<bf16x8*>(pk + PK_BTL + o) = lo;
+      }
+    }
+  }
+
+  // conv history hand-over of the group's B and C channels
+  if (CONV && c == nc - 1 && a.conv_state_out != nullptr) {
+    const int K = a.conv_k;
+    Tin* out = static_cast<Tin*>(a.conv_state_out);
+    const Tin* hin = static_cast<const Tin*>(a.conv_state_in);
+    for (int i = tid; i < (K - 1) * 2 * N; i += PACK_THREADS) {
+      const int j = i / (2 * N), cl = i % (2 * N);
+      const int m = cl / N, n = cl % N;
+      const int ch = HP + m * GN + g * N + n;
+      const int tau = L - (K - 1) + j;  // < L
+      Tin v = from_f32<Tin>(0.f);
+      if (tau >= 0) {
+        const Tin* src = static_cast<const Tin*>(m == 0 ? a.Bm : a.Cm);
+        v = src[((int64_t)b * L + tau) * (m == 0 ? a.b_stride : a.c_stride) + g * N + n];
+      } else if (hin != nullptr) {
+        v = hin[((int64_t)b * (K - 1) + (K - 1) + tau) * cdim + ch];
+      }
+      out[((int64_t)b * (K - 1) + j) * cdim + ch] = v;
+    }
+  }
+}
+
+// ------------------------------------------------------------ x staging
+
 // One chunk's x for the whole workgroup: thread (xv = tid % 8, xr = tid / 8)
-// owns rows [2 xr, 2 xr + 2) x channels [8 xv, 8 xv + 8) (raw values of type
-// Tx with 3 rows of history in front when XCONV, post-conv otherwise).
+// owns tokens [2 xr, 2 xr + 2) x channels [8 xv, 8 xv + 8) (raw values of
+// type Tx with 3 rows of history in front when XCONV, post-conv otherwise).
 template <typename Tx, bool XCONV>
 struct StageX {
   static constexpr int HX = XCONV ? 3 : 0;
@@ -267,20 +378,16 @@ struct StageX {
             t0 + 2 * xr - HX);
   }
 
-  // 2 rows x 8 channels, transposed into sX32[p][t]
-  __device__ __forceinline__ void store(const ScanArgs& a, const float* cw, int t0, int Lc,
-                                        float* sX32) const {
+  // the thread's 2 x 8 post-conv values, tmp[8 i + e] = x[2 xr + i][8 xv + e]
+  // (zero past the end of the sequence)
+  __device__ __forceinline__ void compute(const ScanArgs& a, const float* cw, int t0, int Lc,
+                                          float* tmp) const {
     const int tid = threadIdx.x;
     const int xv = tid & 7, xr = tid >> 3;
-    float tmp[2 * 8];
     if constexpr (XCONV)
-      conv_rows_to<Tx, 2>(a, rx, t0 + 2 * xr - 3, cw, 8 * xv, 2 * xr, Lc, tmp, 8);
+      conv_rows_to<Tx, 2>(a, rx, t0 + 2 * xr - 3, cw, P, 8 * xv, 2 * xr, Lc, tmp, 8);
     else
       copy_rows_to<Tx, 2>(a, rx, t0 + 2 * xr, 2 * xr, Lc, tmp, 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      *reinterpret_cast<float2*>(sX32 + (8 * xv + e) * LDX32 + 2 * xr) =
-          make_float2(tmp[e], tmp[8 + e]);
   }
 };
 
@@ -324,12 +431,15 @@ __device__ __forceinline__ Walker walker_of(int lin, int total, int H, int G, in
   return Walker{b, g * hpg + hh, seg};
 }
 
-template <typename Tx, typename Tbc, typename Ta, typename Ty, bool XCONV, bool STATE_ONLY>
+template <typename Tx, typename Ta, typename Ty, bool XCONV, bool STATE_ONLY>
 __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
-  __shared__ __attribute__((aligned(16))) float sB32[Q * LDB32];
-  __shared__ __attribute__((aligned(16))) float sX32[P * LDX32];
-  __shared__ __attribute__((aligned(16))) bf16 sC[STATE_ONLY ? 8 : Q * LDB];
-  __shared__ __attribute__((aligned(16))) bf16 sH[STATE_ONLY ? 8 : P * LDB];
+  constexpr bool OUT = !STATE_ONLY;
+  __shared__ __attribute__((aligned(16))) bf16 sBn[OUT ? Q * LDB : 8];    // B hi [s][n]
+  __shared__ __attribute__((aligned(16))) bf16 sXh[OUT ? P * LDT : 8];    // x hi [p][s]
+  __shared__ __attribute__((aligned(16))) bf16 sXWh[P * LDT];              // (x o w) hi [p][s]
+  __shared__ __attribute__((aligned(16))) bf16 sXWl[P * LDT];              // (x o w) lo [p][s]
+  __shared__ __attribute__((aligned(16))) float sX32[OUT ? Q * LDX : 4];  // x [t][p]
+  __shared__ __attribute__((aligned(16))) bf16 sH[OUT ? P * LDB : 8];     // H [p][n]
   __shared__ __attribute__((aligned(16))) float sLam[Q];
   __shared__ __attribute__((aligned(16))) float sDel[Q];
   __shared__ __attribute__((aligned(16))) float sW[Q];
@@ -347,18 +457,21 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
   const int nc = (L + Q - 1) / Q;
   const int cbeg = seg * a.seg_chunks;
   const int cend = min(nc, cbeg + a.seg_chunks);
+  const bf16* pack = static_cast<const bf16*>(a.bc_pack) + (int64_t)(b * G + g) * nc * PACK;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, q = lane >> 4;
-  const int rt = w < 4 ? w : 11 - w;  // output row tile: rows [16 rt, 16 rt + 16)
+  const int rt = w < 4 ? w : 11 - w;  // output tokens [16 rt, 16 rt + 16)
+  const int tcol = 16 * rt + l16;     // output token of this lane
   const int ncol = 16 * w + l16;      // state column n of this lane
+  const int xv = tid & 7, xr = tid >> 3;  // x staging: channels 8 xv.., tokens 2 xr..
   const float Ah = a.A[h];
   const float Dh = a.D ? a.D[h] : 0.f;
   const Tx* xg = static_cast<const Tx*>(a.x);
 
   // ---- incoming state: element r of hacc[pt] is (p = 16 pt + 4 q + r, n = ncol)
   const float* h_in = nullptr;
-  if (!STATE_ONLY) {
+  if (OUT) {
     if (a.nseg > 1)
       h_in = a.seg_state + ((int64_t)bh * a.nseg + seg) * P * N;
     else
@@ -371,7 +484,7 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     for (int r = 0; r < 4; ++r) {
       const int p = 16 * pt + 4 * q + r;
       hacc[pt][r] = h_in ? h_in[p * N + ncol] : 0.f;
-      if (!STATE_ONLY) sH[p * LDB + ncol] = (bf16)hacc[pt][r];
+      if (OUT) sH[p * LDB + ncol] = (bf16)hacc[pt][r];
     }
   float log_decay = 0.f;  // sum of delta*A over the segment (state-only pass)
   if (XCONV && tid < P) {
@@ -387,17 +500,23 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     sCw[4 * P + tid] = a.conv_b ? a.conv_b[ch] : 0.f;
   }
 
-  // Chunk c+1's x and dt are loaded as soon as chunk c is in LDS, so they are
-  // in flight while chunk c is computed.  B and C, which the heads of a group
-  // share through L2, are loaded at the top of their own chunk, and z after
-  // the staging, ahead of its use in the epilogue.
+  // Chunk c+1's x, dt and B [s][n] are loaded as soon as chunk c is staged, so
+  // they are in flight while chunk c is computed.  The per-wave operands (C
+  // rows, B columns) and z are loaded at the top of their own chunk, ahead of
+  // their first use after the decay scan.
   StageX<Tx, XCONV> sx;
   float dtv = 0.f;
+  bf16x8 bnx[4];  // thread's 64 bytes of B [s][n]: row tid / 4, columns 32 (tid % 4) ..
   auto prefetch = [&](int cc) {
     const int tt0 = cc * Q;
     sx.load(a, b, h, tt0);
     if (tid < Q)
       dtv = ld1<Ta>(a.dt, ((int64_t)b * L + min(tt0 + tid, L - 1)) * a.dt_stride + h);
+    if (OUT) {
+      const bf16* src = pack + (int64_t)cc * PACK + PK_BN + (tid >> 2) * N + 32 * (tid & 3);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bnx[j] = ldg8(src + 8 * j);
+    }
   };
   if (cbeg < cend) prefetch(cbeg);
 
@@ -405,29 +524,55 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     const int t0 = c * Q;
     const int Lc = min(Q, L - t0);
     const int64_t row0 = (int64_t)b * L + t0;
-    StageBC<Tbc, !STATE_ONLY> sbc;
-    sbc.load(a, b, g, t0);
+    const bf16* pk = pack + (int64_t)c * PACK;
+
+    // this wave's operands: C rows of its tokens (cf, B-operand layout
+    // [k = n][j = t]) and B columns of its state columns (bth/btl, [k = s][j = n])
+    bf16x8 cf[4], bth[4], btl[4];
+    Raw4<Ta> zr[4];  // z of token tcol, channels 16 pj + 4 q ..
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (OUT) cf[kk] = ldg8(pk + PK_C + tcol * N + 32 * kk + 8 * q);
+      bth[kk] = ldg8(pk + PK_BTH + ncol * Q + 32 * kk + 8 * q);
+      btl[kk] = ldg8(pk + PK_BTL + ncol * Q + 32 * kk + 8 * q);
+    }
+    if (OUT && a.z != nullptr) {
+      // tokens past the end re-read the last one and are never stored
+      const Ta* zrow = static_cast<const Ta*>(a.z) + (row0 + min(tcol, Lc - 1)) * a.z_stride +
+                       h * P + 4 * q;
+#pragma unroll
+      for (int pj = 0; pj < 4; ++pj) zr[pj].load(zrow + 16 * pj);
+    }
+
     __syncthreads();  // the previous chunk is done with every LDS buffer
     if (tid < Q) {
       const float d = tid < Lc ? make_delta(dtv, a.dt_bias, h, a.dt_softplus) : 0.f;
       sDel[tid] = d;
       sLam[tid] = d * Ah;
     }
-    sx.store(a, sCw, t0, Lc, sX32);
-    sbc.store(a, t0, Lc, sB32, sC);
-    if (c + 1 < cend) prefetch(c + 1);
-    // z in the accumulator layout: zr[pj][r] is (t = 16 rt + 4 q + r,
-    // p = 16 pj + l16); rows past the end re-read the last row, never stored
-    float zr[4][4];
+    float xt[16];  // xt[8 i + e] = x[2 xr + i][8 xv + e], post-conv fp32
+    sx.compute(a, sCw, t0, Lc, xt);
+    if (OUT) {
 #pragma unroll
-    for (int pj = 0; pj < 4; ++pj)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = min(16 * rt + 4 * q + r, Lc - 1);
-        zr[pj][r] = (!STATE_ONLY && a.z != nullptr)
-                        ? ld1<Ta>(a.z, (row0 + t) * a.z_stride + h * P + 16 * pj + l16)
-                        : 0.f;
+      for (int i = 0; i < 2; ++i) {
+        float* d = sX32 + (2 * xr + i) * LDX + 8 * xv;
+        *reinterpret_cast<float4*>(d) = make_float4(xt[8 * i], xt[8 * i + 1], xt[8 * i + 2],
+                                                    xt[8 * i + 3]);
+        *reinterpret_cast<float4*>(d + 4) = make_float4(xt[8 * i + 4], xt[8 * i + 5],
+                                                        xt[8 * i + 6], xt[8 * i + 7]);
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bf16x2 v2;
+        v2[0] = (bf16)xt[e];
+        v2[1] = (bf16)xt[8 + e];
+        *reinterpret_cast<bf16x2*>(sXh + (8 * xv + e) * LDT + 2 * xr) = v2;
+      }
+      bf16* d = sBn + (tid >> 2) * LDB + 32 * (tid & 3);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<bf16x8*>(d + 8 * j) = bnx[j];
+    }
+    if (c + 1 < cend) prefetch(c + 1);
     __syncthreads();
     scan_lam(sLam, sRed);
     const float lam_last = sLam[Q - 1];
@@ -435,109 +580,119 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     if (tid < Q) sW[tid] = __expf(lam_last - sLam[tid]) * sDel[tid];
     __syncthreads();
 
-    if (!STATE_ONLY) {
-      // ---- inter-chunk read-out: Y = diag(exp Lam) C H^T;
-      //      element r of yacc[pj] is (t = 16 rt + 4 q + r, p = 16 pj + l16)
-      f32x4 yacc[4] = {};
-      const bf16* crow = sC + (16 * rt + l16) * LDB + 8 * q;
+    // ---- (x o w) split into bf16 hi + lo, [p][s], once per workgroup; read
+    //      by the state product after the next barrier
+    {
+      const float w0 = sW[2 * xr], w1 = sW[2 * xr + 1];
 #pragma unroll
-      for (int kk = 0; kk < N / 32; ++kk) {
-        const bf16x8 af = lds8(crow + 32 * kk);
+      for (int e = 0; e < 8; ++e) {
+        bf16x2 hi, lo;
+        bf16 hh, ll;
+        split1(xt[e] * w0, hh, ll);
+        hi[0] = hh;
+        lo[0] = ll;
+        split1(xt[8 + e] * w1, hh, ll);
+        hi[1] = hh;
+        lo[1] = ll;
+        *reinterpret_cast<bf16x2*>(sXWh + (8 * xv + e) * LDT + 2 * xr) = hi;
+        *reinterpret_cast<bf16x2*>(sXWl + (8 * xv + e) * LDT + 2 * xr) = lo;
+      }
+    }
+
+    if (OUT) {
+      // ---- inter-chunk read-out, transposed: Y^T = H C^T scaled by exp(Lam_t);
+      //      element r of yacc[pj] is (p = 16 pj + 4 q + r, t = tcol)
+      f32x4 yacc[4] = {};
+#pragma unroll
+      for (int kk = 0; kk < N / 32; ++kk)
 #pragma unroll
         for (int pj = 0; pj < 4; ++pj)
-          yacc[pj] = mfma(af, lds8(sH + (16 * pj + l16) * LDB + 32 * kk + 8 * q), yacc[pj]);
-      }
+          yacc[pj] = mfma(lds8(sH + (16 * pj + l16) * LDB + 32 * kk + 8 * q), cf[kk], yacc[pj]);
+      const float lam_t = sLam[tcol];
+      {
+        const float e = __expf(lam_t);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float e = __expf(sLam[16 * rt + 4 * q + r]);
-#pragma unroll
-        for (int pj = 0; pj < 4; ++pj) yacc[pj][r] *= e;
+        for (int pj = 0; pj < 4; ++pj) yacc[pj] *= e;
       }
 
-      // ---- intra-chunk: Y += (C B^T o decay mask) X over the source tiles
-      //      u <= rt, two 16-token tiles per K=32 step
-      const int tcol = 16 * rt + l16;
-      const float lam_t = sLam[tcol];
+      // ---- intra-chunk: Y^T += X^T (C B^T o decay mask)^T over the source
+      //      tiles u <= rt, two 16-token tiles per K=32 step
       for (int u0 = 0; u0 <= rt; u0 += 2) {
-        bf16x8 mf;
+        bf16x8 mf;  // element 4 half + r: M[t = tcol][s = 16 (u0 + half) + 4 q + r]
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int u = u0 + half;
-          f32x4 cb = {};
-          if (u <= rt) {
-            const float* brow = sB32 + (16 * u + l16) * LDB32 + 8 * q;
+          if (u > rt) {  // past the diagonal tile (rt even): a zero K half
 #pragma unroll
-            for (int kk = 0; kk < N / 32; ++kk) {
-              const float4* bp = reinterpret_cast<const float4*>(brow + 32 * kk);
-              cb = mfma(to_bf16x8(bp[0], bp[1]), lds8(crow + 32 * kk), cb);
-            }
+            for (int r = 0; r < 4; ++r) mf[4 * half + r] = (bf16)0.f;
+            continue;
           }
+          f32x4 cb = {};
+          const bf16* brow = sBn + (16 * u + l16) * LDB + 8 * q;
+#pragma unroll
+          for (int kk = 0; kk < N / 32; ++kk) cb = mfma(lds8(brow + 32 * kk), cf[kk], cb);
           // cb[r] = (B C^T)[s = 16 u + 4 q + r][t = tcol]
+          const int s0 = 16 * u + 4 * q;
+          const float4 l4 = *reinterpret_cast<const float4*>(sLam + s0);
+          const float4 d4 = *reinterpret_cast<const float4*>(sDel + s0);
+          const float ls[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float ds[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int s = 16 * u + 4 * q + r;
-            const float m = (u <= rt && s <= tcol) ? cb[r] * __expf(lam_t - sLam[s]) * sDel[s] : 0.f;
+            const float m = s0 + r <= tcol ? cb[r] * __expf(lam_t - ls[r]) * ds[r] : 0.f;
             mf[4 * half + r] = (bf16)m;
           }
         }
 #pragma unroll
         for (int pj = 0; pj < 4; ++pj) {
-          const float* xp = sX32 + (16 * pj + l16) * LDX32 + 4 * q;
-          const bf16x8 xf = to_bf16x8(*reinterpret_cast<const float4*>(xp + 16 * u0),
-                                      *reinterpret_cast<const float4*>(xp + 16 * u0 + 16));
-          yacc[pj] = mfma(mf, xf, yacc[pj]);
+          const bf16* xp = sXh + (16 * pj + l16) * LDT + 16 * u0 + 4 * q;
+          const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(xp);
+          const bf16x4 x1 = *reinterpret_cast<const bf16x4*>(xp + 16);
+          const bf16x8 xf = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          yacc[pj] = mfma(xf, mf, yacc[pj]);
         }
       }
 
-      // ---- epilogue: skip, gate, store
-      Ty* yg = static_cast<Ty*>(a.y);
-      const int tb = 16 * rt + 4 * q;
+      // ---- epilogue: skip, gate, store 4 consecutive channels per pj
+      if (tcol < Lc) {
+        Ty* yrow = static_cast<Ty*>(a.y) + (row0 + tcol) * a.y_stride + h * P + 4 * q;
+        const float* xrow = sX32 + tcol * LDX + 4 * q;
 #pragma unroll
-      for (int pj = 0; pj < 4; ++pj) {
-        const float4 xq = *reinterpret_cast<const float4*>(sX32 + (16 * pj + l16) * LDX32 + tb);
-        const float xs[4] = {xq.x, xq.y, xq.z, xq.w};
+        for (int pj = 0; pj < 4; ++pj) {
+          const float4 x4 = *reinterpret_cast<const float4*>(xrow + 16 * pj);
+          const float xs[4] = {x4.x, x4.y, x4.z, x4.w};
+          float zs[4];
+          if (a.z != nullptr) zr[pj].get(zs);
+          float yv[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (tb + r < Lc) {
-            float yv = yacc[pj][r] + Dh * xs[r];
-            if (a.z != nullptr) yv *= silu_f32(zr[pj][r]);
-            yg[(row0 + tb + r) * a.y_stride + h * P + 16 * pj + l16] = from_f32<Ty>(yv);
+          for (int r = 0; r < 4; ++r) {
+            yv[r] = yacc[pj][r] + Dh * xs[r];
+            if (a.z != nullptr) yv[r] *= silu_f32(zs[r]);
           }
+          store4(yrow + 16 * pj, yv);
         }
       }
-      __syncthreads();  // every wave is done reading sH
     }
+    __syncthreads();  // every wave is done reading sH; (x o w) is complete
 
     // ---- state: H <- exp(Lam_last) H + (X o w)^T B, operands split hi + lo;
-    //      this wave's columns n = 16 w + l16, all 64 rows p
+    //      this wave's columns n = ncol, all 64 rows p
     const float gamma = __expf(lam_last);
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) hacc[pt] *= gamma;
 #pragma unroll
     for (int kk = 0; kk < Q / 32; ++kk) {
-      const int s0 = 32 * kk + 8 * q;
-      float bv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) bv[e] = sB32[(s0 + e) * LDB32 + ncol];
-      bf16x8 bhi, blo;
-      split8(bv, bhi, blo);
-      const float4 w0 = *reinterpret_cast<const float4*>(sW + s0);
-      const float4 w1 = *reinterpret_cast<const float4*>(sW + s0 + 4);
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
-        const float* xr = sX32 + (16 * pt + l16) * LDX32 + s0;
-        const float4 x0 = *reinterpret_cast<const float4*>(xr);
-        const float4 x1 = *reinterpret_cast<const float4*>(xr + 4);
-        const float xw[8] = {x0.x * w0.x, x0.y * w0.y, x0.z * w0.z, x0.w * w0.w,
-                             x1.x * w1.x, x1.y * w1.y, x1.z * w1.z, x1.w * w1.w};
-        bf16x8 ahi, alo;
-        split8(xw, ahi, alo);
-        hacc[pt] = mfma(ahi, bhi, hacc[pt]);
-        hacc[pt] = mfma(ahi, blo, hacc[pt]);
-        hacc[pt] = mfma(alo, bhi, hacc[pt]);
+        const int o = (16 * pt + l16) * LDT + 32 * kk + 8 * q;
+        const bf16x8 ahi = lds8(sXWh + o);
+        const bf16x8 alo = lds8(sXWl + o);
+        hacc[pt] = mfma(ahi, bth[kk], hacc[pt]);
+        hacc[pt] = mfma(ahi, btl[kk], hacc[pt]);
+        hacc[pt] = mfma(alo, bth[kk], hacc[pt]);
       }
     }
-    if (!STATE_ONLY) {
+    if (OUT) {
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
@@ -561,8 +716,8 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
   if (STATE_ONLY && tid == 0) a.seg_logdecay[(int64_t)bh * a.nseg + seg] = log_decay;
 
   // ---- conv history hand-over of this head's x channels (last segment; the
-  //      B and C channels are handed over by their conv pass)
-  if (XCONV && !STATE_ONLY && seg == a.nseg - 1 && a.conv_state_out != nullptr) {
+  //      B and C channels are handed over by the pack kernel)
+  if (XCONV && OUT && seg == a.nseg - 1 && a.conv_state_out != nullptr) {
     const int K = a.conv_k;
     Tx* out = static_cast<Tx*>(a.conv_state_out);
     const Tx* hin = static_cast<const Tx*>(a.conv_state_in);
@@ -595,26 +750,30 @@ __global__ __launch_bounds__(THREADS) void combine_segments_kernel(ScanArgs a) {
   }
 }
 
-template <typename Tx, typename Tbc, typename Ta, typename Ty, bool XCONV>
+template <typename Tx, typename Ta, typename Ty, bool XCONV>
 hipError_t launch_walkers(const ScanArgs& a, hipStream_t stream) {
+  const int nc = (a.seqlen + Q - 1) / Q;
+  hipLaunchKernelGGL((bc_pack_kernel<Tx, XCONV>), dim3(nc, a.ngroups, a.batch),
+                     dim3(PACK_THREADS), 0, stream, a,
+                     static_cast<bf16*>(const_cast<void*>(a.bc_pack)));
   const int BH = a.batch * a.nheads;
   if (a.nseg > 1) {
-    hipLaunchKernelGGL((scan_bf16_kernel<Tx, Tbc, Ta, Ty, XCONV, true>), dim3(BH * (a.nseg - 1)),
+    hipLaunchKernelGGL((scan_bf16_kernel<Tx, Ta, Ty, XCONV, true>), dim3(BH * (a.nseg - 1)),
                        dim3(THREADS), 0, stream, a);
     hipLaunchKernelGGL(combine_segments_kernel, dim3(BH), dim3(THREADS), 0, stream, a);
   }
-  hipLaunchKernelGGL((scan_bf16_kernel<Tx, Tbc, Ta, Ty, XCONV, false>), dim3(BH * a.nseg),
+  hipLaunchKernelGGL((scan_bf16_kernel<Tx, Ta, Ty, XCONV, false>), dim3(BH * a.nseg),
                      dim3(THREADS), 0, stream, a);
   return hipGetLastError();
 }
 
 template <typename Ta, typename Ty>
 hipError_t pick_x(const ScanArgs& a, ssd_dtype_t xd, hipStream_t s) {
-  if (a.conv_w != nullptr)  // raw x, post-conv fp32 B and C from the conv pass
-    return xd == SSD_BF16 ? launch_walkers<bf16, float, Ta, Ty, true>(a, s)
-                          : launch_walkers<float, float, Ta, Ty, true>(a, s);
-  return xd == SSD_BF16 ? launch_walkers<bf16, bf16, Ta, Ty, false>(a, s)
-                        : launch_walkers<float, float, Ta, Ty, false>(a, s);
+  if (a.conv_w != nullptr)  // raw x|B|C: conv in the pack kernel and the walker
+    return xd == SSD_BF16 ? launch_walkers<bf16, Ta, Ty, true>(a, s)
+                          : launch_walkers<float, Ta, Ty, true>(a, s);
+  return xd == SSD_BF16 ? launch_walkers<bf16, Ta, Ty, false>(a, s)
+                        : launch_walkers<float, Ta, Ty, false>(a, s);
 }
 
 }  // namespace
@@ -624,6 +783,11 @@ hipError_t launch_scan_bf16(const ScanArgs& a, ssd_dtype_t xd, ssd_dtype_t ad, s
   if (ad == SSD_BF16)
     return yd == SSD_F32 ? pick_x<bf16, float>(a, xd, s) : pick_x<bf16, bf16>(a, xd, s);
   return yd == SSD_F32 ? pick_x<float, float>(a, xd, s) : pick_x<float, bf16>(a, xd, s);
+}
+
+size_t scan_bf16_pack_bytes(int batch, int seqlen, int ngroups) {
+  const size_t nc = ((size_t)seqlen + Q - 1) / Q;
+  return (size_t)batch * ngroups * nc * PACK * sizeof(bf16);
 }
 
 }  // namespace ssd

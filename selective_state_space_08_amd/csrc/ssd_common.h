@@ -58,6 +58,9 @@ struct ScanArgs {
   int nseg, seg_chunks;
   float* seg_state;      // [B, H, nseg, P, N] workspace (nseg > 1)
   float* seg_logdecay;   // [B, H, nseg]       workspace (nseg > 1)
+  // matrix-core path: per (sequence, group, chunk) B and C in the layouts its
+  // products read, written by the pack pass (workspace)
+  const void* bc_pack;
 };
 
 // ------------------------------------------------------------------ launchers
@@ -74,8 +77,11 @@ hipError_t launch_causal_conv1d(const void* x, int64_t x_stride, ssd_dtype_t x_d
 hipError_t launch_scan_f32(const ScanArgs& a, ssd_dtype_t xbc_dtype, ssd_dtype_t act_dtype,
                            ssd_dtype_t y_dtype, hipStream_t stream);
 
+// Runs the B|C pack pass and the walkers; a.bc_pack must hold
+// scan_bf16_pack_bytes(batch, seqlen, ngroups) bytes of workspace.
 hipError_t launch_scan_bf16(const ScanArgs& a, ssd_dtype_t xbc_dtype, ssd_dtype_t act_dtype,
                             ssd_dtype_t y_dtype, hipStream_t stream);
+size_t scan_bf16_pack_bytes(int batch, int seqlen, int ngroups);
 
 hipError_t launch_state_update(float* state, const void* xbc, ssd_dtype_t xbc_dtype,
                                void* ring, const float* conv_w, const float* conv_b, int K,
