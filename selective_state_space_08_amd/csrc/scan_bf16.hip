@@ -442,7 +442,6 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 sH[OUT ? P * LDB : 8];     // H [p][n]
   __shared__ __attribute__((aligned(16))) float sLam[Q];
   __shared__ __attribute__((aligned(16))) float sDel[Q];
-  __shared__ __attribute__((aligned(16))) float sW[Q];
   __shared__ float sRed[4];
   __shared__ __attribute__((aligned(16))) float sCw[XCONV ? 5 * P : 4];  // x-channel conv
 
@@ -526,22 +525,14 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     const int64_t row0 = (int64_t)b * L + t0;
     const bf16* pk = pack + (int64_t)c * PACK;
 
-    // this wave's operands: C rows of its tokens (cf, B-operand layout
-    // [k = n][j = t]) and B columns of its state columns (bth/btl, [k = s][j = n])
+    // this wave's operands: B columns of its state columns (bth/btl, layout
+    // [k = s][j = n]) now, C rows of its tokens (cf, [k = n][j = t]) and z
+    // after the staging
     bf16x8 cf[4], bth[4], btl[4];
-    Raw4<Ta> zr[4];  // z of token tcol, channels 16 pj + 4 q ..
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      if (OUT) cf[kk] = ldg8(pk + PK_C + tcol * N + 32 * kk + 8 * q);
       bth[kk] = ldg8(pk + PK_BTH + ncol * Q + 32 * kk + 8 * q);
       btl[kk] = ldg8(pk + PK_BTL + ncol * Q + 32 * kk + 8 * q);
-    }
-    if (OUT && a.z != nullptr) {
-      // tokens past the end re-read the last one and are never stored
-      const Ta* zrow = static_cast<const Ta*>(a.z) + (row0 + min(tcol, Lc - 1)) * a.z_stride +
-                       h * P + 4 * q;
-#pragma unroll
-      for (int pj = 0; pj < 4; ++pj) zr[pj].load(zrow + 16 * pj);
     }
 
     __syncthreads();  // the previous chunk is done with every LDS buffer
@@ -573,17 +564,29 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
       for (int j = 0; j < 4; ++j) *reinterpret_cast<bf16x8*>(d + 8 * j) = bnx[j];
     }
     if (c + 1 < cend) prefetch(c + 1);
+    // z of token tcol, channels 16 pj + 4 q .. (tokens past the end re-read
+    // the last one and are never stored)
+    Raw4<Ta> zr[4];
+    if (OUT) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) cf[kk] = ldg8(pk + PK_C + tcol * N + 32 * kk + 8 * q);
+      if (a.z != nullptr) {
+        const Ta* zrow = static_cast<const Ta*>(a.z) +
+                         (row0 + min(tcol, Lc - 1)) * a.z_stride + h * P + 4 * q;
+#pragma unroll
+        for (int pj = 0; pj < 4; ++pj) zr[pj].load(zrow + 16 * pj);
+      }
+    }
     __syncthreads();
-    scan_lam(sLam, sRed);
+    scan_lam(sLam, sRed);  // ends with a barrier
     const float lam_last = sLam[Q - 1];
     if (STATE_ONLY) log_decay += lam_last;
-    if (tid < Q) sW[tid] = __expf(lam_last - sLam[tid]) * sDel[tid];
-    __syncthreads();
 
-    // ---- (x o w) split into bf16 hi + lo, [p][s], once per workgroup; read
-    //      by the state product after the next barrier
+    // ---- (x o w) split into bf16 hi + lo, [p][s], once per workgroup, with
+    //      w_s = exp(Lam_last - Lam_s) delta_s of the thread's two tokens
     {
-      const float w0 = sW[2 * xr], w1 = sW[2 * xr + 1];
+      const float w0 = __expf(lam_last - sLam[2 * xr]) * sDel[2 * xr];
+      const float w1 = __expf(lam_last - sLam[2 * xr + 1]) * sDel[2 * xr + 1];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         bf16x2 hi, lo;
@@ -597,6 +600,31 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
         *reinterpret_cast<bf16x2*>(sXWh + (8 * xv + e) * LDT + 2 * xr) = hi;
         *reinterpret_cast<bf16x2*>(sXWl + (8 * xv + e) * LDT + 2 * xr) = lo;
       }
+    }
+
+    __syncthreads();  // (x o w) is complete
+
+    // ---- state: H <- exp(Lam_last) H + (X o w)^T B, operands split hi + lo;
+    //      this wave's columns n = ncol, all 64 rows p.  The read-out below
+    //      still uses the previous state through its bf16 copy in sH, which
+    //      is replaced at the end of the chunk.
+    const float gamma = __expf(lam_last);
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) hacc[pt] *= gamma;
+#pragma unroll
+    for (int kk = 0; kk < Q / 32; ++kk) {
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        const int o = (16 * pt + l16) * LDT + 32 * kk + 8 * q;
+        const bf16x8 ahi = lds8(sXWh + o);
+        const bf16x8 alo = lds8(sXWl + o);
+        hacc[pt] = mfma(ahi, bth[kk], hacc[pt]);
+        hacc[pt] = mfma(ahi, btl[kk], hacc[pt]);
+        hacc[pt] = mfma(alo, bth[kk], hacc[pt]);
+      }
+      // keep the operand loads of the next K step below this one's products
+      // (hoisting them all at once costs more registers than the wave has)
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     if (OUT) {
@@ -673,26 +701,8 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
         }
       }
     }
-    __syncthreads();  // every wave is done reading sH; (x o w) is complete
-
-    // ---- state: H <- exp(Lam_last) H + (X o w)^T B, operands split hi + lo;
-    //      this wave's columns n = ncol, all 64 rows p
-    const float gamma = __expf(lam_last);
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt) hacc[pt] *= gamma;
-#pragma unroll
-    for (int kk = 0; kk < Q / 32; ++kk) {
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        const int o = (16 * pt + l16) * LDT + 32 * kk + 8 * q;
-        const bf16x8 ahi = lds8(sXWh + o);
-        const bf16x8 alo = lds8(sXWl + o);
-        hacc[pt] = mfma(ahi, bth[kk], hacc[pt]);
-        hacc[pt] = mfma(ahi, btl[kk], hacc[pt]);
-        hacc[pt] = mfma(alo, bth[kk], hacc[pt]);
-      }
-    }
     if (OUT) {
+      __syncthreads();  // every wave is done reading the previous state in sH
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
