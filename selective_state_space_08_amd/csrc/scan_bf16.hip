@@ -65,12 +65,22 @@ constexpr int LDB = N + 8;       // bf16 row stride of [.][n] tiles (272 B)
 constexpr int LDT = Q + 8;       // bf16 row stride of [p][s] tiles (272 B)
 constexpr int LDX = P + 4;       // fp32 row stride of x [t][p] (272 B)
 
-// One (sequence, group, chunk) of the B|C pack, in bf16 elements
-constexpr int PK_C = 0;            // C  [t][n]
-constexpr int PK_BN = Q * N;       // B  [s][n] (hi part)
-constexpr int PK_BTH = 2 * Q * N;  // B  [n][s] hi
-constexpr int PK_BTL = 3 * Q * N;  // B  [n][s] lo
+// One (sequence, group, chunk) of the B|C pack, in bf16 elements.  C and the
+// hi/lo parts of B^T are stored in MFMA fragment order, so that a wave reads
+// the operand of one 16-row tile and one K=32 step as 1 KiB in one piece:
+// fragment (tile i16, step kk) holds, for lane l, the 8 elements
+// M[16 i16 + l % 16][32 kk + 8 (l / 16) + e], e < 8, at
+// ((i16 * 4 + kk) * 64 + l) * 8 + e, with M = C [t][n] or B^T [n][s].
+constexpr int PK_C = 0;            // C  [t][n], fragment order
+constexpr int PK_BN = Q * N;       // B  [s][n] (hi part), row-major
+constexpr int PK_BTH = 2 * Q * N;  // B^T [n][s] hi, fragment order
+constexpr int PK_BTL = 3 * Q * N;  // B^T [n][s] lo, fragment order
 constexpr int PACK = 4 * Q * N;
+
+// element offset of M[r][k] in fragment order (r < 128, k < 128)
+__host__ __device__ constexpr int frag_off(int r, int k) {
+  return (((r >> 4) * 4 + (k >> 5)) * 64 + (r & 15) + 16 * ((k & 31) >> 3)) * 8 + (k & 7);
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -89,6 +99,20 @@ __device__ __forceinline__ bf16x8 lds8(const bf16* p) {
 
 __device__ __forceinline__ bf16x8 ldg8(const bf16* p) {
   return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// Workgroup barrier for LDS traffic only.  __syncthreads() also waits for
+// every outstanding global load and store of the wave (it is a fence on all
+// memory); no thread here reads another thread's global writes, so waiting
+// for this wave's LDS operations (lgkmcnt = 0; vmcnt and expcnt left at their
+// maxima in the gfx9 s_waitcnt encoding) is enough, and global loads issued
+// ahead of time stay in flight across the barrier.  The signal fences keep
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // hi = bf16(v), lo = bf16(v - hi)
@@ -294,7 +318,7 @@ __global__ __launch_bounds__(PACK_THREADS) void bc_pack_kernel(ScanArgs a, bf16*
       sCw[j * 2 * N + tid] = k >= 0 ? a.conv_w[(int64_t)ch * K + k] : 0.f;
     }
     sCw[4 * 2 * N + tid] = a.conv_b ? a.conv_b[ch] : 0.f;
-    __syncthreads();
+    lds_barrier();
   }
 
   const int tstart = t0 + 8 * rg - HALO;
@@ -310,14 +334,16 @@ __global__ __launch_bounds__(PACK_THREADS) void bc_pack_kernel(ScanArgs a, bf16*
       conv_rows_to<Tin, 8>(a, rl, tstart, sCw, 2 * N, m * N + 8 * cv, 8 * rg, Lc, &v[0][0], 8);
     else
       copy_rows_to<Tin, 8>(a, rl, tstart, 8 * rg, Lc, &v[0][0], 8);
-    // natural [t][n]: C, or the hi part of B
-    bf16* nat = pk + (m == 0 ? PK_BN : PK_C) + (8 * rg) * N + 8 * cv;
+    // [t][n]: the hi part of B row-major, C in fragment order (the 8
+    // channels 8 cv .. 8 cv + 7 of a row are 8 consecutive elements in both)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       bf16x8 r;
 #pragma unroll
       for (int e = 0; e < 8; ++e) r[e] = (bf16)v[i][e];
-      *reinterpret_cast<bf16x8*>(nat + i * N) = r;
+      const int t = 8 * rg + i;
+      bf16* dst = m == 0 ? pk + PK_BN + t * N + 8 * cv : pk + PK_C + frag_off(t, 8 * cv);
+      *reinterpret_cast<bf16x8*>(dst) = r;
     }
     if (m == 0) {
       // B transposed [n][s], hi and lo
@@ -331,7 +357,9 @@ __global__ __launch_bounds__(PACK_THREADS) void bc_pack_kernel(ScanArgs a, bf16*
           hi[i] = hh;
           lo[i] = ll;
         }
-        const int64_t o = (int64_t)(8 * cv + e) * Q + 8 * rg;
+        // B^T row n = 8 cv + e, columns s = 8 rg .. 8 rg + 7: 8 consecutive
+        // elements in fragment order
+        const int o = frag_off(8 * cv + e, 8 * rg);
         *reinterpret_cast<bf16x8*>(pk + PK_BTH + o) = hi;
         *reinterpret_cast<bf16x8*>(pk + PK_BTL + o) = lo;
       }
@@ -404,10 +432,10 @@ __device__ __forceinline__ void scan_lam(float* s, float* red) {
     }
     if (lane == 63) red[w] = v;
   }
-  __syncthreads();
+  lds_barrier();
   if (tid >= 64 && tid < Q) s[tid] = v + red[0];
   if (tid < 64) s[tid] = v;
-  __syncthreads();
+  lds_barrier();
 }
 
 // Walker index of this workgroup: (sequence b, head h, segment seg), with
@@ -505,16 +533,16 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
   // their first use after the decay scan.
   StageX<Tx, XCONV> sx;
   float dtv = 0.f;
-  bf16x8 bnx[4];  // thread's 64 bytes of B [s][n]: row tid / 4, columns 32 (tid % 4) ..
+  bf16x8 bnx[4];  // B [s][n] elements 8 tid + 4096 j (j < 4): 1 KiB per wave and j
   auto prefetch = [&](int cc) {
     const int tt0 = cc * Q;
     sx.load(a, b, h, tt0);
     if (tid < Q)
       dtv = ld1<Ta>(a.dt, ((int64_t)b * L + min(tt0 + tid, L - 1)) * a.dt_stride + h);
     if (OUT) {
-      const bf16* src = pack + (int64_t)cc * PACK + PK_BN + (tid >> 2) * N + 32 * (tid & 3);
+      const bf16* src = pack + (int64_t)cc * PACK + PK_BN + 8 * tid;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bnx[j] = ldg8(src + 8 * j);
+      for (int j = 0; j < 4; ++j) bnx[j] = ldg8(src + 4096 * j);
     }
   };
   if (cbeg < cend) prefetch(cbeg);
@@ -531,11 +559,11 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     bf16x8 cf[4], bth[4], btl[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      bth[kk] = ldg8(pk + PK_BTH + ncol * Q + 32 * kk + 8 * q);
-      btl[kk] = ldg8(pk + PK_BTL + ncol * Q + 32 * kk + 8 * q);
+      bth[kk] = ldg8(pk + PK_BTH + ((w * 4 + kk) * 64 + lane) * 8);
+      btl[kk] = ldg8(pk + PK_BTL + ((w * 4 + kk) * 64 + lane) * 8);
     }
 
-    __syncthreads();  // the previous chunk is done with every LDS buffer
+    lds_barrier();  // the previous chunk is done with every LDS buffer
     if (tid < Q) {
       const float d = tid < Lc ? make_delta(dtv, a.dt_bias, h, a.dt_softplus) : 0.f;
       sDel[tid] = d;
@@ -559,9 +587,10 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
         v2[1] = (bf16)xt[8 + e];
         *reinterpret_cast<bf16x2*>(sXh + (8 * xv + e) * LDT + 2 * xr) = v2;
       }
-      bf16* d = sBn + (tid >> 2) * LDB + 32 * (tid & 3);
+      // element 8 tid + 4096 j is row tid / 16 + 32 j, column 8 (tid % 16)
+      bf16* d = sBn + (tid >> 4) * LDB + 8 * (tid & 15);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) *reinterpret_cast<bf16x8*>(d + 8 * j) = bnx[j];
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<bf16x8*>(d + 32 * j * LDB) = bnx[j];
     }
     if (c + 1 < cend) prefetch(c + 1);
     // z of token tcol, channels 16 pj + 4 q .. (tokens past the end re-read
@@ -569,7 +598,7 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     Raw4<Ta> zr[4];
     if (OUT) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) cf[kk] = ldg8(pk + PK_C + tcol * N + 32 * kk + 8 * q);
+      for (int kk = 0; kk < 4; ++kk) cf[kk] = ldg8(pk + PK_C + ((rt * 4 + kk) * 64 + lane) * 8);
       if (a.z != nullptr) {
         const Ta* zrow = static_cast<const Ta*>(a.z) +
                          (row0 + min(tcol, Lc - 1)) * a.z_stride + h * P + 4 * q;
@@ -577,7 +606,7 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
         for (int pj = 0; pj < 4; ++pj) zr[pj].load(zrow + 16 * pj);
       }
     }
-    __syncthreads();
+    lds_barrier();
     scan_lam(sLam, sRed);  // ends with a barrier
     const float lam_last = sLam[Q - 1];
     if (STATE_ONLY) log_decay += lam_last;
@@ -602,7 +631,7 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
       }
     }
 
-    __syncthreads();  // (x o w) is complete
+    lds_barrier();  // (x o w) is complete
 
     // ---- state: H <- exp(Lam_last) H + (X o w)^T B, operands split hi + lo;
     //      this wave's columns n = ncol, all 64 rows p.  The read-out below
@@ -702,7 +731,7 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
       }
     }
     if (OUT) {
-      __syncthreads();  // every wave is done reading the previous state in sH
+      lds_barrier();  // every wave is done reading the previous state in sH
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
