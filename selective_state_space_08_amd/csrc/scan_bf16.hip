@@ -259,6 +259,21 @@ __device__ __forceinline__ void copy_rows_to(const ScanArgs& a, const RowLoad<Tx
 }
 
 
+// One activation element, kept raw between load and use
+template <typename T> struct Raw1;
+template <> struct Raw1<bf16> {
+  unsigned short u = 0;
+  __device__ __forceinline__ void load(const bf16* p) {
+    u = *reinterpret_cast<const unsigned short*>(p);
+  }
+  __device__ __forceinline__ float get() const { return __uint_as_float((uint32_t)u << 16); }
+};
+template <> struct Raw1<float> {
+  float f = 0.f;
+  __device__ __forceinline__ void load(const float* p) { f = *p; }
+  __device__ __forceinline__ float get() const { return f; }
+};
+
 // 4 consecutive elements of an activation row, kept packed between load and
 // use (z in the epilogue)
 template <typename T> struct Raw4;
@@ -494,6 +509,7 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
   const int xv = tid & 7, xr = tid >> 3;  // x staging: channels 8 xv.., tokens 2 xr..
   const float Ah = a.A[h];
   const float Dh = a.D ? a.D[h] : 0.f;
+  const float dtb = a.dt_bias ? a.dt_bias[h] : 0.f;
   const Tx* xg = static_cast<const Tx*>(a.x);
 
   // ---- incoming state: element r of hacc[pt] is (p = 16 pt + 4 q + r, n = ncol)
@@ -532,13 +548,17 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
   // rows, B columns) and z are loaded at the top of their own chunk, ahead of
   // their first use after the decay scan.
   StageX<Tx, XCONV> sx;
-  float dtv = 0.f;
+  // the prefetched dt stays in its raw form until it is used, so that no
+  // conversion waits for the load while the prefetch is in flight
+  Raw1<Ta> dtv;
   bf16x8 bnx[4];  // B [s][n] elements 8 tid + 4096 j (j < 4): 1 KiB per wave and j
   auto prefetch = [&](int cc) {
     const int tt0 = cc * Q;
     sx.load(a, b, h, tt0);
-    if (tid < Q)
-      dtv = ld1<Ta>(a.dt, ((int64_t)b * L + min(tt0 + tid, L - 1)) * a.dt_stride + h);
+    // every lane loads (threads tid >= Q re-read a token of the chunk and
+    // never use it), so no branch separates these loads from the ones after
+    dtv.load(static_cast<const Ta*>(a.dt) +
+             ((int64_t)b * L + min(tt0 + (tid & (Q - 1)), L - 1)) * a.dt_stride + h);
     if (OUT) {
       const bf16* src = pack + (int64_t)cc * PACK + PK_BN + 8 * tid;
 #pragma unroll
@@ -565,7 +585,9 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
 
     lds_barrier();  // the previous chunk is done with every LDS buffer
     if (tid < Q) {
-      const float d = tid < Lc ? make_delta(dtv, a.dt_bias, h, a.dt_softplus) : 0.f;
+      float d = dtv.get() + dtb;
+      if (a.dt_softplus) d = softplus_f32(d);
+      if (tid >= Lc) d = 0.f;
       sDel[tid] = d;
       sLam[tid] = d * Ah;
     }
@@ -592,20 +614,26 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) *reinterpret_cast<bf16x8*>(d + 32 * j * LDB) = bnx[j];
     }
-    if (c + 1 < cend) prefetch(c + 1);
-    // z of token tcol, channels 16 pj + 4 q .. (tokens past the end re-read
-    // the last one and are never stored)
+    // C rows of this wave's tokens and z of token tcol, channels 16 pj + 4 q ..
+    // (tokens past the end re-read the last one and are never stored), then
+    // the next chunk's prefetch: the memory counter retires loads in order, so
+    // waiting for C and z later does not wait for the prefetch
     Raw4<Ta> zr[4];
     if (OUT) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) cf[kk] = ldg8(pk + PK_C + ((rt * 4 + kk) * 64 + lane) * 8);
-      if (a.z != nullptr) {
-        const Ta* zrow = static_cast<const Ta*>(a.z) +
-                         (row0 + min(tcol, Lc - 1)) * a.z_stride + h * P + 4 * q;
+      // without a gate the loads read the start of the B|C pack instead
+      // (at least 128 KiB of global memory; the values are not used): no
+      // branch, and both pointers stay global so the loads are not flat
+      const Ta* zrow = a.z != nullptr
+                           ? static_cast<const Ta*>(a.z) +
+                                 (row0 + min(tcol, Lc - 1)) * a.z_stride + h * P + 4 * q
+                           : static_cast<const Ta*>(a.bc_pack) + 4 * q;
 #pragma unroll
-        for (int pj = 0; pj < 4; ++pj) zr[pj].load(zrow + 16 * pj);
-      }
+      for (int pj = 0; pj < 4; ++pj) zr[pj].load(zrow + 16 * pj);
     }
+    // unconditional (the last chunk re-reads itself), for the same reason
+    prefetch(min(c + 1, cend - 1));
     lds_barrier();
     scan_lam(sLam, sRed);  // ends with a barrier
     const float lam_last = sLam[Q - 1];
