@@ -29,12 +29,32 @@ __global__ __launch_bounds__(THREADS) void state_update_kernel(
     const Ta* __restrict__ dt, const Ta* __restrict__ z, const float* __restrict__ A,
     const float* __restrict__ D, const float* __restrict__ dt_bias, int softplus,
     Ty* __restrict__ y, int H, int G) {
-  extern __shared__ float sxc[];  // post-conv: x of the group's heads | B | C
+  // LDS: post-conv x of the group's heads | B | C, then the gate silu(z) of
+  // the group's heads, then delta, exp(delta A) and D of each head
+  extern __shared__ float sxc[];
   const int g = blockIdx.x, b = blockIdx.y;
   const int hpg = H / G;
   const int HP = H * P, GN = G * N, C = HP + 2 * GN;
   const int nx = hpg * P, nch = nx + 2 * N;
   const int tid = threadIdx.x;
+  float* sgate = sxc + nch;
+  float* sdel = sgate + nx;
+  float* sdec = sdel + hpg;
+  float* sskip = sdec + hpg;
+
+  // Everything per head that the state loop needs is read here, ahead of it:
+  // inside the loop the only loads are the state stream, so waiting for one
+  // head's state never waits behind a small load issued after the prefetch.
+  const int h0 = g * hpg;
+  for (int i = tid; i < nx; i += THREADS)
+    sgate[i] = z != nullptr ? silu_f32(to_f32(z[(int64_t)b * HP + h0 * P + i])) : 1.f;
+  if (tid < hpg) {
+    const int h = h0 + tid;
+    const float delta = make_delta(to_f32(dt[(int64_t)b * H + h]), dt_bias, h, softplus);
+    sdel[tid] = delta;
+    sdec[tid] = __expf(delta * A[h]);
+    sskip[tid] = D ? D[h] : 0.f;
+  }
 
   // conv step for the group's channels; each channel's ring column is owned
   // by this workgroup alone
@@ -62,7 +82,6 @@ __global__ __launch_bounds__(THREADS) void state_update_kernel(
   const float4 Bv = reinterpret_cast<const float4*>(sxc + nx)[col];
   const float4 Cv = reinterpret_cast<const float4*>(sxc + nx + N)[col];
 
-  const int h0 = g * hpg;
   float4* st = reinterpret_cast<float4*>(state + ((int64_t)b * H + h0) * P * N);
   float4 cur[PASSES];
 #pragma unroll
@@ -76,9 +95,9 @@ __global__ __launch_bounds__(THREADS) void state_update_kernel(
 #pragma unroll
       for (int j = 0; j < PASSES; ++j) nxt[j] = sn[tid + THREADS * j];
     }
-    const float delta = make_delta(to_f32(dt[(int64_t)b * H + h]), dt_bias, h, softplus);
-    const float a = __expf(delta * A[h]);
-    const float Dh = D ? D[h] : 0.f;
+    const float delta = sdel[hh];
+    const float a = sdec[hh];
+    const float Dh = sskip[hh];
     float4* sh = st + (int64_t)hh * (P * N / 4);
 #pragma unroll
     for (int j = 0; j < PASSES; ++j) {
@@ -96,10 +115,8 @@ __global__ __launch_bounds__(THREADS) void state_update_kernel(
 #pragma unroll
       for (int m = 16; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 32);
       if (col == 0) {
-        float yv = acc + Dh * xp;
-        const int64_t o = (int64_t)b * HP + h * P + p;
-        if (z != nullptr) yv *= silu_f32(to_f32(z[o]));
-        y[o] = from_f32<Ty>(yv);
+        const float yv = (acc + Dh * xp) * sgate[hh * P + p];
+        y[(int64_t)b * HP + h * P + p] = from_f32<Ty>(yv);
       }
     }
     if (hh + 1 < hpg) {
@@ -114,7 +131,14 @@ hipError_t launch_typed(float* state, const void* xbc, void* ring, const float* 
                         const float* conv_b, int K, const void* dt, const void* z,
                         const float* A, const float* D, const float* dt_bias, int softplus,
                         void* y, int B, int H, int G, hipStream_t stream) {
-  const size_t lds = sizeof(float) * (size_t)((H / G) * P + 2 * N);
+  const int hpg = H / G;
+  const size_t lds = sizeof(float) * (size_t)(2 * hpg * P + 2 * N + 3 * hpg);
+  if (lds > 64 * 1024) {  // many heads per group: opt in to more than 64 KiB
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&state_update_kernel<Tx, Ta, Ty>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((state_update_kernel<Tx, Ta, Ty>), dim3(G, B), dim3(THREADS), lds, stream,
                      state, static_cast<const Tx*>(xbc), static_cast<Tx*>(ring), conv_w, conv_b,
                      K, static_cast<const Ta*>(dt), static_cast<const Ta*>(z), A, D, dt_bias,

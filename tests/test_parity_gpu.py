@@ -257,28 +257,42 @@ def test_zero_dt_keeps_state():
 
 # ---------------------------------------------------------------- decode
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_state_update_chain(dtype):
-    wl = Workload("d", batch=3, seqlen=1, nheads=16, ngroups=4, dtype=dtype, decode_steps=40,
-                  initial_state=True, seed=23)
+DECODE_CASES = [  # (dtype, B, H, G, steps, gated)
+    ("f32", 3, 16, 4, 40, True), ("bf16", 3, 16, 4, 40, True),
+    # 128 heads in one group: the per-group LDS (x, gate, per-head scalars)
+    # exceeds 64 KiB
+    ("bf16", 2, 128, 1, 6, True),
+    # one head per group, no gate
+    ("f32", 2, 8, 8, 12, False),
+]
+
+
+@pytest.mark.parametrize("dtype,B,H,G,T,gated", DECODE_CASES,
+                         ids=["%s-B%d-H%d-G%d-%s" % (c[0], c[1], c[2], c[3],
+                                                     "gate" if c[5] else "nogate")
+                              for c in DECODE_CASES])
+def test_state_update_chain(dtype, B, H, G, T, gated):
+    wl = Workload("d", batch=B, seqlen=1, nheads=H, ngroups=G, dtype=dtype, decode_steps=T,
+                  initial_state=True, seed=23 + H + G)
     inp = synth.make_decode(wl)
-    T = wl.decode_steps
     xbc, z, dt = inp.steps(0, T)
-    say("decode chain %s" % dtype)
+    say("decode chain %s B=%d H=%d G=%d gated=%s" % (dtype, B, H, G, gated))
     p = params(inp)
     st = dev32(inp.state)
     ring = dev(inp.ring, dtype)
     ys = []
     for t in range(T):
-        ys.append(layer.decode_step(st, dev(xbc[t], dtype), dev(dt[t], dtype), dev(z[t], dtype),
-                                    ring, p).double().cpu().numpy())
+        ys.append(ssd.ssd_state_update(
+            st, dev(xbc[t], dtype), dev(dt[t], dtype), p.A, ngroups=G, conv_state=ring,
+            conv_w=p.conv_w, z=dev(z[t], dtype) if gated else None, D=p.D,
+            dt_bias=p.dt_bias).double().cpu().numpy())
     torch.cuda.synchronize()
     carry = oracle.DecodeState(inp.state, inp.ring)
     yr = []
     for t in range(T):
-        yr.append(oracle.mamba2_decode_step(carry, xbc[t], dt[t], inp.A, nheads=16, headdim=64,
-                                            ngroups=4, dstate=128, conv_w=inp.conv_w, D=inp.D,
-                                            dt_bias=inp.dt_bias, z=z[t]))
+        yr.append(oracle.mamba2_decode_step(carry, xbc[t], dt[t], inp.A, nheads=H, headdim=64,
+                                            ngroups=G, dstate=128, conv_w=inp.conv_w, D=inp.D,
+                                            dt_bias=inp.dt_bias, z=z[t] if gated else None))
     tol = TOL[dtype]
     assert rel_max_err(np.stack(ys), np.stack(yr)) <= tol
     assert rel_max_err(st.cpu().numpy(), carry.state) <= tol
