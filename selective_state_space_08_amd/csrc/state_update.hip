@@ -9,8 +9,9 @@
 // step and is ~98% of the bytes.  One workgroup owns one (sequence, group):
 // it convolves the group's channels once (x of its H/G heads, B and C of the
 // group), so the ring rows it shifts are touched by no other workgroup, then
-// streams the heads' states with 16-byte coalesced accesses, prefetching the
-// next head's state while it updates the current one.
+// streams the heads' states with 16-byte coalesced, non-temporal accesses
+// (512 threads, 4 float4 per thread per head), prefetching the next head's
+// state while it updates the current one.
 #include "ssd_common.h"
 
 namespace ssd {
@@ -18,9 +19,22 @@ namespace {
 
 constexpr int P = 64;
 constexpr int N = 128;
-constexpr int THREADS = 256;
-constexpr int ROWS_PER_PASS = THREADS / (N / 4);  // 8 state rows per pass
-constexpr int PASSES = P / ROWS_PER_PASS;         // 8 float4 per thread per head
+constexpr int THREADS = 512;
+constexpr int ROWS_PER_PASS = THREADS / (N / 4);  // 16 state rows per pass
+constexpr int PASSES = P / ROWS_PER_PASS;         // 4 float4 per thread per head
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// The state is streamed once per step and not reused: non-temporal loads
+// and stores keep it from displacing other data in the caches.
+__device__ __forceinline__ float4 ld_stream(const float4* p) {
+  const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_stream(float4* p, float4 v) {
+  const f32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(p));
+}
 
 template <typename Tx, typename Ta, typename Ty>
 __global__ __launch_bounds__(THREADS) void state_update_kernel(
@@ -76,7 +90,7 @@ __global__ __launch_bounds__(THREADS) void state_update_kernel(
   }
   __syncthreads();
 
-  // thread -> float4 column n4 = tid % 32 (fixed), rows p = tid / 32 + 8 j
+  // thread -> float4 column n4 = tid % 32 (fixed), rows p = tid / 32 + ROWS_PER_PASS j
   const int col = tid & 31;
   const int row0 = tid >> 5;
   const float4 Bv = reinterpret_cast<const float4*>(sxc + nx)[col];
@@ -85,7 +99,7 @@ __global__ __launch_bounds__(THREADS) void state_update_kernel(
   float4* st = reinterpret_cast<float4*>(state + ((int64_t)b * H + h0) * P * N);
   float4 cur[PASSES];
 #pragma unroll
-  for (int j = 0; j < PASSES; ++j) cur[j] = st[tid + THREADS * j];
+  for (int j = 0; j < PASSES; ++j) cur[j] = ld_stream(st + tid + THREADS * j);
 
   for (int hh = 0; hh < hpg; ++hh) {
     const int h = h0 + hh;
@@ -93,7 +107,7 @@ __global__ __launch_bounds__(THREADS) void state_update_kernel(
     if (hh + 1 < hpg) {
       const float4* sn = st + (int64_t)(hh + 1) * (P * N / 4);
 #pragma unroll
-      for (int j = 0; j < PASSES; ++j) nxt[j] = sn[tid + THREADS * j];
+      for (int j = 0; j < PASSES; ++j) nxt[j] = ld_stream(sn + tid + THREADS * j);
     }
     const float delta = sdel[hh];
     const float a = sdec[hh];
@@ -109,7 +123,7 @@ __global__ __launch_bounds__(THREADS) void state_update_kernel(
       s.y = a * s.y + dx * Bv.y;
       s.z = a * s.z + dx * Bv.z;
       s.w = a * s.w + dx * Bv.w;
-      sh[tid + THREADS * j] = s;
+      st_stream(sh + tid + THREADS * j, s);
       float acc = s.x * Cv.x + s.y * Cv.y + s.z * Cv.z + s.w * Cv.w;
       // sum over the 32 lanes holding row p (fixed butterfly order: deterministic)
 #pragma unroll
