@@ -105,10 +105,10 @@ int ssd_causal_conv1d_fwd(const void* x, int64_t x_tok_stride, ssd_dtype_t x_dty
  * SSD_MATH_F32 and for empty inputs); fused_conv is 1 when conv_w will be
  * passed (the size does not depend on it in this version).  The matrix-core
  * path uses the workspace for B and C of every chunk and group, post-conv, in
- * the bf16 layouts its products read (8 bytes per token, group and state
- * column; B and C are convolved and converted once per group rather than once
- * per head), and for per-segment states when it splits a long sequence over
- * more workgroups. */
+ * the bf16 layouts its products read, and for the chunk's causal C B^T tiles
+ * in fp32 (132 KiB per sequence, group and 128-token chunk; all of it is
+ * formed once per group rather than once per head), and for per-segment
+ * states when it splits a long sequence over more workgroups. */
 size_t ssd_chunk_scan_workspace_bytes(int batch, int seqlen, int nheads, int headdim,
                                       int ngroups, int dstate, int chunk,
                                       ssd_math_t math, int fused_conv);

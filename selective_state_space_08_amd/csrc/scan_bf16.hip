@@ -71,11 +71,20 @@ constexpr int LDX = P + 4;       // fp32 row stride of x [t][p] (272 B)
 // fragment (tile i16, step kk) holds, for lane l, the 8 elements
 // M[16 i16 + l % 16][32 kk + 8 (l / 16) + e], e < 8, at
 // ((i16 * 4 + kk) * 64 + l) * 8 + e, with M = C [t][n] or B^T [n][s].
+// The causal 16x16 tiles of B C^T (rows s, columns t, tile (rt, u) with
+// u <= rt holding s in [16 u, 16 u + 16), t in [16 rt, 16 rt + 16)) follow
+// as fp32 in accumulator order: lane l of tile k = rt (rt + 1) / 2 + u holds
+// (B C^T)[16 u + 4 (l / 16) + r][16 rt + l % 16], r < 4, at floats
+// (k * 64 + l) * 4 + r.  They depend on the group only, so they are formed
+// here once instead of once per head.
+constexpr int NTRI = Q / 16 * (Q / 16 + 1) / 2;  // 36 causal tiles
 constexpr int PK_C = 0;            // C  [t][n], fragment order
-constexpr int PK_BN = Q * N;       // B  [s][n] (hi part), row-major
-constexpr int PK_BTH = 2 * Q * N;  // B^T [n][s] hi, fragment order
-constexpr int PK_BTL = 3 * Q * N;  // B^T [n][s] lo, fragment order
-constexpr int PACK = 4 * Q * N;
+constexpr int PK_BTH = Q * N;      // B^T [n][s] hi, fragment order
+constexpr int PK_BTL = 2 * Q * N;  // B^T [n][s] lo, fragment order
+constexpr int PK_CB = 3 * Q * N;   // B C^T causal tiles, fp32 (2 bf16 slots per float)
+constexpr int PACK = 3 * Q * N + 2 * NTRI * 256;
+
+__host__ __device__ constexpr int tri(int rt) { return rt * (rt + 1) / 2; }
 
 // element offset of M[r][k] in fragment order (r < 128, k < 128)
 __host__ __device__ constexpr int frag_off(int r, int k) {
@@ -315,6 +324,8 @@ __device__ __forceinline__ void store4(bf16* p, const float* v) {
 template <typename Tin, bool CONV>
 __global__ __launch_bounds__(PACK_THREADS) void bc_pack_kernel(ScanArgs a, bf16* pack) {
   __shared__ __attribute__((aligned(16))) float sCw[CONV ? 5 * 2 * N : 4];
+  __shared__ __attribute__((aligned(16))) bf16 sPB[Q * LDB];  // B [s][n] bf16
+  __shared__ __attribute__((aligned(16))) bf16 sPC[Q * LDB];  // C [t][n] bf16
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int L = a.seqlen, nc = (L + Q - 1) / Q, G = a.ngroups;
   const int t0 = c * Q, Lc = min(Q, L - t0);
@@ -349,16 +360,16 @@ __global__ __launch_bounds__(PACK_THREADS) void bc_pack_kernel(ScanArgs a, bf16*
       conv_rows_to<Tin, 8>(a, rl, tstart, sCw, 2 * N, m * N + 8 * cv, 8 * rg, Lc, &v[0][0], 8);
     else
       copy_rows_to<Tin, 8>(a, rl, tstart, 8 * rg, Lc, &v[0][0], 8);
-    // [t][n]: the hi part of B row-major, C in fragment order (the 8
-    // channels 8 cv .. 8 cv + 7 of a row are 8 consecutive elements in both)
+    // bf16 rows [t][n] into LDS for the B C^T tiles, and C in fragment order
+    // (the 8 channels 8 cv .. 8 cv + 7 of a row are 8 consecutive elements)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       bf16x8 r;
 #pragma unroll
       for (int e = 0; e < 8; ++e) r[e] = (bf16)v[i][e];
       const int t = 8 * rg + i;
-      bf16* dst = m == 0 ? pk + PK_BN + t * N + 8 * cv : pk + PK_C + frag_off(t, 8 * cv);
-      *reinterpret_cast<bf16x8*>(dst) = r;
+      *reinterpret_cast<bf16x8*>((m == 0 ? sPB : sPC) + t * LDB + 8 * cv) = r;
+      if (m == 1) *reinterpret_cast<bf16x8*>(pk + PK_C + frag_off(t, 8 * cv)) = r;
     }
     if (m == 0) {
       // B transposed [n][s], hi and lo
@@ -378,6 +389,26 @@ __global__ __launch_bounds__(PACK_THREADS) void bc_pack_kernel(ScanArgs a, bf16*
         *reinterpret_cast<bf16x8*>(pk + PK_BTH + o) = hi;
         *reinterpret_cast<bf16x8*>(pk + PK_BTL + o) = lo;
       }
+    }
+  }
+
+  // causal tiles of B C^T (rows s, columns t) with fp32 accumulation, in the
+  // accumulator order the walkers use; 9 tiles per wave
+  lds_barrier();
+  {
+    const int pw = tid >> 6, lane = tid & 63, l16 = lane & 15, q = lane >> 4;
+    float* cbo = reinterpret_cast<float*>(pk + PK_CB);
+    for (int k = pw; k < NTRI; k += PACK_THREADS / 64) {
+      int rt = 0;
+      while (tri(rt + 1) <= k) ++rt;
+      const int u = k - tri(rt);
+      const bf16* brow = sPB + (16 * u + l16) * LDB + 8 * q;
+      const bf16* crow = sPC + (16 * rt + l16) * LDB + 8 * q;
+      f32x4 acc = {};
+#pragma unroll
+      for (int kk = 0; kk < N / 32; ++kk)
+        acc = mfma(lds8(brow + 32 * kk), lds8(crow + 32 * kk), acc);
+      *reinterpret_cast<f32x4*>(cbo + (k * 64 + lane) * 4) = acc;
     }
   }
 
@@ -477,7 +508,6 @@ __device__ __forceinline__ Walker walker_of(int lin, int total, int H, int G, in
 template <typename Tx, typename Ta, typename Ty, bool XCONV, bool STATE_ONLY>
 __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
   constexpr bool OUT = !STATE_ONLY;
-  __shared__ __attribute__((aligned(16))) bf16 sBn[OUT ? Q * LDB : 8];    // B hi [s][n]
   __shared__ __attribute__((aligned(16))) bf16 sXh[OUT ? P * LDT : 8];    // x hi [p][s]
   __shared__ __attribute__((aligned(16))) bf16 sXWh[P * LDT];              // (x o w) hi [p][s]
   __shared__ __attribute__((aligned(16))) bf16 sXWl[P * LDT];              // (x o w) lo [p][s]
@@ -551,7 +581,6 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
   // the prefetched dt stays in its raw form until it is used, so that no
   // conversion waits for the load while the prefetch is in flight
   Raw1<Ta> dtv;
-  bf16x8 bnx[4];  // B [s][n] elements 8 tid + 4096 j (j < 4): 1 KiB per wave and j
   auto prefetch = [&](int cc) {
     const int tt0 = cc * Q;
     sx.load(a, b, h, tt0);
@@ -559,11 +588,6 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     // never use it), so no branch separates these loads from the ones after
     dtv.load(static_cast<const Ta*>(a.dt) +
              ((int64_t)b * L + min(tt0 + (tid & (Q - 1)), L - 1)) * a.dt_stride + h);
-    if (OUT) {
-      const bf16* src = pack + (int64_t)cc * PACK + PK_BN + 8 * tid;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bnx[j] = ldg8(src + 4096 * j);
-    }
   };
   if (cbeg < cend) prefetch(cbeg);
 
@@ -609,19 +633,20 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
         v2[1] = (bf16)xt[8 + e];
         *reinterpret_cast<bf16x2*>(sXh + (8 * xv + e) * LDT + 2 * xr) = v2;
       }
-      // element 8 tid + 4096 j is row tid / 16 + 32 j, column 8 (tid % 16)
-      bf16* d = sBn + (tid >> 4) * LDB + 8 * (tid & 15);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) *reinterpret_cast<bf16x8*>(d + 32 * j * LDB) = bnx[j];
     }
     // C rows of this wave's tokens and z of token tcol, channels 16 pj + 4 q ..
     // (tokens past the end re-read the last one and are never stored), then
     // the next chunk's prefetch: the memory counter retires loads in order, so
     // waiting for C and z later does not wait for the prefetch
     Raw4<Ta> zr[4];
+    f32x4 cbt[Q / 16];  // B C^T tiles u <= rt of this wave's tokens (u > rt: unused)
     if (OUT) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) cf[kk] = ldg8(pk + PK_C + ((rt * 4 + kk) * 64 + lane) * 8);
+      const float* cbsrc = reinterpret_cast<const float*>(pk + PK_CB) + (tri(rt) * 64 + lane) * 4;
+#pragma unroll
+      for (int u = 0; u < Q / 16; ++u)
+        cbt[u] = *reinterpret_cast<const f32x4*>(cbsrc + min(u, rt) * 256);
       // without a gate the loads read the start of the B|C pack instead
       // (at least 128 KiB of global memory; the values are not used): no
       // branch, and both pointers stay global so the loads are not flat
@@ -702,7 +727,9 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
 
       // ---- intra-chunk: Y^T += X^T (C B^T o decay mask)^T over the source
       //      tiles u <= rt, two 16-token tiles per K=32 step
-      for (int u0 = 0; u0 <= rt; u0 += 2) {
+#pragma unroll
+      for (int u0 = 0; u0 < Q / 16; u0 += 2) {
+        if (u0 > rt) break;
         bf16x8 mf;  // element 4 half + r: M[t = tcol][s = 16 (u0 + half) + 4 q + r]
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -712,10 +739,7 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
             for (int r = 0; r < 4; ++r) mf[4 * half + r] = (bf16)0.f;
             continue;
           }
-          f32x4 cb = {};
-          const bf16* brow = sBn + (16 * u + l16) * LDB + 8 * q;
-#pragma unroll
-          for (int kk = 0; kk < N / 32; ++kk) cb = mfma(lds8(brow + 32 * kk), cf[kk], cb);
+          const f32x4 cb = cbt[u];
           // cb[r] = (B C^T)[s = 16 u + 4 q + r][t = tcol]
           const int s0 = 16 * u + 4 * q;
           const float4 l4 = *reinterpret_cast<const float4*>(sLam + s0);

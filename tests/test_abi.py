@@ -65,16 +65,17 @@ def test_workspace_query():
     # fp32 path and short sequences never need a workspace
     for fused in (0, 1):
         assert lib.ssd_chunk_scan_workspace_bytes(1, 131072, 80, 64, 8, 128, 128, 0, fused) == 0
-    # matrix cores: B and C of every chunk and group in bf16, as C [t][n],
-    # B [s][n] and B hi/lo [n][s] (8 bytes per token, group and state column)
+    # matrix cores, per (sequence, group, chunk): C [t][n] and B^T hi/lo
+    # [n][s] in bf16, and the 36 causal 16x16 tiles of B C^T in fp32
+    pack = 3 * 128 * 128 * 2 + 36 * 256 * 4
     for fused in (0, 1):
         assert lib.ssd_chunk_scan_workspace_bytes(4, 128, 128, 64, 8, 128, 128, 1, fused) == \
-            4 * 8 * 1 * 4 * 128 * 128 * 2
+            4 * 8 * 1 * pack
         assert lib.ssd_chunk_scan_workspace_bytes(4, 8192, 128, 64, 8, 128, 128, 1, fused) == \
-            4 * 8 * 64 * 4 * 128 * 128 * 2
+            4 * 8 * 64 * pack
     # a ragged last chunk is stored whole
     assert lib.ssd_chunk_scan_workspace_bytes(2, 129, 128, 64, 2, 128, 128, 1, 1) == \
-        2 * 2 * 2 * 4 * 128 * 128 * 2
+        2 * 2 * 2 * pack
     # one long sequence with few heads is split into segments: per-segment states
     ws = lib.ssd_chunk_scan_workspace_bytes(1, 131072, 80, 64, 8, 128, 128, 1, 0)
     assert ws >= 80 * 2 * 64 * 128 * 4
