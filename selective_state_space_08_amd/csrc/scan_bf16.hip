@@ -63,6 +63,11 @@ constexpr int PACK_THREADS = 256;
 constexpr int NXCD = 8;
 constexpr int LDB = N + 8;       // bf16 row stride of [.][n] tiles (272 B)
 constexpr int LDT = Q + 8;       // bf16 row stride of [p][s] tiles (272 B)
+// Row p of a bf16 [p][s] tile is stored at row p + p / 8: with the 272-byte
+// pitch, the 8 rows 8 apart that one staging store writes then fall into
+// distinct LDS banks, and 16 consecutive rows (an MFMA operand read) still do.
+__host__ __device__ constexpr int prow(int p) { return p + (p >> 3); }
+constexpr int PROWS = P + P / 8;
 constexpr int LDX = P + 4;       // fp32 row stride of x [t][p] (272 B)
 
 // One (sequence, group, chunk) of the B|C pack, in bf16 elements.  C and the
@@ -508,9 +513,9 @@ __device__ __forceinline__ Walker walker_of(int lin, int total, int H, int G, in
 template <typename Tx, typename Ta, typename Ty, bool XCONV, bool STATE_ONLY>
 __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
   constexpr bool OUT = !STATE_ONLY;
-  __shared__ __attribute__((aligned(16))) bf16 sXh[OUT ? P * LDT : 8];    // x hi [p][s]
-  __shared__ __attribute__((aligned(16))) bf16 sXWh[P * LDT];              // (x o w) hi [p][s]
-  __shared__ __attribute__((aligned(16))) bf16 sXWl[P * LDT];              // (x o w) lo [p][s]
+  __shared__ __attribute__((aligned(16))) bf16 sXh[OUT ? PROWS * LDT : 8];  // x hi [p][s]
+  __shared__ __attribute__((aligned(16))) bf16 sXWh[PROWS * LDT];            // (x o w) hi
+  __shared__ __attribute__((aligned(16))) bf16 sXWl[PROWS * LDT];            // (x o w) lo
   __shared__ __attribute__((aligned(16))) float sX32[OUT ? Q * LDX : 4];  // x [t][p]
   __shared__ __attribute__((aligned(16))) bf16 sH[OUT ? P * LDB : 8];     // H [p][n]
   __shared__ __attribute__((aligned(16))) float sLam[Q];
@@ -631,7 +636,7 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
         bf16x2 v2;
         v2[0] = (bf16)xt[e];
         v2[1] = (bf16)xt[8 + e];
-        *reinterpret_cast<bf16x2*>(sXh + (8 * xv + e) * LDT + 2 * xr) = v2;
+        *reinterpret_cast<bf16x2*>(sXh + prow(8 * xv + e) * LDT + 2 * xr) = v2;
       }
     }
     // C rows of this wave's tokens and z of token tcol, channels 16 pj + 4 q ..
@@ -679,8 +684,8 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
         split1(xt[8 + e] * w1, hh, ll);
         hi[1] = hh;
         lo[1] = ll;
-        *reinterpret_cast<bf16x2*>(sXWh + (8 * xv + e) * LDT + 2 * xr) = hi;
-        *reinterpret_cast<bf16x2*>(sXWl + (8 * xv + e) * LDT + 2 * xr) = lo;
+        *reinterpret_cast<bf16x2*>(sXWh + prow(8 * xv + e) * LDT + 2 * xr) = hi;
+        *reinterpret_cast<bf16x2*>(sXWl + prow(8 * xv + e) * LDT + 2 * xr) = lo;
       }
     }
 
@@ -697,7 +702,7 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     for (int kk = 0; kk < Q / 32; ++kk) {
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
-        const int o = (16 * pt + l16) * LDT + 32 * kk + 8 * q;
+        const int o = prow(16 * pt + l16) * LDT + 32 * kk + 8 * q;
         const bf16x8 ahi = lds8(sXWh + o);
         const bf16x8 alo = lds8(sXWl + o);
         hacc[pt] = mfma(ahi, bth[kk], hacc[pt]);
@@ -754,7 +759,7 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
         }
 #pragma unroll
         for (int pj = 0; pj < 4; ++pj) {
-          const bf16* xp = sXh + (16 * pj + l16) * LDT + 16 * u0 + 4 * q;
+          const bf16* xp = sXh + prow(16 * pj + l16) * LDT + 16 * u0 + 4 * q;
           const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(xp);
           const bf16x4 x1 = *reinterpret_cast<const bf16x4*>(xp + 16);
           const bf16x8 xf = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
