@@ -297,10 +297,10 @@ def main():
     fpt = prefill_alg_flops_per_token(wl)
     kernel_ms = pre["median_ms"]
     achieved = bpt * wl.tokens / (kernel_ms / 1e3) / 1e9
-    # The measured unit is one ssd_chunk_scan_fwd call: with the conv fused it
-    # launches causal_conv1d twice (B and C of each group into the fp32
-    # workspace) and then the scan walker; unfused, the step is the conv
-    # kernel over x|B|C followed by the scan walker.
+    # The measured unit is one ssd_chunk_scan_fwd call: the B|C pack kernel
+    # (conv of B and C once per group, their matrix-core layouts and the
+    # chunk's C B^T tiles into the workspace) and then the scan walker;
+    # unfused, the step is the conv kernel over x|B|C followed by that call.
     kfile = ("scan_bf16.hip", "conv1d.hip", "api.hip")
     key = "prefill_fused_call" if pre["fused"] else "prefill_unfused_step"
     traffic = traffic_record(key, src_hash(*kfile))
@@ -326,9 +326,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": key,
-                     "launches": (["causal_conv1d_kernel (B)", "causal_conv1d_kernel (C)",
-                                   "scan_bf16_kernel"] if pre["fused"] else
-                                  ["causal_conv1d_kernel (x|B|C)", "scan_bf16_kernel"]),
+                     "launches": (["bc_pack_kernel", "scan_bf16_kernel"] if pre["fused"] else
+                                  ["causal_conv1d_kernel (x|B|C)", "bc_pack_kernel",
+                                   "scan_bf16_kernel"]),
                      "alg_bytes_per_token": bpt, "tokens_per_launch": wl.tokens,
                      "launch_ms": kernel_ms, "measured_peak": copy_gbs,
                      "frac_of_measured": achieved / copy_gbs},

@@ -589,10 +589,11 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
   auto prefetch = [&](int cc) {
     const int tt0 = cc * Q;
     sx.load(a, b, h, tt0);
-    // every lane loads (threads tid >= Q re-read a token of the chunk and
-    // never use it), so no branch separates these loads from the ones after
+    // every lane loads (threads tid >= Q all re-read the chunk's first token,
+    // one cache line, and never use it), so no branch separates these loads
+    // from the ones after
     dtv.load(static_cast<const Ta*>(a.dt) +
-             ((int64_t)b * L + min(tt0 + (tid & (Q - 1)), L - 1)) * a.dt_stride + h);
+             ((int64_t)b * L + min(tt0 + (tid < Q ? tid : 0), L - 1)) * a.dt_stride + h);
   };
   if (cbeg < cend) prefetch(cbeg);
 
@@ -649,9 +650,11 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) cf[kk] = ldg8(pk + PK_C + ((rt * 4 + kk) * 64 + lane) * 8);
       const float* cbsrc = reinterpret_cast<const float*>(pk + PK_CB) + (tri(rt) * 64 + lane) * 4;
+      // tiles past rt are not loaded (wave-uniform branches; the loads
+      // after these still retire after them)
 #pragma unroll
       for (int u = 0; u < Q / 16; ++u)
-        cbt[u] = *reinterpret_cast<const f32x4*>(cbsrc + min(u, rt) * 256);
+        if (u <= rt) cbt[u] = *reinterpret_cast<const f32x4*>(cbsrc + u * 256);
       // without a gate the loads read the start of the B|C pack instead
       // (at least 128 KiB of global memory; the values are not used): no
       // branch, and both pointers stay global so the loads are not flat
