@@ -56,10 +56,17 @@ __global__ __launch_bounds__(THREADS) void state_update_kernel(
   float* sdec = sdel + hpg;
   float* sskip = sdec + hpg;
 
+  // The first head's state does not depend on the conv step: its loads are
+  // issued first, so they are in flight during it.
+  const int h0 = g * hpg;
+  float4* st = reinterpret_cast<float4*>(state + ((int64_t)b * H + h0) * P * N);
+  float4 cur[PASSES];
+#pragma unroll
+  for (int j = 0; j < PASSES; ++j) cur[j] = ld_stream(st + tid + THREADS * j);
+
   // Everything per head that the state loop needs is read here, ahead of it:
   // inside the loop the only loads are the state stream, so waiting for one
   // head's state never waits behind a small load issued after the prefetch.
-  const int h0 = g * hpg;
   for (int i = tid; i < nx; i += THREADS)
     sgate[i] = z != nullptr ? silu_f32(to_f32(z[(int64_t)b * HP + h0 * P + i])) : 1.f;
   if (tid < hpg) {
@@ -96,10 +103,6 @@ __global__ __launch_bounds__(THREADS) void state_update_kernel(
   const float4 Bv = reinterpret_cast<const float4*>(sxc + nx)[col];
   const float4 Cv = reinterpret_cast<const float4*>(sxc + nx + N)[col];
 
-  float4* st = reinterpret_cast<float4*>(state + ((int64_t)b * H + h0) * P * N);
-  float4 cur[PASSES];
-#pragma unroll
-  for (int j = 0; j < PASSES; ++j) cur[j] = ld_stream(st + tid + THREADS * j);
 
   for (int hh = 0; hh < hpg; ++hh) {
     const int h = h0 + hh;
