@@ -470,25 +470,6 @@ struct StageX {
   }
 };
 
-// In-place inclusive prefix sum of s[0..Q) by waves 0 and 1 (fixed order).
-__device__ __forceinline__ void scan_lam(float* s, float* red) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  float v = 0.f;
-  if (tid < Q) {
-    v = s[tid];
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const float o = __shfl_up(v, d, 64);
-      if (lane >= d) v += o;
-    }
-    if (lane == 63) red[w] = v;
-  }
-  lds_barrier();
-  if (tid >= 64 && tid < Q) s[tid] = v + red[0];
-  if (tid < 64) s[tid] = v;
-  lds_barrier();
-}
-
 // Walker index of this workgroup: (sequence b, head h, segment seg), with
 // the heads of one (b, group, segment) contiguous and dealt to one XCD.
 struct Walker {
@@ -619,7 +600,17 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
       if (a.dt_softplus) d = softplus_f32(d);
       if (tid >= Lc) d = 0.f;
       sDel[tid] = d;
-      sLam[tid] = d * Ah;
+      // inclusive prefix sum of delta A over the wave's 64 tokens (fixed
+      // order); the second wave's values lack the first wave's total, which
+      // the readers add (lam() below)
+      float v = d * Ah;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float u = __shfl_up(v, o, 64);
+        if (lane >= o) v += u;
+      }
+      sLam[tid] = v;
+      if (tid == 63) sRed[0] = v;
     }
     float xt[16];  // xt[8 i + e] = x[2 xr + i][8 xv + e], post-conv fp32
     sx.compute(a, sCw, t0, Lc, xt);
@@ -668,15 +659,17 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     // unconditional (the last chunk re-reads itself), for the same reason
     prefetch(min(c + 1, cend - 1));
     lds_barrier();
-    scan_lam(sLam, sRed);  // ends with a barrier
-    const float lam_last = sLam[Q - 1];
+    // Lam_s, the cumulative log decay of the chunk up to token s
+    const float carry = sRed[0];
+    auto lam = [&](int s) { return sLam[s] + (s >= 64 ? carry : 0.f); };
+    const float lam_last = lam(Q - 1);
     if (STATE_ONLY) log_decay += lam_last;
 
     // ---- (x o w) split into bf16 hi + lo, [p][s], once per workgroup, with
     //      w_s = exp(Lam_last - Lam_s) delta_s of the thread's two tokens
     {
-      const float w0 = __expf(lam_last - sLam[2 * xr]) * sDel[2 * xr];
-      const float w1 = __expf(lam_last - sLam[2 * xr + 1]) * sDel[2 * xr + 1];
+      const float w0 = __expf(lam_last - lam(2 * xr)) * sDel[2 * xr];
+      const float w1 = __expf(lam_last - lam(2 * xr + 1)) * sDel[2 * xr + 1];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         bf16x2 hi, lo;
@@ -726,7 +719,7 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
 #pragma unroll
         for (int pj = 0; pj < 4; ++pj)
           yacc[pj] = mfma(lds8(sH + (16 * pj + l16) * LDB + 32 * kk + 8 * q), cf[kk], yacc[pj]);
-      const float lam_t = sLam[tcol];
+      const float lam_t = lam(tcol);
       {
         const float e = __expf(lam_t);
 #pragma unroll
@@ -752,7 +745,8 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
           const int s0 = 16 * u + 4 * q;
           const float4 l4 = *reinterpret_cast<const float4*>(sLam + s0);
           const float4 d4 = *reinterpret_cast<const float4*>(sDel + s0);
-          const float ls[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float cs = s0 >= 64 ? carry : 0.f;  // the 4 tokens share a wave
+          const float ls[4] = {l4.x + cs, l4.y + cs, l4.z + cs, l4.w + cs};
           const float ds[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
