@@ -595,6 +595,15 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     }
 
     lds_barrier();  // the previous chunk is done with every LDS buffer
+    if (OUT && c > cbeg) {
+      // the bf16 copy of the state for this chunk's read-out (the previous
+      // chunk's read-out of the older state is complete past the barrier)
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          sH[(16 * pt + 4 * q + r) * LDB + ncol] = (bf16)hacc[pt][r];
+    }
     if (tid < Q) {
       float d = dtv.get() + dtb;
       if (a.dt_softplus) d = softplus_f32(d);
@@ -690,7 +699,7 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     // ---- state: H <- exp(Lam_last) H + (X o w)^T B, operands split hi + lo;
     //      this wave's columns n = ncol, all 64 rows p.  The read-out below
     //      still uses the previous state through its bf16 copy in sH, which
-    //      is replaced at the end of the chunk.
+    //      is replaced at the start of the next chunk.
     const float gamma = __expf(lam_last);
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) hacc[pt] *= gamma;
@@ -783,14 +792,6 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
           store4(yrow + 16 * pj, yv);
         }
       }
-    }
-    if (OUT) {
-      lds_barrier();  // every wave is done reading the previous state in sH
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          sH[(16 * pt + 4 * q + r) * LDB + ncol] = (bf16)hacc[pt][r];
     }
   }
 
