@@ -501,6 +501,8 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 sH[OUT ? P * LDB : 8];     // H [p][n]
   __shared__ __attribute__((aligned(16))) float sLam[Q];
   __shared__ __attribute__((aligned(16))) float sDel[Q];
+  // exp(Lam_r - Lam_s) delta_s, r the last token of s's 16-token tile
+  __shared__ __attribute__((aligned(16))) float sE[OUT ? Q : 4];
   __shared__ float sRed[4];
   __shared__ __attribute__((aligned(16))) float sCw[XCONV ? 5 * P : 4];  // x-channel conv
 
@@ -620,6 +622,10 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
       }
       sLam[tid] = v;
       if (tid == 63) sRed[0] = v;
+      // the tile's last token is in the same wave, so the difference needs
+      // no carry; it is <= 0 (the decay only shrinks)
+      const float vr = __shfl(v, lane | 15, 64);
+      if (OUT) sE[tid] = __expf(vr - v) * d;
     }
     float xt[16];  // xt[8 i + e] = x[2 xr + i][8 xv + e], post-conv fp32
     sx.compute(a, sCw, t0, Lc, xt);
@@ -752,15 +758,27 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
           const f32x4 cb = cbt[u];
           // cb[r] = (B C^T)[s = 16 u + 4 q + r][t = tcol]
           const int s0 = 16 * u + 4 * q;
-          const float4 l4 = *reinterpret_cast<const float4*>(sLam + s0);
-          const float4 d4 = *reinterpret_cast<const float4*>(sDel + s0);
-          const float cs = s0 >= 64 ? carry : 0.f;  // the 4 tokens share a wave
-          const float ls[4] = {l4.x + cs, l4.y + cs, l4.z + cs, l4.w + cs};
-          const float ds[4] = {d4.x, d4.y, d4.z, d4.w};
+          if (u < rt) {
+            // below the diagonal every s precedes every t: the decay
+            // exp(Lam_t - Lam_s) factors through the tile's last token r as
+            // exp(Lam_t - Lam_r) exp(Lam_r - Lam_s), both factors <= 1
+            const float f = __expf(lam_t - lam(16 * u + 15));
+            const float4 e4 = *reinterpret_cast<const float4*>(sE + s0);
+            mf[4 * half + 0] = (bf16)(cb[0] * f * e4.x);
+            mf[4 * half + 1] = (bf16)(cb[1] * f * e4.y);
+            mf[4 * half + 2] = (bf16)(cb[2] * f * e4.z);
+            mf[4 * half + 3] = (bf16)(cb[3] * f * e4.w);
+          } else {
+            const float4 l4 = *reinterpret_cast<const float4*>(sLam + s0);
+            const float4 d4 = *reinterpret_cast<const float4*>(sDel + s0);
+            const float cs = s0 >= 64 ? carry : 0.f;  // the 4 tokens share a wave
+            const float ls[4] = {l4.x + cs, l4.y + cs, l4.z + cs, l4.w + cs};
+            const float ds[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float m = s0 + r <= tcol ? cb[r] * __expf(lam_t - ls[r]) * ds[r] : 0.f;
-            mf[4 * half + r] = (bf16)m;
+            for (int r = 0; r < 4; ++r) {
+              const float m = s0 + r <= tcol ? cb[r] * __expf(lam_t - ls[r]) * ds[r] : 0.f;
+              mf[4 * half + r] = (bf16)m;
+            }
           }
         }
 #pragma unroll
