@@ -677,7 +677,10 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     // Lam_s, the cumulative log decay of the chunk up to token s
     const float carry = sRed[0];
     auto lam = [&](int s) { return sLam[s] + (s >= 64 ? carry : 0.f); };
-    const float lam_last = lam(Q - 1);
+    // the decay to the chunk's last token: token Lc - 1, not Q - 1 -- past
+    // the end the increments are 0, but they are summed in another order, so
+    // the two can differ by an ulp, which is large when |Lam| is
+    const float lam_last = lam(Lc - 1);
     if (STATE_ONLY) log_decay += lam_last;
 
     // ---- (x o w) split into bf16 hi + lo, [p][s], once per workgroup, with

@@ -121,7 +121,10 @@ __global__ __launch_bounds__(THREADS) void scan_f32_kernel(ScanArgs a) {
     }
     __syncthreads();
     block_inclusive_scan(sLam, Q, sRed);
-    const float lam_last = sLam[Q - 1];
+    // the decay to the chunk's last token: slot Lc - 1, not Q - 1 -- past the
+    // end the increments are 0, but the scan adds them in another order, so
+    // the two slots can differ by an ulp, which is large when |Lam| is
+    const float lam_last = sLam[Lc - 1];
 
     for (int tt0 = 0; tt0 < Lc; tt0 += TT) {
       for (int i = tid; i < TT * N; i += THREADS) {

@@ -99,6 +99,46 @@ def test_scan_post_conv(math_mode, B, L, H, G):
         assert rel_max_err(hg, hr) <= TOL[math_mode]
 
 
+@pytest.mark.parametrize("math_mode", ["f32", "bf16"])
+@pytest.mark.parametrize("shift", [6.0, 40.0])
+def test_scan_strong_decay(math_mode, shift):
+    """Raw dt shifted far up (delta ~ shift, delta*A down to about -16*shift
+    per token, |Lam| up to ~10^4 within a chunk): the decay factors underflow
+    within a few tokens and only the most recent tokens contribute.  Every
+    output stays finite and matches the oracle, the SSM part included (D = 0,
+    no gate probe).  This also pins the decay of a partial last chunk to its
+    last real token (an ulp of Lam there is a visible factor on the state).
+
+    With delta ~ 40 the SSM term dominates y, whose max error then measures
+    the bf16 rounding of the decayed C B^T tile (2^-9 relative, R26): that
+    case is held to the relative-RMS bound instead."""
+    dtype = "f32" if math_mode == "f32" else "bf16"
+    inp = small(1, 300, 4, 2, dtype, seed=31)
+    inp.dt = inp.dt + np.float32(shift)
+    if dtype == "bf16":
+        synth.round_bf16_(inp.dt)
+    say("strong decay %s shift %g" % (math_mode, shift))
+    pairs = [(0, h) for h in range(4)]
+    for probe in (False, True):
+        p = params(inp, D=not probe)
+        x, Bm, Cm = layer.split_xbc(dev(inp.xbc, dtype), p)
+        fs = torch.empty((1, 4, 64, 128), device="cuda")
+        y = ssd.ssd_chunk_scan_fwd(x, Bm, Cm, dev(inp.dt, dtype), p.A, D=p.D,
+                                   z=None if probe else dev(inp.z, dtype), dt_bias=p.dt_bias,
+                                   initial_state=dev32(inp.h0), final_state=fs,
+                                   chunk=128, math=math_mode)
+        torch.cuda.synchronize()
+        assert torch.isfinite(y).all() and torch.isfinite(fs).all()
+        yr, hr = oracle_pairs(inp, pairs, conv=False, D=not probe, z=not probe)
+        yg = gather_y(y, pairs)
+        hg = np.stack([fs[b, h].double().cpu().numpy() for b, h in pairs])
+        if probe or (math_mode == "bf16" and shift > 10):
+            assert rel_rms_err(yg, yr) <= PROBE_TOL[math_mode]
+        else:
+            assert rel_max_err(yg, yr) <= TOL[math_mode]
+        assert rel_max_err(hg, hr) <= TOL[math_mode]
+
+
 @pytest.mark.parametrize("chunk", [32, 64, 256])
 def test_scan_f32_other_chunks(chunk):
     inp = small(1, 300, 2, 1, "f32")
