@@ -646,13 +646,18 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
         *reinterpret_cast<bf16x2*>(sXh + prow(8 * xv + e) * LDT + 2 * xr) = v2;
       }
     }
-    // C rows of this wave's tokens and z of token tcol, channels 16 pj + 4 q ..
-    // (tokens past the end re-read the last one and are never stored), then
-    // the next chunk's prefetch: the memory counter retires loads in order, so
-    // waiting for C and z later does not wait for the prefetch
+    // The loads of this chunk's per-wave operands are spread over the
+    // chunk (all waves issue theirs at the same time, and they share the
+    // CU's load path): the next chunk's x and dt now, the C rows and C B^T
+    // tiles after the staging barrier, z after the state product.
     Raw4<Ta> zr[4];
     f32x4 cbt[Q / 16];  // B C^T tiles u <= rt of this wave's tokens (u > rt: unused)
+    // unconditional (the last chunk re-reads itself), so that no branch
+    // separates these loads from the ones after
+    prefetch(min(c + 1, cend - 1));
+    lds_barrier();
     if (OUT) {
+      // C rows of this wave's tokens and its C B^T tiles
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) cf[kk] = ldg8(pk + PK_C + ((rt * 4 + kk) * 64 + lane) * 8);
       const float* cbsrc = reinterpret_cast<const float*>(pk + PK_CB) + (tri(rt) * 64 + lane) * 4;
@@ -661,19 +666,7 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
 #pragma unroll
       for (int u = 0; u < Q / 16; ++u)
         if (u <= rt) cbt[u] = *reinterpret_cast<const f32x4*>(cbsrc + u * 256);
-      // without a gate the loads read the start of the B|C pack instead
-      // (at least 128 KiB of global memory; the values are not used): no
-      // branch, and both pointers stay global so the loads are not flat
-      const Ta* zrow = a.z != nullptr
-                           ? static_cast<const Ta*>(a.z) +
-                                 (row0 + min(tcol, Lc - 1)) * a.z_stride + h * P + 4 * q
-                           : static_cast<const Ta*>(a.bc_pack) + 4 * q;
-#pragma unroll
-      for (int pj = 0; pj < 4; ++pj) zr[pj].load(zrow + 16 * pj);
     }
-    // unconditional (the last chunk re-reads itself), for the same reason
-    prefetch(min(c + 1, cend - 1));
-    lds_barrier();
     // Lam_s, the cumulative log decay of the chunk up to token s
     const float carry = sRed[0];
     auto lam = [&](int s) { return sLam[s] + (s >= 64 ? carry : 0.f); };
@@ -728,6 +721,19 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
+    if (OUT) {
+      // z of token tcol, channels 16 pj + 4 q .. (tokens past the end re-read
+      // the last one and are never stored); without a gate the loads read
+      // the start of the B|C pack instead (at least 128 KiB of global memory;
+      // the values are not used): no branch, and both pointers stay global
+      // so the loads are not flat
+      const Ta* zrow = a.z != nullptr
+                           ? static_cast<const Ta*>(a.z) +
+                                 (row0 + min(tcol, Lc - 1)) * a.z_stride + h * P + 4 * q
+                           : static_cast<const Ta*>(a.bc_pack) + 4 * q;
+#pragma unroll
+      for (int pj = 0; pj < 4; ++pj) zr[pj].load(zrow + 16 * pj);
+    }
     if (OUT) {
       // ---- inter-chunk read-out, transposed: Y^T = H C^T scaled by exp(Lam_t);
       //      element r of yacc[pj] is (p = 16 pj + 4 q + r, t = tcol)
