@@ -60,6 +60,10 @@ def _bind(lib):
     lib.oracle_mamba2_decode_step.argtypes = [P, P, P, P, P, I, P, P, P, P, I, P, P,
                                               I, I, I, I, I]
     lib.oracle_mamba2_decode_step.restype = I
+    lib.oracle_rmsnorm.argtypes = [P, P, ctypes.c_double, P, I64, I]
+    lib.oracle_rmsnorm.restype = I
+    lib.oracle_linear.argtypes = [P, P, P, P, I64, I, I]
+    lib.oracle_linear.restype = I
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = I
     return lib
@@ -80,10 +84,12 @@ def _load():
     return _lib
 
 
-def _f32(a):
+def _in(a):
+    """An input as the layer receives it: rounded to fp32, held in fp64
+    (exactly) for the C code."""
     if a is None:
         return None
-    return np.ascontiguousarray(a, dtype=np.float32)
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32), dtype=np.float64)
 
 
 def _f64(a):
@@ -106,12 +112,12 @@ def causal_conv1d(xbc, w, bias=None, conv_state_in=None, apply_silu=True):
     Returns (out [B, L, Cdim] float64, conv_state_out [B, K-1, Cdim] float64).
     """
     lib = _load()
-    x = _f32(xbc)
+    x = _in(xbc)
     B, L, C = x.shape
-    w = _f32(w)
+    w = _in(w)
     K = w.shape[1]
-    bias = _f32(bias)
-    hist = _f32(conv_state_in)
+    bias = _in(bias)
+    hist = _in(conv_state_in)
     out = np.empty((B, L, C), np.float64)
     hist_out = np.empty((B, K - 1, C), np.float64)
     rc = lib.oracle_causal_conv1d(_ptr(x), C, _ptr(w), _ptr(bias), _ptr(hist),
@@ -124,29 +130,33 @@ def causal_conv1d(xbc, w, bias=None, conv_state_in=None, apply_silu=True):
 
 def mamba2_fwd(xbc, dt, A, *, nheads, headdim, ngroups, dstate, conv_w=None,
                conv_b=None, conv_state_in=None, D=None, dt_bias=None,
-               dt_softplus=True, z=None, h0=None):
+               dt_softplus=True, z=None, h0=None, f64_activations=False):
     """The layer, token by token in fp64.
 
     xbc [B, L, Cdim] raw x|B|C (post-conv when conv_w is None); dt [B, L, H];
     A [H]; z [B, L, H, P] or None; h0 [B, H, P, N] or None.
+    Inputs are taken as fp32 values (rounded to fp32 first), except that with
+    f64_activations xbc, dt and z are used unrounded (an fp64 intermediate,
+    as in mamba2_block_fwd).
     Returns (y [B, L, H, P], h_final [B, H, P, N], conv_state_out or None),
     all float64.
     """
     lib = _load()
-    x = _f32(xbc)
+    act = _f64 if f64_activations else _in
+    x = act(xbc)
     B, L, C = x.shape
     H, P, G, N = nheads, headdim, ngroups, dstate
     if C != H * P + 2 * G * N:
         raise ValueError("xbc channel count %d != H*P + 2*G*N" % C)
-    dt = _f32(dt).reshape(B, L, H)
-    A = _f32(A)
-    conv_w = _f32(conv_w)
+    dt = act(dt).reshape(B, L, H)
+    A = _in(A)
+    conv_w = _in(conv_w)
     K = 0 if conv_w is None else conv_w.shape[1]
-    conv_b = _f32(conv_b)
-    hist = _f32(conv_state_in)
-    D = _f32(D)
-    dt_bias = _f32(dt_bias)
-    z = None if z is None else _f32(z).reshape(B, L, H, P)
+    conv_b = _in(conv_b)
+    hist = act(conv_state_in)
+    D = _in(D)
+    dt_bias = _in(dt_bias)
+    z = None if z is None else act(z).reshape(B, L, H, P)
     h0 = None if h0 is None else _f64(h0).reshape(B, H, P, N)
     y = np.empty((B, L, H, P), np.float64)
     hT = np.empty((B, H, P, N), np.float64)
@@ -158,6 +168,72 @@ def mamba2_fwd(xbc, dt, A, *, nheads, headdim, ngroups, dstate, conv_w=None,
     if rc != 0:
         raise ValueError("oracle_mamba2_fwd: bad argument")
     return y, hT, hist_out
+
+
+def rmsnorm(x, w=None, eps=1e-5):
+    """RMSNorm over the last axis: x / sqrt(mean(x^2) + eps) * w, in fp64.
+
+    x [..., dim]; w [dim] or None.  Returns float64 of x's shape."""
+    lib = _load()
+    xa = _in(x)
+    dim = xa.shape[-1]
+    ntok = xa.size // dim
+    out = np.empty(xa.shape, np.float64)
+    if lib.oracle_rmsnorm(_ptr(xa), _ptr(_in(w)), float(eps), _ptr(out), ntok, dim) != 0:
+        raise ValueError("oracle_rmsnorm: bad argument")
+    return out
+
+
+def linear(a, w, residual=None):
+    """a @ w^T (+ residual) in fp64, with w stored [out, in].
+
+    a [..., K] (fp64 values are used as given); w [N, K]; residual [..., N]
+    or None.  Returns float64 [..., N]."""
+    lib = _load()
+    aa = _f64(a)
+    K = aa.shape[-1]
+    M = aa.size // K
+    wa = _in(w)
+    N = wa.shape[0]
+    if wa.shape[1] != K:
+        raise ValueError("linear: weight is [%d, %d], input has %d features" % (N, wa.shape[1], K))
+    res = None if residual is None else _in(residual).reshape(M, N)
+    out = np.empty(aa.shape[:-1] + (N,), np.float64)
+    if lib.oracle_linear(_ptr(aa), _ptr(wa), _ptr(res), _ptr(out), M, N, K) != 0:
+        raise ValueError("oracle_linear: bad argument")
+    return out
+
+
+def mamba2_block_fwd(h, norm_w, in_proj_w, out_proj_w, A, *, nheads, headdim, ngroups,
+                     dstate, conv_w, conv_b=None, conv_state_in=None, D=None,
+                     dt_bias=None, dt_softplus=True, h0=None, norm_eps=1e-5):
+    """The pre-norm residual block around the layer, in fp64:
+    out = h + out_proj(mixer(rmsnorm(h))), with the mixer
+    in_proj -> (z | x B C | dt) -> conv + SiLU on x|B|C -> scan, D skip and
+    SiLU(z) gate -> out_proj.
+
+    h [B, L, d_model]; norm_w [d_model] or None; in_proj_w
+    [2*H*P + 2*G*N + H, d_model] whose output rows are ordered z (H*P),
+    x (H*P), B (G*N), C (G*N), dt (H); out_proj_w [d_model, H*P].
+    Returns (out [B, L, d_model], h_final, conv_state_out), all float64.
+    """
+    H, P, G, N = nheads, headdim, ngroups, dstate
+    HP, GN = H * P, G * N
+    hh = _in(h)
+    Bsz, L, dm = hh.shape
+    u = rmsnorm(hh, norm_w, norm_eps)
+    zxbcdt = linear(u, in_proj_w)
+    if zxbcdt.shape[-1] != 2 * HP + 2 * GN + H:
+        raise ValueError("in_proj has %d outputs, expected %d" % (zxbcdt.shape[-1], 2 * HP + 2 * GN + H))
+    z = zxbcdt[..., :HP].reshape(Bsz, L, H, P)
+    xbc = zxbcdt[..., HP:2 * HP + 2 * GN]
+    dt = zxbcdt[..., 2 * HP + 2 * GN:]
+    y, hT, conv_out = mamba2_fwd(xbc, dt, A, nheads=H, headdim=P, ngroups=G, dstate=N,
+                                 conv_w=conv_w, conv_b=conv_b, conv_state_in=conv_state_in,
+                                 D=D, dt_bias=dt_bias, dt_softplus=dt_softplus, z=z, h0=h0,
+                                 f64_activations=True)
+    out = linear(y.reshape(Bsz, L, HP), out_proj_w, residual=hh)
+    return out, hT, conv_out
 
 
 class DecodeState:
@@ -174,16 +250,16 @@ def mamba2_decode_step(carry: DecodeState, xbc, dt, A, *, nheads, headdim, ngrou
                        dt_softplus=True, z=None):
     """One decode step; updates ``carry`` in place and returns y [B, H*P] float64."""
     lib = _load()
-    x = _f32(xbc)
+    x = _in(xbc)
     B, C = x.shape
     H, P, G, N = nheads, headdim, ngroups, dstate
-    conv_w = _f32(conv_w)
+    conv_w = _in(conv_w)
     K = 0 if conv_w is None else conv_w.shape[1]
     y = np.empty((B, H * P), np.float64)
     rc = lib.oracle_mamba2_decode_step(
-        _ptr(carry.state), _ptr(x), _ptr(carry.ring), _ptr(conv_w), _ptr(_f32(conv_b)), K,
-        _ptr(_f32(dt).reshape(B, H)), _ptr(_f32(A)), _ptr(_f32(D)), _ptr(_f32(dt_bias)),
-        int(bool(dt_softplus)), _ptr(None if z is None else _f32(z).reshape(B, H * P)),
+        _ptr(carry.state), _ptr(x), _ptr(carry.ring), _ptr(conv_w), _ptr(_in(conv_b)), K,
+        _ptr(_in(dt).reshape(B, H)), _ptr(_in(A)), _ptr(_in(D)), _ptr(_in(dt_bias)),
+        int(bool(dt_softplus)), _ptr(None if z is None else _in(z).reshape(B, H * P)),
         _ptr(y), B, H, P, G, N)
     if rc != 0:
         raise ValueError("oracle_mamba2_decode_step: bad argument")

@@ -37,8 +37,12 @@
  *  - head h reads group g = floor(h*G/H);
  *  - gate: out = y * z * sigmoid(z); no gate when z is NULL.
  *
+ * Inputs are double.  The Python wrapper rounds the layer's inputs to fp32
+ * first (the precision they arrive in); the block composition passes its
+ * in_proj output on unrounded.
+ *
  * Layouts (all row-major, innermost index contiguous):
- *   xbc  [B][L][Cdim] with a token stride (in floats), Cdim = H*P + 2*G*N,
+ *   xbc  [B][L][Cdim] with a token stride (in elements), Cdim = H*P + 2*G*N,
  *        channel order x (H*P) | B (G*N) | C (G*N)
  *   dt   [B][L][H]        z, y [B][L][H][P]
  *   h0, h_final [B][H][P][N]   conv_state [B][K-1][Cdim] (oldest row first)
@@ -64,8 +68,8 @@ static double silu(double u) { return u / (1.0 + exp(-u)); }
 
 /* The raw conv input of channel c at position tau of sequence b.  tau < 0
  * reads the history: row (K-1)+tau of conv_state_in, or zero. */
-static double conv_input(const float* xbc, int64_t tok_stride,
-                         const float* hist, int seqlen, int cdim, int width,
+static double conv_input(const double* xbc, int64_t tok_stride,
+                         const double* hist, int seqlen, int cdim, int width,
                          int b, int tau, int c) {
   if (tau >= 0)
     return (double)xbc[((int64_t)b * seqlen + tau) * tok_stride + c];
@@ -75,8 +79,8 @@ static double conv_input(const float* xbc, int64_t tok_stride,
 
 /* Depthwise causal conv of channel c at token t, before the activation:
  * u = bias[c] + sum_k w[c][k] * xin[t - (K-1) + k]. */
-static double conv_pre(const float* xbc, int64_t tok_stride, const float* hist,
-                       const float* w, const float* bias, int seqlen, int cdim,
+static double conv_pre(const double* xbc, int64_t tok_stride, const double* hist,
+                       const double* w, const double* bias, int seqlen, int cdim,
                        int width, int b, int t, int c) {
   double u = bias ? (double)bias[c] : 0.0;
   for (int k = 0; k < width; ++k)
@@ -87,7 +91,7 @@ static double conv_pre(const float* xbc, int64_t tok_stride, const float* hist,
 
 /* The last K-1 raw inputs of each channel after the sequence, oldest first
  * (taken from the old history when the sequence is shorter than K-1). */
-static void conv_history_out(const float* xbc, int64_t tok_stride, const float* hist,
+static void conv_history_out(const double* xbc, int64_t tok_stride, const double* hist,
                              double* hist_out, int batch, int seqlen, int cdim,
                              int width) {
   for (int b = 0; b < batch; ++b)
@@ -103,8 +107,8 @@ static void conv_history_out(const float* xbc, int64_t tok_stride, const float* 
  *   out [B][L][Cdim] (double, dense), hist_out [B][K-1][Cdim] or NULL.
  * Returns 0, or -1 on a bad argument.
  */
-int oracle_causal_conv1d(const float* xbc, int64_t tok_stride, const float* w,
-                         const float* bias, const float* conv_state_in,
+int oracle_causal_conv1d(const double* xbc, int64_t tok_stride, const double* w,
+                         const double* bias, const double* conv_state_in,
                          int apply_silu, double* out, double* conv_state_out,
                          int batch, int seqlen, int cdim, int width) {
   if (!xbc || !w || !out || batch < 0 || seqlen < 0 || cdim <= 0 || width < 1 ||
@@ -142,10 +146,10 @@ int oracle_causal_conv1d(const float* xbc, int64_t tok_stride, const float* w,
  * Any of conv_b, conv_state_in, D, dt_bias, z, h0, h_final, conv_state_out
  * may be NULL.  Returns 0, or -1 on a bad argument.
  */
-int oracle_mamba2_fwd(const float* xbc, int64_t xbc_tok_stride, const float* conv_w,
-                      const float* conv_b, int width, const float* conv_state_in,
-                      const float* dt, const float* A, const float* D,
-                      const float* dt_bias, int dt_softplus, const float* z,
+int oracle_mamba2_fwd(const double* xbc, int64_t xbc_tok_stride, const double* conv_w,
+                      const double* conv_b, int width, const double* conv_state_in,
+                      const double* dt, const double* A, const double* D,
+                      const double* dt_bias, int dt_softplus, const double* z,
                       const double* h0, double* y, double* h_final,
                       double* conv_state_out, int batch, int seqlen, int nheads,
                       int headdim, int ngroups, int dstate) {
@@ -224,10 +228,10 @@ int oracle_mamba2_fwd(const float* xbc, int64_t xbc_tok_stride, const float* con
  * ring drops its oldest row and appends xbc.  The SSM step is the same
  * recurrence as oracle_mamba2_fwd for one token.
  */
-int oracle_mamba2_decode_step(double* state, const float* xbc, double* ring,
-                              const float* conv_w, const float* conv_b, int width,
-                              const float* dt, const float* A, const float* D,
-                              const float* dt_bias, int dt_softplus, const float* z,
+int oracle_mamba2_decode_step(double* state, const double* xbc, double* ring,
+                              const double* conv_w, const double* conv_b, int width,
+                              const double* dt, const double* A, const double* D,
+                              const double* dt_bias, int dt_softplus, const double* z,
                               double* y, int batch, int nheads, int headdim,
                               int ngroups, int dstate) {
   const int H = nheads, P = headdim, G = ngroups, N = dstate;
@@ -280,6 +284,51 @@ int oracle_mamba2_decode_step(double* state, const float* xbc, double* ring,
       }
     }
   free(xc);
+  return 0;
+}
+
+/*
+ * RMSNorm over the last axis of x [ntok][dim] (dense):
+ *   out[t][i] = x[t][i] / sqrt(mean_j x[t][j]^2 + eps) * w[i]
+ * (no weight when w is NULL).  This is the norm of the pre-norm residual
+ * block x + mamba(norm(x)) in "Nemotron-H style Hybrid Mamba-Transformer 3B
+ * feasibility study", section 3.2 (approach A); its definition (root mean
+ * square over the channels, a learned per-channel scale, eps inside the
+ * root) is the standard one.  Returns 0, or -1 on a bad argument.
+ */
+int oracle_rmsnorm(const double* x, const double* w, double eps, double* out,
+                   int64_t ntok, int dim) {
+  if (!x || !out || ntok < 0 || dim <= 0 || !(eps >= 0.0)) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < ntok; ++t) {
+    const double* xr = x + t * dim;
+    double ss = 0.0;
+    for (int i = 0; i < dim; ++i) ss += xr[i] * xr[i];
+    const double r = 1.0 / sqrt(ss / dim + eps);
+    for (int i = 0; i < dim; ++i) out[t * dim + i] = xr[i] * r * (w ? w[i] : 1.0);
+  }
+  return 0;
+}
+
+/*
+ * Linear map with the weight stored [out][in] (a projection's layout):
+ *   out[m][n] = sum_k a[m][k] * w[n][k]  (+ residual[m][n] when given)
+ * a [M][K], w [N][K], residual and out [M][N], all dense.  The in_proj and
+ * out_proj projections of the Mamba-2 mixer (parameters about
+ * 3 * expand * d_model^2 per layer: feasibility study, section 2.4) and the
+ * residual add of section 3.2 are this map.  Returns 0, or -1 on a bad
+ * argument.
+ */
+int oracle_linear(const double* a, const double* w, const double* residual, double* out,
+                  int64_t M, int N, int K) {
+  if (!a || !w || !out || M < 0 || N <= 0 || K <= 0) return -1;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t m = 0; m < M; ++m)
+    for (int n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int k = 0; k < K; ++k) acc += a[m * K + k] * w[(int64_t)n * K + k];
+      out[m * N + n] = residual ? residual[m * N + n] + acc : acc;
+    }
   return 0;
 }
 

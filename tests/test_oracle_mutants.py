@@ -8,6 +8,7 @@ import os
 import pytest
 
 import oracle
+import test_oracle_block_pins as bpins
 import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ssd_oracle.c")
@@ -36,6 +37,16 @@ MUTANTS = [
     ("decode ring appends at the front",
      "if (width > 1) r[(int64_t)(width - 2) * cdim] = xin;",
      "if (width > 1) r[0] = xin;"),
+    ("rmsnorm without eps", "const double r = 1.0 / sqrt(ss / dim + eps);",
+     "const double r = 1.0 / sqrt(ss / dim);"),
+    ("rmsnorm sum instead of mean", "const double r = 1.0 / sqrt(ss / dim + eps);",
+     "const double r = 1.0 / sqrt(ss + eps);"),
+    ("rmsnorm weight reversed", "out[t * dim + i] = xr[i] * r * (w ? w[i] : 1.0);",
+     "out[t * dim + i] = xr[i] * r * (w ? w[dim - 1 - i] : 1.0);"),
+    ("linear weight transposed", "acc += a[m * K + k] * w[(int64_t)n * K + k];",
+     "acc += a[m * K + k] * w[(int64_t)k * N + n];"),
+    ("linear residual dropped", "out[m * N + n] = residual ? residual[m * N + n] + acc : acc;",
+     "out[m * N + n] = acc;"),
     ("decode B x outer product uses C",
      "const double* Bv = xc + (int64_t)b * cdim + HP + g * N;",
      "const double* Bv = xc + (int64_t)b * cdim + HP + GN + g * N;"),
@@ -51,6 +62,11 @@ PINS = [
     lambda: pins.test_layer_equals_conv_then_scan(),
     lambda: pins.test_decode_equals_prefill(),
     lambda: pins.test_decode_without_conv_matches_closed_step(),
+    lambda: bpins.test_rmsnorm_worked_example(),
+    lambda: bpins.test_rmsnorm_constant_row(-2.5, 0.25),
+    lambda: bpins.test_rmsnorm_weight_scales_each_channel(),
+    lambda: bpins.test_linear_matches_numpy_matmul(),
+    lambda: bpins.test_block_matches_independent_composition(),
 ]
 
 
