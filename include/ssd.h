@@ -183,6 +183,89 @@ int ssd_state_update(float* state, const void* xbc, ssd_dtype_t xbc_dtype,
 size_t ssd_decode_cache_bytes(int nheads, int headdim, int ngroups, int dstate, int width,
                               ssd_dtype_t conv_dtype);
 
+/* ------------------------------------------------------------------------
+ * The block around the layer: the pre-norm residual block
+ *   out = h + out_proj(mixer(rmsnorm(h)))
+ * of "Nemotron-H style Hybrid Mamba-Transformer 3B feasibility study",
+ * section 3.2 (approach A), whose mixer is in_proj, the layer above (conv +
+ * SiLU, scan, D skip, SiLU(z) gate) and out_proj; the two projections hold
+ * about 3 * expand * d_model^2 parameters (its section 2.4).
+ * Readings where the pages are silent: RMSNorm is x / sqrt(mean(x^2) + eps)
+ * times a per-channel fp32 weight; in_proj's output rows are ordered
+ * z (H*P) | x (H*P) | B (G*N) | C (G*N) | dt (H); the intermediates (normed
+ * h, in_proj output, layer output) are bf16, the projections accumulate in
+ * fp32.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * RMSNorm of ntok rows: out[t][i] = x[t][i] / sqrt(mean_j x[t][j]^2 + eps) * w[i].
+ *   x   [ntok, dim] x_dtype, row stride x_tok_stride >= dim
+ *   weight [dim] fp32 or NULL (no scale); eps finite, >= 0
+ *   out [ntok, dim] out_dtype, row stride out_tok_stride >= dim; out may be x
+ *       itself (same dtype and stride) but may not overlap it otherwise
+ *   Supported: dim % 8 == 0; rows and weight 16-byte aligned.
+ * The sum of squares is fp32 in a fixed order (bitwise reproducible).
+ */
+int ssd_rmsnorm_fwd(const void* x, int64_t x_tok_stride, ssd_dtype_t x_dtype,
+                    const float* weight, float eps, void* out, int64_t out_tok_stride,
+                    ssd_dtype_t out_dtype, int64_t ntok, int dim, hipStream_t stream);
+
+/*
+ * Projection on the matrix cores: out[m][n] = sum_k a[m][k] * w[n][k]
+ * (+ residual[m][n]), bf16 operands, fp32 accumulation, one rounding to
+ * out_dtype at the end.
+ *   a   [M, K] bf16, row stride lda >= K
+ *   w   [N, K] bf16, row stride ldw >= K (the weight of a projection, stored
+ *       [out][in])
+ *   residual [M, N] res_dtype, row stride ldr >= N, or NULL; out may be the
+ *       residual itself (same dtype and stride: an in-place residual add)
+ *   out [M, N] out_dtype, row stride ldo >= N; may not overlap a or w
+ *   Supported: K % 8 == 0; base pointers and rows 16-byte aligned.
+ * M == 0 is a valid call that does nothing.
+ */
+int ssd_linear_fwd(const void* a, int64_t lda, const void* w, int64_t ldw, const void* residual,
+                   int64_t ldr, ssd_dtype_t res_dtype, void* out, int64_t ldo,
+                   ssd_dtype_t out_dtype, int64_t M, int N, int K, hipStream_t stream);
+
+/* Bytes of device workspace ssd_block_fwd needs (0 on bad input): the normed
+ * input, the in_proj output and the layer output in bf16 (2*d_model +
+ * 2*(2*H*P + 2*G*N + H rounded up to 8) + 2*H*P bytes per token), plus the
+ * layer's ssd_chunk_scan_workspace_bytes. */
+size_t ssd_block_workspace_bytes(int batch, int seqlen, int d_model, int nheads, int headdim,
+                                 int ngroups, int dstate);
+
+/*
+ * The whole block for a batch of sequences (prefill):
+ *   u = rmsnorm(h); [z | x B C | dt] = u in_proj_w^T;
+ *   y = the layer (ssd_chunk_scan_fwd with the fused conv, bf16 math) on them;
+ *   out = h + y out_proj_w^T.
+ *   h   [B, L, d_model] h_dtype, dense
+ *   norm_w [d_model] fp32 or NULL; norm_eps finite, >= 0
+ *   in_proj_w  [2*H*P + 2*G*N + H, d_model] bf16, dense
+ *   conv_w [Cdim, K] fp32, conv_b [Cdim] fp32 or NULL, conv_width K in [1,4],
+ *       Cdim = H*P + 2*G*N (the x|B|C channels)
+ *   A [H], D [H] or NULL, dt_bias [H] or NULL (fp32); dt_softplus 0/1
+ *   out_proj_w [d_model, H*P] bf16, dense
+ *   conv_state_in / conv_state_out [B, K-1, Cdim] bf16 or NULL (raw x|B|C
+ *       rows of the in_proj output, oldest first), as in ssd_chunk_scan_fwd
+ *   initial_state / final_state [B, H, P, N] fp32 or NULL, as in
+ *       ssd_chunk_scan_fwd
+ *   out [B, L, d_model] out_dtype, dense; may be h itself (same dtype: an
+ *       in-place update) but may not overlap it, a parameter or a state
+ *       otherwise
+ *   workspace: at least ssd_block_workspace_bytes(...) bytes, 256-byte
+ *       aligned, overlapping no tensor (NULL allowed when seqlen == 0)
+ *   Supported: P = 64, N = 128, H % G == 0, d_model % 8 == 0.
+ */
+int ssd_block_fwd(const void* h, ssd_dtype_t h_dtype, const float* norm_w, float norm_eps,
+                  const void* in_proj_w, const float* conv_w, const float* conv_b,
+                  int conv_width, const float* A, const float* D, const float* dt_bias,
+                  int dt_softplus, const void* out_proj_w, const void* conv_state_in,
+                  void* conv_state_out, const float* initial_state, float* final_state,
+                  void* out, ssd_dtype_t out_dtype, int batch, int seqlen, int d_model,
+                  int nheads, int headdim, int ngroups, int dstate, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream);
+
 /* Static text for a status code. */
 const char* ssd_status_string(int status);
 

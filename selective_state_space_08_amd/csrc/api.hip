@@ -388,4 +388,224 @@ int ssd_state_update(float* state, const void* xbc, ssd_dtype_t xbc_dtype, void*
   return e == hipSuccess ? SSD_OK : hip_fail(e, "state_update launch");
 }
 
+// ------------------------------------------------------------------ the block
+
+int ssd_rmsnorm_fwd(const void* x, int64_t x_tok_stride, ssd_dtype_t x_dtype,
+                    const float* weight, float eps, void* out, int64_t out_tok_stride,
+                    ssd_dtype_t out_dtype, int64_t ntok, int dim, hipStream_t stream) {
+  g_last_error.clear();
+  if (!valid_dtype(x_dtype) || !valid_dtype(out_dtype))
+    return fail(SSD_ERR_INVALID_ARG, "rmsnorm: bad dtype");
+  if (ntok < 0 || dim <= 0)
+    return fail(SSD_ERR_INVALID_ARG, "rmsnorm: bad size ntok=%lld dim=%d", (long long)ntok, dim);
+  if (dim % 8 != 0) return fail(SSD_ERR_UNSUPPORTED, "rmsnorm: dim %d not a multiple of 8", dim);
+  if (!(eps >= 0.f) || !(eps < 1e30f))
+    return fail(SSD_ERR_INVALID_ARG, "rmsnorm: eps must be finite and >= 0");
+  if (ntok > INT32_MAX) return fail(SSD_ERR_UNSUPPORTED, "rmsnorm: more than 2^31-1 rows");
+  if (x_tok_stride < dim || out_tok_stride < dim)
+    return fail(SSD_ERR_INVALID_ARG, "rmsnorm: token stride below dim");
+  if (ntok > 0 && (x == nullptr || out == nullptr))
+    return fail(SSD_ERR_INVALID_ARG, "rmsnorm: x or out is NULL");
+  const size_t xe = esize(x_dtype), oe = esize(out_dtype);
+  if ((x && !aligned(x, 16)) || (out && !aligned(out, 16)) || (weight && !aligned(weight, 16)) ||
+      (x_tok_stride * (int64_t)xe) % 16 || (out_tok_stride * (int64_t)oe) % 16)
+    return fail(SSD_ERR_INVALID_ARG, "rmsnorm: rows and weight must be 16-byte aligned");
+  const Range rx = tok_range(x, ntok, x_tok_stride, dim, xe);
+  const Range ro = tok_range(out, ntok, out_tok_stride, dim, oe);
+  const bool same = x == out && x_dtype == out_dtype && x_tok_stride == out_tok_stride;
+  if (!same && overlap(rx, ro))
+    return fail(SSD_ERR_INVALID_ARG, "rmsnorm: out overlaps x (only exact in-place is allowed)");
+  if (overlap(ro, dense_range(weight, dim, 4)))
+    return fail(SSD_ERR_INVALID_ARG, "rmsnorm: out overlaps weight");
+  hipError_t e = launch_rmsnorm(x, x_tok_stride, x_dtype, weight, eps, out, out_tok_stride,
+                                out_dtype, ntok, dim, stream);
+  return e == hipSuccess ? SSD_OK : hip_fail(e, "rmsnorm launch");
+}
+
+int ssd_linear_fwd(const void* a, int64_t lda, const void* w, int64_t ldw, const void* residual,
+                   int64_t ldr, ssd_dtype_t res_dtype, void* out, int64_t ldo,
+                   ssd_dtype_t out_dtype, int64_t M, int N, int K, hipStream_t stream) {
+  g_last_error.clear();
+  if (!valid_dtype(out_dtype) || (residual != nullptr && !valid_dtype(res_dtype)))
+    return fail(SSD_ERR_INVALID_ARG, "linear: bad dtype");
+  if (M < 0 || N <= 0 || K <= 0)
+    return fail(SSD_ERR_INVALID_ARG, "linear: bad size M=%lld N=%d K=%d", (long long)M, N, K);
+  if (K % 8 != 0) return fail(SSD_ERR_UNSUPPORTED, "linear: K %d not a multiple of 8", K);
+  if ((M + 255) / 256 * (int64_t)((N + 255) / 256) > INT32_MAX)
+    return fail(SSD_ERR_UNSUPPORTED, "linear: too many output tiles");
+  if (lda < K || ldw < K || ldo < N || (residual != nullptr && ldr < N))
+    return fail(SSD_ERR_INVALID_ARG, "linear: a leading dimension is below its row width");
+  if (w == nullptr || (M > 0 && (a == nullptr || out == nullptr)))
+    return fail(SSD_ERR_INVALID_ARG, "linear: a, w or out is NULL");
+  const size_t oe = esize(out_dtype), re = residual ? esize(res_dtype) : 2;
+  const void* ptrs16[] = {a, w, out, residual};
+  for (const void* p : ptrs16)
+    if (p != nullptr && !aligned(p, 16))
+      return fail(SSD_ERR_INVALID_ARG, "linear: a base pointer is not 16-byte aligned");
+  if ((lda * 2) % 16 || (ldw * 2) % 16 || (ldo * (int64_t)oe) % 16 ||
+      (residual != nullptr && (ldr * (int64_t)re) % 16))
+    return fail(SSD_ERR_INVALID_ARG, "linear: a row stride is not a multiple of 16 bytes");
+  const Range ra = tok_range(a, M, lda, K, 2), rw = tok_range(w, N, ldw, K, 2);
+  const Range ro = tok_range(out, M, ldo, N, oe), rr = tok_range(residual, M, ldr, N, re);
+  if (overlap(ro, ra) || overlap(ro, rw))
+    return fail(SSD_ERR_INVALID_ARG, "linear: out overlaps a or w");
+  const bool same = residual == out && res_dtype == out_dtype && ldr == ldo;
+  if (!same && overlap(ro, rr))
+    return fail(SSD_ERR_INVALID_ARG, "linear: out overlaps residual (only exact in-place is allowed)");
+  hipError_t e = launch_gemm_bf16(a, lda, w, ldw, residual, ldr, res_dtype, out, ldo, out_dtype,
+                                  M, N, K, stream);
+  return e == hipSuccess ? SSD_OK : hip_fail(e, "linear launch");
+}
+
+namespace {
+// Workspace of the block: normed input | in_proj output (z | x B C | dt, rows
+// padded to 8 elements) | layer output y, all bf16, then the layer's own.
+struct BlockWs {
+  int64_t ld_in = 0;
+  size_t u = 0, zx = 0, y = 0, scan = 0, scan_bytes = 0, total = 0;
+};
+BlockWs block_ws(int batch, int seqlen, int d_model, int nheads, int ngroups) {
+  BlockWs w;
+  const int64_t T = (int64_t)batch * seqlen;
+  const int64_t HP = (int64_t)nheads * kP, GN = (int64_t)ngroups * kN;
+  w.ld_in = (2 * HP + 2 * GN + nheads + 7) / 8 * 8;
+  size_t off = 0;
+  w.u = off; off += round_up((size_t)T * d_model * 2, 256);
+  w.zx = off; off += round_up((size_t)T * w.ld_in * 2, 256);
+  w.y = off; off += round_up((size_t)T * HP * 2, 256);
+  w.scan = off;
+  w.scan_bytes = ssd_chunk_scan_workspace_bytes(batch, seqlen, nheads, kP, ngroups, kN,
+                                                kBf16Chunk, SSD_MATH_BF16, 1);
+  off += round_up(w.scan_bytes, 256);
+  w.total = off;
+  return w;
+}
+}  // namespace
+
+size_t ssd_block_workspace_bytes(int batch, int seqlen, int d_model, int nheads, int headdim,
+                                 int ngroups, int dstate) {
+  if (batch <= 0 || seqlen <= 0 || d_model <= 0 || nheads <= 0 || ngroups <= 0 ||
+      headdim != kP || dstate != kN || nheads % ngroups != 0)
+    return 0;
+  return block_ws(batch, seqlen, d_model, nheads, ngroups).total;
+}
+
+int ssd_block_fwd(const void* h, ssd_dtype_t h_dtype, const float* norm_w, float norm_eps,
+                  const void* in_proj_w, const float* conv_w, const float* conv_b,
+                  int conv_width, const float* A, const float* D, const float* dt_bias,
+                  int dt_softplus, const void* out_proj_w, const void* conv_state_in,
+                  void* conv_state_out, const float* initial_state, float* final_state,
+                  void* out, ssd_dtype_t out_dtype, int batch, int seqlen, int d_model,
+                  int nheads, int headdim, int ngroups, int dstate, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  if (!valid_dtype(h_dtype) || !valid_dtype(out_dtype))
+    return fail(SSD_ERR_INVALID_ARG, "block: bad dtype");
+  if (batch < 0 || seqlen < 0 || d_model <= 0 || nheads <= 0 || ngroups <= 0 ||
+      headdim <= 0 || dstate <= 0)
+    return fail(SSD_ERR_INVALID_ARG, "block: bad size");
+  if (nheads % ngroups != 0)
+    return fail(SSD_ERR_INVALID_ARG, "block: nheads %d not a multiple of ngroups %d", nheads,
+                ngroups);
+  if (headdim != kP || dstate != kN)
+    return fail(SSD_ERR_UNSUPPORTED, "block: headdim %d / dstate %d (supported: 64 / 128)",
+                headdim, dstate);
+  if (d_model % 8 != 0)
+    return fail(SSD_ERR_UNSUPPORTED, "block: d_model %d not a multiple of 8", d_model);
+  if (conv_w == nullptr || in_proj_w == nullptr || out_proj_w == nullptr || A == nullptr)
+    return fail(SSD_ERR_INVALID_ARG, "block: conv_w, in_proj_w, out_proj_w or A is NULL");
+  if (conv_width < 1) return fail(SSD_ERR_INVALID_ARG, "block: conv_width %d < 1", conv_width);
+  if (conv_width > 4) return fail(SSD_ERR_UNSUPPORTED, "block: conv_width %d > 4", conv_width);
+  if (!(norm_eps >= 0.f) || !(norm_eps < 1e30f))
+    return fail(SSD_ERR_INVALID_ARG, "block: norm_eps must be finite and >= 0");
+  if (dt_softplus != 0 && dt_softplus != 1)
+    return fail(SSD_ERR_INVALID_ARG, "block: dt_softplus must be 0 or 1");
+  const int64_t T = (int64_t)batch * seqlen;
+  if (T > INT32_MAX) return fail(SSD_ERR_UNSUPPORTED, "block: more than 2^31-1 tokens");
+  if (T > 0 && (h == nullptr || out == nullptr))
+    return fail(SSD_ERR_INVALID_ARG, "block: h or out is NULL");
+  // everything the layer call below would reject is rejected here, before
+  // the first launch
+  const void* ptrs16[] = {h, out, norm_w, in_proj_w, out_proj_w, conv_state_in,
+                          conv_state_out, initial_state, final_state};
+  for (const void* p : ptrs16)
+    if (p != nullptr && !aligned(p, 16))
+      return fail(SSD_ERR_INVALID_ARG, "block: a tensor base pointer is not 16-byte aligned");
+  const int64_t HP = (int64_t)nheads * kP, GN = (int64_t)ngroups * kN;
+  const int64_t d_in = 2 * HP + 2 * GN + nheads, cdim = HP + 2 * GN;
+  if (d_in > INT32_MAX || HP > INT32_MAX)
+    return fail(SSD_ERR_UNSUPPORTED, "block: projection too wide");
+  const size_t he = esize(h_dtype), oe = esize(out_dtype);
+  // out: exact in-place update of h is allowed, any other overlap is not
+  const Range rh = dense_range(h, T * d_model, he), ro = dense_range(out, T * d_model, oe);
+  const bool same = out == h && out_dtype == h_dtype;
+  if (!same && overlap(ro, rh)) return fail(SSD_ERR_INVALID_ARG, "block: out overlaps h");
+  const int64_t nstate = (int64_t)batch * nheads * kP * kN;
+  const int64_t nhist = (int64_t)batch * (conv_width - 1) * cdim;
+  const Range params[] = {dense_range(norm_w, d_model, 4), dense_range(in_proj_w, d_in * d_model, 2),
+                          dense_range(out_proj_w, (int64_t)d_model * HP, 2),
+                          dense_range(conv_w, cdim * conv_width, 4), dense_range(conv_b, cdim, 4),
+                          dense_range(A, nheads, 4), dense_range(D, nheads, 4),
+                          dense_range(dt_bias, nheads, 4), dense_range(conv_state_in, nhist, 2),
+                          dense_range(initial_state, nstate, 4),
+                          dense_range(conv_state_out, nhist, 2),
+                          dense_range(final_state, nstate, 4)};
+  for (const Range& r : params)
+    if (overlap(ro, r)) return fail(SSD_ERR_INVALID_ARG, "block: out overlaps a parameter or state");
+  {
+    const Range rso = dense_range(conv_state_out, nhist, 2);
+    if (overlap(rso, dense_range(conv_state_in, nhist, 2)) ||
+        overlap(rso, dense_range(initial_state, nstate, 4)) ||
+        overlap(rso, dense_range(final_state, nstate, 4)) || overlap(rso, rh))
+      return fail(SSD_ERR_INVALID_ARG, "block: conv_state_out overlaps another tensor");
+    const Range rfs = dense_range(final_state, nstate, 4);
+    if (overlap(rfs, rh) || overlap(rfs, dense_range(conv_state_in, nhist, 2)))
+      return fail(SSD_ERR_INVALID_ARG, "block: final_state overlaps another tensor");
+  }
+  const BlockWs wl = block_ws(batch, seqlen, d_model, nheads, ngroups);
+  if (T > 0) {
+    if (workspace == nullptr || workspace_bytes < wl.total)
+      return fail(SSD_ERR_WORKSPACE, "block: workspace needs %zu bytes, got %zu", wl.total,
+                  workspace == nullptr ? (size_t)0 : workspace_bytes);
+    if (!aligned(workspace, 256))
+      return fail(SSD_ERR_INVALID_ARG, "block: workspace is not 256-byte aligned");
+    const Range rws = dense_range(workspace, (int64_t)wl.total, 1);
+    if (overlap(rws, rh) || overlap(rws, ro))
+      return fail(SSD_ERR_INVALID_ARG, "block: workspace overlaps h or out");
+    for (const Range& r : params)
+      if (overlap(rws, r))
+        return fail(SSD_ERR_INVALID_ARG, "block: workspace overlaps a parameter or state");
+  }
+  if (batch == 0) return SSD_OK;
+  char* ws = static_cast<char*>(workspace);
+  bf16* u = T > 0 ? reinterpret_cast<bf16*>(ws + wl.u) : nullptr;
+  bf16* zx = T > 0 ? reinterpret_cast<bf16*>(ws + wl.zx) : nullptr;
+  bf16* y = T > 0 ? reinterpret_cast<bf16*>(ws + wl.y) : nullptr;
+  hipError_t e = hipSuccess;
+  if (T > 0) {
+    e = launch_rmsnorm(h, d_model, h_dtype, norm_w, norm_eps, u, d_model, SSD_BF16, T, d_model,
+                       stream);
+    if (e != hipSuccess) return hip_fail(e, "block: rmsnorm launch");
+    e = launch_gemm_bf16(u, d_model, in_proj_w, d_model, nullptr, 0, SSD_BF16, zx, wl.ld_in,
+                         SSD_BF16, T, (int)d_in, d_model, stream);
+    if (e != hipSuccess) return hip_fail(e, "block: in_proj launch");
+  }
+  // the layer on the in_proj output: z | x B C | dt, one row per token
+  const int rc = ssd_chunk_scan_fwd(
+      zx ? zx + HP : nullptr, wl.ld_in, zx ? zx + 2 * HP : nullptr, wl.ld_in,
+      zx ? zx + 2 * HP + GN : nullptr, wl.ld_in, SSD_BF16, conv_w, conv_b, conv_width,
+      conv_state_in, conv_state_out, zx ? zx + 2 * HP + 2 * GN : nullptr, wl.ld_in, zx, wl.ld_in,
+      SSD_BF16, A, D, dt_bias, dt_softplus, initial_state, final_state, y, HP, SSD_BF16, batch,
+      seqlen, nheads, kP, ngroups, kN, kBf16Chunk, SSD_MATH_BF16, T > 0 ? ws + wl.scan : nullptr,
+      wl.scan_bytes, stream);
+  if (rc != SSD_OK) {
+    g_last_error = "block: " + g_last_error;
+    return rc;
+  }
+  if (T == 0) return SSD_OK;
+  e = launch_gemm_bf16(y, HP, out_proj_w, HP, h, d_model, h_dtype, out, d_model, out_dtype, T,
+                       d_model, (int)HP, stream);
+  return e == hipSuccess ? SSD_OK : hip_fail(e, "block: out_proj launch");
+}
+
 }  // extern "C"

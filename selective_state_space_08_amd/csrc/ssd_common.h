@@ -90,6 +90,18 @@ hipError_t launch_state_update(float* state, const void* xbc, ssd_dtype_t xbc_dt
                                int softplus, void* y, ssd_dtype_t y_dtype, int batch,
                                int nheads, int ngroups, hipStream_t stream);
 
+// RMSNorm of ntok rows of dim elements (dim % 8 == 0, rows 16-byte aligned).
+hipError_t launch_rmsnorm(const void* x, int64_t xs, ssd_dtype_t x_dtype, const float* w,
+                          float eps, void* out, int64_t os, ssd_dtype_t out_dtype, int64_t ntok,
+                          int dim, hipStream_t stream);
+
+// out = A W^T (+ res) on the matrix cores: A [M, K] and W [N, K] bf16,
+// K % 8 == 0, rows 16-byte aligned; res (res_dtype) and out (out_dtype) [M, N].
+hipError_t launch_gemm_bf16(const void* a, int64_t lda, const void* w, int64_t ldw,
+                            const void* res, int64_t ldr, ssd_dtype_t res_dtype, void* out,
+                            int64_t ldo, ssd_dtype_t out_dtype, int64_t M, int N, int K,
+                            hipStream_t stream);
+
 // Copies (or zero-fills when src is null) n floats / n elements: used for the
 // state hand-through of empty sequences.  A kernel, not hipMemsetAsync.
 hipError_t launch_copy_or_zero(void* dst, const void* src, size_t bytes, hipStream_t stream);

@@ -33,6 +33,11 @@ SIGNATURES = {
     "ssd_state_update": (_I, [_V, _V, _I, _V, _V, _V, _I, _V, _V, _I, _V, _V, _V, _I, _V, _I,
                               _I, _I, _I, _I, _I, _V]),
     "ssd_decode_cache_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "ssd_rmsnorm_fwd": (_I, [_V, _I64, _I, _V, ctypes.c_float, _V, _I64, _I, _I64, _I, _V]),
+    "ssd_linear_fwd": (_I, [_V, _I64, _V, _I64, _V, _I64, _I, _V, _I64, _I, _I64, _I, _I, _V]),
+    "ssd_block_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
+    "ssd_block_fwd": (_I, [_V, _I, _V, ctypes.c_float, _V, _V, _V, _I, _V, _V, _V, _I, _V, _V,
+                           _V, _V, _V, _V, _I, _I, _I, _I, _I, _I, _I, _I, _V, _SZ, _V]),
     "ssd_status_string": (ctypes.c_char_p, [_I]),
     "ssd_last_error": (ctypes.c_char_p, []),
     "ssd_version": (ctypes.c_char_p, []),
@@ -225,3 +230,105 @@ def ssd_state_update(state, xbc, dt, A, *, ngroups, conv_state=None, conv_w=None
                                 _p(dt_bias), int(bool(dt_softplus)), _p(y), _dt(y), B, H, P, G,
                                 N, _stream(state)))
     return y
+
+
+def _rows(t: torch.Tensor, width: int, name: str):
+    """(rows, row stride) of a tensor viewed as [rows, width] with contiguous rows."""
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if t.shape[-1] != width:
+        raise ValueError("%s has %d columns, want %d" % (name, t.shape[-1], width))
+    rows = t.numel() // width if width else 0
+    if rows == 0:
+        return 0, width
+    v = t.view(rows, width)  # raises rather than copies for incompatible layouts
+    if width > 1 and v.stride(1) != 1:
+        raise ValueError("%s: rows must be contiguous" % name)
+    return rows, (v.stride(0) if rows > 1 else width)
+
+
+def ssd_rmsnorm_fwd(x, weight=None, eps=1e-5, out=None, out_dtype=torch.bfloat16):
+    """RMSNorm over the last axis of x [..., dim] -> out (same shape)."""
+    lib = load()
+    dim = x.shape[-1]
+    ntok, xs = _rows(x, dim, "x")
+    _dense(weight, (dim,), "weight", torch.float32)
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype, device=x.device)
+    no, os_ = _rows(out, dim, "out")
+    if no != ntok:
+        raise ValueError("out has %d rows, x has %d" % (no, ntok))
+    _check(lib.ssd_rmsnorm_fwd(_p(x), xs, _dt(x), _p(weight), float(eps), _p(out), os_, _dt(out),
+                               ntok, dim, _stream(x)))
+    return out
+
+
+def ssd_linear_fwd(a, w, residual=None, out=None, out_dtype=torch.float32):
+    """out = a @ w^T (+ residual) on the matrix cores: a [..., K] bf16,
+    w [N, K] bf16, residual [..., N] or None."""
+    lib = load()
+    N, K = w.shape
+    if a.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise TypeError("a and w must be bfloat16")
+    M, lda = _rows(a, K, "a")
+    _, ldw = _rows(w, K, "w")
+    if out is None:
+        out = torch.empty(a.shape[:-1] + (N,), dtype=out_dtype, device=a.device)
+    mo, ldo = _rows(out, N, "out")
+    ldr, rdt = 0, SSD_F32
+    if residual is not None:
+        mr, ldr = _rows(residual, N, "residual")
+        if mr != M:
+            raise ValueError("residual has %d rows, a has %d" % (mr, M))
+        rdt = _dt(residual)
+    if mo != M:
+        raise ValueError("out has %d rows, a has %d" % (mo, M))
+    _check(lib.ssd_linear_fwd(_p(a), lda, _p(w), ldw, _p(residual), ldr, rdt, _p(out), ldo,
+                              _dt(out), M, N, K, _stream(a)))
+    return out
+
+
+def ssd_block_workspace_bytes(batch, seqlen, d_model, nheads, headdim=64, ngroups=8, dstate=128):
+    return load().ssd_block_workspace_bytes(batch, seqlen, d_model, nheads, headdim, ngroups,
+                                            dstate)
+
+
+def ssd_block_fwd(h, norm_w, in_proj_w, conv_w, A, out_proj_w, *, nheads, ngroups, conv_b=None,
+                  D=None, dt_bias=None, dt_softplus=True, norm_eps=1e-5, conv_state_in=None,
+                  conv_state_out=None, initial_state=None, final_state=None, out=None,
+                  out_dtype=torch.float32, workspace=None):
+    """The pre-norm residual block: out = h + out_proj(mixer(rmsnorm(h))).
+    h [B, L, d_model]; in_proj_w [2*H*P + 2*G*N + H, d_model] bf16 (rows
+    z | x | B | C | dt); out_proj_w [d_model, H*P] bf16."""
+    lib = load()
+    B, L, dm = h.shape
+    H, G, P, N = nheads, ngroups, 64, 128
+    HP, GN = H * P, G * N
+    cdim = HP + 2 * GN
+    K = conv_w.shape[1]
+    if not h.is_contiguous() or not h.is_cuda:
+        raise ValueError("h must be a contiguous device tensor")
+    _dense(norm_w, (dm,), "norm_w", torch.float32)
+    _dense(in_proj_w, (2 * HP + 2 * GN + H, dm), "in_proj_w", torch.bfloat16)
+    _dense(out_proj_w, (dm, HP), "out_proj_w", torch.bfloat16)
+    _dense(conv_w, (cdim, K), "conv_w", torch.float32)
+    _dense(conv_b, (cdim,), "conv_b", torch.float32)
+    for n, t in (("A", A), ("D", D), ("dt_bias", dt_bias)):
+        _dense(t, (H,), n, torch.float32)
+    _dense(conv_state_in, (B, K - 1, cdim), "conv_state_in", torch.bfloat16)
+    _dense(conv_state_out, (B, K - 1, cdim), "conv_state_out", torch.bfloat16)
+    _dense(initial_state, (B, H, P, N), "initial_state", torch.float32)
+    _dense(final_state, (B, H, P, N), "final_state", torch.float32)
+    if out is None:
+        out = torch.empty((B, L, dm), dtype=out_dtype, device=h.device)
+    _dense(out, (B, L, dm), "out")
+    need = lib.ssd_block_workspace_bytes(B, L, dm, H, P, G, N)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=h.device)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.ssd_block_fwd(
+        _p(h), _dt(h), _p(norm_w), float(norm_eps), _p(in_proj_w), _p(conv_w), _p(conv_b), K,
+        _p(A), _p(D), _p(dt_bias), int(bool(dt_softplus)), _p(out_proj_w), _p(conv_state_in),
+        _p(conv_state_out), _p(initial_state), _p(final_state), _p(out), _dt(out), B, L, dm, H, P,
+        G, N, _p(workspace), wsz, _stream(h)))
+    return out

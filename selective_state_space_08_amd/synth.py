@@ -24,6 +24,19 @@ sequence b with i = b * ceil(L/4096) + j; for decode, step i.  In each:
 Activations (xbc, z, dt, ring) are rounded to bf16, ties to even, for bf16
 workloads; the rounded values are the ground truth for both sides.
 Parameters and states stay fp32.
+
+The block around the layer (make_block) adds, from block 2^31 - 2 of the
+seed, in this order:
+  norm_w     [d_model]            = 1 + 0.1 N(0,1)             (fp32)
+  in_proj_w  [d_in_proj, d_model] ~ N(0,1) times a per-row scale / sqrt(d_model):
+                                    1 for the z and x rows, 1/sqrt(d_state) for
+                                    the B and C rows, 0.5 for the dt rows, so
+                                    that on a unit-RMS input the projection's
+                                    outputs have the spread of the layer's
+                                    token draws above             (bf16)
+  out_proj_w [d_model, d_inner]   ~ N(0, 1/sqrt(d_inner))       (bf16)
+and the block input h [B, L, d_model] ~ N(0,1) (bf16) from the token blocks
+1 + i as above.  conv_w, A, dt_bias and D are the layer's (block 0).
 """
 from __future__ import annotations
 
@@ -197,3 +210,54 @@ def make_decode(wl: Workload, seed: Optional[int] = None,
     seed = wl.seed if seed is None else seed
     prm = _params(wl, seed, False, decode=True)
     return DecodeInputs(wl, seed, prm.conv_w, prm.A, prm.dt_bias, prm.D, prm.h0, prm.ring)
+
+
+@dataclass
+class BlockInputs:
+    wl: Workload
+    h: np.ndarray               # [B,L,d_model] bf16 values (f32 array)
+    norm_w: np.ndarray          # [d_model] f32
+    in_proj_w: np.ndarray       # [d_in_proj, d_model] bf16 values
+    out_proj_w: np.ndarray      # [d_model, d_inner] bf16 values
+    conv_w: np.ndarray          # [Cdim, K] f32
+    A: np.ndarray               # [H]
+    dt_bias: np.ndarray         # [H]
+    D: np.ndarray               # [H]
+
+
+def make_block(wl: Workload, seed: Optional[int] = None, seqlen: Optional[int] = None,
+               batch: Optional[int] = None, d_model: Optional[int] = None) -> BlockInputs:
+    """Inputs of the pre-norm residual block around the layer (bf16 h and
+    projection weights; see the module notes for the recipe)."""
+    if seqlen is not None:
+        wl = wl.with_(seqlen=seqlen)
+    if batch is not None:
+        wl = wl.with_(batch=batch)
+    seed = wl.seed if seed is None else seed
+    dm = wl.d_model if d_model is None else d_model
+    prm = _params(wl, seed, slow_decay=False, decode=False)
+    HP, GN, H = wl.d_inner, wl.ngroups * wl.dstate, wl.nheads
+    rng = _rng(seed, 2**31 - 2)
+    norm_w = (1.0 + _normal(rng, (dm,), 0.1)).astype(np.float32)
+    scale = np.concatenate([np.ones(2 * HP), np.full(2 * GN, 1.0 / math.sqrt(wl.dstate)),
+                            np.full(H, 0.5)]).astype(np.float32) / np.float32(math.sqrt(dm))
+    in_proj_w = _normal(rng, (wl.d_in_proj, dm))
+    in_proj_w *= scale[:, None]
+    round_bf16_(in_proj_w)
+    out_proj_w = _normal(rng, (dm, HP), 1.0 / math.sqrt(HP))
+    round_bf16_(out_proj_w)
+    B, L = wl.batch, wl.seqlen
+    h = np.empty((B, L, dm), np.float32)
+    nblk = max(1, -(-L // TOKEN_BLOCK))
+
+    def fill(i):
+        b, j = divmod(i, nblk)
+        t0, t1 = j * TOKEN_BLOCK, min(L, (j + 1) * TOKEN_BLOCK)
+        h[b, t0:t1] = _rng(seed, 1 + i).standard_normal((t1 - t0, dm), dtype=np.float32)
+        round_bf16_(h[b, t0:t1])
+
+    if L > 0:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(fill, range(B * nblk)))
+    return BlockInputs(wl, h, norm_w, in_proj_w, out_proj_w, prm.conv_w, prm.A, prm.dt_bias,
+                       prm.D)

@@ -26,10 +26,20 @@ class Workload:
     initial_state: bool = False
     decode_steps: int = 0   # > 0: a chain of one-token decode steps
     seed: int = 8000
+    expand: int = 2         # d_inner / d_model of the block around the layer
 
     @property
     def d_inner(self) -> int:
         return self.nheads * self.headdim
+
+    @property
+    def d_model(self) -> int:
+        return self.d_inner // self.expand
+
+    @property
+    def d_in_proj(self) -> int:
+        """in_proj outputs: z | x | B | C | dt."""
+        return 2 * self.d_inner + 2 * self.ngroups * self.dstate + self.nheads
 
     @property
     def cdim(self) -> int:
