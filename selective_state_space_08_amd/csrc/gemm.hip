@@ -6,8 +6,9 @@
 // section 2.4).
 //
 // gfx950 only.  The projection is a dense contraction, so it runs on the
-// matrix cores: 256 x 256 output tiles per workgroup of 4 waves, each wave a
-// 128 x 128 sub-tile of 16x16x32 bf16 MFMAs with fp32 accumulators, K staged
+// matrix cores: 256 x 256 output tiles per workgroup of 8 waves (two per
+// SIMD, so that one wave's MFMAs cover the other's LDS reads), each wave a
+// 128 x 64 sub-tile of 16x16x32 bf16 MFMAs with fp32 accumulators, K staged
 // through LDS in steps of 64 with double buffering (one barrier per step).
 #include "ssd_common.h"
 
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(RN_THREADS) void rmsnorm_kernel(const Tin* __restri
 
 // ------------------------------------------------------------------ GEMM
 
-constexpr int TM = 256, TN = 256, TK = 64, GEMM_THREADS = 256;
+constexpr int TM = 256, TN = 256, TK = 64, GEMM_THREADS = 512;
 // LDS tiles are [row][64] bf16 (128-byte rows, no padding).  The 16-byte
 // slot that holds chunk c of row r is c ^ (r % 8): the fragment reads of
 // eight consecutive rows then fall on distinct bank groups, and a wave's
@@ -158,7 +159,7 @@ __device__ __forceinline__ void store4(bf16* p, const float v[4]) {
 // row 16-byte aligned (checked by the caller); rows past M or N are read
 // clamped and their products never stored; columns past K are zeroed in LDS.
 template <typename TOut, typename TRes>
-__global__ __launch_bounds__(GEMM_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(GEMM_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_bf16_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) bf16 sA[2][TM * TK];
   __shared__ __attribute__((aligned(1024))) bf16 sW[2][TN * TK];
@@ -167,31 +168,31 @@ void gemm_bf16_kernel(GemmArgs g) {
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, q = lane >> 4;
-  const int wm = wv >> 1, wn = wv & 1;  // this wave's 128 x 128 sub-tile
+  const int wm = wv >> 2, wn = wv & 3;  // this wave's 128 x 64 sub-tile
   int tm, tn;
   tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * TM;
   const int n0 = tn * TN;
 
-  // Direct loads: step i of wave wv fills tile rows 64 wv + 8 i .. + 7; lane l
-  // fills slot l % 8 of row 64 wv + 8 i + l / 8, i.e. that row's chunk
+  // Direct loads: step i of wave wv fills tile rows 32 wv + 8 i .. + 7; lane l
+  // fills slot l % 8 of row 32 wv + 8 i + l / 8, i.e. that row's chunk
   // (l % 8) ^ (l / 8).  Rows past M or N re-read the last row; chunks past K
   // re-read the row's last chunk (and are zeroed below).
   const int lrow = lane >> 3, lchunk = (lane & 7) ^ lrow;
-  const bf16* ga = g.a + min(m0 + 64 * wv + lrow, g.M - 1) * g.lda + 8 * lchunk;
-  const bf16* gw = g.w + (int64_t)min(n0 + 64 * wv + lrow, g.N - 1) * g.ldw + 8 * lchunk;
+  const bf16* ga = g.a + min(m0 + 32 * wv + lrow, g.M - 1) * g.lda + 8 * lchunk;
+  const bf16* gw = g.w + (int64_t)min(n0 + 32 * wv + lrow, g.N - 1) * g.ldw + 8 * lchunk;
   auto dload = [&](int kt, int buf) {
     const int k = min(kt * TK, g.K - 8 * (lchunk + 1));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t ra = min(m0 + 64 * wv + 8 * i + lrow, g.M - 1) - min(m0 + 64 * wv + lrow, g.M - 1);
-      const int64_t rw = min(n0 + 64 * wv + 8 * i + lrow, g.N - 1) - min(n0 + 64 * wv + lrow, g.N - 1);
+    for (int i = 0; i < 4; ++i) {
+      const int64_t ra = min(m0 + 32 * wv + 8 * i + lrow, g.M - 1) - min(m0 + 32 * wv + lrow, g.M - 1);
+      const int64_t rw = min(n0 + 32 * wv + 8 * i + lrow, g.N - 1) - min(n0 + 32 * wv + lrow, g.N - 1);
       __builtin_amdgcn_global_load_lds(
           (const __attribute__((address_space(1))) void*)(ga + ra * g.lda + k),
-          (__attribute__((address_space(3))) void*)&sA[buf][(64 * wv + 8 * i) * TK], 16, 0, 0);
+          (__attribute__((address_space(3))) void*)&sA[buf][(32 * wv + 8 * i) * TK], 16, 0, 0);
       __builtin_amdgcn_global_load_lds(
           (const __attribute__((address_space(1))) void*)(gw + rw * g.ldw + k),
-          (__attribute__((address_space(3))) void*)&sW[buf][(64 * wv + 8 * i) * TK], 16, 0, 0);
+          (__attribute__((address_space(3))) void*)&sW[buf][(32 * wv + 8 * i) * TK], 16, 0, 0);
     }
   };
   // after the loads of step kt have landed: zero the chunks past K
@@ -202,19 +203,19 @@ void gemm_bf16_kernel(GemmArgs g) {
     const int kc = tid & 7, srow = tid >> 3;
     if (kc >= kvalid) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = srow + 32 * i;
+      for (int i = 0; i < 4; ++i) {
+        const int row = srow + 64 * i;
         *reinterpret_cast<u32x4*>(&sA[buf][row * TK + 8 * slot(row, kc)]) = zero;
         *reinterpret_cast<u32x4*>(&sW[buf][row * TK + 8 * slot(row, kc)]) = zero;
       }
     }
   };
 
-  f32x4 acc[8][8];
+  f32x4 acc[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   dload(0, 0);
   if (nk == 1 && kvalid < 8) {
@@ -225,16 +226,18 @@ void gemm_bf16_kernel(GemmArgs g) {
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
     // every fragment of this step first: the next step's direct loads, into
-    // the other buffer, are issued only after this step's LDS reads
-    // (in the order the products use them, so the waits can be graduated)
-    bf16x8 fa[2][8], fw[2][8];
+    // the other buffer, are issued only after this step's LDS reads.  The
+    // wait counter does not tell those loads from LDS reads, so the products
+    // below wait for all of this step's reads; the other wave on the SIMD
+    // runs its products meanwhile.
+    bf16x8 fa[2][8], fw[2][4];
 #pragma unroll
     for (int s = 0; s < TK / 32; ++s) {
       const int c = slot(r16, 4 * s + q);  // rows 16 i + r16: row % 8 == r16 % 8
       fa[s][0] = *reinterpret_cast<const bf16x8*>(&sA[buf][(wm * 128 + r16) * TK + 8 * c]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        fw[s][j] = *reinterpret_cast<const bf16x8*>(&sW[buf][(wn * 128 + 16 * j + r16) * TK + 8 * c]);
+      for (int j = 0; j < 4; ++j)
+        fw[s][j] = *reinterpret_cast<const bf16x8*>(&sW[buf][(wn * 64 + 16 * j + r16) * TK + 8 * c]);
 #pragma unroll
       for (int i = 1; i < 8; ++i)
         fa[s][i] = *reinterpret_cast<const bf16x8*>(&sA[buf][(wm * 128 + 16 * i + r16) * TK + 8 * c]);
@@ -253,7 +256,7 @@ void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = mfma(fw[s][j], fa[s][i], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma(fw[s][j], fa[s][i], acc[i][j]);
     if (kt + 2 == nk && kvalid < 8) {
       __builtin_amdgcn_s_waitcnt(0);
       zero_tail(buf ^ 1);
@@ -269,8 +272,8 @@ void gemm_bf16_kernel(GemmArgs g) {
     const int64_t m = m0 + wm * 128 + 16 * i + r16;
     if (m >= g.M) continue;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int n = n0 + wn * 128 + 16 * j + 4 * q;
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn * 64 + 16 * j + 4 * q;
       if (n >= g.N) continue;
       float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
       if (n + 4 <= g.N) {
