@@ -7,7 +7,9 @@ SiLU(z) gate; bf16 activations, fp32 state and output) through libssd: the
 causal conv, the chunked scan and the gated epilogue.  `value` is prefill
 tokens/s with every input already resident in HBM.  The same run times the
 decode workload (256 sequences x 1000 chained one-token ssd_state_update
-steps, fp32 state) and reports it under "decode".
+steps, fp32 state) and reports it under "decode", and the pre-norm residual
+block around the layer (RMSNorm, in_proj, the layer, out_proj + residual;
+d_model 4096) under "block", with the MFMA roofline of its projections.
 
 Kernel durations come from HIP events recorded on the stream the kernels are
 launched on (torch's current stream, which the binding passes to libssd).
@@ -183,6 +185,52 @@ def time_decode(args, wl, torch, layer, synth, dev, dev32):
     return dict(chain_ms=total_ms, step_ms=total_ms / T, first10_ms=first, last10_ms=last)
 
 
+def events_ms(torch, fn, steps: int, warmup: int):
+    """Mean duration of fn() over `steps` calls, from HIP events on the stream
+    the library launches on (torch's current stream)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def time_block(args, wl, torch, ssd, synth, dev, dev32):
+    """The block h + out_proj(mixer(rmsnorm(h))) at the layer's shape, and its
+    two projections alone (the dominant kernels)."""
+    dm = wl.d_model
+    log("block %s d_model %d: generating inputs" % (wl.name, dm))
+    bi = synth.make_block(wl)
+    h = dev(bi.h, "bf16")
+    norm_w, win, wout = dev32(bi.norm_w), dev(bi.in_proj_w, "bf16"), dev(bi.out_proj_w, "bf16")
+    conv_w, A, D, dtb = dev32(bi.conv_w), dev32(bi.A), dev32(bi.D), dev32(bi.dt_bias)
+    del bi
+    out = torch.empty((wl.batch, wl.seqlen, dm), device="cuda")
+    ws = torch.empty(ssd.ssd_block_workspace_bytes(wl.batch, wl.seqlen, dm, wl.nheads, 64,
+                                                   wl.ngroups, 128), dtype=torch.uint8,
+                     device="cuda")
+    steps, warm = max(3, args.steps // 4), 2
+    call_ms = events_ms(torch, lambda: ssd.ssd_block_fwd(
+        h, norm_w, win, conv_w, A, wout, nheads=wl.nheads, ngroups=wl.ngroups, D=D,
+        dt_bias=dtb, out=out, workspace=ws), steps, warm)
+    T = wl.tokens
+    u = h.view(T, dm)
+    zx = torch.empty((T, wl.d_in_proj), dtype=torch.bfloat16, device="cuda")
+    in_ms = events_ms(torch, lambda: ssd.ssd_linear_fwd(u, win, out=zx), steps, warm)
+    del zx
+    y = torch.zeros((T, wl.d_inner), dtype=torch.bfloat16, device="cuda")
+    o2 = out.view(T, dm)
+    out_ms = events_ms(torch, lambda: ssd.ssd_linear_fwd(y, wout, residual=u, out=o2), steps, warm)
+    log("block: %.3f ms per call; in_proj %.3f ms, out_proj %.3f ms" % (call_ms, in_ms, out_ms))
+    return dict(call_ms=call_ms, in_ms=in_ms, out_ms=out_ms)
+
+
 def calibrate_copy(torch, ssd, reps: int = 3):
     """A plain copy kernel of known size: ssd_chunk_scan_fwd on an empty
     sequence copies initial_state to final_state (the library's
@@ -260,6 +308,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-block", action="store_true",
+                    help="skip the block around the layer (RMSNorm + projections)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--unfused", action="store_true",
                     help="conv kernel + scan kernel instead of the fused scan")
@@ -355,6 +405,25 @@ def main():
                                       "measured_peak": copy_gbs,
                                       "frac_of_measured": dach / copy_gbs,
                                       "alg_bytes_per_step": dbytes}}
+    if not args.no_block:
+        blk = time_block(args, wl, torch, ssd, synth, dev, dev32)
+        T, dm, HP, din = wl.tokens, wl.d_model, wl.d_inner, wl.d_in_proj
+        f_in, f_out = 2.0 * T * dm * din, 2.0 * T * HP * dm
+        tf_in = f_in / (blk["in_ms"] / 1e3) / 1e12
+        out["block"] = {
+            "workload": "nemotron_h_8b_block_b4_l8192_d4096",
+            "ms_per_call": blk["call_ms"], "tokens_per_s": T / (blk["call_ms"] / 1e3),
+            "launches": ["rmsnorm_kernel", "gemm_bf16_kernel (in_proj)", "bc_pack_kernel",
+                         "scan_bf16_kernel", "gemm_bf16_kernel (out_proj + residual)"],
+            "projection_flops_per_call": f_in + f_out,
+            "roofline": {"bound": "mfma", "achieved": tf_in, "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tf_in / BF16_PEAK_TFLOPS, "traffic": None,
+                         "kernel": "gemm_bf16_kernel (in_proj, M=%d N=%d K=%d)" % (T, din, dm),
+                         "alg_flops_per_launch": f_in, "launch_ms": blk["in_ms"]},
+            "out_proj": {"ms": blk["out_ms"],
+                         "tflops": f_out / (blk["out_ms"] / 1e3) / 1e12,
+                         "frac": f_out / (blk["out_ms"] / 1e3) / 1e12 / BF16_PEAK_TFLOPS},
+        }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
