@@ -417,7 +417,8 @@ def main():
                          "scan_bf16_kernel", "gemm_bf16_kernel (out_proj + residual)"],
             "projection_flops_per_call": f_in + f_out,
             "roofline": {"bound": "mfma", "achieved": tf_in, "peak": BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": tf_in / BF16_PEAK_TFLOPS, "traffic": None,
+                         "unit": "TFLOP/s", "frac": tf_in / BF16_PEAK_TFLOPS,
+                         "traffic": traffic_record("block_in_proj", src_hash("gemm.hip", "api.hip")),
                          "kernel": "gemm_bf16_kernel (in_proj, M=%d N=%d K=%d)" % (T, din, dm),
                          "alg_flops_per_launch": f_in, "launch_ms": blk["in_ms"]},
             "out_proj": {"ms": blk["out_ms"],
