@@ -60,6 +60,9 @@ def _bind(lib):
     lib.oracle_mamba2_decode_step.argtypes = [P, P, P, P, P, I, P, P, P, P, I, P, P,
                                               I, I, I, I, I]
     lib.oracle_mamba2_decode_step.restype = I
+    lib.oracle_mamba2_bwd.argtypes = [P, I64, P, P, I, P, P, P, P, P, I, P, P, P, P,
+                                      P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I]
+    lib.oracle_mamba2_bwd.restype = I
     lib.oracle_rmsnorm.argtypes = [P, P, ctypes.c_double, P, I64, I]
     lib.oracle_rmsnorm.restype = I
     lib.oracle_linear.argtypes = [P, P, P, P, I64, I, I]
@@ -130,32 +133,32 @@ def causal_conv1d(xbc, w, bias=None, conv_state_in=None, apply_silu=True):
 
 def mamba2_fwd(xbc, dt, A, *, nheads, headdim, ngroups, dstate, conv_w=None,
                conv_b=None, conv_state_in=None, D=None, dt_bias=None,
-               dt_softplus=True, z=None, h0=None, f64_activations=False):
+               dt_softplus=True, z=None, h0=None, f64_inputs=False):
     """The layer, token by token in fp64.
 
     xbc [B, L, Cdim] raw x|B|C (post-conv when conv_w is None); dt [B, L, H];
     A [H]; z [B, L, H, P] or None; h0 [B, H, P, N] or None.
-    Inputs are taken as fp32 values (rounded to fp32 first), except that with
-    f64_activations xbc, dt and z are used unrounded (an fp64 intermediate,
-    as in mamba2_block_fwd).
+    Inputs are taken as fp32 values (rounded to fp32 first); with f64_inputs
+    every input is used unrounded (an fp64 intermediate, as in
+    mamba2_block_fwd, or a finite-difference probe).
     Returns (y [B, L, H, P], h_final [B, H, P, N], conv_state_out or None),
     all float64.
     """
     lib = _load()
-    act = _f64 if f64_activations else _in
+    act = _f64 if f64_inputs else _in
     x = act(xbc)
     B, L, C = x.shape
     H, P, G, N = nheads, headdim, ngroups, dstate
     if C != H * P + 2 * G * N:
         raise ValueError("xbc channel count %d != H*P + 2*G*N" % C)
     dt = act(dt).reshape(B, L, H)
-    A = _in(A)
-    conv_w = _in(conv_w)
+    A = act(A)
+    conv_w = act(conv_w)
     K = 0 if conv_w is None else conv_w.shape[1]
-    conv_b = _in(conv_b)
+    conv_b = act(conv_b)
     hist = act(conv_state_in)
-    D = _in(D)
-    dt_bias = _in(dt_bias)
+    D = act(D)
+    dt_bias = act(dt_bias)
     z = None if z is None else act(z).reshape(B, L, H, P)
     h0 = None if h0 is None else _f64(h0).reshape(B, H, P, N)
     y = np.empty((B, L, H, P), np.float64)
@@ -168,6 +171,59 @@ def mamba2_fwd(xbc, dt, A, *, nheads, headdim, ngroups, dstate, conv_w=None,
     if rc != 0:
         raise ValueError("oracle_mamba2_fwd: bad argument")
     return y, hT, hist_out
+
+
+def mamba2_bwd(xbc, dt, A, dout, *, nheads, headdim, ngroups, dstate, conv_w=None,
+               conv_b=None, conv_state_in=None, D=None, dt_bias=None, dt_softplus=True,
+               z=None, h0=None, dh_final=None, f64_inputs=False):
+    """The layer's gradients, by reverse-mode differentiation of mamba2_fwd.
+
+    dout [B, L, H, P] and dh_final [B, H, P, N] or None are the gradients of a
+    scalar loss with respect to the layer's output and final state; inputs as
+    in mamba2_fwd.  Returns a dict of float64 gradients: xbc [B, L, Cdim]
+    (raw inputs when conv_w is given), dt [B, L, H], A [H], and, for the
+    inputs that are given, z, D, dt_bias, h0, conv_w, conv_b, conv_state_in.
+    """
+    lib = _load()
+    act = _f64 if f64_inputs else _in
+    x = act(xbc)
+    B, L, C = x.shape
+    H, P, G, N = nheads, headdim, ngroups, dstate
+    if C != H * P + 2 * G * N:
+        raise ValueError("xbc channel count %d != H*P + 2*G*N" % C)
+    dt = act(dt).reshape(B, L, H)
+    A = act(A)
+    conv_w = act(conv_w)
+    K = 0 if conv_w is None else conv_w.shape[1]
+    conv_b = act(conv_b)
+    hist = act(conv_state_in)
+    D = act(D)
+    dt_bias = act(dt_bias)
+    z = None if z is None else act(z).reshape(B, L, H, P)
+    h0 = None if h0 is None else _f64(h0).reshape(B, H, P, N)
+    dout = _f64(dout).reshape(B, L, H, P)
+    dhf = None if dh_final is None else _f64(dh_final).reshape(B, H, P, N)
+    g = {"xbc": np.empty((B, L, C)), "dt": np.empty((B, L, H)), "A": np.empty(H)}
+    if z is not None:
+        g["z"] = np.empty((B, L, H, P))
+    if D is not None:
+        g["D"] = np.empty(H)
+    if dt_bias is not None:
+        g["dt_bias"] = np.empty(H)
+    g["h0"] = np.empty((B, H, P, N))
+    if conv_w is not None:
+        g["conv_w"] = np.empty((C, K))
+        g["conv_b"] = np.empty(C)
+        g["conv_state_in"] = np.empty((B, K - 1, C))
+    rc = lib.oracle_mamba2_bwd(
+        _ptr(x), C, _ptr(conv_w), _ptr(conv_b), K, _ptr(hist), _ptr(dt), _ptr(A), _ptr(D),
+        _ptr(dt_bias), int(bool(dt_softplus)), _ptr(z), _ptr(h0), _ptr(dout), _ptr(dhf),
+        _ptr(g["xbc"]), _ptr(g["dt"]), _ptr(g.get("z")), _ptr(g["A"]), _ptr(g.get("D")),
+        _ptr(g.get("dt_bias")), _ptr(g["h0"]), _ptr(g.get("conv_w")), _ptr(g.get("conv_b")),
+        _ptr(g.get("conv_state_in")), B, L, H, P, G, N)
+    if rc != 0:
+        raise ValueError("oracle_mamba2_bwd: bad argument")
+    return g
 
 
 def rmsnorm(x, w=None, eps=1e-5):
@@ -231,7 +287,7 @@ def mamba2_block_fwd(h, norm_w, in_proj_w, out_proj_w, A, *, nheads, headdim, ng
     y, hT, conv_out = mamba2_fwd(xbc, dt, A, nheads=H, headdim=P, ngroups=G, dstate=N,
                                  conv_w=conv_w, conv_b=conv_b, conv_state_in=conv_state_in,
                                  D=D, dt_bias=dt_bias, dt_softplus=dt_softplus, z=z, h0=h0,
-                                 f64_activations=True)
+                                 f64_inputs=True)
     out = linear(y.reshape(Bsz, L, HP), out_proj_w, residual=hh)
     return out, hT, conv_out
 

@@ -287,6 +287,228 @@ int oracle_mamba2_decode_step(double* state, const double* xbc, double* ring,
   return 0;
 }
 
+/* d silu(u) / du = sigmoid(u) (1 + u (1 - sigmoid(u))). */
+static double silu_grad(double u) {
+  const double sg = 1.0 / (1.0 + exp(-u));
+  return sg * (1.0 + u * (1.0 - sg));
+}
+
+/*
+ * The gradient of the layer (reverse-mode differentiation of
+ * oracle_mamba2_fwd, token by token in reverse order).
+ *
+ * Given dout [B][L][H][P] (the gradient of a scalar loss with respect to the
+ * layer's output) and dh_final [B][H][P][N] or NULL (with respect to the
+ * final state), it returns the loss's gradients with respect to every input:
+ *   dxbc [B][L][Cdim] (raw x|B|C when conv_w is given, else the post-conv
+ *   values), ddt [B][L][H], dz [B][L][H][P] (when z is given), dA [H],
+ *   dD [H], ddt_bias [H], dh0 [B][H][P][N], dconv_w [Cdim][K],
+ *   dconv_b [Cdim], dconv_state_in [B][K-1][Cdim]; each output may be NULL
+ *   when not wanted (except dxbc, ddt, dA).  Outputs are dense and are
+ *   overwritten.
+ *
+ * For each (b, h), with S_t the state after token t (S_{-1} = h0 or 0),
+ * dS the gradient with respect to S_t (dh_final at t = L-1), and
+ * yv_t = S_t C_t + D x_t, out_t = yv_t silu(z_t):
+ *   dyv = dout silu(z);  dz = dout yv silu'(z)
+ *   dD += dyv . x;  dx += D dyv;  dS += dyv C^T;  dC += S_t^T dyv
+ *   from S_t = a S_{t-1} + delta x B^T, a = exp(delta A):
+ *     dx += delta dS B;  dB += delta dS^T x;  ddelta += x^T dS B
+ *     da = <dS, S_{t-1}>;  ddelta += da a A;  dA += da a delta
+ *     dS <- a dS
+ *   ddt = ddelta softplus'(dt + dt_bias) (= sigmoid) or ddelta;
+ *   ddt_bias += ddt;  finally dh0 = dS.
+ * B and C gradients of the heads of one group add up.  Then the conv: with
+ * du = dpost silu'(u), every tap adds w du to its input (or to the conv
+ * history for positions before the sequence), du times the input to dw, and
+ * du to db.  Returns 0, or -1 on a bad argument.
+ */
+int oracle_mamba2_bwd(const double* xbc, int64_t xbc_tok_stride, const double* conv_w,
+                      const double* conv_b, int width, const double* conv_state_in,
+                      const double* dt, const double* A, const double* D,
+                      const double* dt_bias, int dt_softplus, const double* z,
+                      const double* h0, const double* dout, const double* dh_final,
+                      double* dxbc, double* ddt, double* dz, double* dA, double* dD,
+                      double* ddt_bias, double* dh0, double* dconv_w, double* dconv_b,
+                      double* dconv_state_in, int batch, int seqlen, int nheads,
+                      int headdim, int ngroups, int dstate) {
+  const int H = nheads, P = headdim, G = ngroups, N = dstate, L = seqlen;
+  if (!xbc || !dt || !A || !dout || !dxbc || !ddt || !dA || batch < 0 || L < 0 || H <= 0 ||
+      P <= 0 || G <= 0 || N <= 0 || H % G != 0 || (conv_w && width < 1))
+    return -1;
+  const int HP = H * P, GN = G * N, cdim = HP + 2 * GN;
+  if (xbc_tok_stride < cdim) return -1;
+  const int64_t BL = (int64_t)batch * L;
+
+  /* post-conv values (and pre-activations for the conv's gradient) */
+  double* post = (double*)malloc(sizeof(double) * (size_t)(BL * cdim + 1));
+  double* pre = (double*)malloc(sizeof(double) * (size_t)(BL * cdim + 1));
+  for (int b = 0; b < batch; ++b)
+    for (int t = 0; t < L; ++t)
+      for (int c = 0; c < cdim; ++c) {
+        const int64_t o = ((int64_t)b * L + t) * cdim + c;
+        if (conv_w) {
+          pre[o] = conv_pre(xbc, xbc_tok_stride, conv_state_in, conv_w, conv_b, L, cdim, width,
+                            b, t, c);
+          post[o] = silu(pre[o]);
+        } else {
+          pre[o] = 0.0;
+          post[o] = xbc[((int64_t)b * L + t) * xbc_tok_stride + c];
+        }
+      }
+  /* gradient with respect to the post-conv values; B and C per head first */
+  double* dpost = (double*)calloc((size_t)(BL * cdim + 1), sizeof(double));
+  double* dBh = (double*)calloc((size_t)((int64_t)batch * H * L * N + 1), sizeof(double));
+  double* dCh = (double*)calloc((size_t)((int64_t)batch * H * L * N + 1), sizeof(double));
+  double* dA_bh = (double*)calloc((size_t)(batch * H + 1), sizeof(double));
+  double* dD_bh = (double*)calloc((size_t)(batch * H + 1), sizeof(double));
+  double* dbias_bh = (double*)calloc((size_t)(batch * H + 1), sizeof(double));
+
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int b = 0; b < batch; ++b)
+    for (int h = 0; h < H; ++h) {
+      const int g = (int)(((int64_t)h * G) / H);
+      const int64_t PN = (int64_t)P * N;
+      double* S = (double*)malloc(sizeof(double) * (size_t)((L + 1) * PN));  /* S[t+1] = S_t */
+      double* delta = (double*)malloc(sizeof(double) * (size_t)(L + 1));
+      double* av = (double*)malloc(sizeof(double) * (size_t)(L + 1));
+      double* dS = (double*)malloc(sizeof(double) * (size_t)PN);
+      const double Ah = A[h], Dh = D ? D[h] : 0.0;
+      for (int64_t i = 0; i < PN; ++i) S[i] = h0 ? h0[((int64_t)b * H + h) * PN + i] : 0.0;
+      /* forward, keeping every state */
+      for (int t = 0; t < L; ++t) {
+        const double* row = post + ((int64_t)b * L + t) * cdim;
+        const double* xv = row + h * P;
+        const double* Bv = row + HP + g * N;
+        double v = dt[((int64_t)b * L + t) * H + h];
+        if (dt_bias) v += dt_bias[h];
+        delta[t] = dt_softplus ? softplus(v) : v;
+        av[t] = exp(delta[t] * Ah);
+        for (int p = 0; p < P; ++p)
+          for (int n = 0; n < N; ++n)
+            S[(t + 1) * PN + (int64_t)p * N + n] =
+                av[t] * S[t * PN + (int64_t)p * N + n] + delta[t] * xv[p] * Bv[n];
+      }
+      /* reverse */
+      for (int64_t i = 0; i < PN; ++i)
+        dS[i] = dh_final ? dh_final[((int64_t)b * H + h) * PN + i] : 0.0;
+      for (int t = L - 1; t >= 0; --t) {
+        const double* row = post + ((int64_t)b * L + t) * cdim;
+        const double* xv = row + h * P;
+        const double* Bv = row + HP + g * N;
+        const double* Cv = row + HP + GN + g * N;
+        double* dxv = dpost + ((int64_t)b * L + t) * cdim + h * P;
+        double* dBv = dBh + (((int64_t)b * H + h) * L + t) * N;
+        double* dCv = dCh + (((int64_t)b * H + h) * L + t) * N;
+        const double* St = S + (t + 1) * PN;
+        const double* Sp = S + t * PN;
+        double ddelta = 0.0;
+        for (int p = 0; p < P; ++p) {
+          const int64_t o = (((int64_t)b * L + t) * H + h) * P + p;
+          double acc = 0.0;
+          for (int n = 0; n < N; ++n) acc += St[(int64_t)p * N + n] * Cv[n];
+          const double yv = acc + Dh * xv[p];
+          double dyv = dout[o];
+          if (z) {
+            dyv = dout[o] * silu(z[o]);
+            if (dz) dz[o] = dout[o] * yv * silu_grad(z[o]);
+          }
+          dD_bh[b * H + h] += dyv * xv[p];
+          dxv[p] += Dh * dyv;
+          for (int n = 0; n < N; ++n) {
+            dS[(int64_t)p * N + n] += dyv * Cv[n];
+            dCv[n] += dyv * St[(int64_t)p * N + n];
+          }
+        }
+        double da = 0.0;
+        for (int p = 0; p < P; ++p)
+          for (int n = 0; n < N; ++n) {
+            const double d = dS[(int64_t)p * N + n];
+            dxv[p] += delta[t] * d * Bv[n];
+            dBv[n] += delta[t] * d * xv[p];
+            ddelta += d * xv[p] * Bv[n];
+            da += d * Sp[(int64_t)p * N + n];
+          }
+        ddelta += da * av[t] * Ah;
+        dA_bh[b * H + h] += da * av[t] * delta[t];
+        for (int64_t i = 0; i < PN; ++i) dS[i] *= av[t];
+        double v = dt[((int64_t)b * L + t) * H + h];
+        if (dt_bias) v += dt_bias[h];
+        const double dd = dt_softplus ? ddelta / (1.0 + exp(-v)) : ddelta;
+        ddt[((int64_t)b * L + t) * H + h] = dd;
+        dbias_bh[b * H + h] += dd;
+      }
+      if (dh0) memcpy(dh0 + ((int64_t)b * H + h) * PN, dS, sizeof(double) * (size_t)PN);
+      free(dS);
+      free(av);
+      free(delta);
+      free(S);
+    }
+
+  /* the heads of a group share B and C: their gradients add up */
+  for (int b = 0; b < batch; ++b)
+    for (int h = 0; h < H; ++h) {
+      const int g = (int)(((int64_t)h * G) / H);
+      for (int t = 0; t < L; ++t)
+        for (int n = 0; n < N; ++n) {
+          double* row = dpost + ((int64_t)b * L + t) * cdim;
+          row[HP + g * N + n] += dBh[(((int64_t)b * H + h) * L + t) * N + n];
+          row[HP + GN + g * N + n] += dCh[(((int64_t)b * H + h) * L + t) * N + n];
+        }
+    }
+  for (int h = 0; h < H; ++h) {
+    double sa = 0.0, sd = 0.0, sb = 0.0;
+    for (int b = 0; b < batch; ++b) {
+      sa += dA_bh[b * H + h];
+      sd += dD_bh[b * H + h];
+      sb += dbias_bh[b * H + h];
+    }
+    dA[h] = sa;
+    if (dD) dD[h] = sd;
+    if (ddt_bias) ddt_bias[h] = sb;
+  }
+
+  /* the conv */
+  if (conv_w) {
+    for (int64_t i = 0; i < BL * cdim; ++i) dxbc[i] = 0.0;
+    if (dconv_state_in)
+      for (int64_t i = 0; i < (int64_t)batch * (width - 1) * cdim; ++i) dconv_state_in[i] = 0.0;
+    if (dconv_w)
+      for (int64_t i = 0; i < (int64_t)cdim * width; ++i) dconv_w[i] = 0.0;
+    if (dconv_b)
+      for (int c = 0; c < cdim; ++c) dconv_b[c] = 0.0;
+    for (int b = 0; b < batch; ++b)
+      for (int t = 0; t < L; ++t)
+        for (int c = 0; c < cdim; ++c) {
+          const int64_t o = ((int64_t)b * L + t) * cdim + c;
+          const double du = dpost[o] * silu_grad(pre[o]);
+          if (dconv_b) dconv_b[c] += du;
+          for (int k = 0; k < width; ++k) {
+            const int tau = t - (width - 1) + k;
+            const double wk = conv_w[(int64_t)c * width + k];
+            if (dconv_w)
+              dconv_w[(int64_t)c * width + k] +=
+                  du * conv_input(xbc, xbc_tok_stride, conv_state_in, L, cdim, width, b, tau, c);
+            if (tau >= 0)
+              dxbc[((int64_t)b * L + tau) * cdim + c] += wk * du;
+            else if (dconv_state_in)
+              dconv_state_in[((int64_t)b * (width - 1) + (width - 1) + tau) * cdim + c] += wk * du;
+          }
+        }
+  } else {
+    memcpy(dxbc, dpost, sizeof(double) * (size_t)(BL * cdim));
+  }
+  free(dbias_bh);
+  free(dD_bh);
+  free(dA_bh);
+  free(dCh);
+  free(dBh);
+  free(dpost);
+  free(pre);
+  free(post);
+  return 0;
+}
+
 /*
  * RMSNorm over the last axis of x [ntok][dim] (dense):
  *   out[t][i] = x[t][i] / sqrt(mean_j x[t][j]^2 + eps) * w[i]

@@ -9,6 +9,7 @@ import pytest
 
 import oracle
 import test_oracle_block_pins as bpins
+import test_oracle_bwd_pins as gpins
 import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ssd_oracle.c")
@@ -47,6 +48,16 @@ MUTANTS = [
      "acc += a[m * K + k] * w[(int64_t)k * N + n];"),
     ("linear residual dropped", "out[m * N + n] = residual ? residual[m * N + n] + acc : acc;",
      "out[m * N + n] = acc;"),
+    ("bwd: state gradient not decayed", "for (int64_t i = 0; i < PN; ++i) dS[i] *= av[t];",
+     "for (int64_t i = 0; i < PN; ++i) (void)dS[i];"),
+    ("bwd: delta gradient without the decay term", "ddelta += da * av[t] * Ah;", "(void)da;"),
+    ("bwd: SiLU gradient without its u term", "return sg * (1.0 + u * (1.0 - sg));", "return sg;"),
+    ("bwd: conv taps mirrored", "const double wk = conv_w[(int64_t)c * width + k];",
+     "const double wk = conv_w[(int64_t)c * width + (width - 1 - k)];"),
+    ("bwd: dA without delta", "dA_bh[b * H + h] += da * av[t] * delta[t];",
+     "dA_bh[b * H + h] += da * av[t];"),
+    ("bwd: dC from the previous state", "dCv[n] += dyv * St[(int64_t)p * N + n];",
+     "dCv[n] += dyv * Sp[(int64_t)p * N + n];"),
     ("decode B x outer product uses C",
      "const double* Bv = xc + (int64_t)b * cdim + HP + g * N;",
      "const double* Bv = xc + (int64_t)b * cdim + HP + GN + g * N;"),
@@ -67,6 +78,7 @@ PINS = [
     lambda: bpins.test_rmsnorm_weight_scales_each_channel(),
     lambda: bpins.test_linear_matches_numpy_matmul(),
     lambda: bpins.test_block_matches_independent_composition(),
+    lambda: gpins.test_bwd_full_layer(),
 ]
 
 
