@@ -183,6 +183,58 @@ int ssd_state_update(float* state, const void* xbc, ssd_dtype_t xbc_dtype,
 size_t ssd_decode_cache_bytes(int nheads, int headdim, int ngroups, int dstate, int width,
                               ssd_dtype_t conv_dtype);
 
+/* Bytes of device workspace ssd_chunk_scan_bwd needs (0 on bad input;
+ * conv_width 0 when no conv is fused): the post-conv x|B|C in fp32, the state
+ * entering every 32-token chunk (4*P*N bytes per (sequence, head, chunk)),
+ * per-head B and C gradients, and small per-block sums. */
+size_t ssd_chunk_scan_bwd_workspace_bytes(int batch, int seqlen, int nheads, int headdim,
+                                          int ngroups, int dstate, int conv_width);
+
+/*
+ * The layer's backward pass: given the gradient dout of a scalar loss with
+ * respect to ssd_chunk_scan_fwd's output (and d_final_state with respect to
+ * its final state, or NULL), the loss's gradients with respect to its
+ * inputs.  This is reverse-mode differentiation of the recurrence of
+ * "Hybrid Architectures ..." summary, section 2 Background, and of the conv
+ * and gate in front of and behind it; the pages treat the layer as a
+ * trained component ("Nemotron-H style Hybrid Mamba-Transformer 3B
+ * feasibility study", section 3).  All arithmetic is fp32.
+ *
+ *   Inputs: exactly the forward call's (x, Bm, Cm, conv_w/conv_b/
+ *   conv_state_in, dt, z, A, D, dt_bias, dt_softplus, initial_state), with
+ *   the same layouts and strides.
+ *   dout [B, L, H, P] dout_dtype, token stride dout_tok_stride;
+ *   d_final_state [B, H, P, N] fp32 or NULL (zero).
+ *   Outputs, all dense fp32, overwritten:
+ *     dxbc [B, L, Cdim] x|B|C: raw conv inputs when conv_w is given, else the
+ *          post-conv values (required);
+ *     ddt [B, L, H] with respect to the raw dt (required); dA [H] (required);
+ *     dz [B, L, H, P] (NULL, or only when z is given); dD [H], ddt_bias [H],
+ *     d_initial_state [B, H, P, N]: each optional (NULL), and defined also
+ *     when the forward input was NULL (the gradient at zero);
+ *     dconv_w [Cdim, K], dconv_b [Cdim], d_conv_state_in [B, K-1, Cdim]:
+ *     optional, only with conv_w.
+ *   No output may overlap an input or another output.
+ *   Supported: P = 64, N = 128, H % G == 0; any seqlen >= 0.
+ *   workspace: at least ssd_chunk_scan_bwd_workspace_bytes(...) bytes,
+ *   256-byte aligned, overlapping no tensor.
+ * Deterministic: the group sums of the B and C gradients and the parameter
+ * sums are taken in a fixed order.
+ */
+int ssd_chunk_scan_bwd(const void* x, int64_t x_tok_stride, const void* Bm,
+                       int64_t b_tok_stride, const void* Cm, int64_t c_tok_stride,
+                       ssd_dtype_t xbc_dtype, const float* conv_w, const float* conv_b,
+                       int conv_width, const void* conv_state_in, const void* dt,
+                       int64_t dt_tok_stride, const void* z, int64_t z_tok_stride,
+                       ssd_dtype_t act_dtype, const float* A, const float* D,
+                       const float* dt_bias, int dt_softplus, const float* initial_state,
+                       const void* dout, int64_t dout_tok_stride, ssd_dtype_t dout_dtype,
+                       const float* d_final_state, float* dxbc, float* ddt, float* dz,
+                       float* dA, float* dD, float* ddt_bias, float* d_initial_state,
+                       float* dconv_w, float* dconv_b, float* d_conv_state_in, int batch,
+                       int seqlen, int nheads, int headdim, int ngroups, int dstate,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * The block around the layer: the pre-norm residual block
  *   out = h + out_proj(mixer(rmsnorm(h)))

@@ -388,6 +388,152 @@ int ssd_state_update(float* state, const void* xbc, ssd_dtype_t xbc_dtype, void*
   return e == hipSuccess ? SSD_OK : hip_fail(e, "state_update launch");
 }
 
+// ------------------------------------------------------------------ backward
+
+size_t ssd_chunk_scan_bwd_workspace_bytes(int batch, int seqlen, int nheads, int headdim,
+                                          int ngroups, int dstate, int conv_width) {
+  if (batch <= 0 || seqlen < 0 || nheads <= 0 || ngroups <= 0 || headdim != kP ||
+      dstate != kN || nheads % ngroups != 0 || conv_width < 0 || conv_width > 4)
+    return 0;
+  size_t o[7];
+  return scan_bwd_workspace_layout(batch, seqlen, nheads, ngroups, conv_width, &o[0], &o[1],
+                                   &o[2], &o[3], &o[4], &o[5], &o[6]);
+}
+
+int ssd_chunk_scan_bwd(const void* x, int64_t x_tok_stride, const void* Bm,
+                       int64_t b_tok_stride, const void* Cm, int64_t c_tok_stride,
+                       ssd_dtype_t xbc_dtype, const float* conv_w, const float* conv_b,
+                       int conv_width, const void* conv_state_in, const void* dt,
+                       int64_t dt_tok_stride, const void* z, int64_t z_tok_stride,
+                       ssd_dtype_t act_dtype, const float* A, const float* D,
+                       const float* dt_bias, int dt_softplus, const float* initial_state,
+                       const void* dout, int64_t dout_tok_stride, ssd_dtype_t dout_dtype,
+                       const float* d_final_state, float* dxbc, float* ddt, float* dz,
+                       float* dA, float* dD, float* ddt_bias, float* d_initial_state,
+                       float* dconv_w, float* dconv_b, float* d_conv_state_in, int batch,
+                       int seqlen, int nheads, int headdim, int ngroups, int dstate,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  if (!valid_dtype(xbc_dtype) || !valid_dtype(act_dtype) || !valid_dtype(dout_dtype))
+    return fail(SSD_ERR_INVALID_ARG, "scan_bwd: bad dtype");
+  if (batch < 0 || seqlen < 0 || nheads <= 0 || ngroups <= 0 || headdim <= 0 || dstate <= 0)
+    return fail(SSD_ERR_INVALID_ARG, "scan_bwd: bad size");
+  if (nheads % ngroups != 0)
+    return fail(SSD_ERR_INVALID_ARG, "scan_bwd: nheads %d not a multiple of ngroups %d", nheads,
+                ngroups);
+  if (dt_softplus != 0 && dt_softplus != 1)
+    return fail(SSD_ERR_INVALID_ARG, "scan_bwd: dt_softplus must be 0 or 1");
+  if (headdim != kP || dstate != kN)
+    return fail(SSD_ERR_UNSUPPORTED, "scan_bwd: headdim %d / dstate %d (supported: 64 / 128)",
+                headdim, dstate);
+  if (conv_w == nullptr) {
+    if (conv_b || conv_state_in || dconv_w || dconv_b || d_conv_state_in)
+      return fail(SSD_ERR_INVALID_ARG, "scan_bwd: conv arguments given without conv_w");
+  } else {
+    if (conv_width < 1) return fail(SSD_ERR_INVALID_ARG, "scan_bwd: conv_width %d < 1", conv_width);
+    if (conv_width > 4) return fail(SSD_ERR_UNSUPPORTED, "scan_bwd: conv_width %d > 4", conv_width);
+  }
+  if (A == nullptr || dA == nullptr) return fail(SSD_ERR_INVALID_ARG, "scan_bwd: A or dA is NULL");
+  if (z == nullptr && dz != nullptr)
+    return fail(SSD_ERR_INVALID_ARG, "scan_bwd: dz given without z");
+  const int64_t rows = (int64_t)batch * seqlen;
+  const int64_t HP = (int64_t)nheads * kP, GN = (int64_t)ngroups * kN, cdim = HP + 2 * GN;
+  if (rows > 0 && (x == nullptr || Bm == nullptr || Cm == nullptr || dt == nullptr ||
+                   dout == nullptr || dxbc == nullptr || ddt == nullptr))
+    return fail(SSD_ERR_INVALID_ARG, "scan_bwd: x, Bm, Cm, dt, dout, dxbc or ddt is NULL");
+  if (x_tok_stride < HP || b_tok_stride < GN || c_tok_stride < GN || dt_tok_stride < nheads ||
+      dout_tok_stride < HP || (z != nullptr && z_tok_stride < HP))
+    return fail(SSD_ERR_INVALID_ARG, "scan_bwd: a token stride is below its row width");
+  const size_t xe = esize(xbc_dtype), ae = esize(act_dtype), de = esize(dout_dtype);
+  const void* ptrs16[] = {x, Bm, Cm, z, dout, initial_state, d_final_state, conv_state_in,
+                          dxbc, d_initial_state};
+  for (const void* p : ptrs16)
+    if (p != nullptr && !aligned(p, 16))
+      return fail(SSD_ERR_INVALID_ARG, "scan_bwd: a tensor base pointer is not 16-byte aligned");
+  if ((x_tok_stride * (int64_t)xe) % 16 || (b_tok_stride * (int64_t)xe) % 16 ||
+      (c_tok_stride * (int64_t)xe) % 16 || (dout_tok_stride * (int64_t)de) % 16 ||
+      (z != nullptr && (z_tok_stride * (int64_t)ae) % 16))
+    return fail(SSD_ERR_INVALID_ARG, "scan_bwd: a token stride is not a multiple of 16 bytes");
+  // every output is dense fp32; none may overlap an input or another output
+  const int64_t nstate = (int64_t)batch * nheads * kP * kN;
+  const int K = conv_w ? conv_width : 0;
+  const int64_t nhist = conv_w ? (int64_t)batch * (K - 1) * cdim : 0;
+  const Range ins[] = {tok_range(x, rows, x_tok_stride, HP, xe),
+                       tok_range(Bm, rows, b_tok_stride, GN, xe),
+                       tok_range(Cm, rows, c_tok_stride, GN, xe),
+                       tok_range(dt, rows, dt_tok_stride, nheads, ae),
+                       tok_range(z, rows, z_tok_stride, HP, ae),
+                       tok_range(dout, rows, dout_tok_stride, HP, de),
+                       dense_range(initial_state, nstate, 4), dense_range(d_final_state, nstate, 4),
+                       dense_range(conv_state_in, nhist, xe), dense_range(A, nheads, 4),
+                       dense_range(D, nheads, 4), dense_range(dt_bias, nheads, 4),
+                       dense_range(conv_w, cdim * K, 4), dense_range(conv_b, cdim, 4)};
+  const Range outs[] = {dense_range(dxbc, rows * cdim, 4), dense_range(ddt, rows * nheads, 4),
+                        dense_range(dz, rows * HP, 4), dense_range(dA, nheads, 4),
+                        dense_range(dD, nheads, 4), dense_range(ddt_bias, nheads, 4),
+                        dense_range(d_initial_state, nstate, 4),
+                        dense_range(dconv_w, cdim * K, 4), dense_range(dconv_b, cdim, 4),
+                        dense_range(d_conv_state_in, nhist, 4)};
+  const int nouts = (int)(sizeof outs / sizeof outs[0]);
+  for (int i = 0; i < nouts; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return fail(SSD_ERR_INVALID_ARG, "scan_bwd: an output overlaps an input");
+    for (int j = 0; j < i; ++j)
+      if (overlap(outs[i], outs[j])) return fail(SSD_ERR_INVALID_ARG, "scan_bwd: two outputs overlap");
+  }
+  size_t o[7];
+  const size_t need = batch > 0 ? scan_bwd_workspace_layout(batch, seqlen, nheads, ngroups, K,
+                                                            &o[0], &o[1], &o[2], &o[3], &o[4],
+                                                            &o[5], &o[6])
+                                : 0;
+  if (batch > 0) {
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(SSD_ERR_WORKSPACE, "scan_bwd: workspace needs %zu bytes, got %zu", need,
+                  workspace == nullptr ? (size_t)0 : workspace_bytes);
+    if (!aligned(workspace, 256))
+      return fail(SSD_ERR_INVALID_ARG, "scan_bwd: workspace is not 256-byte aligned");
+    const Range rws = dense_range(workspace, (int64_t)need, 1);
+    for (const Range& r : ins)
+      if (overlap(rws, r)) return fail(SSD_ERR_INVALID_ARG, "scan_bwd: workspace overlaps a tensor");
+    for (const Range& r : outs)
+      if (overlap(rws, r)) return fail(SSD_ERR_INVALID_ARG, "scan_bwd: workspace overlaps a tensor");
+  }
+  if (batch == 0) return SSD_OK;
+  if (seqlen == 0) {
+    // nothing to differentiate through: the initial state's gradient is the
+    // final state's, every other gradient is zero
+    hipError_t e = hipSuccess;
+    float* zeros[] = {dA, dD, ddt_bias, dconv_w, dconv_b, d_conv_state_in};
+    const int64_t zn[] = {nheads, nheads, nheads, cdim * K, cdim, nhist};
+    for (int i = 0; i < 6 && e == hipSuccess; ++i)
+      if (zeros[i] != nullptr && zn[i] > 0)
+        e = launch_copy_or_zero(zeros[i], nullptr, (size_t)zn[i] * 4, stream);
+    if (e == hipSuccess && d_initial_state != nullptr)
+      e = launch_copy_or_zero(d_initial_state, d_final_state, (size_t)nstate * 4, stream);
+    return e == hipSuccess ? SSD_OK : hip_fail(e, "scan_bwd: empty sequence");
+  }
+  ScanBwdLaunch l{};
+  l.x = x; l.x_stride = x_tok_stride;
+  l.Bm = Bm; l.b_stride = b_tok_stride;
+  l.Cm = Cm; l.c_stride = c_tok_stride;
+  l.xbc_dtype = xbc_dtype;
+  l.conv_w = conv_w; l.conv_b = conv_b; l.conv_k = K; l.conv_state_in = conv_state_in;
+  l.dt = dt; l.dt_stride = dt_tok_stride;
+  l.z = z; l.z_stride = z_tok_stride;
+  l.act_dtype = act_dtype;
+  l.A = A; l.D = D; l.dt_bias = dt_bias; l.dt_softplus = dt_softplus;
+  l.h0 = initial_state;
+  l.dout = dout; l.dout_stride = dout_tok_stride; l.dout_dtype = dout_dtype;
+  l.dhT = d_final_state;
+  l.dxbc = dxbc; l.ddt = ddt; l.dz = dz; l.dA = dA; l.dD = dD; l.ddt_bias = ddt_bias;
+  l.dh0 = d_initial_state;
+  l.dconv_w = dconv_w; l.dconv_b = dconv_b; l.dconv_state_in = d_conv_state_in;
+  l.batch = batch; l.seqlen = seqlen; l.nheads = nheads; l.ngroups = ngroups;
+  l.workspace = workspace;
+  hipError_t e = launch_scan_bwd(l, stream);
+  return e == hipSuccess ? SSD_OK : hip_fail(e, "scan_bwd launch");
+}
+
 // ------------------------------------------------------------------ the block
 
 int ssd_rmsnorm_fwd(const void* x, int64_t x_tok_stride, ssd_dtype_t x_dtype,

@@ -1,0 +1,748 @@
+// The layer's backward pass: the gradients of a loss with respect to every
+// input of ssd_chunk_scan_fwd, given the gradient of its output (and of its
+// final state).  Reverse-mode differentiation of the recurrence of "Hybrid
+// Architectures for Language Models: Systematic Analysis and Design
+// Insights" (Korean summary), section 2 Background, in the chunked form the
+// forward pass uses, fp32 throughout on the vector ALUs.
+//
+// Kernels, in launch order:
+//   1. the post-conv x|B|C in fp32 (the conv kernel, or a conversion);
+//   2. fwd_states_kernel: the state entering every chunk, per (b, h);
+//   3. bwd_chunk_kernel: per (b, h), the chunks in reverse order with the
+//      state's gradient carried in registers; per chunk it forms the
+//      gradients of x (this head), of B and C (this head's share), of dt and
+//      z, and the per-(b, h) sums for A, D and dt_bias;
+//   4. reduce_bc_kernel: the heads of a group add up their B and C shares;
+//   5. (conv) conv_bwd_kernel: the gradients of the raw inputs, of the conv
+//      history, and per-block sums for the conv weights and bias;
+//   6. reduce_params_kernel: those per-block and per-(b, h) sums, in a fixed
+//      order (no atomics: the result is bitwise reproducible).
+#include "ssd_common.h"
+
+namespace ssd {
+namespace {
+
+constexpr int BQ = 32;    // tokens per chunk
+constexpr int BP = 64;    // head dim
+constexpr int BN = 128;   // state dim
+constexpr int BT = 256;   // threads
+// LDS row pitches: rows of B, C, H differ by 4 banks, rows of x, dy by 4
+// banks, so that 8 consecutive lanes reading 8 consecutive rows at one
+// column use distinct banks
+constexpr int PN = BN + 4;
+constexpr int PP = BP + 4;
+constexpr int PQ = BQ + 1;
+
+template <typename T> __device__ __forceinline__ float ld(const T* p) { return to_f32(*p); }
+
+__device__ __forceinline__ float silu_grad_f32(float u) {
+  const float sg = 1.f / (1.f + __expf(-u));
+  return sg * (1.f + u * (1.f - sg));
+}
+
+struct BwdArgs {
+  const float* post;          // [B, L, Cdim] post-conv x|B|C, fp32
+  const void* dt; int64_t dt_stride;
+  const void* z; int64_t z_stride;
+  const void* dout; int64_t dout_stride;
+  const float* A; const float* D; const float* dt_bias; int dt_softplus;
+  const float* h0; const float* dhT;
+  float* states;              // [B, H, nc, P, N]
+  float* dpost;               // [B, L, Cdim]: x part written here
+  float* dBh; float* dCh;     // [B, H, L, N]
+  float* ddt;                 // [B, L, H]
+  float* dz;                  // [B, L, H, P] or null
+  float* dh0;                 // [B, H, P, N] or null
+  float* part;                // [B, H, 3]: dA, dD, dt_bias sums
+  int batch, seqlen, nheads, ngroups, nc, cdim;
+};
+
+// delta of token t (0 past the end); v is dt + dt_bias (for softplus')
+template <typename Ta>
+__device__ __forceinline__ float delta_of(const BwdArgs& a, int64_t row, int h, bool valid,
+                                          float& v) {
+  v = 0.f;
+  if (!valid) return 0.f;
+  v = ld(static_cast<const Ta*>(a.dt) + row * a.dt_stride + h) + (a.dt_bias ? a.dt_bias[h] : 0.f);
+  return a.dt_softplus ? softplus_f32(v) : v;
+}
+
+// ---------------------------------------------------------------- states
+
+// The state entering each chunk, for every (b, h): states[b][h][c] = H before
+// chunk c.  Thread (lane, wave w) owns H[p = lane][n in 32 w .. 32 w + 31].
+template <typename Ta>
+__global__ __launch_bounds__(BT) void fwd_states_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) float sX[BQ][PP];
+  __shared__ __attribute__((aligned(16))) float sB[BQ][PN];
+  __shared__ float sW[BQ];
+  __shared__ float sGam;
+  const int H = a.nheads, G = a.ngroups, L = a.seqlen;
+  const int b = blockIdx.x / H, h = blockIdx.x % H, g = h / (H / G);
+  const int HP = H * BP;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  float hr[32];
+  const float* h0 = a.h0 ? a.h0 + ((int64_t)b * H + h) * BP * BN + lane * BN + 32 * w : nullptr;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) hr[e] = h0 ? h0[e] : 0.f;
+  const float Ah = a.A[h];
+  for (int c = 0; c < a.nc; ++c) {
+    float* st = a.states + (((int64_t)b * H + h) * a.nc + c) * BP * BN + lane * BN + 32 * w;
+#pragma unroll
+    for (int e = 0; e < 32; e += 4)
+      *reinterpret_cast<float4*>(st + e) = make_float4(hr[e], hr[e + 1], hr[e + 2], hr[e + 3]);
+    const int t0 = c * BQ, Lc = min(BQ, L - t0);
+    for (int i = tid; i < BQ * BP; i += BT) {
+      const int t = i / BP, p = i % BP;
+      sX[t][p] = t < Lc ? a.post[((int64_t)b * L + t0 + t) * a.cdim + h * BP + p] : 0.f;
+    }
+    for (int i = tid; i < BQ * BN; i += BT) {
+      const int t = i / BN, n = i % BN;
+      sB[t][n] = t < Lc ? a.post[((int64_t)b * L + t0 + t) * a.cdim + HP + g * BN + n] : 0.f;
+    }
+    if (tid < 64) {
+      float v;
+      const float d = tid < BQ ? delta_of<Ta>(a, (int64_t)b * L + t0 + tid, h, tid < Lc, v) : 0.f;
+      float lam = d * Ah;
+      for (int o = 1; o < 32; o <<= 1) {
+        const float u = __shfl_up(lam, o, 64);
+        if ((tid & 31) >= o) lam += u;
+      }
+      const float last = __shfl(lam, Lc - 1, 64);
+      if (tid < BQ) sW[tid] = __expf(last - lam) * d;
+      if (tid == 0) sGam = __expf(last);
+    }
+    __syncthreads();
+    const float gam = sGam;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) hr[e] *= gam;
+    for (int s = 0; s < BQ; ++s) {
+      const float xs = sX[s][lane] * sW[s];
+#pragma unroll
+      for (int e = 0; e < 32; e += 4) {
+        const float4 bv = *reinterpret_cast<const float4*>(&sB[s][32 * w + e]);
+        hr[e] = fmaf(xs, bv.x, hr[e]);
+        hr[e + 1] = fmaf(xs, bv.y, hr[e + 1]);
+        hr[e + 2] = fmaf(xs, bv.z, hr[e + 2]);
+        hr[e + 3] = fmaf(xs, bv.w, hr[e + 3]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- backward
+
+// Block sum of one value per thread (fixed order), returned to every thread.
+__device__ __forceinline__ float block_sum(float v, float* sred) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sred[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return sred[0] + sred[1] + sred[2] + sred[3];
+}
+
+template <typename Ta, typename Td>
+__global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) float sX[BQ][PP];
+  __shared__ __attribute__((aligned(16))) float sDY[BQ][PP];
+  __shared__ __attribute__((aligned(16))) float sHB[BQ][PP];
+  __shared__ __attribute__((aligned(16))) float sB[BQ][PN];
+  __shared__ __attribute__((aligned(16))) float sC[BQ][PN];
+  __shared__ __attribute__((aligned(16))) float sH[BP][PN];    // state entering the chunk
+  __shared__ __attribute__((aligned(16))) float sDH[BP][PN];   // gradient of the state leaving it
+  __shared__ float sM[BQ][PQ];    // M_ts = (C_t . B_s) exp(lam_t - lam_s) delta_s, s <= t
+  __shared__ float sS[BQ][PQ];    // C_t . B_s
+  __shared__ float sDS[BQ][PQ];   // dM_ts exp(lam_t - lam_s) delta_s
+  __shared__ float sE[BQ][PQ];    // dM_ts S_ts exp(lam_t - lam_s)
+  __shared__ float sDel[BQ], sLam[BQ], sV[BQ], sDLoff[BQ], sDW[BQ];
+  __shared__ float sRed[4];
+
+  const int H = a.nheads, G = a.ngroups, L = a.seqlen;
+  const int b = blockIdx.x / H, h = blockIdx.x % H, g = h / (H / G);
+  const int HP = H * BP, GN = G * BN;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tq = tid >> 3, r8 = tid & 7;   // token-and-8-lane mapping
+  const float Ah = a.A[h], Dh = a.D ? a.D[h] : 0.f;
+
+  // the state's gradient: thread owns dH[p = lane][n in 32 w .. 32 w + 31]
+  float dh[32];
+  {
+    const float* src = a.dhT ? a.dhT + ((int64_t)b * H + h) * BP * BN + lane * BN + 32 * w : nullptr;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) dh[e] = src ? src[e] : 0.f;
+  }
+  float dD_part = 0.f, dA_part = 0.f, dbias_part = 0.f;
+
+  for (int c = a.nc - 1; c >= 0; --c) {
+    const int t0 = c * BQ, Lc = min(BQ, L - t0);
+    const int64_t row0 = (int64_t)b * L + t0;
+    // ---- load the chunk
+    for (int i = tid; i < BQ * BP; i += BT) {
+      const int t = i / BP, p = i % BP;
+      sX[t][p] = t < Lc ? a.post[(row0 + t) * a.cdim + h * BP + p] : 0.f;
+    }
+    for (int i = tid; i < BQ * BN; i += BT) {
+      const int t = i / BN, n = i % BN;
+      const bool ok = t < Lc;
+      sB[t][n] = ok ? a.post[(row0 + t) * a.cdim + HP + g * BN + n] : 0.f;
+      sC[t][n] = ok ? a.post[(row0 + t) * a.cdim + HP + GN + g * BN + n] : 0.f;
+    }
+    {
+      const float* st = a.states + (((int64_t)b * H + h) * a.nc + c) * BP * BN;
+      for (int i = tid; i < BP * BN / 4; i += BT) {
+        const int p = i / (BN / 4), n4 = i % (BN / 4);
+        *reinterpret_cast<float4*>(&sH[p][4 * n4]) =
+            *reinterpret_cast<const float4*>(st + p * BN + 4 * n4);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 32; e += 4)
+      *reinterpret_cast<float4*>(&sDH[lane][32 * w + e]) =
+          make_float4(dh[e], dh[e + 1], dh[e + 2], dh[e + 3]);
+    if (tid < 64) {
+      float v;
+      const float d = tid < BQ ? delta_of<Ta>(a, row0 + tid, h, tid < Lc, v) : 0.f;
+      float lam = d * Ah;
+      for (int o = 1; o < 32; o <<= 1) {
+        const float u = __shfl_up(lam, o, 64);
+        if ((tid & 31) >= o) lam += u;
+      }
+      if (tid < BQ) {
+        sDel[tid] = d;
+        sLam[tid] = lam;
+        sV[tid] = v;
+      }
+    }
+    __syncthreads();
+    const float lam_last = sLam[Lc - 1];
+    const float gam = __expf(lam_last);
+
+    // ---- S, M (4 entries per thread) and the inter-chunk read-out Yoff
+    for (int j = 0; j < 4; ++j) {
+      const int e = tid + BT * j, t = e >> 5, s = e & 31;
+      float S = 0.f, M = 0.f;
+      if (s <= t) {
+        for (int n = 0; n < BN; n += 4) {
+          const float4 cv = *reinterpret_cast<const float4*>(&sC[t][n]);
+          const float4 bv = *reinterpret_cast<const float4*>(&sB[s][n]);
+          S = fmaf(cv.x, bv.x, S); S = fmaf(cv.y, bv.y, S);
+          S = fmaf(cv.z, bv.z, S); S = fmaf(cv.w, bv.w, S);
+        }
+        M = S * __expf(sLam[t] - sLam[s]) * sDel[s];
+      }
+      sS[t][s] = S;
+      sM[t][s] = M;
+    }
+    float yoff[8];  // (t = tq, p = r8 + 8 i)
+    {
+      const float el = __expf(sLam[tq]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) yoff[i] = 0.f;
+      for (int n = 0; n < BN; n += 4) {
+        const float4 cv = *reinterpret_cast<const float4*>(&sC[tq][n]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float4 hv = *reinterpret_cast<const float4*>(&sH[r8 + 8 * i][n]);
+          yoff[i] = fmaf(cv.x, hv.x, fmaf(cv.y, hv.y, fmaf(cv.z, hv.z, fmaf(cv.w, hv.w, yoff[i]))));
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) yoff[i] *= el;
+    }
+    __syncthreads();
+
+    // ---- forward output, the gate and its gradient: (t = tq, p = r8 + 8 i)
+    {
+      const int t = tq;
+      const bool ok = t < Lc;
+      float dl = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int p = r8 + 8 * i;
+        float yv = yoff[i] + Dh * sX[t][p];
+        for (int s = 0; s <= t; ++s) yv = fmaf(sM[t][s], sX[s][p], yv);
+        float dyv = 0.f;
+        if (ok) {
+          const int64_t o = (row0 + t) * a.dout_stride + h * BP + p;
+          const float dout = ld(static_cast<const Td*>(a.dout) + o);
+          if (a.z) {
+            const float zz = ld(static_cast<const Ta*>(a.z) + (row0 + t) * a.z_stride + h * BP + p);
+            dyv = dout * silu_f32(zz);
+            if (a.dz) a.dz[((row0 + t) * H + h) * BP + p] = dout * yv * silu_grad_f32(zz);
+          } else {
+            dyv = dout;
+          }
+        }
+        sDY[t][p] = dyv;
+        dD_part = fmaf(dyv, sX[t][p], dD_part);
+        dl = fmaf(dyv, yoff[i], dl);
+      }
+      dl += __shfl_xor(dl, 1, 64);
+      dl += __shfl_xor(dl, 2, 64);
+      dl += __shfl_xor(dl, 4, 64);
+      if (r8 == 0) sDLoff[t] = dl;
+    }
+    __syncthreads();
+
+    // ---- dM, dS, E (4 entries per thread) and HB_s = dH_out B_s (s = tq)
+    for (int j = 0; j < 4; ++j) {
+      const int e = tid + BT * j, t = e >> 5, s = e & 31;
+      float ds = 0.f, ee = 0.f;
+      if (s <= t) {
+        float dm = 0.f;
+        for (int p = 0; p < BP; p += 4) {
+          const float4 yv = *reinterpret_cast<const float4*>(&sDY[t][p]);
+          const float4 xv = *reinterpret_cast<const float4*>(&sX[s][p]);
+          dm = fmaf(yv.x, xv.x, dm); dm = fmaf(yv.y, xv.y, dm);
+          dm = fmaf(yv.z, xv.z, dm); dm = fmaf(yv.w, xv.w, dm);
+        }
+        const float ex = __expf(sLam[t] - sLam[s]);
+        ds = dm * ex * sDel[s];
+        ee = dm * sS[t][s] * ex;
+      }
+      sDS[t][s] = ds;
+      sE[t][s] = ee;
+    }
+    {
+      float hb[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) hb[i] = 0.f;
+      for (int n = 0; n < BN; n += 4) {
+        const float4 bv = *reinterpret_cast<const float4*>(&sB[tq][n]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float4 dv = *reinterpret_cast<const float4*>(&sDH[r8 + 8 * i][n]);
+          hb[i] = fmaf(bv.x, dv.x, fmaf(bv.y, dv.y, fmaf(bv.z, dv.z, fmaf(bv.w, dv.w, hb[i]))));
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sHB[tq][r8 + 8 * i] = hb[i];
+    }
+    // <dH_out, H_in> for the gradient of the chunk's total decay
+    float hh = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) hh = fmaf(dh[e], sH[lane][32 * w + e], hh);
+    const float dot_hh = block_sum(hh, sRed);  // (includes the barrier)
+
+    // ---- dC_t, dB_s (n = 4 r8 + 32 j), dx_s (p = r8 + 8 i); token = tq
+    {
+      const int t = tq;
+      const bool ok = t < Lc;
+      const float el = __expf(sLam[t]);
+      const float ws = __expf(lam_last - sLam[t]) * sDel[t];
+      float dcv[16], dbv[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) dcv[k] = dbv[k] = 0.f;
+      for (int s = 0; s < BQ; ++s) {
+        const float a1 = sDS[t][s];   // dC_t += dS_ts B_s
+        const float a2 = sDS[s][t];   // dB_t += dS_st C_s
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 bv = *reinterpret_cast<const float4*>(&sB[s][4 * r8 + 32 * j]);
+          const float4 cv = *reinterpret_cast<const float4*>(&sC[s][4 * r8 + 32 * j]);
+          dcv[4 * j] = fmaf(a1, bv.x, dcv[4 * j]);
+          dcv[4 * j + 1] = fmaf(a1, bv.y, dcv[4 * j + 1]);
+          dcv[4 * j + 2] = fmaf(a1, bv.z, dcv[4 * j + 2]);
+          dcv[4 * j + 3] = fmaf(a1, bv.w, dcv[4 * j + 3]);
+          dbv[4 * j] = fmaf(a2, cv.x, dbv[4 * j]);
+          dbv[4 * j + 1] = fmaf(a2, cv.y, dbv[4 * j + 1]);
+          dbv[4 * j + 2] = fmaf(a2, cv.z, dbv[4 * j + 2]);
+          dbv[4 * j + 3] = fmaf(a2, cv.w, dbv[4 * j + 3]);
+        }
+      }
+      float oc[16], ob[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) oc[k] = ob[k] = 0.f;
+      for (int p = 0; p < BP; ++p) {
+        const float yv = sDY[t][p];   // dC_t += e^lam_t dy_t H_in
+        const float xv = sX[t][p];    // dB_t += w_t x_t dH_out
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 hv = *reinterpret_cast<const float4*>(&sH[p][4 * r8 + 32 * j]);
+          const float4 dv = *reinterpret_cast<const float4*>(&sDH[p][4 * r8 + 32 * j]);
+          oc[4 * j] = fmaf(yv, hv.x, oc[4 * j]);
+          oc[4 * j + 1] = fmaf(yv, hv.y, oc[4 * j + 1]);
+          oc[4 * j + 2] = fmaf(yv, hv.z, oc[4 * j + 2]);
+          oc[4 * j + 3] = fmaf(yv, hv.w, oc[4 * j + 3]);
+          ob[4 * j] = fmaf(xv, dv.x, ob[4 * j]);
+          ob[4 * j + 1] = fmaf(xv, dv.y, ob[4 * j + 1]);
+          ob[4 * j + 2] = fmaf(xv, dv.z, ob[4 * j + 2]);
+          ob[4 * j + 3] = fmaf(xv, dv.w, ob[4 * j + 3]);
+        }
+      }
+      if (ok) {
+        float* dc = a.dCh + (((int64_t)b * H + h) * L + t0 + t) * BN;
+        float* db = a.dBh + (((int64_t)b * H + h) * L + t0 + t) * BN;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = 4 * r8 + 32 * j;
+          *reinterpret_cast<float4*>(dc + n) =
+              make_float4(fmaf(el, oc[4 * j], dcv[4 * j]), fmaf(el, oc[4 * j + 1], dcv[4 * j + 1]),
+                          fmaf(el, oc[4 * j + 2], dcv[4 * j + 2]), fmaf(el, oc[4 * j + 3], dcv[4 * j + 3]));
+          *reinterpret_cast<float4*>(db + n) =
+              make_float4(fmaf(ws, ob[4 * j], dbv[4 * j]), fmaf(ws, ob[4 * j + 1], dbv[4 * j + 1]),
+                          fmaf(ws, ob[4 * j + 2], dbv[4 * j + 2]), fmaf(ws, ob[4 * j + 3], dbv[4 * j + 3]));
+        }
+      }
+      // dx_t = D dy_t + sum_t' M_t't dy_t' + w_t HB_t;  dw_t = x_t . HB_t
+      float dwp = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int p = r8 + 8 * i;
+        float dx = Dh * sDY[t][p] + ws * sHB[t][p];
+        for (int u = t; u < BQ; ++u) dx = fmaf(sM[u][t], sDY[u][p], dx);
+        if (ok) a.dpost[(row0 + t) * a.cdim + h * BP + p] = dx;
+        dwp = fmaf(sX[t][p], sHB[t][p], dwp);
+      }
+      dwp += __shfl_xor(dwp, 1, 64);
+      dwp += __shfl_xor(dwp, 2, 64);
+      dwp += __shfl_xor(dwp, 4, 64);
+      if (r8 == 0) sDW[t] = dwp;
+    }
+    __syncthreads();
+
+    // ---- the decays and delta: one lane per token (wave 0)
+    if (tid < 64) {
+      const int t = tid & 31;
+      const bool real = tid < BQ;
+      const float del = real ? sDel[t] : 0.f, lam = sLam[t];
+      const float wt = __expf(lam_last - lam) * del;
+      float rowg = 0.f, colg = 0.f, cole = 0.f;
+      for (int s = 0; s < BQ; ++s) {
+        rowg = fmaf(sE[t][s], sDel[s], rowg);
+        colg = fmaf(sE[s][t], del, colg);
+        cole += sE[s][t];
+      }
+      // gradient of the chunk's total log-decay (through w and the carry)
+      float dwl = real ? sDW[t] * wt : 0.f;
+      for (int o = 16; o > 0; o >>= 1) dwl += __shfl_xor(dwl, o, 32);
+      const float dlam_last = dwl + gam * dot_hh;
+      float dlam = real ? rowg - colg + sDLoff[t] - sDW[t] * wt : 0.f;
+      if (real && t == Lc - 1) dlam += dlam_last;
+      // suffix sums over the chunk: lam_t = A sum_{r <= t} delta_r
+      float suf = dlam;
+      for (int o = 1; o < 32; o <<= 1) {
+        const float u = __shfl_down(suf, o, 32);
+        if (t + o < 32) suf += u;
+      }
+      const float ddel = cole + (real ? sDW[t] * __expf(lam_last - lam) : 0.f) + Ah * suf;
+      if (real) {
+        dA_part = fmaf(del, suf, dA_part);
+        const float sg = a.dt_softplus ? 1.f / (1.f + __expf(-sV[t])) : 1.f;
+        const float dd = ddel * sg;
+        if (t < Lc) {
+          a.ddt[(row0 + t) * H + h] = dd;
+          dbias_part += dd;
+        }
+      }
+    }
+
+    // ---- the state's gradient entering the chunk:
+    //      dH_in = e^lam_last dH_out + sum_t e^lam_t dy_t C_t^T
+#pragma unroll
+    for (int e = 0; e < 32; ++e) dh[e] *= gam;
+    for (int t = 0; t < BQ; ++t) {
+      const float yv = sDY[t][lane] * __expf(sLam[t]);
+#pragma unroll
+      for (int e = 0; e < 32; e += 4) {
+        const float4 cv = *reinterpret_cast<const float4*>(&sC[t][32 * w + e]);
+        dh[e] = fmaf(yv, cv.x, dh[e]);
+        dh[e + 1] = fmaf(yv, cv.y, dh[e + 1]);
+        dh[e + 2] = fmaf(yv, cv.z, dh[e + 2]);
+        dh[e + 3] = fmaf(yv, cv.w, dh[e + 3]);
+      }
+    }
+    __syncthreads();
+  }
+
+  if (a.dh0) {
+    float* dst = a.dh0 + ((int64_t)b * H + h) * BP * BN + lane * BN + 32 * w;
+#pragma unroll
+    for (int e = 0; e < 32; e += 4)
+      *reinterpret_cast<float4*>(dst + e) = make_float4(dh[e], dh[e + 1], dh[e + 2], dh[e + 3]);
+  }
+  const float sA = block_sum(dA_part, sRed);
+  const float sD = block_sum(dD_part, sRed);
+  const float sb = block_sum(dbias_part, sRed);
+  if (tid == 0) {
+    float* pp = a.part + ((int64_t)b * H + h) * 3;
+    pp[0] = sA;
+    pp[1] = sD;
+    pp[2] = sb;
+  }
+}
+
+// The B and C gradients of a group: the sum of its heads' shares, in head
+// order.  One thread per (b, t, 4 consecutive n of B or C).
+__global__ void reduce_bc_kernel(const float* __restrict__ dBh, const float* __restrict__ dCh,
+                                 float* __restrict__ dpost, int batch, int seqlen, int nheads,
+                                 int ngroups, int cdim) {
+  const int GN4 = ngroups * BN / 4;
+  const int64_t total = (int64_t)batch * seqlen * 2 * GN4;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int k = (int)(i % (2 * GN4));
+  const int64_t bt = i / (2 * GN4);
+  const int b = (int)(bt / seqlen), t = (int)(bt % seqlen);
+  const bool isC = k >= GN4;
+  const int gn = (isC ? k - GN4 : k) * 4;
+  const int g = gn / BN, n = gn % BN;
+  const int hpg = nheads / ngroups;
+  const float* src = isC ? dCh : dBh;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < hpg; ++j) {
+    const int h = g * hpg + j;
+    const float4 v = *reinterpret_cast<const float4*>(src + (((int64_t)b * nheads + h) * seqlen + t) * BN + n);
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  const int HP = nheads * BP;
+  *reinterpret_cast<float4*>(dpost + bt * cdim + HP + (isC ? ngroups * BN : 0) + gn) = acc;
+}
+
+// ---------------------------------------------------------------- conv
+
+constexpr int CT = 64;   // tokens per conv block
+
+// One thread per (b, channel, block of CT tokens): du = dpost silu'(u) over
+// the block and the K-1 tokens after it, the raw inputs' gradients of the
+// block (and of the history, in the first block), and the block's sums for
+// the conv weights and bias.
+template <typename Tx>
+__global__ void conv_bwd_kernel(const void* x, int64_t xs, const void* Bm, int64_t bs,
+                                const void* Cm, int64_t cs, const float* __restrict__ w,
+                                const float* __restrict__ bias, const void* hist,
+                                const float* __restrict__ dpost, float* __restrict__ dxbc,
+                                float* __restrict__ dhist, float* __restrict__ wpart,
+                                int batch, int seqlen, int cdim, int HP, int GN, int K) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  const int blk = blockIdx.y, b = blockIdx.z;
+  if (c >= cdim) return;
+  const Tx* src;
+  int64_t st;
+  int cc;
+  if (c < HP) { src = static_cast<const Tx*>(x); st = xs; cc = c; }
+  else if (c < HP + GN) { src = static_cast<const Tx*>(Bm); st = bs; cc = c - HP; }
+  else { src = static_cast<const Tx*>(Cm); st = cs; cc = c - HP - GN; }
+  const Tx* hs = static_cast<const Tx*>(hist);
+  auto raw = [&](int tau) -> float {  // raw input at position tau (history below 0)
+    if (tau >= 0) return to_f32(src[((int64_t)b * seqlen + tau) * st + cc]);
+    if (hs == nullptr) return 0.f;
+    return to_f32(hs[((int64_t)b * (K - 1) + (K - 1) + tau) * cdim + c]);
+  };
+  float wk[4];
+  for (int k = 0; k < 4; ++k) wk[k] = k < K ? w[c * K + k] : 0.f;
+  const float bc = bias ? bias[c] : 0.f;
+  const int t0 = blk * CT, t1 = min(seqlen, t0 + CT);
+  // du over [t0, t1 + K - 1) (the taps that reach back into this block)
+  float du[CT + 3];
+  float win[4] = {0.f, 0.f, 0.f, 0.f};  // raw inputs t - K + 1 .. t
+  // after the first shift, win[4 - K + k] must hold raw(t0 - (K - 1) + k)
+  for (int k = 0; k < K - 1; ++k) win[5 - K + k] = raw(t0 - (K - 1) + k);
+  float gw[4] = {0.f, 0.f, 0.f, 0.f}, gb = 0.f;
+  const int tend = min(seqlen, t1 + K - 1);
+  for (int t = t0; t < tend; ++t) {
+    for (int k = 0; k < 3; ++k) win[k] = win[k + 1];
+    win[3] = raw(t);
+    float u = bc;
+    for (int k = 0; k < K; ++k) u = fmaf(wk[k], win[4 - K + k], u);
+    const float d = dpost[((int64_t)b * seqlen + t) * cdim + c] * silu_grad_f32(u);
+    du[t - t0] = d;
+    if (t < t1) {
+      gb += d;
+      for (int k = 0; k < K; ++k) gw[k] = fmaf(d, win[4 - K + k], gw[k]);
+    }
+  }
+  // d raw[tau] = sum_k w[k] du[tau + K - 1 - k]
+  for (int tau = t0; tau < t1; ++tau) {
+    float s = 0.f;
+    for (int k = 0; k < K; ++k) {
+      const int t = tau + K - 1 - k;
+      if (t < tend) s = fmaf(wk[k], du[t - t0], s);
+    }
+    dxbc[((int64_t)b * seqlen + tau) * cdim + c] = s;
+  }
+  if (blk == 0 && dhist != nullptr) {
+    for (int j = 0; j < K - 1; ++j) {  // history row j is position tau = j - (K - 1)
+      const int tau = j - (K - 1);
+      float s = 0.f;
+      for (int k = 0; k < K; ++k) {
+        const int t = tau + K - 1 - k;
+        if (t >= 0 && t < tend) s = fmaf(wk[k], du[t - t0], s);
+      }
+      dhist[((int64_t)b * (K - 1) + j) * cdim + c] = s;
+    }
+  }
+  const int nblk = gridDim.y;
+  float* wp = wpart + (((int64_t)b * nblk + blk) * cdim + c) * 5;
+  for (int k = 0; k < 4; ++k) wp[k] = gw[k];
+  wp[4] = gb;
+}
+
+// Fixed-order sums: dA, dD, dt_bias over the batch; the conv weights and bias
+// over (b, block).
+__global__ void reduce_params_kernel(const float* __restrict__ part, int batch, int nheads,
+                                     float* dA, float* dD, float* dbias,
+                                     const float* __restrict__ wpart, int nparts, int cdim, int K,
+                                     float* dw, float* db) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nheads) {
+    float sa = 0.f, sd = 0.f, sb = 0.f;
+    for (int b = 0; b < batch; ++b) {
+      const float* p = part + ((int64_t)b * nheads + i) * 3;
+      sa += p[0]; sd += p[1]; sb += p[2];
+    }
+    dA[i] = sa;
+    if (dD) dD[i] = sd;
+    if (dbias) dbias[i] = sb;
+  }
+  if (wpart != nullptr && i < cdim) {
+    float s[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < nparts; ++j)
+      for (int k = 0; k < 5; ++k) s[k] += wpart[((int64_t)j * cdim + i) * 5 + k];
+    if (dw)
+      for (int k = 0; k < K; ++k) dw[i * K + k] = s[k];
+    if (db) db[i] = s[4];
+  }
+}
+
+// x|B|C (post-conv inputs) to fp32 [B, L, Cdim]
+template <typename Tx>
+__global__ void gather_post_kernel(const void* x, int64_t xs, const void* Bm, int64_t bs,
+                                   const void* Cm, int64_t cs, float* __restrict__ post,
+                                   int64_t rows, int cdim, int HP, int GN) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * cdim) return;
+  const int64_t r = i / cdim;
+  const int c = (int)(i % cdim);
+  float v;
+  if (c < HP) v = to_f32(static_cast<const Tx*>(x)[r * xs + c]);
+  else if (c < HP + GN) v = to_f32(static_cast<const Tx*>(Bm)[r * bs + c - HP]);
+  else v = to_f32(static_cast<const Tx*>(Cm)[r * cs + c - HP - GN]);
+  post[i] = v;
+}
+
+}  // namespace
+
+size_t scan_bwd_workspace_layout(int batch, int seqlen, int nheads, int ngroups, int conv_width,
+                                 size_t* off_post, size_t* off_states, size_t* off_dbh,
+                                 size_t* off_dch, size_t* off_dpost, size_t* off_part,
+                                 size_t* off_wpart) {
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  const size_t T = (size_t)batch * seqlen;
+  const size_t cdim = (size_t)nheads * BP + 2 * (size_t)ngroups * BN;
+  const size_t nc = (size_t)(seqlen + BQ - 1) / BQ;
+  const size_t nblk = (size_t)(seqlen + CT - 1) / CT;
+  size_t o = 0;
+  *off_post = o; o += up(T * cdim * 4);
+  *off_states = o; o += up((size_t)batch * nheads * nc * BP * BN * 4);
+  *off_dbh = o; o += up((size_t)batch * nheads * seqlen * BN * 4);
+  *off_dch = o; o += up((size_t)batch * nheads * seqlen * BN * 4);
+  *off_dpost = o; o += up(conv_width > 0 ? T * cdim * 4 : 0);
+  *off_part = o; o += up((size_t)batch * nheads * 3 * 4);
+  *off_wpart = o; o += up(conv_width > 0 ? (size_t)batch * nblk * cdim * 5 * 4 : 0);
+  return o;
+}
+
+hipError_t launch_scan_bwd(const ScanBwdLaunch& l, hipStream_t stream) {
+  const int B = l.batch, L = l.seqlen, H = l.nheads, G = l.ngroups;
+  const int HP = H * BP, GN = G * BN, cdim = HP + 2 * GN;
+  const int64_t T = (int64_t)B * L;
+  size_t o_post, o_st, o_db, o_dc, o_dp, o_part, o_wp;
+  scan_bwd_workspace_layout(B, L, H, G, l.conv_w ? l.conv_k : 0, &o_post, &o_st, &o_db, &o_dc,
+                            &o_dp, &o_part, &o_wp);
+  char* ws = static_cast<char*>(l.workspace);
+  float* post = reinterpret_cast<float*>(ws + o_post);
+  const bool bf = l.xbc_dtype == SSD_BF16;
+  hipError_t e;
+  // 1. post-conv x|B|C in fp32
+  if (l.conv_w) {
+    // x, B and C are separate tensors: the conv runs on each channel range
+    const void* srcs[3] = {l.x, l.Bm, l.Cm};
+    const int64_t strides[3] = {l.x_stride, l.b_stride, l.c_stride};
+    const int widths[3] = {HP, GN, GN};
+    int c0 = 0;
+    for (int k = 0; k < 3; ++k) {
+      const size_t es = bf ? 2 : 4;
+      const void* hist = l.conv_state_in
+                             ? static_cast<const char*>(l.conv_state_in) + (size_t)c0 * es
+                             : nullptr;
+      e = launch_causal_conv1d(srcs[k], strides[k], l.xbc_dtype, l.conv_w + (size_t)c0 * l.conv_k,
+                               l.conv_b ? l.conv_b + c0 : nullptr, hist, nullptr, cdim, post + c0,
+                               cdim, SSD_F32, B, L, widths[k], l.conv_k, 1, stream);
+      if (e != hipSuccess) return e;
+      c0 += widths[k];
+    }
+  } else {
+    const int64_t n = T * cdim;
+    const unsigned grid = (unsigned)((n + 255) / 256);
+    if (bf)
+      gather_post_kernel<bf16><<<grid, 256, 0, stream>>>(l.x, l.x_stride, l.Bm, l.b_stride, l.Cm,
+                                                          l.c_stride, post, T, cdim, HP, GN);
+    else
+      gather_post_kernel<float><<<grid, 256, 0, stream>>>(l.x, l.x_stride, l.Bm, l.b_stride, l.Cm,
+                                                           l.c_stride, post, T, cdim, HP, GN);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  BwdArgs a{};
+  a.post = post;
+  a.dt = l.dt; a.dt_stride = l.dt_stride;
+  a.z = l.z; a.z_stride = l.z_stride;
+  a.dout = l.dout; a.dout_stride = l.dout_stride;
+  a.A = l.A; a.D = l.D; a.dt_bias = l.dt_bias; a.dt_softplus = l.dt_softplus;
+  a.h0 = l.h0; a.dhT = l.dhT;
+  a.states = reinterpret_cast<float*>(ws + o_st);
+  // without a conv the post-conv gradient is the answer
+  a.dpost = l.conv_w ? reinterpret_cast<float*>(ws + o_dp) : l.dxbc;
+  a.dBh = reinterpret_cast<float*>(ws + o_db);
+  a.dCh = reinterpret_cast<float*>(ws + o_dc);
+  a.ddt = l.ddt; a.dz = l.dz; a.dh0 = l.dh0;
+  a.part = reinterpret_cast<float*>(ws + o_part);
+  a.batch = B; a.seqlen = L; a.nheads = H; a.ngroups = G; a.nc = (L + BQ - 1) / BQ;
+  a.cdim = cdim;
+  const dim3 grid_bh((unsigned)(B * H));
+  const bool abf = l.act_dtype == SSD_BF16, dbf = l.dout_dtype == SSD_BF16;
+  // 2. the state entering each chunk
+  if (abf) fwd_states_kernel<bf16><<<grid_bh, BT, 0, stream>>>(a);
+  else fwd_states_kernel<float><<<grid_bh, BT, 0, stream>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // 3. the chunks in reverse
+  if (abf && dbf) bwd_chunk_kernel<bf16, bf16><<<grid_bh, BT, 0, stream>>>(a);
+  else if (abf) bwd_chunk_kernel<bf16, float><<<grid_bh, BT, 0, stream>>>(a);
+  else if (dbf) bwd_chunk_kernel<float, bf16><<<grid_bh, BT, 0, stream>>>(a);
+  else bwd_chunk_kernel<float, float><<<grid_bh, BT, 0, stream>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // 4. B and C of each group
+  {
+    const int64_t n = T * 2 * (GN / 4);
+    reduce_bc_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(a.dBh, a.dCh, a.dpost, B, L,
+                                                                      H, G, cdim);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // 5. the conv
+  const int nblk = (L + CT - 1) / CT;
+  float* wpart = reinterpret_cast<float*>(ws + o_wp);
+  if (l.conv_w) {
+    const dim3 grid((unsigned)((cdim + 255) / 256), (unsigned)nblk, (unsigned)B);
+    if (bf)
+      conv_bwd_kernel<bf16><<<grid, 256, 0, stream>>>(
+          l.x, l.x_stride, l.Bm, l.b_stride, l.Cm, l.c_stride, l.conv_w, l.conv_b,
+          l.conv_state_in, a.dpost, l.dxbc, l.dconv_state_in, wpart, B, L, cdim, HP, GN, l.conv_k);
+    else
+      conv_bwd_kernel<float><<<grid, 256, 0, stream>>>(
+          l.x, l.x_stride, l.Bm, l.b_stride, l.Cm, l.c_stride, l.conv_w, l.conv_b,
+          l.conv_state_in, a.dpost, l.dxbc, l.dconv_state_in, wpart, B, L, cdim, HP, GN, l.conv_k);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // 6. parameter sums
+  {
+    const int n = l.conv_w ? (cdim > H ? cdim : H) : H;
+    reduce_params_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(
+        a.part, B, H, l.dA, l.dD, l.ddt_bias, l.conv_w ? wpart : nullptr, B * nblk, cdim,
+        l.conv_k, l.dconv_w, l.dconv_b);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace ssd

@@ -90,6 +90,32 @@ hipError_t launch_state_update(float* state, const void* xbc, ssd_dtype_t xbc_dt
                                int softplus, void* y, ssd_dtype_t y_dtype, int batch,
                                int nheads, int ngroups, hipStream_t stream);
 
+// Everything the backward pass needs (validated by the caller).
+struct ScanBwdLaunch {
+  const void* x; int64_t x_stride;
+  const void* Bm; int64_t b_stride;
+  const void* Cm; int64_t c_stride;
+  ssd_dtype_t xbc_dtype;
+  const float* conv_w; const float* conv_b; int conv_k; const void* conv_state_in;
+  const void* dt; int64_t dt_stride;
+  const void* z; int64_t z_stride;
+  ssd_dtype_t act_dtype;
+  const float* A; const float* D; const float* dt_bias; int dt_softplus;
+  const float* h0;
+  const void* dout; int64_t dout_stride; ssd_dtype_t dout_dtype;
+  const float* dhT;
+  float* dxbc; float* ddt; float* dz; float* dA; float* dD; float* ddt_bias; float* dh0;
+  float* dconv_w; float* dconv_b; float* dconv_state_in;
+  int batch, seqlen, nheads, ngroups;
+  void* workspace;
+};
+hipError_t launch_scan_bwd(const ScanBwdLaunch& l, hipStream_t stream);
+// Workspace of the backward pass (total bytes) and its parts' offsets.
+size_t scan_bwd_workspace_layout(int batch, int seqlen, int nheads, int ngroups, int conv_width,
+                                 size_t* off_post, size_t* off_states, size_t* off_dbh,
+                                 size_t* off_dch, size_t* off_dpost, size_t* off_part,
+                                 size_t* off_wpart);
+
 // RMSNorm of ntok rows of dim elements (dim % 8 == 0, rows 16-byte aligned).
 hipError_t launch_rmsnorm(const void* x, int64_t xs, ssd_dtype_t x_dtype, const float* w,
                           float eps, void* out, int64_t os, ssd_dtype_t out_dtype, int64_t ntok,

@@ -33,6 +33,10 @@ SIGNATURES = {
     "ssd_state_update": (_I, [_V, _V, _I, _V, _V, _V, _I, _V, _V, _I, _V, _V, _V, _I, _V, _I,
                               _I, _I, _I, _I, _I, _V]),
     "ssd_decode_cache_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "ssd_chunk_scan_bwd_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
+    "ssd_chunk_scan_bwd": (_I, [_V, _I64, _V, _I64, _V, _I64, _I, _V, _V, _I, _V, _V, _I64, _V,
+                                _I64, _I, _V, _V, _V, _I, _V, _V, _I64, _I, _V, _V, _V, _V, _V,
+                                _V, _V, _V, _V, _V, _V, _I, _I, _I, _I, _I, _I, _V, _SZ, _V]),
     "ssd_rmsnorm_fwd": (_I, [_V, _I64, _I, _V, ctypes.c_float, _V, _I64, _I, _I64, _I, _V]),
     "ssd_linear_fwd": (_I, [_V, _I64, _V, _I64, _V, _I64, _I, _V, _I64, _I, _I64, _I, _I, _V]),
     "ssd_block_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
@@ -332,3 +336,65 @@ def ssd_block_fwd(h, norm_w, in_proj_w, conv_w, A, out_proj_w, *, nheads, ngroup
         _p(conv_state_out), _p(initial_state), _p(final_state), _p(out), _dt(out), B, L, dm, H, P,
         G, N, _p(workspace), wsz, _stream(h)))
     return out
+
+
+def ssd_chunk_scan_bwd_workspace_bytes(batch, seqlen, nheads, headdim=64, ngroups=8, dstate=128,
+                                       conv_width=0):
+    return load().ssd_chunk_scan_bwd_workspace_bytes(batch, seqlen, nheads, headdim, ngroups,
+                                                     dstate, conv_width)
+
+
+def ssd_chunk_scan_bwd(x, Bm, Cm, dt, A, dout, *, D=None, z=None, dt_bias=None, dt_softplus=True,
+                       initial_state=None, d_final_state=None, conv_w=None, conv_b=None,
+                       conv_state_in=None, want_initial_state=True, workspace=None):
+    """Gradients of ssd_chunk_scan_fwd.  Inputs as there; dout [B, L, H, P] and
+    d_final_state [B, H, P, N] or None.  Returns a dict of fp32 device tensors:
+    xbc [B, L, Cdim] (raw conv inputs when conv_w is given), dt [B, L, H], A,
+    and where applicable z, D, dt_bias, initial_state, conv_w, conv_b,
+    conv_state_in."""
+    lib = load()
+    B, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    dev = x.device
+    cdim = H * P + 2 * G * N
+    if Bm.dtype != x.dtype or Cm.dtype != x.dtype:
+        raise TypeError("x, Bm, Cm must share a dtype")
+    if z is not None and z.dtype != dt.dtype:
+        raise TypeError("z and dt must share a dtype")
+    xs, bs, cs = _tok(x, B, L, H * P, "x"), _tok(Bm, B, L, G * N, "Bm"), _tok(Cm, B, L, G * N, "Cm")
+    dts, zs = _tok(dt, B, L, H, "dt"), _tok(z, B, L, H * P, "z")
+    ds = _tok(dout, B, L, H * P, "dout")
+    for n, t in (("A", A), ("D", D), ("dt_bias", dt_bias)):
+        _dense(t, (H,), n, torch.float32)
+    _dense(initial_state, (B, H, P, N), "initial_state", torch.float32)
+    _dense(d_final_state, (B, H, P, N), "d_final_state", torch.float32)
+    K = 0
+    if conv_w is not None:
+        K = conv_w.shape[1]
+        _dense(conv_w, (cdim, K), "conv_w", torch.float32)
+        _dense(conv_b, (cdim,), "conv_b", torch.float32)
+        _dense(conv_state_in, (B, K - 1, cdim), "conv_state_in", x.dtype)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"xbc": torch.empty((B, L, cdim), **f32), "dt": torch.empty((B, L, H), **f32),
+         "A": torch.empty((H,), **f32), "D": torch.empty((H,), **f32),
+         "dt_bias": torch.empty((H,), **f32)}
+    if z is not None:
+        g["z"] = torch.empty((B, L, H, P), **f32)
+    if want_initial_state:
+        g["initial_state"] = torch.empty((B, H, P, N), **f32)
+    if conv_w is not None:
+        g["conv_w"] = torch.empty((cdim, K), **f32)
+        g["conv_b"] = torch.empty((cdim,), **f32)
+        g["conv_state_in"] = torch.empty((B, K - 1, cdim), **f32)
+    need = lib.ssd_chunk_scan_bwd_workspace_bytes(B, L, H, P, G, N, K)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.ssd_chunk_scan_bwd(
+        _p(x), xs, _p(Bm), bs, _p(Cm), cs, _dt(x), _p(conv_w), _p(conv_b), K, _p(conv_state_in),
+        _p(dt), dts, _p(z), zs, _dt(dt), _p(A), _p(D), _p(dt_bias), int(bool(dt_softplus)),
+        _p(initial_state), _p(dout), ds, _dt(dout), _p(d_final_state), _p(g["xbc"]), _p(g["dt"]),
+        _p(g.get("z")), _p(g["A"]), _p(g["D"]), _p(g["dt_bias"]), _p(g.get("initial_state")),
+        _p(g.get("conv_w")), _p(g.get("conv_b")), _p(g.get("conv_state_in")), B, L, H, P, G, N,
+        _p(workspace), wsz, _stream(x)))
+    return g
