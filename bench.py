@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (packed FMA), TFLOP/s
 
 
 def log(msg):
@@ -185,6 +186,42 @@ def time_decode(args, wl, torch, layer, synth, dev, dev32):
     return dict(chain_ms=total_ms, step_ms=total_ms / T, first10_ms=first, last10_ms=last)
 
 
+def bwd_flops_per_token(wl, Q: int = 32) -> float:
+    """Flops per token of the backward pass in its chunked form (chunks of Q
+    tokens), counting each contraction once (causal ones at half): per head,
+    the intra-chunk C B^T and its gradient products, the inter-chunk read-out
+    and its gradients, the state products, and the forward state pass."""
+    P, N = wl.headdim, wl.dstate
+    per_head = 2.0 * (Q / 2 * N + P * N + Q / 2 * P + Q / 2 * P + P * N + Q * N + Q * N
+                      + P * N + P * N + Q / 2 * P + P * N) + 2.0 * P * N
+    return per_head * wl.nheads
+
+
+def time_backward(args, wl, torch, ssd, synth, dev, dev32):
+    """ssd_chunk_scan_bwd at the prefill workload's shape (conv fused, gate,
+    skip, bias; bf16 inputs and output gradient)."""
+    log("backward %s: generating inputs" % wl.name)
+    inp = synth.make_prefill(wl)
+    B, L, H, G = wl.batch, wl.seqlen, wl.nheads, wl.ngroups
+    HP, GN = wl.d_inner, G * wl.dstate
+    xbc = dev(inp.xbc, "bf16")
+    x = xbc[:, :, :HP].unflatten(-1, (H, wl.headdim))
+    Bm = xbc[:, :, HP:HP + GN].unflatten(-1, (G, wl.dstate))
+    Cm = xbc[:, :, HP + GN:].unflatten(-1, (G, wl.dstate))
+    dt, z = dev(inp.dt, "bf16"), dev(inp.z, "bf16")
+    A, D, dtb, cw = dev32(inp.A), dev32(inp.D), dev32(inp.dt_bias), dev32(inp.conv_w)
+    del inp
+    dout = torch.randn(B, L, H, wl.headdim, device="cuda").to(torch.bfloat16)
+    ws = torch.empty(ssd.ssd_chunk_scan_bwd_workspace_bytes(B, L, H, wl.headdim, G, wl.dstate,
+                                                            wl.width), dtype=torch.uint8,
+                     device="cuda")
+    ms = events_ms(torch, lambda: ssd.ssd_chunk_scan_bwd(x, Bm, Cm, dt, A, dout, D=D, z=z,
+                                                         dt_bias=dtb, conv_w=cw, workspace=ws),
+                   max(2, args.steps // 10), 1)
+    log("backward: %.3f ms per call" % ms)
+    return ms
+
+
 def events_ms(torch, fn, steps: int, warmup: int):
     """Mean duration of fn() over `steps` calls, from HIP events on the stream
     the library launches on (torch's current stream)."""
@@ -308,6 +345,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the layer's backward pass")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the block around the layer (RMSNorm + projections)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -424,6 +463,18 @@ def main():
             "out_proj": {"ms": blk["out_ms"],
                          "tflops": f_out / (blk["out_ms"] / 1e3) / 1e12,
                          "frac": f_out / (blk["out_ms"] / 1e3) / 1e12 / BF16_PEAK_TFLOPS},
+        }
+    if not args.no_backward:
+        bms = time_backward(args, wl, torch, ssd, synth, dev, dev32)
+        fpt_b = bwd_flops_per_token(wl)
+        tf_b = fpt_b * wl.tokens / (bms / 1e3) / 1e12
+        out["backward"] = {
+            "workload": wl.name, "ms_per_call": bms, "tokens_per_s": wl.tokens / (bms / 1e3),
+            "dtype": "f32",
+            "roofline": {"bound": "alu", "achieved": tf_b, "peak": FP32_VALU_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tf_b / FP32_VALU_PEAK_TFLOPS,
+                         "traffic": None, "kernel": "ssd_chunk_scan_bwd call (6 kernels)",
+                         "alg_flops_per_token": fpt_b},
         }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")

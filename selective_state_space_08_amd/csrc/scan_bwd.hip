@@ -70,7 +70,10 @@ __device__ __forceinline__ float delta_of(const BwdArgs& a, int64_t row, int h, 
 // ---------------------------------------------------------------- states
 
 // The state entering each chunk, for every (b, h): states[b][h][c] = H before
-// chunk c.  Thread (lane, wave w) owns H[p = lane][n in 32 w .. 32 w + 31].
+// chunk c.  Thread tid owns the float4s tid + BT j (j < 8) of the [P][N]
+// state, so that its stores to HBM are coalesced: p = tid / 32 + 8 j,
+// n = 4 (tid % 32) .. + 3.  The next chunk's x, B and dt are loaded into
+// registers while this chunk is applied.
 template <typename Ta>
 __global__ __launch_bounds__(BT) void fwd_states_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float sX[BQ][PP];
@@ -80,29 +83,48 @@ __global__ __launch_bounds__(BT) void fwd_states_kernel(BwdArgs a) {
   const int H = a.nheads, G = a.ngroups, L = a.seqlen;
   const int b = blockIdx.x / H, h = blockIdx.x % H, g = h / (H / G);
   const int HP = H * BP;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  float hr[32];
-  const float* h0 = a.h0 ? a.h0 + ((int64_t)b * H + h) * BP * BN + lane * BN + 32 * w : nullptr;
+  const int tid = threadIdx.x;
+  const int pr = tid >> 5, n0 = 4 * (tid & 31);
+  float4 hr[8];
+  {
+    const float* h0 = a.h0 ? a.h0 + ((int64_t)b * H + h) * BP * BN : nullptr;
 #pragma unroll
-  for (int e = 0; e < 32; ++e) hr[e] = h0 ? h0[e] : 0.f;
+    for (int j = 0; j < 8; ++j)
+      hr[j] = h0 ? *reinterpret_cast<const float4*>(h0 + (pr + 8 * j) * BN + n0)
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   const float Ah = a.A[h];
-  for (int c = 0; c < a.nc; ++c) {
-    float* st = a.states + (((int64_t)b * H + h) * a.nc + c) * BP * BN + lane * BN + 32 * w;
-#pragma unroll
-    for (int e = 0; e < 32; e += 4)
-      *reinterpret_cast<float4*>(st + e) = make_float4(hr[e], hr[e + 1], hr[e + 2], hr[e + 3]);
+  // staging: x as 2 float4s per thread (t = tid / 16 + 16 k, p4 = 4 (tid % 16)),
+  // B as 4 float4s (t = tid / 32 + 8 k, n4 = 4 (tid % 32)), and dt (tid < 32)
+  float4 px[2], pb[4];
+  float pdv = 0.f, pd = 0.f;
+  auto fetch = [&](int c) {
     const int t0 = c * BQ, Lc = min(BQ, L - t0);
-    for (int i = tid; i < BQ * BP; i += BT) {
-      const int t = i / BP, p = i % BP;
-      sX[t][p] = t < Lc ? a.post[((int64_t)b * L + t0 + t) * a.cdim + h * BP + p] : 0.f;
+    const int64_t row0 = (int64_t)b * L + t0;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int t = (tid >> 4) + 16 * k;
+      px[k] = t < Lc ? *reinterpret_cast<const float4*>(a.post + (row0 + t) * a.cdim + h * BP + 4 * (tid & 15))
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    for (int i = tid; i < BQ * BN; i += BT) {
-      const int t = i / BN, n = i % BN;
-      sB[t][n] = t < Lc ? a.post[((int64_t)b * L + t0 + t) * a.cdim + HP + g * BN + n] : 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int t = (tid >> 5) + 8 * k;
+      pb[k] = t < Lc ? *reinterpret_cast<const float4*>(a.post + (row0 + t) * a.cdim + HP + g * BN + n0)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    if (tid < BQ) pd = delta_of<Ta>(a, row0 + tid, h, tid < Lc, pdv);
+  };
+  if (a.nc > 0) fetch(0);
+  for (int c = 0; c < a.nc; ++c) {
+    const int t0 = c * BQ, Lc = min(BQ, L - t0);
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      *reinterpret_cast<float4*>(&sX[(tid >> 4) + 16 * k][4 * (tid & 15)]) = px[k];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) *reinterpret_cast<float4*>(&sB[(tid >> 5) + 8 * k][n0]) = pb[k];
     if (tid < 64) {
-      float v;
-      const float d = tid < BQ ? delta_of<Ta>(a, (int64_t)b * L + t0 + tid, h, tid < Lc, v) : 0.f;
+      const float d = tid < BQ ? pd : 0.f;
       float lam = d * Ah;
       for (int o = 1; o < 32; o <<= 1) {
         const float u = __shfl_up(lam, o, 64);
@@ -113,18 +135,26 @@ __global__ __launch_bounds__(BT) void fwd_states_kernel(BwdArgs a) {
       if (tid == 0) sGam = __expf(last);
     }
     __syncthreads();
+    if (c + 1 < a.nc) fetch(c + 1);
+    float* st = a.states + (((int64_t)b * H + h) * a.nc + c) * BP * BN;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) *reinterpret_cast<float4*>(st + (pr + 8 * j) * BN + n0) = hr[j];
     const float gam = sGam;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) hr[e] *= gam;
+    for (int j = 0; j < 8; ++j) {
+      hr[j].x *= gam; hr[j].y *= gam; hr[j].z *= gam; hr[j].w *= gam;
+    }
+#pragma unroll 4
     for (int s = 0; s < BQ; ++s) {
-      const float xs = sX[s][lane] * sW[s];
+      const float ws = sW[s];
+      const float4 bv = *reinterpret_cast<const float4*>(&sB[s][n0]);
 #pragma unroll
-      for (int e = 0; e < 32; e += 4) {
-        const float4 bv = *reinterpret_cast<const float4*>(&sB[s][32 * w + e]);
-        hr[e] = fmaf(xs, bv.x, hr[e]);
-        hr[e + 1] = fmaf(xs, bv.y, hr[e + 1]);
-        hr[e + 2] = fmaf(xs, bv.z, hr[e + 2]);
-        hr[e + 3] = fmaf(xs, bv.w, hr[e + 3]);
+      for (int j = 0; j < 8; ++j) {
+        const float xs = sX[s][pr + 8 * j] * ws;
+        hr[j].x = fmaf(xs, bv.x, hr[j].x);
+        hr[j].y = fmaf(xs, bv.y, hr[j].y);
+        hr[j].z = fmaf(xs, bv.z, hr[j].z);
+        hr[j].w = fmaf(xs, bv.w, hr[j].w);
       }
     }
     __syncthreads();
@@ -134,16 +164,37 @@ __global__ __launch_bounds__(BT) void fwd_states_kernel(BwdArgs a) {
 // ---------------------------------------------------------------- backward
 
 // Block sum of one value per thread (fixed order), returned to every thread.
+template <int NW>
 __device__ __forceinline__ float block_sum(float v, float* sred) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) sred[threadIdx.x >> 6] = v;
   __syncthreads();
-  return sred[0] + sred[1] + sred[2] + sred[3];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) s += sred[i];
+  return s;
 }
 
+constexpr int WT = 512;  // threads of the reverse walker: 8 waves, two per SIMD
+
+// Sum over the 16 lanes of a token group (lanes 16 k .. 16 k + 15).
+__device__ __forceinline__ float sum16(float v) {
+  v += __shfl_xor(v, 1, 64);
+  v += __shfl_xor(v, 2, 64);
+  v += __shfl_xor(v, 4, 64);
+  v += __shfl_xor(v, 8, 64);
+  return v;
+}
+
+// The reverse walk over one (b, h).  Mappings: the state's gradient dH[p][n]
+// lives in registers, thread (lane, wave w) owning p = lane and
+// n in 16 w .. 16 w + 15; token-shaped work uses 16 lanes per token
+// (t = tid / 16, r = tid % 16), with head channels p = r + 16 i and state
+// channels n = 4 r + 64 j .. + 3, so that the 16 lanes read 16 consecutive
+// LDS rows or 16 consecutive float4s.
 template <typename Ta, typename Td>
-__global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdArgs a) {
+__global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float sX[BQ][PP];
   __shared__ __attribute__((aligned(16))) float sDY[BQ][PP];
   __shared__ __attribute__((aligned(16))) float sHB[BQ][PP];
@@ -155,22 +206,21 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdArgs a) {
   __shared__ float sS[BQ][PQ];    // C_t . B_s
   __shared__ float sDS[BQ][PQ];   // dM_ts exp(lam_t - lam_s) delta_s
   __shared__ float sE[BQ][PQ];    // dM_ts S_ts exp(lam_t - lam_s)
-  __shared__ float sDel[BQ], sLam[BQ], sV[BQ], sDLoff[BQ], sDW[BQ];
-  __shared__ float sRed[4];
+  __shared__ float sDel[BQ], sLam[BQ], sEl[BQ], sV[BQ], sDLoff[BQ], sDW[BQ];
+  __shared__ float sRed[WT / 64];
 
   const int H = a.nheads, G = a.ngroups, L = a.seqlen;
   const int b = blockIdx.x / H, h = blockIdx.x % H, g = h / (H / G);
   const int HP = H * BP, GN = G * BN;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int tq = tid >> 3, r8 = tid & 7;   // token-and-8-lane mapping
+  const int tq = tid >> 4, r = tid & 15;
   const float Ah = a.A[h], Dh = a.D ? a.D[h] : 0.f;
 
-  // the state's gradient: thread owns dH[p = lane][n in 32 w .. 32 w + 31]
-  float dh[32];
+  float dh[16];
   {
-    const float* src = a.dhT ? a.dhT + ((int64_t)b * H + h) * BP * BN + lane * BN + 32 * w : nullptr;
+    const float* src = a.dhT ? a.dhT + ((int64_t)b * H + h) * BP * BN + lane * BN + 16 * w : nullptr;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) dh[e] = src ? src[e] : 0.f;
+    for (int e = 0; e < 16; ++e) dh[e] = src ? src[e] : 0.f;
   }
   float dD_part = 0.f, dA_part = 0.f, dbias_part = 0.f;
 
@@ -178,27 +228,33 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdArgs a) {
     const int t0 = c * BQ, Lc = min(BQ, L - t0);
     const int64_t row0 = (int64_t)b * L + t0;
     // ---- load the chunk
-    for (int i = tid; i < BQ * BP; i += BT) {
-      const int t = i / BP, p = i % BP;
-      sX[t][p] = t < Lc ? a.post[(row0 + t) * a.cdim + h * BP + p] : 0.f;
+    for (int i = tid; i < BQ * BP / 4; i += WT) {
+      const int t = i / (BP / 4), p4 = 4 * (i % (BP / 4));
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (t < Lc) v = *reinterpret_cast<const float4*>(a.post + (row0 + t) * a.cdim + h * BP + p4);
+      *reinterpret_cast<float4*>(&sX[t][p4]) = v;
     }
-    for (int i = tid; i < BQ * BN; i += BT) {
-      const int t = i / BN, n = i % BN;
-      const bool ok = t < Lc;
-      sB[t][n] = ok ? a.post[(row0 + t) * a.cdim + HP + g * BN + n] : 0.f;
-      sC[t][n] = ok ? a.post[(row0 + t) * a.cdim + HP + GN + g * BN + n] : 0.f;
+    for (int i = tid; i < BQ * BN / 4; i += WT) {
+      const int t = i / (BN / 4), n4 = 4 * (i % (BN / 4));
+      float4 vb = make_float4(0.f, 0.f, 0.f, 0.f), vc = vb;
+      if (t < Lc) {
+        const float* rowp = a.post + (row0 + t) * a.cdim;
+        vb = *reinterpret_cast<const float4*>(rowp + HP + g * BN + n4);
+        vc = *reinterpret_cast<const float4*>(rowp + HP + GN + g * BN + n4);
+      }
+      *reinterpret_cast<float4*>(&sB[t][n4]) = vb;
+      *reinterpret_cast<float4*>(&sC[t][n4]) = vc;
     }
     {
       const float* st = a.states + (((int64_t)b * H + h) * a.nc + c) * BP * BN;
-      for (int i = tid; i < BP * BN / 4; i += BT) {
-        const int p = i / (BN / 4), n4 = i % (BN / 4);
-        *reinterpret_cast<float4*>(&sH[p][4 * n4]) =
-            *reinterpret_cast<const float4*>(st + p * BN + 4 * n4);
+      for (int i = tid; i < BP * BN / 4; i += WT) {
+        const int p = i / (BN / 4), n4 = 4 * (i % (BN / 4));
+        *reinterpret_cast<float4*>(&sH[p][n4]) = *reinterpret_cast<const float4*>(st + p * BN + n4);
       }
     }
 #pragma unroll
-    for (int e = 0; e < 32; e += 4)
-      *reinterpret_cast<float4*>(&sDH[lane][32 * w + e]) =
+    for (int e = 0; e < 16; e += 4)
+      *reinterpret_cast<float4*>(&sDH[lane][16 * w + e]) =
           make_float4(dh[e], dh[e + 1], dh[e + 2], dh[e + 3]);
     if (tid < 64) {
       float v;
@@ -211,6 +267,7 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdArgs a) {
       if (tid < BQ) {
         sDel[tid] = d;
         sLam[tid] = lam;
+        sEl[tid] = __expf(lam);
         sV[tid] = v;
       }
     }
@@ -218,11 +275,12 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdArgs a) {
     const float lam_last = sLam[Lc - 1];
     const float gam = __expf(lam_last);
 
-    // ---- S, M (4 entries per thread) and the inter-chunk read-out Yoff
-    for (int j = 0; j < 4; ++j) {
-      const int e = tid + BT * j, t = e >> 5, s = e & 31;
+    // ---- S and M (2 entries per thread)
+    for (int j = 0; j < 2; ++j) {
+      const int e = tid + WT * j, t = e >> 5, s = e & 31;
       float S = 0.f, M = 0.f;
       if (s <= t) {
+#pragma unroll 2
         for (int n = 0; n < BN; n += 4) {
           const float4 cv = *reinterpret_cast<const float4*>(&sC[t][n]);
           const float4 bv = *reinterpret_cast<const float4*>(&sB[s][n]);
@@ -234,42 +292,50 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdArgs a) {
       sS[t][s] = S;
       sM[t][s] = M;
     }
-    float yoff[8];  // (t = tq, p = r8 + 8 i)
+    // ---- the inter-chunk read-out Yoff[t][p] = e^lam_t C_t . H_in[p]
+    float yoff[4];
     {
-      const float el = __expf(sLam[tq]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) yoff[i] = 0.f;
+      for (int i = 0; i < 4; ++i) yoff[i] = 0.f;
+#pragma unroll 2
       for (int n = 0; n < BN; n += 4) {
         const float4 cv = *reinterpret_cast<const float4*>(&sC[tq][n]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float4 hv = *reinterpret_cast<const float4*>(&sH[r8 + 8 * i][n]);
+        for (int i = 0; i < 4; ++i) {
+          const float4 hv = *reinterpret_cast<const float4*>(&sH[r + 16 * i][n]);
           yoff[i] = fmaf(cv.x, hv.x, fmaf(cv.y, hv.y, fmaf(cv.z, hv.z, fmaf(cv.w, hv.w, yoff[i]))));
         }
       }
+      const float el = sEl[tq];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) yoff[i] *= el;
+      for (int i = 0; i < 4; ++i) yoff[i] *= el;
     }
     __syncthreads();
 
-    // ---- forward output, the gate and its gradient: (t = tq, p = r8 + 8 i)
+    // ---- forward output, the gate and its gradient (t = tq, p = r + 16 i)
     {
       const int t = tq;
       const bool ok = t < Lc;
+      float yv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) yv[i] = yoff[i] + Dh * sX[t][r + 16 * i];
+#pragma unroll 2
+      for (int s = 0; s <= t; ++s) {
+        const float m = sM[t][s];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) yv[i] = fmaf(m, sX[s][r + 16 * i], yv[i]);
+      }
       float dl = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int p = r8 + 8 * i;
-        float yv = yoff[i] + Dh * sX[t][p];
-        for (int s = 0; s <= t; ++s) yv = fmaf(sM[t][s], sX[s][p], yv);
+      for (int i = 0; i < 4; ++i) {
+        const int p = r + 16 * i;
         float dyv = 0.f;
         if (ok) {
-          const int64_t o = (row0 + t) * a.dout_stride + h * BP + p;
-          const float dout = ld(static_cast<const Td*>(a.dout) + o);
+          const float dout = ld(static_cast<const Td*>(a.dout) + (row0 + t) * a.dout_stride + h * BP + p);
           if (a.z) {
             const float zz = ld(static_cast<const Ta*>(a.z) + (row0 + t) * a.z_stride + h * BP + p);
             dyv = dout * silu_f32(zz);
-            if (a.dz) a.dz[((row0 + t) * H + h) * BP + p] = dout * yv * silu_grad_f32(zz);
+            if (a.dz) a.dz[((row0 + t) * H + h) * BP + p] = dout * yv[i] * silu_grad_f32(zz);
           } else {
             dyv = dout;
           }
@@ -278,19 +344,18 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdArgs a) {
         dD_part = fmaf(dyv, sX[t][p], dD_part);
         dl = fmaf(dyv, yoff[i], dl);
       }
-      dl += __shfl_xor(dl, 1, 64);
-      dl += __shfl_xor(dl, 2, 64);
-      dl += __shfl_xor(dl, 4, 64);
-      if (r8 == 0) sDLoff[t] = dl;
+      dl = sum16(dl);
+      if (r == 0) sDLoff[t] = dl;
     }
     __syncthreads();
 
-    // ---- dM, dS, E (4 entries per thread) and HB_s = dH_out B_s (s = tq)
-    for (int j = 0; j < 4; ++j) {
-      const int e = tid + BT * j, t = e >> 5, s = e & 31;
+    // ---- dM, dS, E (2 entries per thread) and HB_s = dH_out B_s (s = tq)
+    for (int j = 0; j < 2; ++j) {
+      const int e = tid + WT * j, t = e >> 5, s = e & 31;
       float ds = 0.f, ee = 0.f;
       if (s <= t) {
         float dm = 0.f;
+#pragma unroll 2
         for (int p = 0; p < BP; p += 4) {
           const float4 yv = *reinterpret_cast<const float4*>(&sDY[t][p]);
           const float4 xv = *reinterpret_cast<const float4*>(&sX[s][p]);
@@ -305,100 +370,99 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdArgs a) {
       sE[t][s] = ee;
     }
     {
-      float hb[8];
+      float hb[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) hb[i] = 0.f;
+      for (int i = 0; i < 4; ++i) hb[i] = 0.f;
+#pragma unroll 2
       for (int n = 0; n < BN; n += 4) {
         const float4 bv = *reinterpret_cast<const float4*>(&sB[tq][n]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float4 dv = *reinterpret_cast<const float4*>(&sDH[r8 + 8 * i][n]);
+        for (int i = 0; i < 4; ++i) {
+          const float4 dv = *reinterpret_cast<const float4*>(&sDH[r + 16 * i][n]);
           hb[i] = fmaf(bv.x, dv.x, fmaf(bv.y, dv.y, fmaf(bv.z, dv.z, fmaf(bv.w, dv.w, hb[i]))));
         }
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sHB[tq][r8 + 8 * i] = hb[i];
+      for (int i = 0; i < 4; ++i) sHB[tq][r + 16 * i] = hb[i];
     }
     // <dH_out, H_in> for the gradient of the chunk's total decay
     float hh = 0.f;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) hh = fmaf(dh[e], sH[lane][32 * w + e], hh);
-    const float dot_hh = block_sum(hh, sRed);  // (includes the barrier)
+    for (int e = 0; e < 16; e += 4) {
+      const float4 hv = *reinterpret_cast<const float4*>(&sH[lane][16 * w + e]);
+      hh = fmaf(dh[e], hv.x, fmaf(dh[e + 1], hv.y, fmaf(dh[e + 2], hv.z, fmaf(dh[e + 3], hv.w, hh))));
+    }
+    const float dot_hh = block_sum<WT / 64>(hh, sRed);  // (includes the barrier)
 
-    // ---- dC_t, dB_s (n = 4 r8 + 32 j), dx_s (p = r8 + 8 i); token = tq
+    // ---- dC_t, dB_t (n = 4 r + 64 j), dx_t (p = r + 16 i); token t = tq
     {
       const int t = tq;
       const bool ok = t < Lc;
-      const float el = __expf(sLam[t]);
+      const float el = sEl[t];
       const float ws = __expf(lam_last - sLam[t]) * sDel[t];
-      float dcv[16], dbv[16];
+      float4 dc[2], db[2], oc[2], ob[2];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) dcv[k] = dbv[k] = 0.f;
+      for (int j = 0; j < 2; ++j) dc[j] = db[j] = oc[j] = ob[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 2
       for (int s = 0; s < BQ; ++s) {
         const float a1 = sDS[t][s];   // dC_t += dS_ts B_s
         const float a2 = sDS[s][t];   // dB_t += dS_st C_s
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float4 bv = *reinterpret_cast<const float4*>(&sB[s][4 * r8 + 32 * j]);
-          const float4 cv = *reinterpret_cast<const float4*>(&sC[s][4 * r8 + 32 * j]);
-          dcv[4 * j] = fmaf(a1, bv.x, dcv[4 * j]);
-          dcv[4 * j + 1] = fmaf(a1, bv.y, dcv[4 * j + 1]);
-          dcv[4 * j + 2] = fmaf(a1, bv.z, dcv[4 * j + 2]);
-          dcv[4 * j + 3] = fmaf(a1, bv.w, dcv[4 * j + 3]);
-          dbv[4 * j] = fmaf(a2, cv.x, dbv[4 * j]);
-          dbv[4 * j + 1] = fmaf(a2, cv.y, dbv[4 * j + 1]);
-          dbv[4 * j + 2] = fmaf(a2, cv.z, dbv[4 * j + 2]);
-          dbv[4 * j + 3] = fmaf(a2, cv.w, dbv[4 * j + 3]);
+        for (int j = 0; j < 2; ++j) {
+          const float4 bv = *reinterpret_cast<const float4*>(&sB[s][4 * r + 64 * j]);
+          const float4 cv = *reinterpret_cast<const float4*>(&sC[s][4 * r + 64 * j]);
+          dc[j].x = fmaf(a1, bv.x, dc[j].x); dc[j].y = fmaf(a1, bv.y, dc[j].y);
+          dc[j].z = fmaf(a1, bv.z, dc[j].z); dc[j].w = fmaf(a1, bv.w, dc[j].w);
+          db[j].x = fmaf(a2, cv.x, db[j].x); db[j].y = fmaf(a2, cv.y, db[j].y);
+          db[j].z = fmaf(a2, cv.z, db[j].z); db[j].w = fmaf(a2, cv.w, db[j].w);
         }
       }
-      float oc[16], ob[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) oc[k] = ob[k] = 0.f;
+#pragma unroll 2
       for (int p = 0; p < BP; ++p) {
         const float yv = sDY[t][p];   // dC_t += e^lam_t dy_t H_in
         const float xv = sX[t][p];    // dB_t += w_t x_t dH_out
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float4 hv = *reinterpret_cast<const float4*>(&sH[p][4 * r8 + 32 * j]);
-          const float4 dv = *reinterpret_cast<const float4*>(&sDH[p][4 * r8 + 32 * j]);
-          oc[4 * j] = fmaf(yv, hv.x, oc[4 * j]);
-          oc[4 * j + 1] = fmaf(yv, hv.y, oc[4 * j + 1]);
-          oc[4 * j + 2] = fmaf(yv, hv.z, oc[4 * j + 2]);
-          oc[4 * j + 3] = fmaf(yv, hv.w, oc[4 * j + 3]);
-          ob[4 * j] = fmaf(xv, dv.x, ob[4 * j]);
-          ob[4 * j + 1] = fmaf(xv, dv.y, ob[4 * j + 1]);
-          ob[4 * j + 2] = fmaf(xv, dv.z, ob[4 * j + 2]);
-          ob[4 * j + 3] = fmaf(xv, dv.w, ob[4 * j + 3]);
+        for (int j = 0; j < 2; ++j) {
+          const float4 hv = *reinterpret_cast<const float4*>(&sH[p][4 * r + 64 * j]);
+          const float4 dv = *reinterpret_cast<const float4*>(&sDH[p][4 * r + 64 * j]);
+          oc[j].x = fmaf(yv, hv.x, oc[j].x); oc[j].y = fmaf(yv, hv.y, oc[j].y);
+          oc[j].z = fmaf(yv, hv.z, oc[j].z); oc[j].w = fmaf(yv, hv.w, oc[j].w);
+          ob[j].x = fmaf(xv, dv.x, ob[j].x); ob[j].y = fmaf(xv, dv.y, ob[j].y);
+          ob[j].z = fmaf(xv, dv.z, ob[j].z); ob[j].w = fmaf(xv, dv.w, ob[j].w);
         }
       }
       if (ok) {
-        float* dc = a.dCh + (((int64_t)b * H + h) * L + t0 + t) * BN;
-        float* db = a.dBh + (((int64_t)b * H + h) * L + t0 + t) * BN;
+        float* dcp = a.dCh + (((int64_t)b * H + h) * L + t0 + t) * BN;
+        float* dbp = a.dBh + (((int64_t)b * H + h) * L + t0 + t) * BN;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = 4 * r8 + 32 * j;
-          *reinterpret_cast<float4*>(dc + n) =
-              make_float4(fmaf(el, oc[4 * j], dcv[4 * j]), fmaf(el, oc[4 * j + 1], dcv[4 * j + 1]),
-                          fmaf(el, oc[4 * j + 2], dcv[4 * j + 2]), fmaf(el, oc[4 * j + 3], dcv[4 * j + 3]));
-          *reinterpret_cast<float4*>(db + n) =
-              make_float4(fmaf(ws, ob[4 * j], dbv[4 * j]), fmaf(ws, ob[4 * j + 1], dbv[4 * j + 1]),
-                          fmaf(ws, ob[4 * j + 2], dbv[4 * j + 2]), fmaf(ws, ob[4 * j + 3], dbv[4 * j + 3]));
+        for (int j = 0; j < 2; ++j) {
+          const int n = 4 * r + 64 * j;
+          *reinterpret_cast<float4*>(dcp + n) =
+              make_float4(fmaf(el, oc[j].x, dc[j].x), fmaf(el, oc[j].y, dc[j].y),
+                          fmaf(el, oc[j].z, dc[j].z), fmaf(el, oc[j].w, dc[j].w));
+          *reinterpret_cast<float4*>(dbp + n) =
+              make_float4(fmaf(ws, ob[j].x, db[j].x), fmaf(ws, ob[j].y, db[j].y),
+                          fmaf(ws, ob[j].z, db[j].z), fmaf(ws, ob[j].w, db[j].w));
         }
       }
-      // dx_t = D dy_t + sum_t' M_t't dy_t' + w_t HB_t;  dw_t = x_t . HB_t
-      float dwp = 0.f;
+      // dx_t = D dy_t + sum_u M_ut dy_u + w_t HB_t;  dw_t = x_t . HB_t
+      float dx[4], dwp = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int p = r8 + 8 * i;
-        float dx = Dh * sDY[t][p] + ws * sHB[t][p];
-        for (int u = t; u < BQ; ++u) dx = fmaf(sM[u][t], sDY[u][p], dx);
-        if (ok) a.dpost[(row0 + t) * a.cdim + h * BP + p] = dx;
+      for (int i = 0; i < 4; ++i) dx[i] = Dh * sDY[t][r + 16 * i] + ws * sHB[t][r + 16 * i];
+#pragma unroll 2
+      for (int u = t; u < BQ; ++u) {
+        const float m = sM[u][t];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dx[i] = fmaf(m, sDY[u][r + 16 * i], dx[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int p = r + 16 * i;
+        if (ok) a.dpost[(row0 + t) * a.cdim + h * BP + p] = dx[i];
         dwp = fmaf(sX[t][p], sHB[t][p], dwp);
       }
-      dwp += __shfl_xor(dwp, 1, 64);
-      dwp += __shfl_xor(dwp, 2, 64);
-      dwp += __shfl_xor(dwp, 4, 64);
-      if (r8 == 0) sDW[t] = dwp;
+      dwp = sum16(dwp);
+      if (r == 0) sDW[t] = dwp;
     }
     __syncthreads();
 
@@ -409,6 +473,7 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdArgs a) {
       const float del = real ? sDel[t] : 0.f, lam = sLam[t];
       const float wt = __expf(lam_last - lam) * del;
       float rowg = 0.f, colg = 0.f, cole = 0.f;
+#pragma unroll 2
       for (int s = 0; s < BQ; ++s) {
         rowg = fmaf(sE[t][s], sDel[s], rowg);
         colg = fmaf(sE[s][t], del, colg);
@@ -441,12 +506,13 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdArgs a) {
     // ---- the state's gradient entering the chunk:
     //      dH_in = e^lam_last dH_out + sum_t e^lam_t dy_t C_t^T
 #pragma unroll
-    for (int e = 0; e < 32; ++e) dh[e] *= gam;
+    for (int e = 0; e < 16; ++e) dh[e] *= gam;
+#pragma unroll 2
     for (int t = 0; t < BQ; ++t) {
-      const float yv = sDY[t][lane] * __expf(sLam[t]);
+      const float yv = sDY[t][lane] * sEl[t];
 #pragma unroll
-      for (int e = 0; e < 32; e += 4) {
-        const float4 cv = *reinterpret_cast<const float4*>(&sC[t][32 * w + e]);
+      for (int e = 0; e < 16; e += 4) {
+        const float4 cv = *reinterpret_cast<const float4*>(&sC[t][16 * w + e]);
         dh[e] = fmaf(yv, cv.x, dh[e]);
         dh[e + 1] = fmaf(yv, cv.y, dh[e + 1]);
         dh[e + 2] = fmaf(yv, cv.z, dh[e + 2]);
@@ -457,14 +523,14 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdArgs a) {
   }
 
   if (a.dh0) {
-    float* dst = a.dh0 + ((int64_t)b * H + h) * BP * BN + lane * BN + 32 * w;
+    float* dst = a.dh0 + ((int64_t)b * H + h) * BP * BN + lane * BN + 16 * w;
 #pragma unroll
-    for (int e = 0; e < 32; e += 4)
+    for (int e = 0; e < 16; e += 4)
       *reinterpret_cast<float4*>(dst + e) = make_float4(dh[e], dh[e + 1], dh[e + 2], dh[e + 3]);
   }
-  const float sA = block_sum(dA_part, sRed);
-  const float sD = block_sum(dD_part, sRed);
-  const float sb = block_sum(dbias_part, sRed);
+  const float sA = block_sum<WT / 64>(dA_part, sRed);
+  const float sD = block_sum<WT / 64>(dD_part, sRed);
+  const float sb = block_sum<WT / 64>(dbias_part, sRed);
   if (tid == 0) {
     float* pp = a.part + ((int64_t)b * H + h) * 3;
     pp[0] = sA;
@@ -504,10 +570,13 @@ __global__ void reduce_bc_kernel(const float* __restrict__ dBh, const float* __r
 
 constexpr int CT = 64;   // tokens per conv block
 
-// One thread per (b, channel, block of CT tokens): du = dpost silu'(u) over
-// the block and the K-1 tokens after it, the raw inputs' gradients of the
-// block (and of the history, in the first block), and the block's sums for
-// the conv weights and bias.
+// One thread per (b, channel, block of CT tokens).  The block owns the raw
+// positions [t0, t1); they receive w[k] du[t] from the tokens t in
+// [t0, t1 + K - 1).  Walking t upwards with the last four raw inputs and the
+// four open positions' sums in registers (weights zero-padded to four taps),
+// each position is written once all its taps are in.  The first block also
+// writes the conv history's gradient; every block writes its sums for the
+// conv weights and bias over its own tokens.
 template <typename Tx>
 __global__ void conv_bwd_kernel(const void* x, int64_t xs, const void* Bm, int64_t bs,
                                 const void* Cm, int64_t cs, const float* __restrict__ w,
@@ -527,56 +596,55 @@ __global__ void conv_bwd_kernel(const void* x, int64_t xs, const void* Bm, int64
   const Tx* hs = static_cast<const Tx*>(hist);
   auto raw = [&](int tau) -> float {  // raw input at position tau (history below 0)
     if (tau >= 0) return to_f32(src[((int64_t)b * seqlen + tau) * st + cc]);
-    if (hs == nullptr) return 0.f;
+    if (hs == nullptr || tau < -(K - 1)) return 0.f;
     return to_f32(hs[((int64_t)b * (K - 1) + (K - 1) + tau) * cdim + c]);
   };
-  float wk[4];
-  for (int k = 0; k < 4; ++k) wk[k] = k < K ? w[c * K + k] : 0.f;
+  // taps right-aligned in four slots: slot j meets raw position t - 3 + j
+  float wp[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) wp[j] = j >= 4 - K ? w[c * K + (j - (4 - K))] : 0.f;
   const float bc = bias ? bias[c] : 0.f;
   const int t0 = blk * CT, t1 = min(seqlen, t0 + CT);
-  // du over [t0, t1 + K - 1) (the taps that reach back into this block)
-  float du[CT + 3];
-  float win[4] = {0.f, 0.f, 0.f, 0.f};  // raw inputs t - K + 1 .. t
-  // after the first shift, win[4 - K + k] must hold raw(t0 - (K - 1) + k)
-  for (int k = 0; k < K - 1; ++k) win[5 - K + k] = raw(t0 - (K - 1) + k);
-  float gw[4] = {0.f, 0.f, 0.f, 0.f}, gb = 0.f;
   const int tend = min(seqlen, t1 + K - 1);
+  float win[4];   // raw inputs at t - 3 .. t (after the shift at the top of step t)
+  float acc[4];   // open sums of raw positions t - 3 .. t
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    win[j] = j > 0 ? raw(t0 - 4 + j) : 0.f;
+    acc[j] = 0.f;
+  }
+  float gw[4] = {0.f, 0.f, 0.f, 0.f}, gb = 0.f;
+  auto emit = [&](int pos, float v) {
+    if (pos >= t0 && pos < t1) dxbc[((int64_t)b * seqlen + pos) * cdim + c] = v;
+    else if (pos < 0 && blk == 0 && dhist != nullptr && pos >= -(K - 1))
+      dhist[((int64_t)b * (K - 1) + (K - 1) + pos) * cdim + c] = v;
+  };
   for (int t = t0; t < tend; ++t) {
-    for (int k = 0; k < 3; ++k) win[k] = win[k + 1];
+    win[0] = win[1]; win[1] = win[2]; win[2] = win[3];
     win[3] = raw(t);
     float u = bc;
-    for (int k = 0; k < K; ++k) u = fmaf(wk[k], win[4 - K + k], u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) u = fmaf(wp[j], win[j], u);
     const float d = dpost[((int64_t)b * seqlen + t) * cdim + c] * silu_grad_f32(u);
-    du[t - t0] = d;
     if (t < t1) {
       gb += d;
-      for (int k = 0; k < K; ++k) gw[k] = fmaf(d, win[4 - K + k], gw[k]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) gw[j] = fmaf(d, win[j], gw[j]);
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = fmaf(wp[j], d, acc[j]);
+    emit(t - 3, acc[0]);  // position t - 3 has all its taps
+    acc[0] = acc[1]; acc[1] = acc[2]; acc[2] = acc[3]; acc[3] = 0.f;
   }
-  // d raw[tau] = sum_k w[k] du[tau + K - 1 - k]
-  for (int tau = t0; tau < t1; ++tau) {
-    float s = 0.f;
-    for (int k = 0; k < K; ++k) {
-      const int t = tau + K - 1 - k;
-      if (t < tend) s = fmaf(wk[k], du[t - t0], s);
-    }
-    dxbc[((int64_t)b * seqlen + tau) * cdim + c] = s;
-  }
-  if (blk == 0 && dhist != nullptr) {
-    for (int j = 0; j < K - 1; ++j) {  // history row j is position tau = j - (K - 1)
-      const int tau = j - (K - 1);
-      float s = 0.f;
-      for (int k = 0; k < K; ++k) {
-        const int t = tau + K - 1 - k;
-        if (t >= 0 && t < tend) s = fmaf(wk[k], du[t - t0], s);
-      }
-      dhist[((int64_t)b * (K - 1) + j) * cdim + c] = s;
-    }
-  }
+  // the positions still open (their later taps lie past the sequence)
+  emit(tend - 3, acc[0]);
+  emit(tend - 2, acc[1]);
+  emit(tend - 1, acc[2]);
   const int nblk = gridDim.y;
-  float* wp = wpart + (((int64_t)b * nblk + blk) * cdim + c) * 5;
-  for (int k = 0; k < 4; ++k) wp[k] = gw[k];
-  wp[4] = gb;
+  float* wq = wpart + (((int64_t)b * nblk + blk) * cdim + c) * 5;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) wq[k] = k < K ? gw[k + (4 - K)] : 0.f;
+  wq[4] = gb;
 }
 
 // Fixed-order sums: dA, dD, dt_bias over the batch; the conv weights and bias
@@ -707,10 +775,10 @@ hipError_t launch_scan_bwd(const ScanBwdLaunch& l, hipStream_t stream) {
   else fwd_states_kernel<float><<<grid_bh, BT, 0, stream>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // 3. the chunks in reverse
-  if (abf && dbf) bwd_chunk_kernel<bf16, bf16><<<grid_bh, BT, 0, stream>>>(a);
-  else if (abf) bwd_chunk_kernel<bf16, float><<<grid_bh, BT, 0, stream>>>(a);
-  else if (dbf) bwd_chunk_kernel<float, bf16><<<grid_bh, BT, 0, stream>>>(a);
-  else bwd_chunk_kernel<float, float><<<grid_bh, BT, 0, stream>>>(a);
+  if (abf && dbf) bwd_chunk_kernel<bf16, bf16><<<grid_bh, WT, 0, stream>>>(a);
+  else if (abf) bwd_chunk_kernel<bf16, float><<<grid_bh, WT, 0, stream>>>(a);
+  else if (dbf) bwd_chunk_kernel<float, bf16><<<grid_bh, WT, 0, stream>>>(a);
+  else bwd_chunk_kernel<float, float><<<grid_bh, WT, 0, stream>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // 4. B and C of each group
   {
