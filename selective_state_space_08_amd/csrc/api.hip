@@ -603,6 +603,8 @@ int ssd_linear_fwd(const void* a, int64_t lda, const void* w, int64_t ldw, const
   return e == hipSuccess ? SSD_OK : hip_fail(e, "linear launch");
 }
 
+}  // extern "C"
+
 namespace {
 // Workspace of the block: normed input | in_proj output (z | x B C | dt, rows
 // padded to 8 elements) | layer output y, all bf16, then the layer's own.
@@ -627,6 +629,8 @@ BlockWs block_ws(int batch, int seqlen, int d_model, int nheads, int ngroups) {
   return w;
 }
 }  // namespace
+
+extern "C" {
 
 size_t ssd_block_workspace_bytes(int batch, int seqlen, int d_model, int nheads, int headdim,
                                  int ngroups, int dstate) {

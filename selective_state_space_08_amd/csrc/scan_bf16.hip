@@ -28,9 +28,10 @@
 // state goes to HBM between chunks.  Wave w owns the 16 output tokens of row
 // tile rt(w) = w < 4 ? w : 11 - w (the two waves of a SIMD together own tiles
 // i and 7 - i, which balances the causal triangle of C B^T) and the 16 state
-// columns n in [16 w, 16 w + 16).  Each wave loads the C rows of its tokens
-// and the B columns of its state columns straight into registers; B (as bf16
-// [s][n]), x and H, which every wave reads whole, go through LDS.
+// columns n in [16 w, 16 w + 16), held as rows of H^T.  Each wave loads the
+// C rows of its tokens and the B^T rows of its state columns straight into
+// registers; x and the bf16 copy of H, which every wave reads whole, go
+// through LDS.
 //
 // Outputs are produced transposed (Y^T = H C^T + X^T (M)^T, rows p, columns
 // t), so that each lane ends with 4 consecutive channels p of one token: z is
@@ -107,12 +108,50 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 v) {
+  return bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+}
+
 __device__ __forceinline__ bf16x8 lds8(const bf16* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
 __device__ __forceinline__ bf16x8 ldg8(const bf16* p) {
   return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// v moved across lanes by the DPP control CTRL (lanes whose source is
+// outside the pattern, or outside ROW_MASK's rows, read 0)
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_or0(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave, in registers: shifts by
+// 1, 2, 4 and 8 lanes within each row of 16 (row_shr), then the last lane of
+// rows 0 and 2 added to rows 1 and 3 (row_bcast:15), then the last lane of
+// row 1 added to rows 2 and 3 (row_bcast:31).  The order of the additions
+// is fixed for every lane.
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+  v += dpp_or0<0x111, 0xf>(v);
+  v += dpp_or0<0x112, 0xf>(v);
+  v += dpp_or0<0x114, 0xf>(v);
+  v += dpp_or0<0x118, 0xf>(v);
+  v += dpp_or0<0x142, 0xa>(v);
+  v += dpp_or0<0x143, 0xc>(v);
+  return v;
+}
+
+// base + off bytes, for a wave-uniform base and a per-lane offset below
+// 4 GiB: the address form of a global access with a scalar base and a 32-bit
+// vector offset, in place of a 64-bit address computed per lane
+template <typename T>
+__device__ __forceinline__ const T* at_bytes(const T* base, uint32_t off) {
+  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + off);
+}
+template <typename T>
+__device__ __forceinline__ T* at_bytes(T* base, uint32_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off);
 }
 
 // Workgroup barrier for LDS traffic only.  __syncthreads() also waits for
@@ -185,9 +224,12 @@ __device__ __forceinline__ void put8(bf16* dst, const float* v) {
 // its end re-read the last row -- and values outside the sequence and its
 // history are zeroed when read back, so all loads of a chunk are in flight
 // together.
+// HIST = false: the caller knows that no position precedes the sequence
+// (tstart >= 0), so the conv history is never read.
 template <typename Tx, int NR>
 struct RowLoad {
   Raw8<Tx> v[NR];
+  template <bool HIST = true>
   __device__ __forceinline__ void load(const ScanArgs& a, const Tx* src, int64_t stride, int col,
                                        int c0, int cdim, int b, int tstart) {
     const int L = a.seqlen, K = a.conv_k;
@@ -195,18 +237,19 @@ struct RowLoad {
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const int tau = tstart + i;
-      const Tx* p;
-      if (tau < 0 && hist != nullptr && tau >= -(K - 1))
-        p = hist + ((int64_t)b * (K - 1) + (K - 1) + tau) * cdim + c0;
-      else
-        p = src + ((int64_t)b * L + min(max(tau, 0), L - 1)) * stride + col;
+      const Tx* p = src + ((int64_t)b * L + min(max(tau, 0), L - 1)) * stride + col;
+      if (HIST) {
+        const bool h = (tau < 0) & (hist != nullptr) & (tau >= -(K - 1));
+        p = h ? hist + ((int64_t)b * (K - 1) + (K - 1) + tau) * cdim + c0 : p;
+      }
       v[i].load(p);
     }
   }
   __device__ __forceinline__ void get(const ScanArgs& a, int tstart, int i, float* out) const {
     const int tau = tstart + i;
-    const bool ok = tau < a.seqlen &&
-                    (tau >= 0 || (a.conv_state_in != nullptr && tau >= -(a.conv_k - 1)));
+    // bitwise, not short-circuit: a per-lane test without branches
+    const bool ok = (tau < a.seqlen) &
+                    ((tau >= 0) | ((a.conv_state_in != nullptr) & (tau >= -(a.conv_k - 1))));
     v[i].get(out);
     if (!ok) {
 #pragma unroll
@@ -248,7 +291,8 @@ __device__ __forceinline__ void conv_rows_to(const ScanArgs& a, const RowLoad<Tx
     for (int e = 0; e < 8; ++e) {
       const float u = bv[e] + w4[0][e] * win[0][e] + w4[1][e] * win[1][e] +
                       w4[2][e] * win[2][e] + w4[3][e] * cur[e];
-      o[e] = ok ? silu_f32(u) : 0.f;
+      const float sv = silu_f32(u);  // for every lane, then selected
+      o[e] = ok ? sv : 0.f;
       win[0][e] = win[1][e];
       win[1][e] = win[2][e];
       win[2][e] = cur[e];
@@ -449,12 +493,13 @@ struct StageX {
   static constexpr int HX = XCONV ? 3 : 0;
   RowLoad<Tx, 2 + HX> rx;
 
+  template <bool HIST>
   __device__ __forceinline__ void load(const ScanArgs& a, int b, int h, int t0) {
     const int tid = threadIdx.x;
     const int xv = tid & 7, xr = tid >> 3;
     const int cdim = a.nheads * P + 2 * a.ngroups * N;
-    rx.load(a, static_cast<const Tx*>(a.x), a.x_stride, h * P + 8 * xv, h * P + 8 * xv, cdim, b,
-            t0 + 2 * xr - HX);
+    rx.template load<HIST>(a, static_cast<const Tx*>(a.x), a.x_stride, h * P + 8 * xv,
+                           h * P + 8 * xv, cdim, b, t0 + 2 * xr - HX);
   }
 
   // the thread's 2 x 8 post-conv values, tmp[8 i + e] = x[2 xr + i][8 xv + e]
@@ -520,17 +565,21 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
   const bf16* pack = static_cast<const bf16*>(a.bc_pack) + (int64_t)(b * G + g) * nc * PACK;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, q = lane >> 4;
+  // the wave index is uniform over the wave: held in a scalar register, the
+  // branches on it below are scalar branches, not lane masks
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l16 = lane & 15, q = lane >> 4;
   const int rt = w < 4 ? w : 11 - w;  // output tokens [16 rt, 16 rt + 16)
   const int tcol = 16 * rt + l16;     // output token of this lane
-  const int ncol = 16 * w + l16;      // state column n of this lane
   const int xv = tid & 7, xr = tid >> 3;  // x staging: channels 8 xv.., tokens 2 xr..
   const float Ah = a.A[h];
   const float Dh = a.D ? a.D[h] : 0.f;
   const float dtb = a.dt_bias ? a.dt_bias[h] : 0.f;
   const Tx* xg = static_cast<const Tx*>(a.x);
 
-  // ---- incoming state: element r of hacc[pt] is (p = 16 pt + 4 q + r, n = ncol)
+  // ---- incoming state.  The state is accumulated transposed, as H^T [n][p]:
+  //      element r of hacc[pt] is (n = 16 w + 4 q + r, p = 16 pt + l16), so
+  //      that each lane holds 4 consecutive n of one row p of H [p][n].
   const float* h_in = nullptr;
   if (OUT) {
     if (a.nseg > 1)
@@ -538,15 +587,14 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     else
       h_in = a.initial_state ? a.initial_state + (int64_t)bh * P * N : nullptr;
   }
+  const int hoff = 16 * w + 4 * q;  // the lane's first n in a row of H
   f32x4 hacc[4];
 #pragma unroll
-  for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int p = 16 * pt + 4 * q + r;
-      hacc[pt][r] = h_in ? h_in[p * N + ncol] : 0.f;
-      if (OUT) sH[p * LDB + ncol] = (bf16)hacc[pt][r];
-    }
+  for (int pt = 0; pt < 4; ++pt) {
+    const int p = 16 * pt + l16;
+    hacc[pt] = h_in ? *reinterpret_cast<const f32x4*>(h_in + p * N + hoff) : f32x4{};
+    if (OUT) *reinterpret_cast<bf16x4*>(sH + p * LDB + hoff) = to_bf16x4(hacc[pt]);
+  }
   float log_decay = 0.f;  // sum of delta*A over the segment (state-only pass)
   if (XCONV && tid < P) {
     // the conv of this head's x channels: read at every chunk from LDS (the
@@ -569,31 +617,39 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
   // the prefetched dt stays in its raw form until it is used, so that no
   // conversion waits for the load while the prefetch is in flight
   Raw1<Ta> dtv;
-  auto prefetch = [&](int cc) {
+  // (HIST: whether the chunk may be the first, whose conv reads the history)
+  auto prefetch = [&](int cc, auto hist) {
     const int tt0 = cc * Q;
-    sx.load(a, b, h, tt0);
+    sx.template load<decltype(hist)::value>(a, b, h, tt0);
     // every lane loads (threads tid >= Q all re-read the chunk's first token,
     // one cache line, and never use it), so no branch separates these loads
     // from the ones after
     dtv.load(static_cast<const Ta*>(a.dt) +
              ((int64_t)b * L + min(tt0 + (tid < Q ? tid : 0), L - 1)) * a.dt_stride + h);
   };
-  if (cbeg < cend) prefetch(cbeg);
+  if (cbeg < cend) prefetch(cbeg, std::true_type{});
 
   for (int c = cbeg; c < cend; ++c) {
     const int t0 = c * Q;
     const int Lc = min(Q, L - t0);
     const int64_t row0 = (int64_t)b * L + t0;
     const bf16* pk = pack + (int64_t)c * PACK;
+    // rt, re-read at every chunk through an empty asm statement: the
+    // compiler then evaluates the scalar tests on it where they are used
+    // instead of hoisting them out of the loop as lane masks, which exhausts
+    // the scalar registers
+    int rtc = rt;
+    asm volatile("" : "+s"(rtc));
 
-    // this wave's operands: B columns of its state columns (bth/btl, layout
-    // [k = s][j = n]) now, C rows of its tokens (cf, [k = n][j = t]) and z
+    // this wave's operands: B^T rows of its state columns (bth/btl, A operand
+    // [i = n][k = s]) now, C rows of its tokens (cf, [k = n][j = t]) and z
     // after the staging
     bf16x8 cf[4], bth[4], btl[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      bth[kk] = ldg8(pk + PK_BTH + ((w * 4 + kk) * 64 + lane) * 8);
-      btl[kk] = ldg8(pk + PK_BTL + ((w * 4 + kk) * 64 + lane) * 8);
+      const uint32_t o = (((w * 4 + kk) * 64 + lane) * 8) * 2;
+      bth[kk] = ldg8(at_bytes(pk + PK_BTH, o));
+      btl[kk] = ldg8(at_bytes(pk + PK_BTL, o));
     }
 
     lds_barrier();  // the previous chunk is done with every LDS buffer
@@ -602,9 +658,7 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
       // chunk's read-out of the older state is complete past the barrier)
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          sH[(16 * pt + 4 * q + r) * LDB + ncol] = (bf16)hacc[pt][r];
+        *reinterpret_cast<bf16x4*>(sH + (16 * pt + l16) * LDB + hoff) = to_bf16x4(hacc[pt]);
     }
     if (tid < Q) {
       float d = dtv.get() + dtb;
@@ -614,12 +668,7 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
       // inclusive prefix sum of delta A over the wave's 64 tokens (fixed
       // order); the second wave's values lack the first wave's total, which
       // the readers add (lam() below)
-      float v = d * Ah;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float u = __shfl_up(v, o, 64);
-        if (lane >= o) v += u;
-      }
+      const float v = wave_prefix_sum(d * Ah);
       sLam[tid] = v;
       if (tid == 63) sRed[0] = v;
       // the tile's last token is in the same wave, so the difference needs
@@ -654,18 +703,22 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     f32x4 cbt[Q / 16];  // B C^T tiles u <= rt of this wave's tokens (u > rt: unused)
     // unconditional (the last chunk re-reads itself), so that no branch
     // separates these loads from the ones after
-    prefetch(min(c + 1, cend - 1));
+    // (chunk c + 1 >= 1 reads no history; at the last chunk the loads repeat
+    // it and go unused)
+    prefetch(min(c + 1, cend - 1), std::false_type{});
     lds_barrier();
     if (OUT) {
       // C rows of this wave's tokens and its C B^T tiles
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) cf[kk] = ldg8(pk + PK_C + ((rt * 4 + kk) * 64 + lane) * 8);
-      const float* cbsrc = reinterpret_cast<const float*>(pk + PK_CB) + (tri(rt) * 64 + lane) * 4;
+      for (int kk = 0; kk < 4; ++kk)
+        cf[kk] = ldg8(at_bytes(pk + PK_C, (uint32_t)(((rt * 4 + kk) * 64 + lane) * 8) * 2));
+      const float* cbsrc = at_bytes(reinterpret_cast<const float*>(pk + PK_CB) + tri(rt) * 256,
+                                    (uint32_t)lane * 16);
       // tiles past rt are not loaded (wave-uniform branches; the loads
       // after these still retire after them)
 #pragma unroll
       for (int u = 0; u < Q / 16; ++u)
-        if (u <= rt) cbt[u] = *reinterpret_cast<const f32x4*>(cbsrc + u * 256);
+        if (u <= rtc) cbt[u] = *reinterpret_cast<const f32x4*>(cbsrc + u * 256);
     }
     // Lam_s, the cumulative log decay of the chunk up to token s
     const float carry = sRed[0];
@@ -698,8 +751,8 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
 
     lds_barrier();  // (x o w) is complete
 
-    // ---- state: H <- exp(Lam_last) H + (X o w)^T B, operands split hi + lo;
-    //      this wave's columns n = ncol, all 64 rows p.  The read-out below
+    // ---- state: H^T <- exp(Lam_last) H^T + B^T (X o w), operands split
+    //      hi + lo; this wave's rows n of H^T, all 64 columns p.  The read-out below
     //      still uses the previous state through its bf16 copy in sH, which
     //      is replaced at the start of the next chunk.
     const float gamma = __expf(lam_last);
@@ -710,11 +763,11 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
         const int o = prow(16 * pt + l16) * LDT + 32 * kk + 8 * q;
-        const bf16x8 ahi = lds8(sXWh + o);
-        const bf16x8 alo = lds8(sXWl + o);
-        hacc[pt] = mfma(ahi, bth[kk], hacc[pt]);
-        hacc[pt] = mfma(ahi, btl[kk], hacc[pt]);
-        hacc[pt] = mfma(alo, bth[kk], hacc[pt]);
+        const bf16x8 xhi = lds8(sXWh + o);
+        const bf16x8 xlo = lds8(sXWl + o);
+        hacc[pt] = mfma(bth[kk], xhi, hacc[pt]);
+        hacc[pt] = mfma(btl[kk], xhi, hacc[pt]);
+        hacc[pt] = mfma(bth[kk], xlo, hacc[pt]);
       }
       // keep the operand loads of the next K step below this one's products
       // (hoisting them all at once costs more registers than the wave has)
@@ -754,12 +807,22 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
       //      tiles u <= rt, two 16-token tiles per K=32 step
 #pragma unroll
       for (int u0 = 0; u0 < Q / 16; u0 += 2) {
-        if (u0 > rt) break;
+        if (u0 > rtc) break;
+        // the step's x operands first, so that their LDS latency is hidden
+        // behind the mask arithmetic
+        bf16x8 xf[4];
+#pragma unroll
+        for (int pj = 0; pj < 4; ++pj) {
+          const bf16* xp = sXh + prow(16 * pj + l16) * LDT + 16 * u0 + 4 * q;
+          const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(xp);
+          const bf16x4 x1 = *reinterpret_cast<const bf16x4*>(xp + 16);
+          xf[pj] = bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        }
         bf16x8 mf;  // element 4 half + r: M[t = tcol][s = 16 (u0 + half) + 4 q + r]
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int u = u0 + half;
-          if (u > rt) {  // past the diagonal tile (rt even): a zero K half
+          if (u > rtc) {  // past the diagonal tile (rt even): a zero K half
 #pragma unroll
             for (int r = 0; r < 4; ++r) mf[4 * half + r] = (bf16)0.f;
             continue;
@@ -767,7 +830,7 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
           const f32x4 cb = cbt[u];
           // cb[r] = (B C^T)[s = 16 u + 4 q + r][t = tcol]
           const int s0 = 16 * u + 4 * q;
-          if (u < rt) {
+          if (u < rtc) {
             // below the diagonal every s precedes every t: the decay
             // exp(Lam_t - Lam_s) factors through the tile's last token r as
             // exp(Lam_t - Lam_r) exp(Lam_r - Lam_s), both factors <= 1
@@ -780,24 +843,21 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
           } else {
             const float4 l4 = *reinterpret_cast<const float4*>(sLam + s0);
             const float4 d4 = *reinterpret_cast<const float4*>(sDel + s0);
-            const float cs = s0 >= 64 ? carry : 0.f;  // the 4 tokens share a wave
+            const float cs = u >= 4 ? carry : 0.f;  // the 4 tokens share a wave
             const float ls[4] = {l4.x + cs, l4.y + cs, l4.z + cs, l4.w + cs};
             const float ds[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const float m = s0 + r <= tcol ? cb[r] * __expf(lam_t - ls[r]) * ds[r] : 0.f;
-              mf[4 * half + r] = (bf16)m;
+              // computed for every lane and then selected (no lane branch);
+              // above the diagonal the exponent is positive and discarded.
+              // In the diagonal tile s <= t is 4 q + r <= l16.
+              const float m = cb[r] * __expf(lam_t - ls[r]) * ds[r];
+              mf[4 * half + r] = (bf16)(4 * q + r <= l16 ? m : 0.f);
             }
           }
         }
 #pragma unroll
-        for (int pj = 0; pj < 4; ++pj) {
-          const bf16* xp = sXh + prow(16 * pj + l16) * LDT + 16 * u0 + 4 * q;
-          const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(xp);
-          const bf16x4 x1 = *reinterpret_cast<const bf16x4*>(xp + 16);
-          const bf16x8 xf = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-          yacc[pj] = mfma(xf, mf, yacc[pj]);
-        }
+        for (int pj = 0; pj < 4; ++pj) yacc[pj] = mfma(xf[pj], mf, yacc[pj]);
       }
 
       // ---- epilogue: skip, gate, store 4 consecutive channels per pj
@@ -831,8 +891,7 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
   if (h_out != nullptr) {
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) h_out[(16 * pt + 4 * q + r) * N + ncol] = hacc[pt][r];
+      *reinterpret_cast<f32x4*>(h_out + (16 * pt + l16) * N + hoff) = hacc[pt];
   }
   if (STATE_ONLY && tid == 0) a.seg_logdecay[(int64_t)bh * a.nseg + seg] = log_decay;
 

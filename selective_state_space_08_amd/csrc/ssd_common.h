@@ -21,9 +21,18 @@ template <> __device__ __forceinline__ float from_f32<float>(float v) { return v
 // round to nearest even (gfx950 converts in hardware)
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
 
-// softplus(v) = log(1 + e^v) in the form that neither overflows nor cancels.
+// softplus(v) = log(1 + e^v) in the form that neither overflows nor cancels,
+// max(v, 0) + log1p(e) with e = exp(-|v|) in (0, 1].  log1p(e) is taken as
+// log(u) e / (u - 1), u = fl(1 + e): the quotient cancels the rounding of
+// 1 + e (D. Goldberg, "What every computer scientist should know about
+// floating-point arithmetic", 1991, theorem 4), a few ulps in all, with the
+// hardware logarithm; where u rounds to 1, log1p(e) = e to within rounding.
 __device__ __forceinline__ float softplus_f32(float v) {
-  return fmaxf(v, 0.f) + log1pf(__expf(-fabsf(v)));
+  const float e = __expf(-fabsf(v));
+  const float u = 1.f + e;
+  const float d = u - 1.f;
+  const float l = d == 0.f ? e : __logf(u) * (e * __builtin_amdgcn_rcpf(d));
+  return fmaxf(v, 0.f) + l;
 }
 
 // SiLU(u) = u * sigmoid(u), with the hardware reciprocal (1 ulp) in place of
