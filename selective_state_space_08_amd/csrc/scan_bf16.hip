@@ -544,11 +544,13 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 sXWl[PROWS * LDT];            // (x o w) lo
   __shared__ __attribute__((aligned(16))) float sX32[OUT ? Q * LDX : 4];  // x [t][p]
   __shared__ __attribute__((aligned(16))) bf16 sH[OUT ? P * LDB : 8];     // H [p][n]
-  __shared__ __attribute__((aligned(16))) float sLam[Q];
-  __shared__ __attribute__((aligned(16))) float sDel[Q];
+  // the decay of a chunk, in two buffers (chunk c in buffer c % 2): the next
+  // chunk's is computed while the current one is in use
+  __shared__ __attribute__((aligned(16))) float sLam[2 * Q];
+  __shared__ __attribute__((aligned(16))) float sDel[2 * Q];
   // exp(Lam_r - Lam_s) delta_s, r the last token of s's 16-token tile
-  __shared__ __attribute__((aligned(16))) float sE[OUT ? Q : 4];
-  __shared__ float sRed[4];
+  __shared__ __attribute__((aligned(16))) float sE[OUT ? 2 * Q : 4];
+  __shared__ float sRed[2];
   __shared__ __attribute__((aligned(16))) float sCw[XCONV ? 5 * P : 4];  // x-channel conv
 
   const int H = a.nheads, G = a.ngroups, L = a.seqlen;
@@ -609,10 +611,14 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     sCw[4 * P + tid] = a.conv_b ? a.conv_b[ch] : 0.f;
   }
 
-  // Chunk c+1's x, dt and B [s][n] are loaded as soon as chunk c is staged, so
-  // they are in flight while chunk c is computed.  The per-wave operands (C
-  // rows, B columns) and z are loaded at the top of their own chunk, ahead of
-  // their first use after the decay scan.
+  // Two barriers per chunk.  After the first: the bf16 copy of the state,
+  // the conv of x and its staging, and the split of x o w (the chunk's decay
+  // is already in LDS).  After the second: the state product, the read-out,
+  // the intra-chunk product and the epilogue, and then waves 0 and 1 compute
+  // the next chunk's decay.  Chunk c+1's x and dt are loaded as soon as
+  // chunk c is staged, so they are in flight while chunk c is computed.  The
+  // per-wave operands (B^T rows, C rows, C B^T tiles) and z are loaded
+  // within their own chunk, ahead of their first use.
   StageX<Tx, XCONV> sx;
   // the prefetched dt stays in its raw form until it is used, so that no
   // conversion waits for the load while the prefetch is in flight
@@ -627,7 +633,30 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     dtv.load(static_cast<const Ta*>(a.dt) +
              ((int64_t)b * L + min(tt0 + (tid < Q ? tid : 0), L - 1)) * a.dt_stride + h);
   };
-  if (cbeg < cend) prefetch(cbeg, std::true_type{});
+  // delta, the cumulative log decay and the tile decays of chunk cc into
+  // buffer cc % 2, by waves 0 and 1 (one token per lane) from the dt in dtv
+  auto delta_step = [&](int cc) {
+    const int Lcc = min(Q, L - cc * Q);
+    const int buf = (cc & 1) * Q;
+    float d = dtv.get() + dtb;
+    if (a.dt_softplus) d = softplus_f32(d);
+    if (tid >= Lcc) d = 0.f;
+    sDel[buf + tid] = d;
+    // inclusive prefix sum of delta A over the wave's 64 tokens (fixed
+    // order); the second wave's values lack the first wave's total, which
+    // the readers add (lam() below)
+    const float v = wave_prefix_sum(d * Ah);
+    sLam[buf + tid] = v;
+    if (tid == 63) sRed[cc & 1] = v;
+    // the tile's last token is in the same wave, so the difference needs
+    // no carry; it is <= 0 (the decay only shrinks)
+    const float vr = __shfl(v, lane | 15, 64);
+    if (OUT) sE[buf + tid] = __expf(vr - v) * d;
+  };
+  if (cbeg < cend) {
+    prefetch(cbeg, std::true_type{});
+    if (w < 2) delta_step(cbeg);  // visible past the first barrier of the loop
+  }
 
   for (int c = cbeg; c < cend; ++c) {
     const int t0 = c * Q;
@@ -660,22 +689,19 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
       for (int pt = 0; pt < 4; ++pt)
         *reinterpret_cast<bf16x4*>(sH + (16 * pt + l16) * LDB + hoff) = to_bf16x4(hacc[pt]);
     }
-    if (tid < Q) {
-      float d = dtv.get() + dtb;
-      if (a.dt_softplus) d = softplus_f32(d);
-      if (tid >= Lc) d = 0.f;
-      sDel[tid] = d;
-      // inclusive prefix sum of delta A over the wave's 64 tokens (fixed
-      // order); the second wave's values lack the first wave's total, which
-      // the readers add (lam() below)
-      const float v = wave_prefix_sum(d * Ah);
-      sLam[tid] = v;
-      if (tid == 63) sRed[0] = v;
-      // the tile's last token is in the same wave, so the difference needs
-      // no carry; it is <= 0 (the decay only shrinks)
-      const float vr = __shfl(v, lane | 15, 64);
-      if (OUT) sE[tid] = __expf(vr - v) * d;
-    }
+    // this chunk's decay (computed during the previous chunk, or before the
+    // loop): Lam_s, the cumulative log decay of the chunk up to token s
+    const float* cLam = sLam + (c & 1) * Q;
+    const float* cDel = sDel + (c & 1) * Q;
+    const float* cE = sE + (OUT ? (c & 1) * Q : 0);
+    const float carry = sRed[c & 1];
+    auto lam = [&](int s) { return cLam[s] + (s >= 64 ? carry : 0.f); };
+    // the decay to the chunk's last token: token Lc - 1, not Q - 1 -- past
+    // the end the increments are 0, but they are summed in another order, so
+    // the two can differ by an ulp, which is large when |Lam| is
+    const float lam_last = lam(Lc - 1);
+    if (STATE_ONLY) log_decay += lam_last;
+
     float xt[16];  // xt[8 i + e] = x[2 xr + i][8 xv + e], post-conv fp32
     sx.compute(a, sCw, t0, Lc, xt);
     if (OUT) {
@@ -695,45 +721,12 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
         *reinterpret_cast<bf16x2*>(sXh + prow(8 * xv + e) * LDT + 2 * xr) = v2;
       }
     }
-    // The loads of this chunk's per-wave operands are spread over the
-    // chunk (all waves issue theirs at the same time, and they share the
-    // CU's load path): the next chunk's x and dt now, the C rows and C B^T
-    // tiles after the staging barrier, z after the state product.
-    Raw4<Ta> zr[4];
-    f32x4 cbt[Q / 16];  // B C^T tiles u <= rt of this wave's tokens (u > rt: unused)
-    // unconditional (the last chunk re-reads itself), so that no branch
-    // separates these loads from the ones after
-    // (chunk c + 1 >= 1 reads no history; at the last chunk the loads repeat
-    // it and go unused)
-    prefetch(min(c + 1, cend - 1), std::false_type{});
-    lds_barrier();
-    if (OUT) {
-      // C rows of this wave's tokens and its C B^T tiles
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        cf[kk] = ldg8(at_bytes(pk + PK_C, (uint32_t)(((rt * 4 + kk) * 64 + lane) * 8) * 2));
-      const float* cbsrc = at_bytes(reinterpret_cast<const float*>(pk + PK_CB) + tri(rt) * 256,
-                                    (uint32_t)lane * 16);
-      // tiles past rt are not loaded (wave-uniform branches; the loads
-      // after these still retire after them)
-#pragma unroll
-      for (int u = 0; u < Q / 16; ++u)
-        if (u <= rtc) cbt[u] = *reinterpret_cast<const f32x4*>(cbsrc + u * 256);
-    }
-    // Lam_s, the cumulative log decay of the chunk up to token s
-    const float carry = sRed[0];
-    auto lam = [&](int s) { return sLam[s] + (s >= 64 ? carry : 0.f); };
-    // the decay to the chunk's last token: token Lc - 1, not Q - 1 -- past
-    // the end the increments are 0, but they are summed in another order, so
-    // the two can differ by an ulp, which is large when |Lam| is
-    const float lam_last = lam(Lc - 1);
-    if (STATE_ONLY) log_decay += lam_last;
 
     // ---- (x o w) split into bf16 hi + lo, [p][s], once per workgroup, with
     //      w_s = exp(Lam_last - Lam_s) delta_s of the thread's two tokens
     {
-      const float w0 = __expf(lam_last - lam(2 * xr)) * sDel[2 * xr];
-      const float w1 = __expf(lam_last - lam(2 * xr + 1)) * sDel[2 * xr + 1];
+      const float w0 = __expf(lam_last - lam(2 * xr)) * cDel[2 * xr];
+      const float w1 = __expf(lam_last - lam(2 * xr + 1)) * cDel[2 * xr + 1];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         bf16x2 hi, lo;
@@ -749,8 +742,31 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
       }
     }
 
-    lds_barrier();  // (x o w) is complete
-
+    // The loads of this chunk's per-wave operands are spread over the
+    // chunk (all waves issue theirs at the same time, and they share the
+    // CU's load path): the next chunk's x and dt now, the C rows and C B^T
+    // tiles after the staging barrier, z after the state product.
+    Raw4<Ta> zr[4];
+    f32x4 cbt[Q / 16];  // B C^T tiles u <= rt of this wave's tokens (u > rt: unused)
+    // unconditional (the last chunk re-reads itself), so that no branch
+    // separates these loads from the ones after
+    // (chunk c + 1 >= 1 reads no history; at the last chunk the loads repeat
+    // it and go unused)
+    prefetch(min(c + 1, cend - 1), std::false_type{});
+    lds_barrier();  // x, its bf16 copy and (x o w) are complete
+    if (OUT) {
+      // C rows of this wave's tokens and its C B^T tiles
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        cf[kk] = ldg8(at_bytes(pk + PK_C, (uint32_t)(((rt * 4 + kk) * 64 + lane) * 8) * 2));
+      const float* cbsrc = at_bytes(reinterpret_cast<const float*>(pk + PK_CB) + tri(rt) * 256,
+                                    (uint32_t)lane * 16);
+      // tiles past rt are not loaded (wave-uniform branches; the loads
+      // after these still retire after them)
+#pragma unroll
+      for (int u = 0; u < Q / 16; ++u)
+        if (u <= rtc) cbt[u] = *reinterpret_cast<const f32x4*>(cbsrc + u * 256);
+    }
     // ---- state: H^T <- exp(Lam_last) H^T + B^T (X o w), operands split
     //      hi + lo; this wave's rows n of H^T, all 64 columns p.  The read-out below
     //      still uses the previous state through its bf16 copy in sH, which
@@ -835,14 +851,14 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
             // exp(Lam_t - Lam_s) factors through the tile's last token r as
             // exp(Lam_t - Lam_r) exp(Lam_r - Lam_s), both factors <= 1
             const float f = __expf(lam_t - lam(16 * u + 15));
-            const float4 e4 = *reinterpret_cast<const float4*>(sE + s0);
+            const float4 e4 = *reinterpret_cast<const float4*>(cE + s0);
             mf[4 * half + 0] = (bf16)(cb[0] * f * e4.x);
             mf[4 * half + 1] = (bf16)(cb[1] * f * e4.y);
             mf[4 * half + 2] = (bf16)(cb[2] * f * e4.z);
             mf[4 * half + 3] = (bf16)(cb[3] * f * e4.w);
           } else {
-            const float4 l4 = *reinterpret_cast<const float4*>(sLam + s0);
-            const float4 d4 = *reinterpret_cast<const float4*>(sDel + s0);
+            const float4 l4 = *reinterpret_cast<const float4*>(cLam + s0);
+            const float4 d4 = *reinterpret_cast<const float4*>(cDel + s0);
             const float cs = u >= 4 ? carry : 0.f;  // the 4 tokens share a wave
             const float ls[4] = {l4.x + cs, l4.y + cs, l4.z + cs, l4.w + cs};
             const float ds[4] = {d4.x, d4.y, d4.z, d4.w};
@@ -864,22 +880,35 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
       if (tcol < Lc) {
         Ty* yrow = static_cast<Ty*>(a.y) + (row0 + tcol) * a.y_stride + h * P + 4 * q;
         const float* xrow = sX32 + tcol * LDX + 4 * q;
+        // one straight-line copy per case of the (uniform) gate test, so
+        // that the exponentials of all 16 outputs can be in flight together
+        auto emit = [&](auto gated) {
 #pragma unroll
-        for (int pj = 0; pj < 4; ++pj) {
-          const float4 x4 = *reinterpret_cast<const float4*>(xrow + 16 * pj);
-          const float xs[4] = {x4.x, x4.y, x4.z, x4.w};
-          float zs[4];
-          if (a.z != nullptr) zr[pj].get(zs);
-          float yv[4];
+          for (int pj = 0; pj < 4; ++pj) {
+            const float4 x4 = *reinterpret_cast<const float4*>(xrow + 16 * pj);
+            const float xs[4] = {x4.x, x4.y, x4.z, x4.w};
+            float zs[4];
+            if constexpr (decltype(gated)::value) zr[pj].get(zs);
+            float yv[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            yv[r] = yacc[pj][r] + Dh * xs[r];
-            if (a.z != nullptr) yv[r] *= silu_f32(zs[r]);
+            for (int r = 0; r < 4; ++r) {
+              yv[r] = yacc[pj][r] + Dh * xs[r];
+              if constexpr (decltype(gated)::value) yv[r] *= silu_f32(zs[r]);
+            }
+            store4(yrow + 16 * pj, yv);
           }
-          store4(yrow + 16 * pj, yv);
-        }
+        };
+        if (a.z != nullptr)
+          emit(std::true_type{});
+        else
+          emit(std::false_type{});
       }
     }
+
+    // ---- the next chunk's decay, by waves 0 and 1 (the two with the least
+    //      intra-chunk work), into the other buffer: read past the next
+    //      chunk's first barrier, while this chunk's buffer is still in use
+    if (w < 2 && c + 1 < cend) delta_step(c + 1);
   }
 
   // ---- outgoing state
