@@ -3,7 +3,8 @@
 // final state).  Reverse-mode differentiation of the recurrence of "Hybrid
 // Architectures for Language Models: Systematic Analysis and Design
 // Insights" (Korean summary), section 2 Background, in the chunked form the
-// forward pass uses, fp32 throughout on the vector ALUs.
+// forward pass uses, fp32 throughout: the products of size P x N on the
+// fp32 matrix cores, the rest on the vector ALUs.
 //
 // Kernels, in launch order:
 //   1. the post-conv x|B|C in fp32 (the conv kernel, or a conversion);
@@ -31,7 +32,12 @@ constexpr int BT = 256;   // threads
 // column use distinct banks
 constexpr int PN = BN + 4;
 constexpr int PP = BP + 4;
-constexpr int PQ = BQ + 1;
+// pitches of the reverse walker's LDS tiles (12 mod 64 floats)
+constexpr int QN = BN + 12;
+constexpr int QP = BP + 12;
+constexpr int QQ = BQ + 12;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T> __device__ __forceinline__ float ld(const T* p) { return to_f32(*p); }
 
@@ -187,40 +193,61 @@ __device__ __forceinline__ float sum16(float v) {
   return v;
 }
 
-// The reverse walk over one (b, h).  Mappings: the state's gradient dH[p][n]
-// lives in registers, thread (lane, wave w) owning p = lane and
-// n in 16 w .. 16 w + 15; token-shaped work uses 16 lanes per token
-// (t = tid / 16, r = tid % 16), with head channels p = r + 16 i and state
-// channels n = 4 r + 64 j .. + 3, so that the 16 lanes read 16 consecutive
-// LDS rows or 16 consecutive float4s.
+// D = A B + D for one 16x16 fp32 tile and K = 4 on the matrix cores.  Lane
+// l = i + 16 q holds A[i][q] and B[q][i] and ends with D[4 q + r][i], r < 4.
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// The reverse walk over one (b, h), 8 waves.  The five products of size
+// P x N per chunk run on the fp32 matrix cores, 16x16 tiles:
+//   Yoff = e^lam C H_in^T and HB = B dH_out^T ([t][p], one tile per wave,
+//   K = N), dC = e^lam dY H_in + dS B and dB = w X dH_out + dS^T C ([t][n],
+//   two tiles per wave, K = P then K = Q), and the update of dH ([p][n],
+//   four tiles per wave, K = Q).  The state's gradient dH[p][n] stays in
+//   accumulator registers across the chunks: wave w holds the tiles
+//   (p tile w / 2, n tiles 4 (w % 2) .. + 3), lane l = i + 16 q the rows
+//   p = 16 (w / 2) + 4 q + r and the column n = 16 nt + i.  The rest is
+//   token-shaped vector work with 16 lanes per token (t = tid / 16,
+//   r = tid % 16, head channels p = r + 16 i).  LDS pitches are 12 mod 64
+//   floats, so that 16 lanes reading 16 rows at one column, or 16 columns
+//   of one row, hit distinct banks.
 template <typename Ta, typename Td>
 __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) float sX[BQ][PP];
-  __shared__ __attribute__((aligned(16))) float sDY[BQ][PP];
-  __shared__ __attribute__((aligned(16))) float sHB[BQ][PP];
-  __shared__ __attribute__((aligned(16))) float sB[BQ][PN];
-  __shared__ __attribute__((aligned(16))) float sC[BQ][PN];
-  __shared__ __attribute__((aligned(16))) float sH[BP][PN];    // state entering the chunk
-  __shared__ __attribute__((aligned(16))) float sDH[BP][PN];   // gradient of the state leaving it
-  __shared__ float sM[BQ][PQ];    // M_ts = (C_t . B_s) exp(lam_t - lam_s) delta_s, s <= t
-  __shared__ float sS[BQ][PQ];    // C_t . B_s
-  __shared__ float sDS[BQ][PQ];   // dM_ts exp(lam_t - lam_s) delta_s
-  __shared__ float sE[BQ][PQ];    // dM_ts S_ts exp(lam_t - lam_s)
+  __shared__ __attribute__((aligned(16))) float sX[BQ][QP];
+  __shared__ __attribute__((aligned(16))) float sDY[BQ][QP];
+  __shared__ __attribute__((aligned(16))) float sHB[BQ][QP];   // Yoff, then HB
+  __shared__ __attribute__((aligned(16))) float sB[BQ][QN];
+  __shared__ __attribute__((aligned(16))) float sC[BQ][QN];
+  __shared__ __attribute__((aligned(16))) float sH[BP][QN];    // state entering the chunk
+  __shared__ __attribute__((aligned(16))) float sDH[BP][QN];   // gradient of the state leaving it
+  __shared__ float sSX[BQ][QQ];   // (C_t . B_s) exp(lam_t - lam_s), s <= t; M_ts = sSX delta_s
+  __shared__ float sDS[BQ][QQ];   // dM_ts exp(lam_t - lam_s) delta_s
+  __shared__ float sE[BQ][QQ];    // dM_ts S_ts exp(lam_t - lam_s)
   __shared__ float sDel[BQ], sLam[BQ], sEl[BQ], sV[BQ], sDLoff[BQ], sDW[BQ];
   __shared__ float sRed[WT / 64];
 
   const int H = a.nheads, G = a.ngroups, L = a.seqlen;
   const int b = blockIdx.x / H, h = blockIdx.x % H, g = h / (H / G);
   const int HP = H * BP, GN = G * BN;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tq = tid >> 4, r = tid & 15;
+  const int li = lane & 15, lq = lane >> 4;  // matrix-core lane coordinates
   const float Ah = a.A[h], Dh = a.D ? a.D[h] : 0.f;
+  // this wave's tiles: [t][p] tile (ty, py); [t][n] tiles (ty, nb + 0/1);
+  // dH tiles (hp, hn + 0..3)
+  const int ty = w >> 2, py = w & 3, nb = 2 * (w & 3);
+  const int hp = w >> 1, hn = 4 * (w & 1);
 
-  float dh[16];
+  f32x4 dh[4];
   {
-    const float* src = a.dhT ? a.dhT + ((int64_t)b * H + h) * BP * BN + lane * BN + 16 * w : nullptr;
+    const float* src = a.dhT ? a.dhT + ((int64_t)b * H + h) * BP * BN : nullptr;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) dh[e] = src ? src[e] : 0.f;
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        dh[j][e] = src ? src[(16 * hp + 4 * lq + e) * BN + 16 * (hn + j) + li] : 0.f;
   }
   float dD_part = 0.f, dA_part = 0.f, dbias_part = 0.f;
 
@@ -253,9 +280,9 @@ __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
       }
     }
 #pragma unroll
-    for (int e = 0; e < 16; e += 4)
-      *reinterpret_cast<float4*>(&sDH[lane][16 * w + e]) =
-          make_float4(dh[e], dh[e + 1], dh[e + 2], dh[e + 3]);
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sDH[16 * hp + 4 * lq + e][16 * (hn + j) + li] = dh[j][e];
     if (tid < 64) {
       float v;
       const float d = tid < BQ ? delta_of<Ta>(a, row0 + tid, h, tid < Lc, v) : 0.f;
@@ -275,11 +302,12 @@ __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
     const float lam_last = sLam[Lc - 1];
     const float gam = __expf(lam_last);
 
-    // ---- S and M (2 entries per thread)
+    // ---- S o exp(lam_t - lam_s) (2 entries per thread)
     for (int j = 0; j < 2; ++j) {
       const int e = tid + WT * j, t = e >> 5, s = e & 31;
-      float S = 0.f, M = 0.f;
+      float sx = 0.f;
       if (s <= t) {
+        float S = 0.f;
 #pragma unroll 2
         for (int n = 0; n < BN; n += 4) {
           const float4 cv = *reinterpret_cast<const float4*>(&sC[t][n]);
@@ -287,28 +315,23 @@ __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
           S = fmaf(cv.x, bv.x, S); S = fmaf(cv.y, bv.y, S);
           S = fmaf(cv.z, bv.z, S); S = fmaf(cv.w, bv.w, S);
         }
-        M = S * __expf(sLam[t] - sLam[s]) * sDel[s];
+        sx = S * __expf(sLam[t] - sLam[s]);
       }
-      sS[t][s] = S;
-      sM[t][s] = M;
+      sSX[t][s] = sx;
     }
-    // ---- the inter-chunk read-out Yoff[t][p] = e^lam_t C_t . H_in[p]
-    float yoff[4];
+    // ---- the inter-chunk read-out Yoff[t][p] = e^lam_t C_t . H_in[p] (into sHB)
     {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) yoff[i] = 0.f;
-#pragma unroll 2
-      for (int n = 0; n < BN; n += 4) {
-        const float4 cv = *reinterpret_cast<const float4*>(&sC[tq][n]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float4 hv = *reinterpret_cast<const float4*>(&sH[r + 16 * i][n]);
-          yoff[i] = fmaf(cv.x, hv.x, fmaf(cv.y, hv.y, fmaf(cv.z, hv.z, fmaf(cv.w, hv.w, yoff[i]))));
-        }
+      f32x4 acc0 = {}, acc1 = {};
+#pragma unroll 4
+      for (int m = 0; m < BN / 4; m += 2) {
+        acc0 = mfma4(sC[16 * ty + li][4 * m + lq], sH[16 * py + li][4 * m + lq], acc0);
+        acc1 = mfma4(sC[16 * ty + li][4 * m + 4 + lq], sH[16 * py + li][4 * m + 4 + lq], acc1);
       }
-      const float el = sEl[tq];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) yoff[i] *= el;
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * ty + 4 * lq + e;
+        sHB[t][16 * py + li] = (acc0[e] + acc1[e]) * sEl[t];
+      }
     }
     __syncthreads();
 
@@ -316,12 +339,15 @@ __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
     {
       const int t = tq;
       const bool ok = t < Lc;
-      float yv[4];
+      float yoff[4], yv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) yv[i] = yoff[i] + Dh * sX[t][r + 16 * i];
+      for (int i = 0; i < 4; ++i) {
+        yoff[i] = sHB[t][r + 16 * i];
+        yv[i] = yoff[i] + Dh * sX[t][r + 16 * i];
+      }
 #pragma unroll 2
       for (int s = 0; s <= t; ++s) {
-        const float m = sM[t][s];
+        const float m = sSX[t][s] * sDel[s];
 #pragma unroll
         for (int i = 0; i < 4; ++i) yv[i] = fmaf(m, sX[s][r + 16 * i], yv[i]);
       }
@@ -349,7 +375,7 @@ __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
     }
     __syncthreads();
 
-    // ---- dM, dS, E (2 entries per thread) and HB_s = dH_out B_s (s = tq)
+    // ---- dS, E (2 entries per thread) and HB_s = dH_out B_s (into sHB)
     for (int j = 0; j < 2; ++j) {
       const int e = tid + WT * j, t = e >> 5, s = e & 31;
       float ds = 0.f, ee = 0.f;
@@ -364,94 +390,90 @@ __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
         }
         const float ex = __expf(sLam[t] - sLam[s]);
         ds = dm * ex * sDel[s];
-        ee = dm * sS[t][s] * ex;
+        ee = dm * sSX[t][s];
       }
       sDS[t][s] = ds;
       sE[t][s] = ee;
     }
     {
-      float hb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) hb[i] = 0.f;
-#pragma unroll 2
-      for (int n = 0; n < BN; n += 4) {
-        const float4 bv = *reinterpret_cast<const float4*>(&sB[tq][n]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float4 dv = *reinterpret_cast<const float4*>(&sDH[r + 16 * i][n]);
-          hb[i] = fmaf(bv.x, dv.x, fmaf(bv.y, dv.y, fmaf(bv.z, dv.z, fmaf(bv.w, dv.w, hb[i]))));
-        }
+      f32x4 acc0 = {}, acc1 = {};
+#pragma unroll 4
+      for (int m = 0; m < BN / 4; m += 2) {
+        acc0 = mfma4(sB[16 * ty + li][4 * m + lq], sDH[16 * py + li][4 * m + lq], acc0);
+        acc1 = mfma4(sB[16 * ty + li][4 * m + 4 + lq], sDH[16 * py + li][4 * m + 4 + lq], acc1);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sHB[tq][r + 16 * i] = hb[i];
+      for (int e = 0; e < 4; ++e) sHB[16 * ty + 4 * lq + e][16 * py + li] = acc0[e] + acc1[e];
     }
     // <dH_out, H_in> for the gradient of the chunk's total decay
     float hh = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; e += 4) {
-      const float4 hv = *reinterpret_cast<const float4*>(&sH[lane][16 * w + e]);
-      hh = fmaf(dh[e], hv.x, fmaf(dh[e + 1], hv.y, fmaf(dh[e + 2], hv.z, fmaf(dh[e + 3], hv.w, hh))));
-    }
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        hh = fmaf(dh[j][e], sH[16 * hp + 4 * lq + e][16 * (hn + j) + li], hh);
     const float dot_hh = block_sum<WT / 64>(hh, sRed);  // (includes the barrier)
 
-    // ---- dC_t, dB_t (n = 4 r + 64 j), dx_t (p = r + 16 i); token t = tq
+    // ---- dC and dB of this wave's two [t][n] tiles, written to HBM
+    {
+      f32x4 dc[2] = {}, db[2] = {};
+#pragma unroll 4
+      for (int m = 0; m < BP / 4; ++m) {
+        const float ay = sDY[16 * ty + li][4 * m + lq];   // dC += dY H_in
+        const float ax = sX[16 * ty + li][4 * m + lq];    // dB += X dH_out
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          dc[k] = mfma4(ay, sH[4 * m + lq][16 * (nb + k) + li], dc[k]);
+          db[k] = mfma4(ax, sDH[4 * m + lq][16 * (nb + k) + li], db[k]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * ty + 4 * lq + e;
+        const float el = sEl[t];
+        const float ws = __expf(lam_last - sLam[t]) * sDel[t];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          dc[k][e] *= el;
+          db[k][e] *= ws;
+        }
+      }
+#pragma unroll 4
+      for (int m = 0; m < BQ / 4; ++m) {
+        const float as = sDS[16 * ty + li][4 * m + lq];   // dC_t += dS_ts B_s
+        const float at = sDS[4 * m + lq][16 * ty + li];   // dB_t += dS_st C_s
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          dc[k] = mfma4(as, sB[4 * m + lq][16 * (nb + k) + li], dc[k]);
+          db[k] = mfma4(at, sC[4 * m + lq][16 * (nb + k) + li], db[k]);
+        }
+      }
+      float* dcp = a.dCh + (((int64_t)b * H + h) * L + t0) * BN;
+      float* dbp = a.dBh + (((int64_t)b * H + h) * L + t0) * BN;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * ty + 4 * lq + e;
+        if (t < Lc) {
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            dcp[t * BN + 16 * (nb + k) + li] = dc[k][e];
+            dbp[t * BN + 16 * (nb + k) + li] = db[k][e];
+          }
+        }
+      }
+    }
+    // ---- dx_t = D dy_t + sum_u M_ut dy_u + w_t HB_t;  dw_t = x_t . HB_t
     {
       const int t = tq;
       const bool ok = t < Lc;
-      const float el = sEl[t];
       const float ws = __expf(lam_last - sLam[t]) * sDel[t];
-      float4 dc[2], db[2], oc[2], ob[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) dc[j] = db[j] = oc[j] = ob[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 2
-      for (int s = 0; s < BQ; ++s) {
-        const float a1 = sDS[t][s];   // dC_t += dS_ts B_s
-        const float a2 = sDS[s][t];   // dB_t += dS_st C_s
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const float4 bv = *reinterpret_cast<const float4*>(&sB[s][4 * r + 64 * j]);
-          const float4 cv = *reinterpret_cast<const float4*>(&sC[s][4 * r + 64 * j]);
-          dc[j].x = fmaf(a1, bv.x, dc[j].x); dc[j].y = fmaf(a1, bv.y, dc[j].y);
-          dc[j].z = fmaf(a1, bv.z, dc[j].z); dc[j].w = fmaf(a1, bv.w, dc[j].w);
-          db[j].x = fmaf(a2, cv.x, db[j].x); db[j].y = fmaf(a2, cv.y, db[j].y);
-          db[j].z = fmaf(a2, cv.z, db[j].z); db[j].w = fmaf(a2, cv.w, db[j].w);
-        }
-      }
-#pragma unroll 2
-      for (int p = 0; p < BP; ++p) {
-        const float yv = sDY[t][p];   // dC_t += e^lam_t dy_t H_in
-        const float xv = sX[t][p];    // dB_t += w_t x_t dH_out
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const float4 hv = *reinterpret_cast<const float4*>(&sH[p][4 * r + 64 * j]);
-          const float4 dv = *reinterpret_cast<const float4*>(&sDH[p][4 * r + 64 * j]);
-          oc[j].x = fmaf(yv, hv.x, oc[j].x); oc[j].y = fmaf(yv, hv.y, oc[j].y);
-          oc[j].z = fmaf(yv, hv.z, oc[j].z); oc[j].w = fmaf(yv, hv.w, oc[j].w);
-          ob[j].x = fmaf(xv, dv.x, ob[j].x); ob[j].y = fmaf(xv, dv.y, ob[j].y);
-          ob[j].z = fmaf(xv, dv.z, ob[j].z); ob[j].w = fmaf(xv, dv.w, ob[j].w);
-        }
-      }
-      if (ok) {
-        float* dcp = a.dCh + (((int64_t)b * H + h) * L + t0 + t) * BN;
-        float* dbp = a.dBh + (((int64_t)b * H + h) * L + t0 + t) * BN;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int n = 4 * r + 64 * j;
-          *reinterpret_cast<float4*>(dcp + n) =
-              make_float4(fmaf(el, oc[j].x, dc[j].x), fmaf(el, oc[j].y, dc[j].y),
-                          fmaf(el, oc[j].z, dc[j].z), fmaf(el, oc[j].w, dc[j].w));
-          *reinterpret_cast<float4*>(dbp + n) =
-              make_float4(fmaf(ws, ob[j].x, db[j].x), fmaf(ws, ob[j].y, db[j].y),
-                          fmaf(ws, ob[j].z, db[j].z), fmaf(ws, ob[j].w, db[j].w));
-        }
-      }
-      // dx_t = D dy_t + sum_u M_ut dy_u + w_t HB_t;  dw_t = x_t . HB_t
+      const float dt_ = sDel[t];
       float dx[4], dwp = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) dx[i] = Dh * sDY[t][r + 16 * i] + ws * sHB[t][r + 16 * i];
 #pragma unroll 2
       for (int u = t; u < BQ; ++u) {
-        const float m = sM[u][t];
+        const float m = sSX[u][t] * dt_;
 #pragma unroll
         for (int i = 0; i < 4; ++i) dx[i] = fmaf(m, sDY[u][r + 16 * i], dx[i]);
       }
@@ -506,27 +528,23 @@ __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
     // ---- the state's gradient entering the chunk:
     //      dH_in = e^lam_last dH_out + sum_t e^lam_t dy_t C_t^T
 #pragma unroll
-    for (int e = 0; e < 16; ++e) dh[e] *= gam;
-#pragma unroll 2
-    for (int t = 0; t < BQ; ++t) {
-      const float yv = sDY[t][lane] * sEl[t];
+    for (int j = 0; j < 4; ++j) dh[j] *= gam;
+#pragma unroll 4
+    for (int m = 0; m < BQ / 4; ++m) {
+      const int t = 4 * m + lq;
+      const float ay = sDY[t][16 * hp + li] * sEl[t];
 #pragma unroll
-      for (int e = 0; e < 16; e += 4) {
-        const float4 cv = *reinterpret_cast<const float4*>(&sC[t][16 * w + e]);
-        dh[e] = fmaf(yv, cv.x, dh[e]);
-        dh[e + 1] = fmaf(yv, cv.y, dh[e + 1]);
-        dh[e + 2] = fmaf(yv, cv.z, dh[e + 2]);
-        dh[e + 3] = fmaf(yv, cv.w, dh[e + 3]);
-      }
+      for (int j = 0; j < 4; ++j) dh[j] = mfma4(ay, sC[t][16 * (hn + j) + li], dh[j]);
     }
     __syncthreads();
   }
 
   if (a.dh0) {
-    float* dst = a.dh0 + ((int64_t)b * H + h) * BP * BN + lane * BN + 16 * w;
+    float* dst = a.dh0 + ((int64_t)b * H + h) * BP * BN;
 #pragma unroll
-    for (int e = 0; e < 16; e += 4)
-      *reinterpret_cast<float4*>(dst + e) = make_float4(dh[e], dh[e + 1], dh[e + 2], dh[e + 3]);
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[(16 * hp + 4 * lq + e) * BN + 16 * (hn + j) + li] = dh[j][e];
   }
   const float sA = block_sum<WT / 64>(dA_part, sRed);
   const float sD = block_sum<WT / 64>(dD_part, sRed);
