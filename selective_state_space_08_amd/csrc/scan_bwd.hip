@@ -199,46 +199,130 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// The reverse walk over one (b, h), 8 waves.  The five products of size
-// P x N per chunk run on the fp32 matrix cores, 16x16 tiles:
-//   Yoff = e^lam C H_in^T and HB = B dH_out^T ([t][p], one tile per wave,
-//   K = N), dC = e^lam dY H_in + dS B and dB = w X dH_out + dS^T C ([t][n],
-//   two tiles per wave, K = P then K = Q), and the update of dH ([p][n],
-//   four tiles per wave, K = Q).  The state's gradient dH[p][n] stays in
-//   accumulator registers across the chunks: wave w holds the tiles
-//   (p tile w / 2, n tiles 4 (w % 2) .. + 3), lane l = i + 16 q the rows
-//   p = 16 (w / 2) + 4 q + r and the column n = 16 nt + i.  The rest is
-//   token-shaped vector work with 16 lanes per token (t = tid / 16,
-//   r = tid % 16, head channels p = r + 16 i).  LDS pitches are 12 mod 64
-//   floats, so that 16 lanes reading 16 rows at one column, or 16 columns
-//   of one row, hit distinct banks.
+// One activation element, kept raw between its load and its use, so that a
+// load issued ahead of time is not waited for at the load.
+template <typename T> struct RawS;
+template <> struct RawS<bf16> {
+  unsigned short u = 0;
+  __device__ __forceinline__ void load(const bf16* p) {
+    u = *reinterpret_cast<const unsigned short*>(p);
+  }
+  __device__ __forceinline__ float get() const { return __uint_as_float((uint32_t)u << 16); }
+};
+template <> struct RawS<float> {
+  float f = 0.f;
+  __device__ __forceinline__ void load(const float* p) { f = *p; }
+  __device__ __forceinline__ float get() const { return f; }
+};
+
+// One chunk's x, B, C (post-conv rows), the state entering it and dt, in
+// registers: thread tid holds the float4 tid of x [t][p], the float4s
+// tid + WT k of B and C [t][n] and of the state [p][n], and (threads of
+// wave 0) dt of token tid % 32.  Every load is unconditional (rows past the
+// end of the sequence re-read its last row), so that none waits for another
+// and no address is selected per lane; the rows past the end are zeroed
+// when stored (store()).
+template <typename Ta>
+struct ChunkRegs {
+  f32x4 x, b0, b1, c0, c1, h0, h1, h2, h3;
+  RawS<Ta> dt;
+
+  __device__ __forceinline__ void load(const BwdArgs& a, const float* st, int64_t row0, int Lc,
+                                       int h, int g) {
+    const int tid = threadIdx.x;
+    const int HP = a.nheads * BP, GN = a.ngroups * BN;
+    auto row = [&](int t) { return a.post + (row0 + min(t, Lc - 1)) * a.cdim; };
+    {
+      const int t = tid >> 4, p4 = 4 * (tid & 15);
+      x = *reinterpret_cast<const f32x4*>(row(t) + h * BP + p4);
+    }
+    {
+      const int t = tid >> 5, n4 = 4 * (tid & 31);
+      b0 = *reinterpret_cast<const f32x4*>(row(t) + HP + g * BN + n4);
+      c0 = *reinterpret_cast<const f32x4*>(row(t) + HP + GN + g * BN + n4);
+      b1 = *reinterpret_cast<const f32x4*>(row(t + 16) + HP + g * BN + n4);
+      c1 = *reinterpret_cast<const f32x4*>(row(t + 16) + HP + GN + g * BN + n4);
+    }
+    {
+      const f32x4* s4 = reinterpret_cast<const f32x4*>(st) + tid;
+      h0 = s4[0];
+      h1 = s4[WT];
+      h2 = s4[2 * WT];
+      h3 = s4[3 * WT];
+    }
+    // (every lane loads; lanes past the chunk re-read its first token)
+    const int t = tid & 31;
+    dt.load(static_cast<const Ta*>(a.dt) + (row0 + min(t, Lc - 1)) * a.dt_stride + h);
+  }
+
+  // x, B, C and the state into LDS, rows t >= Lc of x, B, C as zeros
+  __device__ __forceinline__ void store(float (*sX)[QP], float (*sB)[QN], float (*sC)[QN],
+                                        float (*sH)[QN], int Lc) const {
+    const int tid = threadIdx.x;
+    const f32x4 zero4 = {};
+    {
+      const int t = tid >> 4;
+      *reinterpret_cast<f32x4*>(&sX[t][4 * (tid & 15)]) = t < Lc ? x : zero4;
+    }
+    const int t = tid >> 5, n4 = 4 * (tid & 31);
+    *reinterpret_cast<f32x4*>(&sB[t][n4]) = t < Lc ? b0 : zero4;
+    *reinterpret_cast<f32x4*>(&sC[t][n4]) = t < Lc ? c0 : zero4;
+    *reinterpret_cast<f32x4*>(&sB[t + 16][n4]) = t + 16 < Lc ? b1 : zero4;
+    *reinterpret_cast<f32x4*>(&sC[t + 16][n4]) = t + 16 < Lc ? c1 : zero4;
+    *reinterpret_cast<f32x4*>(&sH[t][n4]) = h0;
+    *reinterpret_cast<f32x4*>(&sH[t + 16][n4]) = h1;
+    *reinterpret_cast<f32x4*>(&sH[t + 32][n4]) = h2;
+    *reinterpret_cast<f32x4*>(&sH[t + 48][n4]) = h3;
+  }
+};
+
+// The reverse walk over one (b, h), 8 waves, five barriers per chunk.  All
+// products run on the fp32 matrix cores in 16x16 tiles (lane l = i + 16 q
+// of a tile holds rows 4 q .. 4 q + 3 of column i):
+//   - S = C B^T and dM = dY X^T: the three causal [t][s] tiles (S in two K
+//     halves on waves 0..5, dM on waves 5..7);
+//   - Yoff = e^lam C H_in^T + M X, and HB = B dH_out^T + ... for dx: the
+//     [t][p] tile (w / 4, w % 4) of each wave, where the gate and the
+//     gradient of x are then formed element by element;
+//   - dC = e^lam dY H_in + dS B and dB = w X dH_out + dS^T C: the [t][n]
+//     tiles (w / 4, 2 (w % 4) + 0/1);
+//   - dH <- e^lam_last dH + (e^lam dY)^T C: the [p][n] tiles (w / 2,
+//     4 (w % 2) + 0..3), kept in accumulator registers across the chunks.
+// The next chunk's x, B, C, entering state and dt are loaded into
+// registers while the current chunk is computed (dout and z one phase
+// later).  LDS pitches are 12 mod 64 floats, so that 16 lanes reading 16
+// rows at one column, or 16 columns of one row, hit distinct banks.
 template <typename Ta, typename Td>
 __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float sX[BQ][QP];
   __shared__ __attribute__((aligned(16))) float sDY[BQ][QP];
-  __shared__ __attribute__((aligned(16))) float sHB[BQ][QP];   // Yoff, then HB
   __shared__ __attribute__((aligned(16))) float sB[BQ][QN];
   __shared__ __attribute__((aligned(16))) float sC[BQ][QN];
   __shared__ __attribute__((aligned(16))) float sH[BP][QN];    // state entering the chunk
   __shared__ __attribute__((aligned(16))) float sDH[BP][QN];   // gradient of the state leaving it
   __shared__ float sSX[BQ][QQ];   // (C_t . B_s) exp(lam_t - lam_s), s <= t; M_ts = sSX delta_s
-  __shared__ float sDS[BQ][QQ];   // dM_ts exp(lam_t - lam_s) delta_s
-  __shared__ float sE[BQ][QQ];    // dM_ts S_ts exp(lam_t - lam_s)
-  __shared__ float sDel[BQ], sLam[BQ], sEl[BQ], sV[BQ], sDLoff[BQ], sDW[BQ];
+  // dM_ts exp(lam_t - lam_s) delta_s, and dM_ts S_ts exp(lam_t - lam_s);
+  // before that, the two K halves of S
+  __shared__ float sDS[BQ][QQ];
+  __shared__ float sE[BQ][QQ];
+  __shared__ float sDel[BQ], sLam[BQ], sEl[BQ], sV[BQ];
+  // per-tile partial sums over p (4 p tiles) and over s or t (2 tiles)
+  __shared__ float sDLp[4][BQ], sDWp[4][BQ], sRowP[2][BQ], sColP[2][BQ];
   __shared__ float sRed[WT / 64];
 
   const int H = a.nheads, G = a.ngroups, L = a.seqlen;
   const int b = blockIdx.x / H, h = blockIdx.x % H, g = h / (H / G);
-  const int HP = H * BP, GN = G * BN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tq = tid >> 4, r = tid & 15;
   const int li = lane & 15, lq = lane >> 4;  // matrix-core lane coordinates
   const float Ah = a.A[h], Dh = a.D ? a.D[h] : 0.f;
+  const float dtb = a.dt_bias ? a.dt_bias[h] : 0.f;
   // this wave's tiles: [t][p] tile (ty, py); [t][n] tiles (ty, nb + 0/1);
   // dH tiles (hp, hn + 0..3)
   const int ty = w >> 2, py = w & 3, nb = 2 * (w & 3);
   const int hp = w >> 1, hn = 4 * (w & 1);
+  const int pcol = 16 * py + li;  // the lane's column p in its [t][p] tile
+  const float* states_bh = a.states + ((int64_t)b * H + h) * a.nc * BP * BN;
 
   f32x4 dh[4];
   {
@@ -251,182 +335,241 @@ __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
   }
   float dD_part = 0.f, dA_part = 0.f, dbias_part = 0.f;
 
+  // ---- the next chunk's operands, in registers
+  ChunkRegs<Ta> nx;
+  auto fetch_main = [&](int c) {
+    const int t0 = c * BQ;
+    nx.load(a, states_bh + (int64_t)c * BP * BN, (int64_t)b * L + t0, min(BQ, L - t0), h, g);
+  };
+  // dout and z of the lane's 4 elements (t = 16 ty + 4 lq + e, p = pcol)
+  RawS<Td> pdo[4];
+  RawS<Ta> pz[4];
+  auto fetch_gate = [&](int c) {
+    const int t0 = c * BQ, Lc = min(BQ, L - t0);
+    const int64_t row0 = (int64_t)b * L + t0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = min(16 * ty + 4 * lq + e, Lc - 1);  // (rows past the end: never used)
+      pdo[e].load(static_cast<const Td*>(a.dout) + (row0 + t) * a.dout_stride + h * BP + pcol);
+      if (a.z) pz[e].load(static_cast<const Ta*>(a.z) + (row0 + t) * a.z_stride + h * BP + pcol);
+    }
+  };
+  if (a.nc > 0) {
+    fetch_main(a.nc - 1);
+    fetch_gate(a.nc - 1);
+  }
+
   for (int c = a.nc - 1; c >= 0; --c) {
     const int t0 = c * BQ, Lc = min(BQ, L - t0);
     const int64_t row0 = (int64_t)b * L + t0;
-    // ---- load the chunk
-    for (int i = tid; i < BQ * BP / 4; i += WT) {
-      const int t = i / (BP / 4), p4 = 4 * (i % (BP / 4));
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (t < Lc) v = *reinterpret_cast<const float4*>(a.post + (row0 + t) * a.cdim + h * BP + p4);
-      *reinterpret_cast<float4*>(&sX[t][p4]) = v;
-    }
-    for (int i = tid; i < BQ * BN / 4; i += WT) {
-      const int t = i / (BN / 4), n4 = 4 * (i % (BN / 4));
-      float4 vb = make_float4(0.f, 0.f, 0.f, 0.f), vc = vb;
-      if (t < Lc) {
-        const float* rowp = a.post + (row0 + t) * a.cdim;
-        vb = *reinterpret_cast<const float4*>(rowp + HP + g * BN + n4);
-        vc = *reinterpret_cast<const float4*>(rowp + HP + GN + g * BN + n4);
-      }
-      *reinterpret_cast<float4*>(&sB[t][n4]) = vb;
-      *reinterpret_cast<float4*>(&sC[t][n4]) = vc;
-    }
-    {
-      const float* st = a.states + (((int64_t)b * H + h) * a.nc + c) * BP * BN;
-      for (int i = tid; i < BP * BN / 4; i += WT) {
-        const int p = i / (BN / 4), n4 = 4 * (i % (BN / 4));
-        *reinterpret_cast<float4*>(&sH[p][n4]) = *reinterpret_cast<const float4*>(st + p * BN + n4);
-      }
-    }
+
+    // ---- P0: the chunk into LDS; the next chunk's loads; delta and lam
+    nx.store(sX, sB, sC, sH, Lc);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) sDH[16 * hp + 4 * lq + e][16 * (hn + j) + li] = dh[j][e];
-    if (tid < 64) {
-      float v;
-      const float d = tid < BQ ? delta_of<Ta>(a, row0 + tid, h, tid < Lc, v) : 0.f;
+    if (w == 0) {
+      const int t = lane & 31;
+      const bool real = lane < BQ && t < Lc;
+      const float v = real ? nx.dt.get() + dtb : 0.f;
+      float d = a.dt_softplus ? softplus_f32(v) : v;
+      if (!real) d = 0.f;
       float lam = d * Ah;
       for (int o = 1; o < 32; o <<= 1) {
         const float u = __shfl_up(lam, o, 64);
-        if ((tid & 31) >= o) lam += u;
+        if (t >= o) lam += u;
       }
-      if (tid < BQ) {
-        sDel[tid] = d;
-        sLam[tid] = lam;
-        sEl[tid] = __expf(lam);
-        sV[tid] = v;
+      if (lane < BQ) {
+        sDel[t] = d;
+        sLam[t] = lam;
+        sEl[t] = __expf(lam);
+        sV[t] = v;
       }
     }
-    __syncthreads();
+    if (c > 0) fetch_main(c - 1);
+    __syncthreads();  // B1
     const float lam_last = sLam[Lc - 1];
     const float gam = __expf(lam_last);
 
-    // ---- S o exp(lam_t - lam_s) (2 entries per thread)
-    for (int j = 0; j < 2; ++j) {
-      const int e = tid + WT * j, t = e >> 5, s = e & 31;
-      float sx = 0.f;
-      if (s <= t) {
-        float S = 0.f;
-#pragma unroll 2
-        for (int n = 0; n < BN; n += 4) {
-          const float4 cv = *reinterpret_cast<const float4*>(&sC[t][n]);
-          const float4 bv = *reinterpret_cast<const float4*>(&sB[s][n]);
-          S = fmaf(cv.x, bv.x, S); S = fmaf(cv.y, bv.y, S);
-          S = fmaf(cv.z, bv.z, S); S = fmaf(cv.w, bv.w, S);
-        }
-        sx = S * __expf(sLam[t] - sLam[s]);
+    // ---- P1: S (two K halves, waves 0..5), Yoff and HB tiles, <dH, H_in>
+    if (w < 6) {
+      const int tsel = w >> 1, kh = w & 1;
+      const int tt = tsel == 0 ? 0 : 1, ts = tsel == 2 ? 1 : 0;
+      f32x4 sp = {};
+#pragma unroll 4
+      for (int m = 0; m < BN / 8; ++m) {
+        const int k = 64 * kh + 4 * m + lq;
+        sp = mfma4(sC[16 * tt + li][k], sB[16 * ts + li][k], sp);
       }
-      sSX[t][s] = sx;
+      float(*dst)[QQ] = kh == 0 ? sDS : sE;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[16 * tt + 4 * lq + e][16 * ts + li] = sp[e];
     }
-    // ---- the inter-chunk read-out Yoff[t][p] = e^lam_t C_t . H_in[p] (into sHB)
+    f32x4 yo = {}, hb = {};
     {
-      f32x4 acc0 = {}, acc1 = {};
+      f32x4 y1 = {}, h1 = {};
 #pragma unroll 4
       for (int m = 0; m < BN / 4; m += 2) {
-        acc0 = mfma4(sC[16 * ty + li][4 * m + lq], sH[16 * py + li][4 * m + lq], acc0);
-        acc1 = mfma4(sC[16 * ty + li][4 * m + 4 + lq], sH[16 * py + li][4 * m + 4 + lq], acc1);
+        yo = mfma4(sC[16 * ty + li][4 * m + lq], sH[pcol][4 * m + lq], yo);
+        y1 = mfma4(sC[16 * ty + li][4 * m + 4 + lq], sH[pcol][4 * m + 4 + lq], y1);
+        hb = mfma4(sB[16 * ty + li][4 * m + lq], sDH[pcol][4 * m + lq], hb);
+        h1 = mfma4(sB[16 * ty + li][4 * m + 4 + lq], sDH[pcol][4 * m + 4 + lq], h1);
       }
+      yo += y1;
+      hb += h1;
+    }
+    {
+      float hh = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          hh = fmaf(dh[j][e], sH[16 * hp + 4 * lq + e][16 * (hn + j) + li], hh);
+      for (int o = 32; o > 0; o >>= 1) hh += __shfl_xor(hh, o, 64);
+      if (lane == 0) sRed[w] = hh;
+    }
+    __syncthreads();  // B2
+
+    // ---- P2: M = (S o exp) delta (this wave's rows, written once to sSX),
+    //      y = Yoff + M X + D x, the gate and its gradient; dw partials
+    {
+      // e^lam_t Yoff, the inter-chunk part of y (also for the gradient of lam)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) yo[e] *= sEl[16 * ty + 4 * lq + e];
+      f32x4 yv = yo;
+      const int ta = 16 * ty + li;   // the A operand's row t
+      const float lam_a = sLam[ta];
+#pragma unroll
+      for (int m = 0; m < BQ / 4; ++m) {
+        const int s = 4 * m + lq;
+        const float sx = s <= ta ? (sDS[ta][s] + sE[ta][s]) * __expf(lam_a - sLam[s]) : 0.f;
+        if (py == 0) sSX[ta][s] = sx;
+        yv = mfma4(sx * sDel[s], sX[s][pcol], yv);
+      }
+      float dl[4], dw[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * ty + 4 * lq + e;
-        sHB[t][16 * py + li] = (acc0[e] + acc1[e]) * sEl[t];
-      }
-    }
-    __syncthreads();
-
-    // ---- forward output, the gate and its gradient (t = tq, p = r + 16 i)
-    {
-      const int t = tq;
-      const bool ok = t < Lc;
-      float yoff[4], yv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        yoff[i] = sHB[t][r + 16 * i];
-        yv[i] = yoff[i] + Dh * sX[t][r + 16 * i];
-      }
-#pragma unroll 2
-      for (int s = 0; s <= t; ++s) {
-        const float m = sSX[t][s] * sDel[s];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) yv[i] = fmaf(m, sX[s][r + 16 * i], yv[i]);
-      }
-      float dl = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int p = r + 16 * i;
+        const bool ok = t < Lc;
+        const float xv = sX[t][pcol];
+        const float y = yv[e] + Dh * xv;
         float dyv = 0.f;
         if (ok) {
-          const float dout = ld(static_cast<const Td*>(a.dout) + (row0 + t) * a.dout_stride + h * BP + p);
+          const float dout = pdo[e].get();
           if (a.z) {
-            const float zz = ld(static_cast<const Ta*>(a.z) + (row0 + t) * a.z_stride + h * BP + p);
+            const float zz = pz[e].get();
             dyv = dout * silu_f32(zz);
-            if (a.dz) a.dz[((row0 + t) * H + h) * BP + p] = dout * yv[i] * silu_grad_f32(zz);
+            if (a.dz) a.dz[((row0 + t) * H + h) * BP + pcol] = dout * y * silu_grad_f32(zz);
           } else {
             dyv = dout;
           }
         }
-        sDY[t][p] = dyv;
-        dD_part = fmaf(dyv, sX[t][p], dD_part);
-        dl = fmaf(dyv, yoff[i], dl);
+        sDY[t][pcol] = dyv;
+        dD_part = fmaf(dyv, xv, dD_part);
+        dl[e] = sum16(dyv * yo[e]);
+        dw[e] = sum16(xv * hb[e]);
       }
-      dl = sum16(dl);
-      if (r == 0) sDLoff[t] = dl;
-    }
-    __syncthreads();
-
-    // ---- dS, E (2 entries per thread) and HB_s = dH_out B_s (into sHB)
-    for (int j = 0; j < 2; ++j) {
-      const int e = tid + WT * j, t = e >> 5, s = e & 31;
-      float ds = 0.f, ee = 0.f;
-      if (s <= t) {
-        float dm = 0.f;
-#pragma unroll 2
-        for (int p = 0; p < BP; p += 4) {
-          const float4 yv = *reinterpret_cast<const float4*>(&sDY[t][p]);
-          const float4 xv = *reinterpret_cast<const float4*>(&sX[s][p]);
-          dm = fmaf(yv.x, xv.x, dm); dm = fmaf(yv.y, xv.y, dm);
-          dm = fmaf(yv.z, xv.z, dm); dm = fmaf(yv.w, xv.w, dm);
-        }
-        const float ex = __expf(sLam[t] - sLam[s]);
-        ds = dm * ex * sDel[s];
-        ee = dm * sSX[t][s];
-      }
-      sDS[t][s] = ds;
-      sE[t][s] = ee;
-    }
-    {
-      f32x4 acc0 = {}, acc1 = {};
-#pragma unroll 4
-      for (int m = 0; m < BN / 4; m += 2) {
-        acc0 = mfma4(sB[16 * ty + li][4 * m + lq], sDH[16 * py + li][4 * m + lq], acc0);
-        acc1 = mfma4(sB[16 * ty + li][4 * m + 4 + lq], sDH[16 * py + li][4 * m + 4 + lq], acc1);
-      }
+      if (li == 0) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sHB[16 * ty + 4 * lq + e][16 * py + li] = acc0[e] + acc1[e];
-    }
-    // <dH_out, H_in> for the gradient of the chunk's total decay
-    float hh = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        hh = fmaf(dh[j][e], sH[16 * hp + 4 * lq + e][16 * (hn + j) + li], hh);
-    const float dot_hh = block_sum<WT / 64>(hh, sRed);  // (includes the barrier)
-
-    // ---- dC and dB of this wave's two [t][n] tiles, written to HBM
-    {
-      f32x4 dc[2] = {}, db[2] = {};
-#pragma unroll 4
-      for (int m = 0; m < BP / 4; ++m) {
-        const float ay = sDY[16 * ty + li][4 * m + lq];   // dC += dY H_in
-        const float ax = sX[16 * ty + li][4 * m + lq];    // dB += X dH_out
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          dc[k] = mfma4(ay, sH[4 * m + lq][16 * (nb + k) + li], dc[k]);
-          db[k] = mfma4(ax, sDH[4 * m + lq][16 * (nb + k) + li], db[k]);
+        for (int e = 0; e < 4; ++e) {
+          sDLp[py][16 * ty + 4 * lq + e] = dl[e];
+          sDWp[py][16 * ty + 4 * lq + e] = dw[e];
         }
       }
+    }
+    if (c > 0) fetch_gate(c - 1);
+    __syncthreads();  // B3
+
+    // ---- P3: dM, dS, E and their row / column sums (waves 5..7); the first
+    //      parts of dC and dB; dx; the update of dH
+    if (w >= 5) {
+      const int tsel = w - 5;
+      const int tt = tsel == 0 ? 0 : 1, ts = tsel == 2 ? 1 : 0;
+      f32x4 dm = {};
+#pragma unroll 4
+      for (int m = 0; m < BP / 4; ++m)
+        dm = mfma4(sDY[16 * tt + li][4 * m + lq], sX[16 * ts + li][4 * m + lq], dm);
+      const int s = 16 * ts + li;
+      const float lam_s = sLam[s], del_s = sDel[s];
+      float rowp[4], colp = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * tt + 4 * lq + e;
+        const bool ok = s <= t;
+        const float ds = dm[e] * __expf(sLam[t] - lam_s) * del_s;
+        const float ee = dm[e] * sSX[t][s];  // (0 above the diagonal)
+        sDS[t][s] = ok ? ds : 0.f;
+        sE[t][s] = ee;
+        rowp[e] = sum16(ee * del_s);
+        colp += ee;
+      }
+      colp += __shfl_xor(colp, 16, 64);
+      colp += __shfl_xor(colp, 32, 64);
+      if (li == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sRowP[ts][16 * tt + 4 * lq + e] = rowp[e];
+      }
+      if (lq == 0) sColP[tt][s] = colp;
+    } else if (w == 4) {
+      // the [t][s] tile above the diagonal (t < 16 <= s) is zero
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sDS[4 * lq + e][16 + li] = 0.f;
+        sE[4 * lq + e][16 + li] = 0.f;
+      }
+      if (lane < 16) {
+        sRowP[1][lane] = 0.f;
+        sColP[0][16 + lane] = 0.f;
+      }
+    }
+    f32x4 dc[2] = {}, db[2] = {};
+#pragma unroll 4
+    for (int m = 0; m < BP / 4; ++m) {
+      const float ay = sDY[16 * ty + li][4 * m + lq];   // dC += dY H_in
+      const float ax = sX[16 * ty + li][4 * m + lq];    // dB += X dH_out
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        dc[k] = mfma4(ay, sH[4 * m + lq][16 * (nb + k) + li], dc[k]);
+        db[k] = mfma4(ax, sDH[4 * m + lq][16 * (nb + k) + li], db[k]);
+      }
+    }
+    {
+      // dx_t = D dy_t + w_t HB_t + sum_u M_ut dy_u, in the [t][p] tile
+      f32x4 dx;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * ty + 4 * lq + e;
+        dx[e] = hb[e] * (__expf(lam_last - sLam[t]) * sDel[t]);
+      }
+      const int ta = 16 * ty + li;
+      const float del_a = sDel[ta];
+#pragma unroll
+      for (int m = 0; m < BQ / 4; ++m) {
+        const int u = 4 * m + lq;
+        dx = mfma4(sSX[u][ta] * del_a, sDY[u][pcol], dx);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * ty + 4 * lq + e;
+        if (t < Lc) a.dpost[(row0 + t) * a.cdim + h * BP + pcol] = dx[e] + Dh * sDY[t][pcol];
+      }
+    }
+    // dH_in = e^lam_last dH_out + sum_t e^lam_t dy_t C_t^T
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dh[j] *= gam;
+#pragma unroll 4
+    for (int m = 0; m < BQ / 4; ++m) {
+      const int t = 4 * m + lq;
+      const float ay = sDY[t][16 * hp + li] * sEl[t];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dh[j] = mfma4(ay, sC[t][16 * (hn + j) + li], dh[j]);
+    }
+    __syncthreads();  // B4
+
+    // ---- P4: the second parts of dC and dB, written to HBM; the decays and
+    //      delta (wave 0, one lane per token)
+    {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * ty + 4 * lq + e;
@@ -462,50 +605,24 @@ __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
         }
       }
     }
-    // ---- dx_t = D dy_t + sum_u M_ut dy_u + w_t HB_t;  dw_t = x_t . HB_t
-    {
-      const int t = tq;
-      const bool ok = t < Lc;
-      const float ws = __expf(lam_last - sLam[t]) * sDel[t];
-      const float dt_ = sDel[t];
-      float dx[4], dwp = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dx[i] = Dh * sDY[t][r + 16 * i] + ws * sHB[t][r + 16 * i];
-#pragma unroll 2
-      for (int u = t; u < BQ; ++u) {
-        const float m = sSX[u][t] * dt_;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dx[i] = fmaf(m, sDY[u][r + 16 * i], dx[i]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int p = r + 16 * i;
-        if (ok) a.dpost[(row0 + t) * a.cdim + h * BP + p] = dx[i];
-        dwp = fmaf(sX[t][p], sHB[t][p], dwp);
-      }
-      dwp = sum16(dwp);
-      if (r == 0) sDW[t] = dwp;
-    }
-    __syncthreads();
-
-    // ---- the decays and delta: one lane per token (wave 0)
-    if (tid < 64) {
-      const int t = tid & 31;
-      const bool real = tid < BQ;
+    if (w == 0) {
+      const int t = lane & 31;
+      const bool real = lane < BQ;
       const float del = real ? sDel[t] : 0.f, lam = sLam[t];
       const float wt = __expf(lam_last - lam) * del;
-      float rowg = 0.f, colg = 0.f, cole = 0.f;
-#pragma unroll 2
-      for (int s = 0; s < BQ; ++s) {
-        rowg = fmaf(sE[t][s], sDel[s], rowg);
-        colg = fmaf(sE[s][t], del, colg);
-        cole += sE[s][t];
-      }
+      const float dw = sDWp[0][t] + sDWp[1][t] + sDWp[2][t] + sDWp[3][t];
+      const float dlo = sDLp[0][t] + sDLp[1][t] + sDLp[2][t] + sDLp[3][t];
+      const float rowg = sRowP[0][t] + sRowP[1][t];
+      const float cole = sColP[0][t] + sColP[1][t];
+      const float colg = cole * del;
+      float dot_hh = 0.f;
+#pragma unroll
+      for (int i = 0; i < WT / 64; ++i) dot_hh += sRed[i];
       // gradient of the chunk's total log-decay (through w and the carry)
-      float dwl = real ? sDW[t] * wt : 0.f;
+      float dwl = real ? dw * wt : 0.f;
       for (int o = 16; o > 0; o >>= 1) dwl += __shfl_xor(dwl, o, 32);
       const float dlam_last = dwl + gam * dot_hh;
-      float dlam = real ? rowg - colg + sDLoff[t] - sDW[t] * wt : 0.f;
+      float dlam = real ? rowg - colg + dlo - dw * wt : 0.f;
       if (real && t == Lc - 1) dlam += dlam_last;
       // suffix sums over the chunk: lam_t = A sum_{r <= t} delta_r
       float suf = dlam;
@@ -513,7 +630,7 @@ __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
         const float u = __shfl_down(suf, o, 32);
         if (t + o < 32) suf += u;
       }
-      const float ddel = cole + (real ? sDW[t] * __expf(lam_last - lam) : 0.f) + Ah * suf;
+      const float ddel = cole + (real ? dw * __expf(lam_last - lam) : 0.f) + Ah * suf;
       if (real) {
         dA_part = fmaf(del, suf, dA_part);
         const float sg = a.dt_softplus ? 1.f / (1.f + __expf(-sV[t])) : 1.f;
@@ -524,19 +641,7 @@ __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
         }
       }
     }
-
-    // ---- the state's gradient entering the chunk:
-    //      dH_in = e^lam_last dH_out + sum_t e^lam_t dy_t C_t^T
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dh[j] *= gam;
-#pragma unroll 4
-    for (int m = 0; m < BQ / 4; ++m) {
-      const int t = 4 * m + lq;
-      const float ay = sDY[t][16 * hp + li] * sEl[t];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dh[j] = mfma4(ay, sC[t][16 * (hn + j) + li], dh[j]);
-    }
-    __syncthreads();
+    __syncthreads();  // B5
   }
 
   if (a.dh0) {
