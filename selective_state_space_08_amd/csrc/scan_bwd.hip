@@ -199,6 +199,17 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// The products of one group of 16 k.  Lane (i, q) holds the 4 consecutive
+// k = 4 q .. 4 q + 3 of the group: for operands stored with k contiguous
+// they are one float4 read; step e takes k = 4 q + e on both sides, which
+// is a permutation of the group's 16 k.
+__device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 mfma_k16(f32x4 a4, f32x4 b4, f32x4 acc) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = mfma4(a4[e], b4[e], acc);
+  return acc;
+}
+
 // One activation element, kept raw between its load and its use, so that a
 // load issued ahead of time is not waited for at the load.
 template <typename T> struct RawS;
@@ -300,12 +311,15 @@ __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float sC[BQ][QN];
   __shared__ __attribute__((aligned(16))) float sH[BP][QN];    // state entering the chunk
   __shared__ __attribute__((aligned(16))) float sDH[BP][QN];   // gradient of the state leaving it
-  __shared__ float sSX[BQ][QQ];   // (C_t . B_s) exp(lam_t - lam_s), s <= t; M_ts = sSX delta_s
+  __shared__ __attribute__((aligned(16))) float sSX[BQ][QQ];  // (C_t . B_s) exp(lam_t - lam_s), s <= t; M_ts = sSX delta_s
   // dM_ts exp(lam_t - lam_s) delta_s, and dM_ts S_ts exp(lam_t - lam_s);
   // before that, the two K halves of S
-  __shared__ float sDS[BQ][QQ];
-  __shared__ float sE[BQ][QQ];
-  __shared__ float sDel[BQ], sLam[BQ], sEl[BQ], sV[BQ];
+  __shared__ __attribute__((aligned(16))) float sDS[BQ][QQ];
+  __shared__ __attribute__((aligned(16))) float sE[BQ][QQ];
+  __shared__ __attribute__((aligned(16))) float sDel[BQ];
+  __shared__ __attribute__((aligned(16))) float sLam[BQ];
+  __shared__ __attribute__((aligned(16))) float sEl[BQ];
+  __shared__ float sV[BQ];
   // per-tile partial sums over p (4 p tiles) and over s or t (2 tiles)
   __shared__ float sDLp[4][BQ], sDWp[4][BQ], sRowP[2][BQ], sColP[2][BQ];
   __shared__ float sRed[WT / 64];
@@ -397,27 +411,26 @@ __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
       const int tsel = w >> 1, kh = w & 1;
       const int tt = tsel == 0 ? 0 : 1, ts = tsel == 2 ? 1 : 0;
       f32x4 sp = {};
-#pragma unroll 4
-      for (int m = 0; m < BN / 8; ++m) {
-        const int k = 64 * kh + 4 * m + lq;
-        sp = mfma4(sC[16 * tt + li][k], sB[16 * ts + li][k], sp);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k0 = 64 * kh + 16 * j + 4 * lq;
+        sp = mfma_k16(lds4(&sC[16 * tt + li][k0]), lds4(&sB[16 * ts + li][k0]), sp);
       }
       float(*dst)[QQ] = kh == 0 ? sDS : sE;
 #pragma unroll
       for (int e = 0; e < 4; ++e) dst[16 * tt + 4 * lq + e][16 * ts + li] = sp[e];
     }
     f32x4 yo = {}, hb = {};
-    {
-      f32x4 y1 = {}, h1 = {};
-#pragma unroll 4
-      for (int m = 0; m < BN / 4; m += 2) {
-        yo = mfma4(sC[16 * ty + li][4 * m + lq], sH[pcol][4 * m + lq], yo);
-        y1 = mfma4(sC[16 * ty + li][4 * m + 4 + lq], sH[pcol][4 * m + 4 + lq], y1);
-        hb = mfma4(sB[16 * ty + li][4 * m + lq], sDH[pcol][4 * m + lq], hb);
-        h1 = mfma4(sB[16 * ty + li][4 * m + 4 + lq], sDH[pcol][4 * m + 4 + lq], h1);
+#pragma unroll 2
+    for (int j = 0; j < BN / 16; ++j) {
+      const int k0 = 16 * j + 4 * lq;
+      const f32x4 c4 = lds4(&sC[16 * ty + li][k0]), h4 = lds4(&sH[pcol][k0]);
+      const f32x4 b4 = lds4(&sB[16 * ty + li][k0]), d4 = lds4(&sDH[pcol][k0]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        yo = mfma4(c4[e], h4[e], yo);
+        hb = mfma4(b4[e], d4[e], hb);
       }
-      yo += y1;
-      hb += h1;
     }
     {
       float hh = 0.f;
@@ -441,11 +454,20 @@ __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
       const int ta = 16 * ty + li;   // the A operand's row t
       const float lam_a = sLam[ta];
 #pragma unroll
-      for (int m = 0; m < BQ / 4; ++m) {
-        const int s = 4 * m + lq;
-        const float sx = s <= ta ? (sDS[ta][s] + sE[ta][s]) * __expf(lam_a - sLam[s]) : 0.f;
-        if (py == 0) sSX[ta][s] = sx;
-        yv = mfma4(sx * sDel[s], sX[s][pcol], yv);
+      for (int j = 0; j < BQ / 16; ++j) {
+        const int s0 = 16 * j + 4 * lq;
+        const f32x4 p0 = lds4(&sDS[ta][s0]), p1 = lds4(&sE[ta][s0]);
+        const f32x4 l4 = lds4(&sLam[s0]), d4 = lds4(&sDel[s0]);
+        float xb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xb[e] = sX[s0 + e][pcol];
+        f32x4 sx;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sx[e] = s0 + e <= ta ? (p0[e] + p1[e]) * __expf(lam_a - l4[e]) : 0.f;
+        if (py == 0) *reinterpret_cast<f32x4*>(&sSX[ta][s0]) = sx;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) yv = mfma4(sx[e] * d4[e], xb[e], yv);
       }
       float dl[4], dw[4];
 #pragma unroll
@@ -487,9 +509,11 @@ __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
       const int tsel = w - 5;
       const int tt = tsel == 0 ? 0 : 1, ts = tsel == 2 ? 1 : 0;
       f32x4 dm = {};
-#pragma unroll 4
-      for (int m = 0; m < BP / 4; ++m)
-        dm = mfma4(sDY[16 * tt + li][4 * m + lq], sX[16 * ts + li][4 * m + lq], dm);
+#pragma unroll
+      for (int j = 0; j < BP / 16; ++j) {
+        const int k0 = 16 * j + 4 * lq;
+        dm = mfma_k16(lds4(&sDY[16 * tt + li][k0]), lds4(&sX[16 * ts + li][k0]), dm);
+      }
       const int s = 16 * ts + li;
       const float lam_s = sLam[s], del_s = sDel[s];
       float rowp[4], colp = 0.f;
@@ -524,15 +548,26 @@ __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
       }
     }
     f32x4 dc[2] = {}, db[2] = {};
-#pragma unroll 4
-    for (int m = 0; m < BP / 4; ++m) {
-      const float ay = sDY[16 * ty + li][4 * m + lq];   // dC += dY H_in
-      const float ax = sX[16 * ty + li][4 * m + lq];    // dB += X dH_out
+#pragma unroll 2
+    for (int j = 0; j < BP / 16; ++j) {
+      const int k0 = 16 * j + 4 * lq;
+      const f32x4 ay = lds4(&sDY[16 * ty + li][k0]);   // dC += dY H_in
+      const f32x4 ax = lds4(&sX[16 * ty + li][k0]);    // dB += X dH_out
+      float bh[4][2], bd[4][2];
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        dc[k] = mfma4(ay, sH[4 * m + lq][16 * (nb + k) + li], dc[k]);
-        db[k] = mfma4(ax, sDH[4 * m + lq][16 * (nb + k) + li], db[k]);
-      }
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          bh[e][k] = sH[k0 + e][16 * (nb + k) + li];
+          bd[e][k] = sDH[k0 + e][16 * (nb + k) + li];
+        }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          dc[k] = mfma4(ay[e], bh[e][k], dc[k]);
+          db[k] = mfma4(ax[e], bd[e][k], db[k]);
+        }
     }
     {
       // dx_t = D dy_t + w_t HB_t + sum_u M_ut dy_u, in the [t][p] tile
@@ -545,9 +580,16 @@ __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
       const int ta = 16 * ty + li;
       const float del_a = sDel[ta];
 #pragma unroll
-      for (int m = 0; m < BQ / 4; ++m) {
-        const int u = 4 * m + lq;
-        dx = mfma4(sSX[u][ta] * del_a, sDY[u][pcol], dx);
+      for (int j = 0; j < BQ / 16; ++j) {
+        const int u0 = 16 * j + 4 * lq;
+        float am[4], by[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          am[e] = sSX[u0 + e][ta];
+          by[e] = sDY[u0 + e][pcol];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dx = mfma4(am[e] * del_a, by[e], dx);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -558,12 +600,21 @@ __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
     // dH_in = e^lam_last dH_out + sum_t e^lam_t dy_t C_t^T
 #pragma unroll
     for (int j = 0; j < 4; ++j) dh[j] *= gam;
-#pragma unroll 4
-    for (int m = 0; m < BQ / 4; ++m) {
-      const int t = 4 * m + lq;
-      const float ay = sDY[t][16 * hp + li] * sEl[t];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dh[j] = mfma4(ay, sC[t][16 * (hn + j) + li], dh[j]);
+    for (int jg = 0; jg < BQ / 16; ++jg) {
+      const int t0g = 16 * jg + 4 * lq;
+      const f32x4 el4 = lds4(&sEl[t0g]);
+      float ay[4], bc[4][4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ay[e] = sDY[t0g + e][16 * hp + li] * el4[e];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bc[e][j] = sC[t0g + e][16 * (hn + j) + li];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dh[j] = mfma4(ay[e], bc[e][j], dh[j]);
     }
     __syncthreads();  // B4
 
@@ -581,15 +632,27 @@ __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
           db[k][e] *= ws;
         }
       }
-#pragma unroll 4
-      for (int m = 0; m < BQ / 4; ++m) {
-        const float as = sDS[16 * ty + li][4 * m + lq];   // dC_t += dS_ts B_s
-        const float at = sDS[4 * m + lq][16 * ty + li];   // dB_t += dS_st C_s
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          dc[k] = mfma4(as, sB[4 * m + lq][16 * (nb + k) + li], dc[k]);
-          db[k] = mfma4(at, sC[4 * m + lq][16 * (nb + k) + li], db[k]);
+      for (int j = 0; j < BQ / 16; ++j) {
+        const int s0 = 16 * j + 4 * lq;
+        const f32x4 as = lds4(&sDS[16 * ty + li][s0]);   // dC_t += dS_ts B_s
+        float at[4], bb[4][2], bc[4][2];                 // dB_t += dS_st C_s
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          at[e] = sDS[s0 + e][16 * ty + li];
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            bb[e][k] = sB[s0 + e][16 * (nb + k) + li];
+            bc[e][k] = sC[s0 + e][16 * (nb + k) + li];
+          }
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            dc[k] = mfma4(as[e], bb[e][k], dc[k]);
+            db[k] = mfma4(at[e], bc[e][k], db[k]);
+          }
       }
       float* dcp = a.dCh + (((int64_t)b * H + h) * L + t0) * BN;
       float* dbp = a.dBh + (((int64_t)b * H + h) * L + t0) * BN;
