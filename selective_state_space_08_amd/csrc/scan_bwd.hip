@@ -27,12 +27,9 @@ constexpr int BQ = 32;    // tokens per chunk
 constexpr int BP = 64;    // head dim
 constexpr int BN = 128;   // state dim
 constexpr int BT = 256;   // threads
-// LDS row pitches: rows of B, C, H differ by 4 banks, rows of x, dy by 4
-// banks, so that 8 consecutive lanes reading 8 consecutive rows at one
-// column use distinct banks
-constexpr int PN = BN + 4;
-constexpr int PP = BP + 4;
-// pitches of the reverse walker's LDS tiles (12 mod 64 floats)
+// LDS pitches of the [.][n], [.][p] and [.][s] tiles: 12 mod 64 floats, so
+// that 16 lanes reading 16 rows at one column, or 16 columns of one row,
+// hit distinct banks
 constexpr int QN = BN + 12;
 constexpr int QP = BP + 12;
 constexpr int QQ = BQ + 12;
@@ -73,126 +70,6 @@ __device__ __forceinline__ float delta_of(const BwdArgs& a, int64_t row, int h, 
   return a.dt_softplus ? softplus_f32(v) : v;
 }
 
-// ---------------------------------------------------------------- states
-
-// The state entering each chunk, for every (b, h): states[b][h][c] = H before
-// chunk c.  Thread tid owns the float4s tid + BT j (j < 8) of the [P][N]
-// state, so that its stores to HBM are coalesced: p = tid / 32 + 8 j,
-// n = 4 (tid % 32) .. + 3.  The next chunk's x, B and dt are loaded into
-// registers while this chunk is applied.
-template <typename Ta>
-__global__ __launch_bounds__(BT) void fwd_states_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) float sX[BQ][PP];
-  __shared__ __attribute__((aligned(16))) float sB[BQ][PN];
-  __shared__ float sW[BQ];
-  __shared__ float sGam;
-  const int H = a.nheads, G = a.ngroups, L = a.seqlen;
-  const int b = blockIdx.x / H, h = blockIdx.x % H, g = h / (H / G);
-  const int HP = H * BP;
-  const int tid = threadIdx.x;
-  const int pr = tid >> 5, n0 = 4 * (tid & 31);
-  float4 hr[8];
-  {
-    const float* h0 = a.h0 ? a.h0 + ((int64_t)b * H + h) * BP * BN : nullptr;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      hr[j] = h0 ? *reinterpret_cast<const float4*>(h0 + (pr + 8 * j) * BN + n0)
-                 : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  const float Ah = a.A[h];
-  // staging: x as 2 float4s per thread (t = tid / 16 + 16 k, p4 = 4 (tid % 16)),
-  // B as 4 float4s (t = tid / 32 + 8 k, n4 = 4 (tid % 32)), and dt (tid < 32)
-  float4 px[2], pb[4];
-  float pdv = 0.f, pd = 0.f;
-  auto fetch = [&](int c) {
-    const int t0 = c * BQ, Lc = min(BQ, L - t0);
-    const int64_t row0 = (int64_t)b * L + t0;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int t = (tid >> 4) + 16 * k;
-      px[k] = t < Lc ? *reinterpret_cast<const float4*>(a.post + (row0 + t) * a.cdim + h * BP + 4 * (tid & 15))
-                     : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int t = (tid >> 5) + 8 * k;
-      pb[k] = t < Lc ? *reinterpret_cast<const float4*>(a.post + (row0 + t) * a.cdim + HP + g * BN + n0)
-                     : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    if (tid < BQ) pd = delta_of<Ta>(a, row0 + tid, h, tid < Lc, pdv);
-  };
-  if (a.nc > 0) fetch(0);
-  for (int c = 0; c < a.nc; ++c) {
-    const int t0 = c * BQ, Lc = min(BQ, L - t0);
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-      *reinterpret_cast<float4*>(&sX[(tid >> 4) + 16 * k][4 * (tid & 15)]) = px[k];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) *reinterpret_cast<float4*>(&sB[(tid >> 5) + 8 * k][n0]) = pb[k];
-    if (tid < 64) {
-      const float d = tid < BQ ? pd : 0.f;
-      float lam = d * Ah;
-      for (int o = 1; o < 32; o <<= 1) {
-        const float u = __shfl_up(lam, o, 64);
-        if ((tid & 31) >= o) lam += u;
-      }
-      const float last = __shfl(lam, Lc - 1, 64);
-      if (tid < BQ) sW[tid] = __expf(last - lam) * d;
-      if (tid == 0) sGam = __expf(last);
-    }
-    __syncthreads();
-    if (c + 1 < a.nc) fetch(c + 1);
-    float* st = a.states + (((int64_t)b * H + h) * a.nc + c) * BP * BN;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) *reinterpret_cast<float4*>(st + (pr + 8 * j) * BN + n0) = hr[j];
-    const float gam = sGam;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      hr[j].x *= gam; hr[j].y *= gam; hr[j].z *= gam; hr[j].w *= gam;
-    }
-#pragma unroll 4
-    for (int s = 0; s < BQ; ++s) {
-      const float ws = sW[s];
-      const float4 bv = *reinterpret_cast<const float4*>(&sB[s][n0]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float xs = sX[s][pr + 8 * j] * ws;
-        hr[j].x = fmaf(xs, bv.x, hr[j].x);
-        hr[j].y = fmaf(xs, bv.y, hr[j].y);
-        hr[j].z = fmaf(xs, bv.z, hr[j].z);
-        hr[j].w = fmaf(xs, bv.w, hr[j].w);
-      }
-    }
-    __syncthreads();
-  }
-}
-
-// ---------------------------------------------------------------- backward
-
-// Block sum of one value per thread (fixed order), returned to every thread.
-template <int NW>
-__device__ __forceinline__ float block_sum(float v, float* sred) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sred[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) s += sred[i];
-  return s;
-}
-
-constexpr int WT = 512;  // threads of the reverse walker: 8 waves, two per SIMD
-
-// Sum over the 16 lanes of a token group (lanes 16 k .. 16 k + 15).
-__device__ __forceinline__ float sum16(float v) {
-  v += __shfl_xor(v, 1, 64);
-  v += __shfl_xor(v, 2, 64);
-  v += __shfl_xor(v, 4, 64);
-  v += __shfl_xor(v, 8, 64);
-  return v;
-}
-
 // D = A B + D for one 16x16 fp32 tile and K = 4 on the matrix cores.  Lane
 // l = i + 16 q holds A[i][q] and B[q][i] and ends with D[4 q + r][i], r < 4.
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
@@ -225,6 +102,133 @@ template <> struct RawS<float> {
   __device__ __forceinline__ void load(const float* p) { f = *p; }
   __device__ __forceinline__ float get() const { return f; }
 };
+
+// ---------------------------------------------------------------- states
+
+// The state entering each chunk, for every (b, h): states[b][h][c] = H before
+// chunk c, with H <- e^lam_last H + (x o w)^T B per chunk on the fp32 matrix
+// cores.  4 waves; wave w holds the [p][n] tiles (w, 0..7) of the state in
+// accumulator registers (lane l = i + 16 q: p = 16 w + 4 q + r,
+// n = 16 nt + i).  x and B are staged transposed ([p][s], [n][s]) so that
+// each lane reads 4 consecutive s as one float4.  The next chunk's x, B and
+// dt are loaded into registers (unconditionally; rows past the end of the
+// sequence are zeroed when staged) while this chunk is applied.
+template <typename Ta>
+__global__ __launch_bounds__(BT) void fwd_states_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) float sXT[BP][QQ];
+  __shared__ __attribute__((aligned(16))) float sBT[BN][QQ];
+  __shared__ __attribute__((aligned(16))) float sW[BQ];
+  __shared__ float sGam;
+  const int H = a.nheads, G = a.ngroups, L = a.seqlen;
+  const int b = blockIdx.x / H, h = blockIdx.x % H, g = h / (H / G);
+  const int HP = H * BP;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lq = lane >> 4;
+  f32x4 hs[8];
+  {
+    const float* h0 = a.h0 ? a.h0 + ((int64_t)b * H + h) * BP * BN : nullptr;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        hs[nt][e] = h0 ? h0[(16 * w + 4 * lq + e) * BN + 16 * nt + li] : 0.f;
+  }
+  const float Ah = a.A[h];
+  const float dtb = a.dt_bias ? a.dt_bias[h] : 0.f;
+  // staging: x as 2 float4s per thread (t = tid / 16 + 16 k, p4 = 4 (tid % 16)),
+  // B as 4 float4s (t = tid / 32 + 8 k, n4 = 4 (tid % 32)), dt (lane t % 32)
+  const int xt = tid >> 4, p4 = 4 * (tid & 15), bt = tid >> 5, n4 = 4 * (tid & 31);
+  f32x4 px0, px1, pb0, pb1, pb2, pb3;
+  RawS<Ta> pdt;
+  auto fetch = [&](int c) {
+    const int t0 = c * BQ, Lc = min(BQ, L - t0);
+    const int64_t row0 = (int64_t)b * L + t0;
+    auto row = [&](int t) { return a.post + (row0 + min(t, Lc - 1)) * a.cdim; };
+    px0 = *reinterpret_cast<const f32x4*>(row(xt) + h * BP + p4);
+    px1 = *reinterpret_cast<const f32x4*>(row(xt + 16) + h * BP + p4);
+    pb0 = *reinterpret_cast<const f32x4*>(row(bt) + HP + g * BN + n4);
+    pb1 = *reinterpret_cast<const f32x4*>(row(bt + 8) + HP + g * BN + n4);
+    pb2 = *reinterpret_cast<const f32x4*>(row(bt + 16) + HP + g * BN + n4);
+    pb3 = *reinterpret_cast<const f32x4*>(row(bt + 24) + HP + g * BN + n4);
+    pdt.load(static_cast<const Ta*>(a.dt) + (row0 + min(tid & 31, Lc - 1)) * a.dt_stride + h);
+  };
+  if (a.nc > 0) fetch(0);
+  for (int c = 0; c < a.nc; ++c) {
+    const int t0 = c * BQ, Lc = min(BQ, L - t0);
+    {
+      auto put = [&](float (*dst)[QQ], int r0, int t, f32x4 v) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[r0 + e][t] = t < Lc ? v[e] : 0.f;
+      };
+      put(sXT, p4, xt, px0);
+      put(sXT, p4, xt + 16, px1);
+      put(sBT, n4, bt, pb0);
+      put(sBT, n4, bt + 8, pb1);
+      put(sBT, n4, bt + 16, pb2);
+      put(sBT, n4, bt + 24, pb3);
+    }
+    if (w == 0) {
+      const int t = lane & 31;
+      const bool real = lane < BQ && t < Lc;
+      const float v = pdt.get() + dtb;
+      float d = a.dt_softplus ? softplus_f32(v) : v;
+      if (!real) d = 0.f;
+      float lam = d * Ah;
+      for (int o = 1; o < 32; o <<= 1) {
+        const float u = __shfl_up(lam, o, 64);
+        if (t >= o) lam += u;
+      }
+      const float last = __shfl(lam, Lc - 1, 64);
+      if (lane < BQ) sW[t] = __expf(last - lam) * d;
+      if (lane == 0) sGam = __expf(last);
+    }
+    __syncthreads();
+    if (c + 1 < a.nc) fetch(c + 1);
+    float* st = a.states + (((int64_t)b * H + h) * a.nc + c) * BP * BN;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st[(16 * w + 4 * lq + e) * BN + 16 * nt + li] = hs[nt][e];
+    const float gam = sGam;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) hs[nt] *= gam;
+#pragma unroll
+    for (int gq = 0; gq < BQ / 16; ++gq) {
+      const int s0 = 16 * gq + 4 * lq;
+      const f32x4 a4 = lds4(&sXT[16 * w + li][s0]) * lds4(&sW[s0]);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) hs[nt] = mfma_k16(a4, lds4(&sBT[16 * nt + li][s0]), hs[nt]);
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- backward
+
+// Block sum of one value per thread (fixed order), returned to every thread.
+template <int NW>
+__device__ __forceinline__ float block_sum(float v, float* sred) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sred[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) s += sred[i];
+  return s;
+}
+
+constexpr int WT = 512;  // threads of the reverse walker: 8 waves, two per SIMD
+
+// Sum over the 16 lanes of a token group (lanes 16 k .. 16 k + 15).
+__device__ __forceinline__ float sum16(float v) {
+  v += __shfl_xor(v, 1, 64);
+  v += __shfl_xor(v, 2, 64);
+  v += __shfl_xor(v, 4, 64);
+  v += __shfl_xor(v, 8, 64);
+  return v;
+}
 
 // One chunk's x, B, C (post-conv rows), the state entering it and dt, in
 // registers: thread tid holds the float4 tid of x [t][p], the float4s
