@@ -39,7 +39,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 template <typename T> __device__ __forceinline__ float ld(const T* p) { return to_f32(*p); }
 
 __device__ __forceinline__ float silu_grad_f32(float u) {
-  const float sg = 1.f / (1.f + __expf(-u));
+  const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-u));
   return sg * (1.f + u * (1.f - sg));
 }
 
@@ -221,12 +221,21 @@ __device__ __forceinline__ float block_sum(float v, float* sred) {
 
 constexpr int WT = 512;  // threads of the reverse walker: 8 waves, two per SIMD
 
-// Sum over the 16 lanes of a token group (lanes 16 k .. 16 k + 15).
-__device__ __forceinline__ float sum16(float v) {
-  v += __shfl_xor(v, 1, 64);
-  v += __shfl_xor(v, 2, 64);
-  v += __shfl_xor(v, 4, 64);
-  v += __shfl_xor(v, 8, 64);
+// v moved across lanes by the DPP control CTRL within each row of 16 lanes
+// (lanes whose source is outside the row read 0)
+template <int CTRL>
+__device__ __forceinline__ float dpp_row_or0(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the 16 lanes of a row (lanes 16 k .. 16 k + 15) by DPP row shifts
+// (1, 2, 4, 8: an inclusive prefix sum), in registers; complete in the row's
+// last lane (16 k + 15), in a fixed order.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_row_or0<0x111>(v);
+  v += dpp_row_or0<0x112>(v);
+  v += dpp_row_or0<0x114>(v);
+  v += dpp_row_or0<0x118>(v);
   return v;
 }
 
@@ -365,11 +374,13 @@ __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
   auto fetch_gate = [&](int c) {
     const int t0 = c * BQ, Lc = min(BQ, L - t0);
     const int64_t row0 = (int64_t)b * L + t0;
+    const Td* dob = static_cast<const Td*>(a.dout) + row0 * a.dout_stride + h * BP + pcol;
+    const Ta* zb = a.z ? static_cast<const Ta*>(a.z) + row0 * a.z_stride + h * BP + pcol : nullptr;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int t = min(16 * ty + 4 * lq + e, Lc - 1);  // (rows past the end: never used)
-      pdo[e].load(static_cast<const Td*>(a.dout) + (row0 + t) * a.dout_stride + h * BP + pcol);
-      if (a.z) pz[e].load(static_cast<const Ta*>(a.z) + (row0 + t) * a.z_stride + h * BP + pcol);
+      pdo[e].load(dob + (int64_t)t * a.dout_stride);
+      if (a.z) pz[e].load(zb + (int64_t)t * a.z_stride);
     }
   };
   if (a.nc > 0) {
@@ -451,6 +462,8 @@ __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
     // ---- P2: M = (S o exp) delta (this wave's rows, written once to sSX),
     //      y = Yoff + M X + D x, the gate and its gradient; dw partials
     {
+      // dz of this lane's column p at token t: dzrow[t * H * P]
+      float* dzrow = a.dz ? a.dz + (row0 * H + h) * BP + pcol : nullptr;
       // e^lam_t Yoff, the inter-chunk part of y (also for the gradient of lam)
 #pragma unroll
       for (int e = 0; e < 4; ++e) yo[e] *= sEl[16 * ty + 4 * lq + e];
@@ -486,17 +499,17 @@ __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
           if (a.z) {
             const float zz = pz[e].get();
             dyv = dout * silu_f32(zz);
-            if (a.dz) a.dz[((row0 + t) * H + h) * BP + pcol] = dout * y * silu_grad_f32(zz);
+            if (a.dz) dzrow[(int64_t)t * (H * BP)] = dout * y * silu_grad_f32(zz);
           } else {
             dyv = dout;
           }
         }
         sDY[t][pcol] = dyv;
         dD_part = fmaf(dyv, xv, dD_part);
-        dl[e] = sum16(dyv * yo[e]);
-        dw[e] = sum16(xv * hb[e]);
+        dl[e] = row_sum16(dyv * yo[e]);
+        dw[e] = row_sum16(xv * hb[e]);
       }
-      if (li == 0) {
+      if (li == 15) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           sDLp[py][16 * ty + 4 * lq + e] = dl[e];
@@ -529,12 +542,12 @@ __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
         const float ee = dm[e] * sSX[t][s];  // (0 above the diagonal)
         sDS[t][s] = ok ? ds : 0.f;
         sE[t][s] = ee;
-        rowp[e] = sum16(ee * del_s);
+        rowp[e] = row_sum16(ee * del_s);
         colp += ee;
       }
       colp += __shfl_xor(colp, 16, 64);
       colp += __shfl_xor(colp, 32, 64);
-      if (li == 0) {
+      if (li == 15) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) sRowP[ts][16 * tt + 4 * lq + e] = rowp[e];
       }
@@ -700,7 +713,7 @@ __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
       const float ddel = cole + (real ? dw * __expf(lam_last - lam) : 0.f) + Ah * suf;
       if (real) {
         dA_part = fmaf(del, suf, dA_part);
-        const float sg = a.dt_softplus ? 1.f / (1.f + __expf(-sV[t])) : 1.f;
+        const float sg = a.dt_softplus ? __builtin_amdgcn_rcpf(1.f + __expf(-sV[t])) : 1.f;
         const float dd = ddel * sg;
         if (t < Lc) {
           a.ddt[(row0 + t) * H + h] = dd;
