@@ -141,6 +141,7 @@ def time_prefill(args, wl, torch, layer, synth, dev, dev32):
 
 
 def time_decode(args, wl, torch, layer, synth, dev, dev32):
+    from selective_state_space_08_amd import ssd
     T = args.decode_steps
     log("decode %s: generating %d steps of inputs" % (wl.name, T))
     inp = synth.make_decode(wl)
@@ -160,11 +161,14 @@ def time_decode(args, wl, torch, layer, synth, dev, dev32):
     ring0 = dev(inp.ring, "bf16")
     st, ring = st0.clone(), ring0.clone()
     y = torch.empty((T, wl.batch, wl.d_inner), device="cuda")
+    ws = torch.empty(ssd.ssd_state_update_workspace_bytes(wl.batch, wl.nheads, wl.headdim,
+                                                          wl.ngroups, wl.dstate),
+                     dtype=torch.uint8, device="cuda")
     log("decode: inputs resident (%.1f GB)" % ((xbc.numel() + z.numel()) * 2 / 1e9))
 
     def chain(n):
         for t in range(n):
-            layer.decode_step(st, xbc[t], dt[t], z[t], ring, p, y=y[t])
+            layer.decode_step(st, xbc[t], dt[t], z[t], ring, p, y=y[t], workspace=ws)
 
     chain(min(T, 20))
     torch.cuda.synchronize()
@@ -175,7 +179,7 @@ def time_decode(args, wl, torch, layer, synth, dev, dev32):
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(T + 1)]
     marks[0].record(stream)
     for t in range(T):
-        layer.decode_step(st, xbc[t], dt[t], z[t], ring, p, y=y[t])
+        layer.decode_step(st, xbc[t], dt[t], z[t], ring, p, y=y[t], workspace=ws)
         marks[t + 1].record(stream)
     torch.cuda.synchronize()
     total_ms = marks[0].elapsed_time(marks[T])
@@ -440,7 +444,7 @@ def main():
                                       "traffic": traffic_record(
                                           "decode_state_update",
                                           src_hash("state_update.hip", "api.hip")),
-                                      "kernel": "state_update_kernel",
+                                      "kernel": "conv_step_kernel + state_stream_kernel",
                                       "measured_peak": copy_gbs,
                                       "frac_of_measured": dach / copy_gbs,
                                       "alg_bytes_per_step": dbytes}}

@@ -167,7 +167,7 @@ int ssd_chunk_scan_fwd(const void* x, int64_t x_tok_stride, const void* Bm,
  *   dt [B, H] act_dtype;  z [B, H*P] act_dtype or NULL
  *   A, D, dt_bias, dt_softplus as in ssd_chunk_scan_fwd
  *   y [B, H*P] y_dtype; must not overlap any input
- *   Supported: P = 64, N = 128, H % G == 0.
+ *   Supported: P = 64, N = 128, H % G == 0, B <= 65535.
  */
 int ssd_state_update(float* state, const void* xbc, ssd_dtype_t xbc_dtype,
                      void* conv_state, const float* conv_w, const float* conv_b,
@@ -175,6 +175,33 @@ int ssd_state_update(float* state, const void* xbc, ssd_dtype_t xbc_dtype,
                      const float* A, const float* D, const float* dt_bias, int dt_softplus,
                      void* y, ssd_dtype_t y_dtype, int batch, int nheads, int headdim,
                      int ngroups, int dstate, hipStream_t stream);
+
+/* Bytes of device workspace ssd_state_update_ws needs: the post-conv x|B|C of
+ * the step in fp32, 4 * batch * Cdim (0 on bad input or batch 0). */
+size_t ssd_state_update_workspace_bytes(int batch, int nheads, int headdim, int ngroups,
+                                        int dstate);
+
+/*
+ * The same decode step as ssd_state_update, with the same arguments, results
+ * and in-place updates, taken in two passes through a caller-provided
+ * workspace: the conv step of every channel (writing the post-conv x|B|C to
+ * the workspace and shifting the ring), then the state update and readout
+ * with many small workgroups, which streams the state through HBM faster.
+ * Results agree with ssd_state_update up to the order of the fp32 sum in
+ * y = h C (each path's order is fixed, so each is deterministic).
+ *
+ *   workspace: at least ssd_state_update_workspace_bytes(...) bytes,
+ *   256-byte aligned, overlapping no tensor (may be NULL when batch is 0).
+ *   Its contents on entry are ignored and on return are unspecified.
+ *   Additionally supported: batch * Cdim below 2^31.
+ */
+int ssd_state_update_ws(float* state, const void* xbc, ssd_dtype_t xbc_dtype, void* conv_state,
+                        const float* conv_w, const float* conv_b, int conv_width,
+                        const void* dt, const void* z, ssd_dtype_t act_dtype, const float* A,
+                        const float* D, const float* dt_bias, int dt_softplus, void* y,
+                        ssd_dtype_t y_dtype, int batch, int nheads, int headdim, int ngroups,
+                        int dstate, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
 
 /* Bytes of decode cache per sequence and layer: the fp32 SSM state
  * (4*H*P*N) plus the conv ring ((K-1) * Cdim elements of conv_dtype).

@@ -332,6 +332,71 @@ int ssd_chunk_scan_fwd(const void* x, int64_t x_tok_stride, const void* Bm,
   return e == hipSuccess ? SSD_OK : hip_fail(e, "scan launch");
 }
 
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by both decode entry points; fills the byte ranges
+// of y and of the inputs (state, xbc, conv_state, dt, z) for the workspace
+// check.  `who` prefixes the message.
+int check_state_update(const char* who, float* state, const void* xbc, ssd_dtype_t xbc_dtype,
+                       void* conv_state, const float* conv_w, const float* conv_b,
+                       int conv_width, const void* dt, const void* z, ssd_dtype_t act_dtype,
+                       const float* A, int dt_softplus, void* y, ssd_dtype_t y_dtype, int batch,
+                       int nheads, int headdim, int ngroups, int dstate, Range* ry, Range ins[5]) {
+  if (!valid_dtype(xbc_dtype) || !valid_dtype(act_dtype) || !valid_dtype(y_dtype))
+    return fail(SSD_ERR_INVALID_ARG, "%s: bad dtype", who);
+  if (batch < 0 || nheads <= 0 || ngroups <= 0 || headdim <= 0 || dstate <= 0)
+    return fail(SSD_ERR_INVALID_ARG, "%s: bad size", who);
+  if (nheads % ngroups != 0)
+    return fail(SSD_ERR_INVALID_ARG, "%s: nheads %d not a multiple of ngroups %d", who,
+                nheads, ngroups);
+  if (dt_softplus != 0 && dt_softplus != 1)
+    return fail(SSD_ERR_INVALID_ARG, "%s: dt_softplus must be 0 or 1", who);
+  if (batch > 65535)  // the batch is the second grid dimension of every launch
+    return fail(SSD_ERR_UNSUPPORTED, "%s: batch %d > 65535", who, batch);
+  if (headdim != kP || dstate != kN)
+    return fail(SSD_ERR_UNSUPPORTED, "%s: headdim %d / dstate %d (supported: 64 / 128)", who,
+                headdim, dstate);
+  if (conv_w == nullptr) {
+    if (conv_state != nullptr || conv_b != nullptr)
+      return fail(SSD_ERR_INVALID_ARG, "%s: conv_state/conv_b given without conv_w", who);
+  } else {
+    if (conv_width < 1) return fail(SSD_ERR_INVALID_ARG, "%s: conv_width < 1", who);
+    if (conv_width > 4) return fail(SSD_ERR_UNSUPPORTED, "%s: conv_width > 4", who);
+    if (conv_width > 1 && conv_state == nullptr)
+      return fail(SSD_ERR_INVALID_ARG, "%s: conv_w given without conv_state", who);
+  }
+  if (batch > 0 && (state == nullptr || xbc == nullptr || dt == nullptr || A == nullptr ||
+                    y == nullptr))
+    return fail(SSD_ERR_INVALID_ARG, "%s: state, xbc, dt, A or y is NULL", who);
+  if (state != nullptr && !aligned(state, 16))
+    return fail(SSD_ERR_INVALID_ARG, "%s: state is not 16-byte aligned", who);
+  const int64_t HP = (int64_t)nheads * kP, cdim = HP + 2 * (int64_t)ngroups * kN;
+  const size_t xe = esize(xbc_dtype), ae = esize(act_dtype), ye = esize(y_dtype);
+  *ry = dense_range(y, (int64_t)batch * HP, ye);
+  ins[0] = dense_range(state, (int64_t)batch * nheads * kP * kN, 4);
+  ins[1] = dense_range(xbc, (int64_t)batch * cdim, xe);
+  ins[2] = dense_range(conv_state, conv_w ? (int64_t)batch * (conv_width - 1) * cdim : 0, xe);
+  ins[3] = dense_range(dt, (int64_t)batch * nheads, ae);
+  ins[4] = dense_range(z, (int64_t)batch * HP, ae);
+  for (int i = 0; i < 5; ++i) {
+    const Range& r = ins[i];
+    if (overlap(*ry, r)) return fail(SSD_ERR_INVALID_ARG, "%s: y overlaps an input", who);
+  }
+  for (int i = 1; i < 5; ++i)
+    if (overlap(ins[0], ins[i]))
+      return fail(SSD_ERR_INVALID_ARG, "%s: state overlaps another tensor", who);
+  for (int i = 0; i < 5; ++i)
+    if (i != 2 && overlap(ins[2], ins[i]))
+      return fail(SSD_ERR_INVALID_ARG, "%s: conv_state overlaps another tensor", who);
+  return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int ssd_state_update(float* state, const void* xbc, ssd_dtype_t xbc_dtype, void* conv_state,
                      const float* conv_w, const float* conv_b, int conv_width, const void* dt,
                      const void* z, ssd_dtype_t act_dtype, const float* A, const float* D,
@@ -339,53 +404,60 @@ int ssd_state_update(float* state, const void* xbc, ssd_dtype_t xbc_dtype, void*
                      int batch, int nheads, int headdim, int ngroups, int dstate,
                      hipStream_t stream) {
   g_last_error.clear();
-  if (!valid_dtype(xbc_dtype) || !valid_dtype(act_dtype) || !valid_dtype(y_dtype))
-    return fail(SSD_ERR_INVALID_ARG, "state_update: bad dtype");
-  if (batch < 0 || nheads <= 0 || ngroups <= 0 || headdim <= 0 || dstate <= 0)
-    return fail(SSD_ERR_INVALID_ARG, "state_update: bad size");
-  if (nheads % ngroups != 0)
-    return fail(SSD_ERR_INVALID_ARG, "state_update: nheads %d not a multiple of ngroups %d",
-                nheads, ngroups);
-  if (dt_softplus != 0 && dt_softplus != 1)
-    return fail(SSD_ERR_INVALID_ARG, "state_update: dt_softplus must be 0 or 1");
-  if (headdim != kP || dstate != kN)
-    return fail(SSD_ERR_UNSUPPORTED, "state_update: headdim %d / dstate %d (supported: 64 / 128)",
-                headdim, dstate);
-  if (conv_w == nullptr) {
-    if (conv_state != nullptr || conv_b != nullptr)
-      return fail(SSD_ERR_INVALID_ARG, "state_update: conv_state/conv_b given without conv_w");
-  } else {
-    if (conv_width < 1) return fail(SSD_ERR_INVALID_ARG, "state_update: conv_width < 1");
-    if (conv_width > 4) return fail(SSD_ERR_UNSUPPORTED, "state_update: conv_width > 4");
-    if (conv_width > 1 && conv_state == nullptr)
-      return fail(SSD_ERR_INVALID_ARG, "state_update: conv_w given without conv_state");
-  }
-  if (batch > 0 && (state == nullptr || xbc == nullptr || dt == nullptr || A == nullptr ||
-                    y == nullptr))
-    return fail(SSD_ERR_INVALID_ARG, "state_update: state, xbc, dt, A or y is NULL");
-  if (state != nullptr && !aligned(state, 16))
-    return fail(SSD_ERR_INVALID_ARG, "state_update: state is not 16-byte aligned");
-  const int64_t HP = (int64_t)nheads * kP, cdim = HP + 2 * (int64_t)ngroups * kN;
-  const size_t xe = esize(xbc_dtype), ae = esize(act_dtype), ye = esize(y_dtype);
-  const Range ry = dense_range(y, (int64_t)batch * HP, ye);
-  const Range ins[] = {dense_range(state, (int64_t)batch * nheads * kP * kN, 4),
-                       dense_range(xbc, (int64_t)batch * cdim, xe),
-                       dense_range(conv_state, conv_w ? (int64_t)batch * (conv_width - 1) * cdim : 0, xe),
-                       dense_range(dt, (int64_t)batch * nheads, ae),
-                       dense_range(z, (int64_t)batch * HP, ae)};
-  for (const Range& r : ins)
-    if (overlap(ry, r)) return fail(SSD_ERR_INVALID_ARG, "state_update: y overlaps an input");
-  for (int i = 1; i < 5; ++i)
-    if (overlap(ins[0], ins[i]))
-      return fail(SSD_ERR_INVALID_ARG, "state_update: state overlaps another tensor");
-  for (int i = 0; i < 5; ++i)
-    if (i != 2 && overlap(ins[2], ins[i]))
-      return fail(SSD_ERR_INVALID_ARG, "state_update: conv_state overlaps another tensor");
+  Range ry, ins[5];
+  const int st = check_state_update("state_update", state, xbc, xbc_dtype, conv_state, conv_w,
+                                    conv_b, conv_width, dt, z, act_dtype, A, dt_softplus, y,
+                                    y_dtype, batch, nheads, headdim, ngroups, dstate, &ry, ins);
+  if (st != SSD_OK) return st;
   if (batch == 0) return SSD_OK;
   hipError_t e = launch_state_update(state, xbc, xbc_dtype, conv_state, conv_w, conv_b,
                                      conv_w ? conv_width : 1, dt, z, act_dtype, A, D, dt_bias,
                                      dt_softplus, y, y_dtype, batch, nheads, ngroups, stream);
   return e == hipSuccess ? SSD_OK : hip_fail(e, "state_update launch");
+}
+
+size_t ssd_state_update_workspace_bytes(int batch, int nheads, int headdim, int ngroups,
+                                        int dstate) {
+  if (batch < 0 || nheads <= 0 || ngroups <= 0 || headdim != kP || dstate != kN ||
+      nheads % ngroups != 0)
+    return 0;
+  return 4 * (size_t)batch * ((size_t)nheads * kP + 2 * (size_t)ngroups * kN);
+}
+
+int ssd_state_update_ws(float* state, const void* xbc, ssd_dtype_t xbc_dtype, void* conv_state,
+                        const float* conv_w, const float* conv_b, int conv_width,
+                        const void* dt, const void* z, ssd_dtype_t act_dtype, const float* A,
+                        const float* D, const float* dt_bias, int dt_softplus, void* y,
+                        ssd_dtype_t y_dtype, int batch, int nheads, int headdim, int ngroups,
+                        int dstate, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  g_last_error.clear();
+  Range ry, ins[5];
+  const int st = check_state_update("state_update_ws", state, xbc, xbc_dtype, conv_state,
+                                    conv_w, conv_b, conv_width, dt, z, act_dtype, A, dt_softplus,
+                                    y, y_dtype, batch, nheads, headdim, ngroups, dstate, &ry, ins);
+  if (st != SSD_OK) return st;
+  const int64_t cdim = (int64_t)nheads * kP + 2 * (int64_t)ngroups * kN;
+  if ((int64_t)batch * cdim > ((int64_t)1 << 31) - 256)
+    return fail(SSD_ERR_UNSUPPORTED, "state_update_ws: batch x channels exceeds 2^31");
+  if (batch == 0) return SSD_OK;
+  const size_t need = ssd_state_update_workspace_bytes(batch, nheads, headdim, ngroups, dstate);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(SSD_ERR_WORKSPACE, "state_update_ws: workspace needs %zu bytes, got %zu", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (!aligned(workspace, 256))
+    return fail(SSD_ERR_INVALID_ARG, "state_update_ws: workspace is not 256-byte aligned");
+  const Range rws = dense_range(workspace, (int64_t)need, 1);
+  if (overlap(rws, ry))
+    return fail(SSD_ERR_INVALID_ARG, "state_update_ws: workspace overlaps a tensor");
+  for (int i = 0; i < 5; ++i)
+    if (overlap(rws, ins[i]))
+      return fail(SSD_ERR_INVALID_ARG, "state_update_ws: workspace overlaps a tensor");
+  hipError_t e = launch_state_update_ws(
+      state, xbc, xbc_dtype, conv_state, conv_w, conv_b, conv_w ? conv_width : 1, dt, z,
+      act_dtype, A, D, dt_bias, dt_softplus, y, y_dtype, batch, nheads, ngroups,
+      static_cast<float*>(workspace), stream);
+  return e == hipSuccess ? SSD_OK : hip_fail(e, "state_update_ws launch");
 }
 
 // ------------------------------------------------------------------ backward

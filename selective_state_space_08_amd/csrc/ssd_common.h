@@ -98,6 +98,13 @@ hipError_t launch_state_update(float* state, const void* xbc, ssd_dtype_t xbc_dt
                                const float* A, const float* D, const float* dt_bias,
                                int softplus, void* y, ssd_dtype_t y_dtype, int batch,
                                int nheads, int ngroups, hipStream_t stream);
+// The two-kernel decode step; post must hold batch * Cdim floats.
+hipError_t launch_state_update_ws(float* state, const void* xbc, ssd_dtype_t xbc_dtype,
+                                  void* ring, const float* conv_w, const float* conv_b, int K,
+                                  const void* dt, const void* z, ssd_dtype_t act_dtype,
+                                  const float* A, const float* D, const float* dt_bias,
+                                  int softplus, void* y, ssd_dtype_t y_dtype, int batch,
+                                  int nheads, int ngroups, float* post, hipStream_t stream);
 
 // Everything the backward pass needs (validated by the caller).
 struct ScanBwdLaunch {

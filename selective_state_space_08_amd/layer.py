@@ -7,7 +7,7 @@ Argument marshalling only; the arithmetic is in the library's kernels.
   intermediate and hands views of it to ``ssd_chunk_scan_fwd``; ``fused=True``
   passes the raw x|B|C and the conv weights to ``ssd_chunk_scan_fwd``, which
   convolves inside its prologue.
-* ``decode_step``: one ``ssd_state_update`` call.
+* ``decode_step``: one ``ssd_state_update_ws`` call (or ``ssd_state_update``).
 """
 from __future__ import annotations
 
@@ -69,10 +69,17 @@ def prefill(xbc: torch.Tensor, dt: torch.Tensor, z: Optional[torch.Tensor], p: L
 
 
 def decode_step(state, xbc, dt, z, conv_state, p: LayerParams, *, y=None,
-                y_dtype=torch.float32):
+                y_dtype=torch.float32, workspace=None, fused=False):
     """One token per sequence: state [B,H,P,N] and conv_state [B,K-1,Cdim]
-    are updated in place; returns y [B, H*P]."""
-    return ssd.ssd_state_update(state, xbc, dt, p.A, ngroups=p.ngroups, conv_state=conv_state,
-                                conv_w=p.conv_w, conv_b=p.conv_b, z=z, D=p.D,
-                                dt_bias=p.dt_bias, dt_softplus=p.dt_softplus, y=y,
-                                y_dtype=y_dtype)
+    are updated in place; returns y [B, H*P].  By default the two-kernel step
+    through a workspace (allocated per call when not given); fused=True takes
+    the single-kernel step, which needs none."""
+    if fused:
+        return ssd.ssd_state_update(state, xbc, dt, p.A, ngroups=p.ngroups,
+                                    conv_state=conv_state, conv_w=p.conv_w, conv_b=p.conv_b,
+                                    z=z, D=p.D, dt_bias=p.dt_bias, dt_softplus=p.dt_softplus,
+                                    y=y, y_dtype=y_dtype)
+    return ssd.ssd_state_update_ws(state, xbc, dt, p.A, ngroups=p.ngroups, conv_state=conv_state,
+                                   conv_w=p.conv_w, conv_b=p.conv_b, z=z, D=p.D,
+                                   dt_bias=p.dt_bias, dt_softplus=p.dt_softplus, y=y,
+                                   y_dtype=y_dtype, workspace=workspace)

@@ -32,6 +32,9 @@ SIGNATURES = {
                                 _I, _I, _I, _I, _I, _V, _SZ, _V]),
     "ssd_state_update": (_I, [_V, _V, _I, _V, _V, _V, _I, _V, _V, _I, _V, _V, _V, _I, _V, _I,
                               _I, _I, _I, _I, _I, _V]),
+    "ssd_state_update_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
+    "ssd_state_update_ws": (_I, [_V, _V, _I, _V, _V, _V, _I, _V, _V, _I, _V, _V, _V, _I, _V,
+                                 _I, _I, _I, _I, _I, _I, _V, _SZ, _V]),
     "ssd_decode_cache_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "ssd_chunk_scan_bwd_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "ssd_chunk_scan_bwd": (_I, [_V, _I64, _V, _I64, _V, _I64, _I, _V, _V, _I, _V, _V, _I64, _V,
@@ -207,12 +210,8 @@ def ssd_chunk_scan_fwd(x, Bm, Cm, dt, A, *, D=None, z=None, dt_bias=None, dt_sof
     return y
 
 
-def ssd_state_update(state, xbc, dt, A, *, ngroups, conv_state=None, conv_w=None, conv_b=None,
-                     z=None, D=None, dt_bias=None, dt_softplus=True, y=None,
-                     y_dtype=torch.float32):
-    """One decode step.  state [B, H, P, N] fp32 (in place), xbc [B, Cdim],
-    conv_state [B, K-1, Cdim] (in place), dt [B, H], z [B, H*P] -> y [B, H*P]."""
-    lib = load()
+def _state_update_args(state, xbc, dt, ngroups, conv_state, conv_w, conv_b, z, y, y_dtype):
+    """Shape checks shared by both decode entry points; returns (y, B, H, P, G, N, K)."""
     B, H, P, N = state.shape
     G = ngroups
     cdim = H * P + 2 * G * N
@@ -229,10 +228,46 @@ def ssd_state_update(state, xbc, dt, A, *, ngroups, conv_state=None, conv_w=None
     if y is None:
         y = torch.empty((B, H * P), dtype=y_dtype, device=state.device)
     _dense(y, (B, H * P), "y")
+    return y, B, H, P, G, N, K
+
+
+def ssd_state_update(state, xbc, dt, A, *, ngroups, conv_state=None, conv_w=None, conv_b=None,
+                     z=None, D=None, dt_bias=None, dt_softplus=True, y=None,
+                     y_dtype=torch.float32):
+    """One decode step, one fused kernel.  state [B, H, P, N] fp32 (in place),
+    xbc [B, Cdim], conv_state [B, K-1, Cdim] (in place), dt [B, H],
+    z [B, H*P] -> y [B, H*P]."""
+    lib = load()
+    y, B, H, P, G, N, K = _state_update_args(state, xbc, dt, ngroups, conv_state, conv_w,
+                                             conv_b, z, y, y_dtype)
     _check(lib.ssd_state_update(_p(state), _p(xbc), _dt(xbc), _p(conv_state), _p(conv_w),
                                 _p(conv_b), K, _p(dt), _p(z), _dt(dt), _p(A), _p(D),
                                 _p(dt_bias), int(bool(dt_softplus)), _p(y), _dt(y), B, H, P, G,
                                 N, _stream(state)))
+    return y
+
+
+def ssd_state_update_workspace_bytes(batch, nheads, headdim=64, ngroups=8, dstate=128):
+    return load().ssd_state_update_workspace_bytes(batch, nheads, headdim, ngroups, dstate)
+
+
+def ssd_state_update_ws(state, xbc, dt, A, *, ngroups, conv_state=None, conv_w=None,
+                        conv_b=None, z=None, D=None, dt_bias=None, dt_softplus=True, y=None,
+                        y_dtype=torch.float32, workspace=None):
+    """The same decode step in two kernels through a workspace (allocated
+    here when not given; a uint8 device tensor of at least
+    ssd_state_update_workspace_bytes bytes)."""
+    lib = load()
+    y, B, H, P, G, N, K = _state_update_args(state, xbc, dt, ngroups, conv_state, conv_w,
+                                             conv_b, z, y, y_dtype)
+    need = lib.ssd_state_update_workspace_bytes(B, H, P, G, N)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=state.device)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.ssd_state_update_ws(_p(state), _p(xbc), _dt(xbc), _p(conv_state), _p(conv_w),
+                                   _p(conv_b), K, _p(dt), _p(z), _dt(dt), _p(A), _p(D),
+                                   _p(dt_bias), int(bool(dt_softplus)), _p(y), _dt(y), B, H, P,
+                                   G, N, _p(workspace), wsz, _stream(state)))
     return y
 
 

@@ -236,6 +236,55 @@ def test_state_update_rejects_y_on_state():
     assert update_call(state=s, y=s) == INVALID
 
 
+def update_ws_call(ws=0, wsz=None, **over):
+    f = Fake()
+    a = dict(state=f(), xbc=f(), xd=1, ring=f(), w=f(), cb=None, K=4, dt=f(), z=f(), ad=1, A=f(),
+             D=f(), dtb=f(), sp=1, y=f(), yd=0, B=4, H=16, P=64, G=2, N=128, stream=None)
+    a.update(over)
+    need = ssd.load().ssd_state_update_workspace_bytes(a["B"], a["H"], a["P"], a["G"], a["N"])
+    ptr = f() if ws == 0 else ws
+    return ssd.load().ssd_state_update_ws(
+        *[a[k] for k in ["state", "xbc", "xd", "ring", "w", "cb", "K", "dt", "z", "ad", "A",
+                         "D", "dtb", "sp", "y", "yd", "B", "H", "P", "G", "N"]],
+        ptr, need if wsz is None else wsz, a["stream"])
+
+
+@pytest.mark.parametrize("B,H,G", [(1, 16, 2), (256, 128, 8), (3, 8, 8), (0, 8, 1)])
+def test_state_update_workspace_bytes_closed_form(B, H, G):
+    # one fp32 per post-conv channel of each sequence: H*P x, G*N B, G*N C
+    assert ssd.load().ssd_state_update_workspace_bytes(B, H, 64, G, 128) == \
+        4 * B * (H * 64 + 2 * G * 128)
+
+
+def test_state_update_workspace_bytes_rejects_bad_input():
+    lib = ssd.load()
+    assert lib.ssd_state_update_workspace_bytes(4, 12, 64, 8, 128) == 0   # H % G != 0
+    assert lib.ssd_state_update_workspace_bytes(4, 16, 32, 2, 128) == 0   # P unsupported
+    assert lib.ssd_state_update_workspace_bytes(-1, 16, 64, 2, 128) == 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(P=32), UNSUPPORTED), (dict(G=3), INVALID), (dict(ring=None), INVALID),
+    (dict(w=None), INVALID), (dict(K=5), UNSUPPORTED), (dict(state=None), INVALID),
+    (dict(yd=2), INVALID), (dict(sp=-1), INVALID), (dict(B=70000), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(wsz=1024), WORKSPACE),
+    (dict(ws=ctypes.c_void_p((1 << 41) + 16)), INVALID)])
+def test_state_update_ws_validation(over, status):
+    assert update_ws_call(**over) == status
+    assert ssd.load().ssd_last_error().decode().startswith("state_update_ws")
+
+
+def test_state_update_ws_rejects_workspace_on_a_tensor():
+    f = Fake()
+    s = f()
+    assert update_ws_call(state=s, ws=s) == INVALID
+    assert update_ws_call(y=s, ws=s) == INVALID
+
+
+def test_state_update_rejects_huge_batch():
+    assert update_call(B=70000) == UNSUPPORTED
+
+
 def test_binding_refuses_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(ssd, "_lib", None)
     with pytest.raises(ImportError):
