@@ -380,6 +380,29 @@ def test_state_update_ws_matches_fused_at_full_size():
             assert rel_max_err(st_b.cpu().numpy(), st_a.cpu().numpy()) <= 1e-5
 
 
+@pytest.mark.parametrize("entry", sorted(DECODE_ENTRIES))
+def test_decode_bit_stable(entry):
+    """The same step from the same state, ring and inputs gives the same bytes
+    (y, state and ring) on a second run: no atomics, fixed reduction order."""
+    wl = Workload("d", batch=16, seqlen=1, nheads=128, ngroups=8, dtype="bf16", decode_steps=2,
+                  initial_state=True, seed=37)
+    inp = synth.make_decode(wl)
+    xbc, z, dt = inp.steps(0, 2)
+    say("decode bit-stable %s" % entry)
+    p = params(inp)
+    outs = []
+    for _ in range(2):
+        st = dev32(inp.state)
+        ring = dev(inp.ring, "bf16")
+        ys = [DECODE_ENTRIES[entry](st, dev(xbc[t], "bf16"), dev(dt[t], "bf16"), p.A, ngroups=8,
+                                    conv_state=ring, conv_w=p.conv_w, z=dev(z[t], "bf16"),
+                                    D=p.D, dt_bias=p.dt_bias) for t in range(2)]
+        torch.cuda.synchronize()
+        outs.append((torch.stack(ys).cpu(), st.cpu(), ring.cpu()))
+    for a_, b_ in zip(outs[0], outs[1]):
+        assert torch.equal(a_, b_)
+
+
 def test_decode_equals_prefill_on_gpu():
     """64 one-token steps of ssd_state_update equal one prefill call over the
     same tokens from the same state and conv history (fp32 path)."""
