@@ -281,6 +281,14 @@ def test_state_update_ws_rejects_workspace_on_a_tensor():
     assert update_ws_call(y=s, ws=s) == INVALID
 
 
+def test_state_update_empty_batch_is_a_no_op():
+    # batch 0: nothing to read or write, so NULL tensors and no workspace pass
+    # validation and nothing is launched (no device needed)
+    none = dict(state=None, xbc=None, dt=None, z=None, y=None, A=None, D=None, dtb=None, B=0)
+    assert update_call(**none) == OK
+    assert update_ws_call(ws=None, wsz=0, **none) == OK
+
+
 def test_state_update_rejects_huge_batch():
     assert update_call(B=70000) == UNSUPPORTED
 
