@@ -190,6 +190,15 @@ def time_decode(args, wl, torch, layer, synth, dev, dev32):
     return dict(chain_ms=total_ms, step_ms=total_ms / T, first10_ms=first, last10_ms=last)
 
 
+def bwd_alg_bytes_per_call(wl) -> float:
+    """Bytes a backward call must move at least: raw x|B|C, dt, z and dout in
+    (bf16), dxbc, ddt and dz out (fp32), and the initial-state gradient."""
+    T, H, P, N = wl.tokens, wl.nheads, wl.headdim, wl.dstate
+    reads = 2.0 * T * (wl.cdim + H + 2 * wl.d_inner)
+    writes = 4.0 * T * (wl.cdim + H + wl.d_inner) + 4.0 * wl.batch * H * P * N
+    return reads + writes
+
+
 def bwd_flops_per_token(wl, Q: int = 32) -> float:
     """Flops per token of the backward pass in its chunked form (chunks of Q
     tokens), counting each contraction once (causal ones at half): per head,
@@ -477,8 +486,11 @@ def main():
             "dtype": "f32",
             "roofline": {"bound": "mfma", "achieved": tf_b, "peak": FP32_MFMA_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": tf_b / FP32_MFMA_PEAK_TFLOPS,
-                         "traffic": None, "kernel": "ssd_chunk_scan_bwd call (6 kernels)",
-                         "alg_flops_per_token": fpt_b},
+                         "traffic": traffic_record(
+                             "backward_call", src_hash("scan_bwd.hip", "conv1d.hip", "api.hip")),
+                         "kernel": "ssd_chunk_scan_bwd call (6 kernels)",
+                         "alg_flops_per_token": fpt_b,
+                         "alg_bytes_per_call": bwd_alg_bytes_per_call(wl)},
         }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
