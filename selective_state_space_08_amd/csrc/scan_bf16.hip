@@ -944,17 +944,36 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
 }
 
 // H_in[0] = h0; H_in[k] = exp(log_decay[k-1]) H_in[k-1] + H_loc[k-1], in place:
-// slot k holds H_loc[k-1] on entry and H_in[k] on exit.
-__global__ __launch_bounds__(THREADS) void combine_segments_kernel(ScanArgs a) {
-  const int bh = blockIdx.x;
-  float* slots = a.seg_state + (int64_t)bh * a.nseg * P * N;
+// slot k holds H_loc[k-1] on entry and H_in[k] on exit.  The recurrence is
+// independent per state element: workgroup (bh, part) takes 4 consecutive
+// elements per thread (COMBINE_THREADS * 4 of the head's P*N), and loads
+// the slots of COMBINE_BATCH segments at a time, ahead of the dependent
+// multiply-adds, so that their latencies overlap.
+constexpr int COMBINE_THREADS = 256;
+constexpr int COMBINE_PARTS = P * N / (COMBINE_THREADS * 4);
+constexpr int COMBINE_BATCH = 8;
+__global__ __launch_bounds__(COMBINE_THREADS) void combine_segments_kernel(ScanArgs a) {
+  const int bh = blockIdx.x, part = blockIdx.y;
+  const int64_t i = (int64_t)4 * (part * COMBINE_THREADS + threadIdx.x);
+  f32x4* slots = reinterpret_cast<f32x4*>(a.seg_state + (int64_t)bh * a.nseg * P * N + i);
+  constexpr int64_t SLOT = P * N / 4;  // slot stride in f32x4
   const float* ld = a.seg_logdecay + (int64_t)bh * a.nseg;
-  for (int i = threadIdx.x; i < P * N; i += THREADS) {
-    float carry = a.initial_state ? a.initial_state[(int64_t)bh * P * N + i] : 0.f;
-    slots[i] = carry;
-    for (int k = 1; k < a.nseg; ++k) {
-      carry = __expf(ld[k - 1]) * carry + slots[(int64_t)k * P * N + i];
-      slots[(int64_t)k * P * N + i] = carry;
+  f32x4 carry = {0.f, 0.f, 0.f, 0.f};
+  if (a.initial_state)
+    carry = *reinterpret_cast<const f32x4*>(a.initial_state + (int64_t)bh * P * N + i);
+  slots[0] = carry;
+  for (int k0 = 1; k0 < a.nseg; k0 += COMBINE_BATCH) {
+    const int nb = min(COMBINE_BATCH, a.nseg - k0);
+    f32x4 loc[COMBINE_BATCH];
+#pragma unroll
+    for (int j = 0; j < COMBINE_BATCH; ++j)
+      if (j < nb) loc[j] = slots[(k0 + j) * SLOT];
+#pragma unroll
+    for (int j = 0; j < COMBINE_BATCH; ++j) {
+      if (j < nb) {
+        carry = __expf(ld[k0 + j - 1]) * carry + loc[j];
+        slots[(k0 + j) * SLOT] = carry;
+      }
     }
   }
 }
@@ -969,7 +988,8 @@ hipError_t launch_walkers(const ScanArgs& a, hipStream_t stream) {
   if (a.nseg > 1) {
     hipLaunchKernelGGL((scan_bf16_kernel<Tx, Ta, Ty, XCONV, true>), dim3(BH * (a.nseg - 1)),
                        dim3(THREADS), 0, stream, a);
-    hipLaunchKernelGGL(combine_segments_kernel, dim3(BH), dim3(THREADS), 0, stream, a);
+    hipLaunchKernelGGL(combine_segments_kernel, dim3(BH, COMBINE_PARTS), dim3(COMBINE_THREADS), 0,
+                       stream, a);
   }
   hipLaunchKernelGGL((scan_bf16_kernel<Tx, Ta, Ty, XCONV, false>), dim3(BH * a.nseg),
                      dim3(THREADS), 0, stream, a);
