@@ -100,6 +100,40 @@ def test_scan_post_conv(math_mode, B, L, H, G):
 
 
 @pytest.mark.parametrize("math_mode", ["f32", "bf16"])
+@pytest.mark.parametrize("xd,ad,yd", [("bf16", "f32", "f32"), ("f32", "bf16", "bf16"),
+                                      ("bf16", "bf16", "bf16")])
+def test_prefill_dtype_mix(math_mode, xd, ad, yd):
+    """The fused prefill with x|B|C in one dtype, dt and z in another and y in
+    a third: every typed instance of both scan paths against the oracle on
+    the same (rounded) values.  A bf16 y adds its own rounding, at most 2^-8
+    of each element, which is bounded per element."""
+    inp = small(2, 300, 4, 2, "f32", seed=43)
+    inp.xbc = np.array(inp.xbc)
+    inp.dt = np.array(inp.dt)
+    inp.z = np.array(inp.z)
+    if xd == "bf16":
+        synth.round_bf16_(inp.xbc)
+    if ad == "bf16":
+        synth.round_bf16_(inp.dt)
+        synth.round_bf16_(inp.z)
+    say("prefill dtypes %s: %s x|B|C, %s dt/z, %s y" % (math_mode, xd, ad, yd))
+    p = params(inp)
+    fs = torch.empty((2, 4, 64, 128), device="cuda")
+    y = layer.prefill(dev(inp.xbc, xd), dev(inp.dt, ad), dev(inp.z, ad).view(2, 300, 4, 64), p,
+                      fused=True, math=math_mode, initial_state=dev32(inp.h0), final_state=fs,
+                      y_dtype=torch.bfloat16 if yd == "bf16" else torch.float32)
+    torch.cuda.synchronize()
+    pairs = [(b, h) for b in range(2) for h in range(4)]
+    yr, hr = oracle_pairs(inp, pairs)
+    yg = gather_y(y, pairs)
+    rms = float(np.sqrt(np.mean(yr * yr)))
+    slack = 2.0 ** -8 * np.abs(yr) if yd == "bf16" else 0.0
+    assert float(np.max(np.abs(yg - yr) - slack)) <= TOL[math_mode] * rms
+    hg = np.stack([fs[b, h].double().cpu().numpy() for b, h in pairs])
+    assert rel_max_err(hg, hr) <= TOL[math_mode]
+
+
+@pytest.mark.parametrize("math_mode", ["f32", "bf16"])
 @pytest.mark.parametrize("shift", [6.0, 40.0])
 def test_scan_strong_decay(math_mode, shift):
     """Raw dt shifted far up (delta ~ shift, delta*A down to about -16*shift
