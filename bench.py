@@ -281,6 +281,27 @@ def time_block(args, wl, torch, ssd, synth, dev, dev32):
     return dict(call_ms=call_ms, in_ms=in_ms, out_ms=out_ms)
 
 
+def measure_bf16_gemm_peak(torch, n: int = 8192, reps: int = 10):
+    """The matrix-core rate this GPU reaches on a large square bf16 product
+    through the vendor GEMM (torch.matmul on contiguous 2-D tensors): the
+    measured counterpart of the nominal bf16 MFMA peak.  Measurement only;
+    nothing on the path uses it.  Returns TFLOP/s."""
+    a = torch.randn((n, n), device="cuda").to(torch.bfloat16)
+    b = torch.randn((n, n), device="cuda").to(torch.bfloat16)
+    for _ in range(2):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    return 2.0 * n ** 3 / (ms / 1e3) / 1e12
+
+
 def calibrate_copy(torch, ssd, reps: int = 3):
     """A plain copy kernel of known size: ssd_chunk_scan_fwd on an empty
     sequence copies initial_state to final_state (the library's
@@ -392,6 +413,8 @@ def main():
         return
     _, copy_gbs = calibrate_copy(torch, ssd, reps=5)
     log("copy kernel: %.0f GB/s (read + write)" % copy_gbs)
+    gemm_tflops = measure_bf16_gemm_peak(torch)
+    log("vendor bf16 GEMM (8192^3): %.0f TFLOP/s" % gemm_tflops)
     wl = WORKLOADS[PREFILL_MAIN]
     pre = time_prefill(args, wl, torch, layer, synth, dev, dev32)
     tok_s = wl.tokens / (pre["step_ms"] / 1e3)
@@ -437,7 +460,9 @@ def main():
         "mfma": {"alg_flops_per_token": fpt,
                  "achieved_tflops": fpt * wl.tokens / (kernel_ms / 1e3) / 1e12,
                  "peak_tflops": BF16_PEAK_TFLOPS,
-                 "frac": fpt * wl.tokens / (kernel_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS},
+                 "frac": fpt * wl.tokens / (kernel_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
+                 "measured_peak_tflops": gemm_tflops,
+                 "frac_of_measured": fpt * wl.tokens / (kernel_ms / 1e3) / 1e12 / gemm_tflops},
     }
     if not args.no_decode:
         dwl = WORKLOADS[DECODE_MAIN].with_(decode_steps=args.decode_steps)
@@ -472,7 +497,8 @@ def main():
                          "unit": "TFLOP/s", "frac": tf_in / BF16_PEAK_TFLOPS,
                          "traffic": traffic_record("block_in_proj", src_hash("gemm.hip", "api.hip")),
                          "kernel": "gemm_bf16_kernel (in_proj, M=%d N=%d K=%d)" % (T, din, dm),
-                         "alg_flops_per_launch": f_in, "launch_ms": blk["in_ms"]},
+                         "alg_flops_per_launch": f_in, "launch_ms": blk["in_ms"],
+                         "measured_peak": gemm_tflops, "frac_of_measured": tf_in / gemm_tflops},
             "out_proj": {"ms": blk["out_ms"],
                          "tflops": f_out / (blk["out_ms"] / 1e3) / 1e12,
                          "frac": f_out / (blk["out_ms"] / 1e3) / 1e12 / BF16_PEAK_TFLOPS},
