@@ -342,6 +342,8 @@ DECODE_CASES = [  # (dtype, B, H, G, steps, gated, conv width; 0: no conv)
     ("bf16", 2, 8, 2, 8, True, 2), ("f32", 2, 8, 2, 6, True, 1),
     # post-conv inputs (no conv in the step)
     ("f32", 2, 8, 2, 6, True, 0),
+    # one sequence at the serving head count
+    ("bf16", 1, 128, 8, 4, True, 4),
 ]
 DECODE_ENTRIES = {"fused": ssd.ssd_state_update, "ws": ssd.ssd_state_update_ws}
 
@@ -459,6 +461,36 @@ def test_state_update_dtype_mix(xd, ad, yd, entry):
     assert float(np.max(np.abs(got - want) - slack)) <= 2 * TOL["f32"] * rms
     assert rel_max_err(st.cpu().numpy(), carry.state) <= TOL["f32"]
     np.testing.assert_array_equal(ring.float().cpu().numpy(), carry.ring)
+
+
+@pytest.mark.parametrize("entry", sorted(DECODE_ENTRIES))
+def test_decode_zero_dt_keeps_state(entry):
+    """dt = 0, no bias, no softplus, post-conv inputs: the decay is exp(0) = 1
+    and the input term 0, so the state comes back bit for bit, and
+    y = (C h + D x) silu(z) from that state (closed form, not the oracle)."""
+    B, H, G = 2, 8, 2
+    wl = Workload("d", batch=B, seqlen=1, nheads=H, ngroups=G, dtype="f32", decode_steps=1,
+                  initial_state=True, seed=47)
+    inp = synth.make_decode(wl)
+    xbc, z, _ = inp.steps(0, 1)
+    say("decode dt = 0 (%s)" % entry)
+    st = dev32(inp.state)
+    y = DECODE_ENTRIES[entry](st, dev(xbc[0], "f32"), torch.zeros((B, H), device="cuda"),
+                              dev32(inp.A), ngroups=G, z=dev(z[0], "f32"), D=dev32(inp.D),
+                              dt_bias=None, dt_softplus=False)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(st.cpu().numpy(), inp.state)
+    from pinforms import silu
+    HP = H * 64
+    want = np.empty((B, H, 64))
+    for h in range(H):
+        g = h // (H // G)
+        Cv = xbc[0][:, HP + G * 128 + g * 128:HP + G * 128 + (g + 1) * 128].astype(np.float64)
+        hs = inp.state[:, h].astype(np.float64)                      # [B, P, N]
+        xv = xbc[0][:, h * 64:(h + 1) * 64].astype(np.float64)
+        want[:, h] = (np.einsum("bpn,bn->bp", hs, Cv) + inp.D[h] * xv) * \
+            silu(z[0][:, h * 64:(h + 1) * 64].astype(np.float64))
+    assert rel_max_err(y.double().cpu().numpy().reshape(B, H, 64), want) <= 1e-5
 
 
 @pytest.mark.parametrize("entry", sorted(DECODE_ENTRIES))
