@@ -7,6 +7,9 @@
 // walks TOK consecutive tokens, keeping the last three inputs in registers,
 // so neighbouring threads read neighbouring 16-byte pieces of one token row
 // (fully coalesced) and the 3-token halo is re-read only once per TOK tokens.
+// The loads of 4 tokens are issued together (0.645 -> 0.578 ms for bf16 in,
+// fp32 out at 4 x 8192 tokens x 10240 channels; 8 together is no faster, and
+// non-temporal output stores make it slower).
 #include "ssd_common.h"
 
 namespace ssd {
@@ -109,19 +112,29 @@ __global__ __launch_bounds__(THREADS) void causal_conv1d_kernel(
     for (int j = 0; j < 3; ++j)
       load_raw<Tin, VEC>(x, x_stride, hist_in, hs, b, L, K, t0 - 3 + j, c, win[j]);
     const int t1 = min(L, t0 + TOK);
-    for (int t = t0; t < t1; ++t) {
-      float cur[VEC], o[VEC];
-      Vec<Tin, VEC>::load(x + ((int64_t)b * L + t) * x_stride + c, cur);
+    // UNR tokens per step: their loads are issued together (rows past the end
+    // re-read the last row and are not stored), so that each thread keeps
+    // UNR loads in flight
+    constexpr int UNR = 4;
+    for (int tb = t0; tb < t1; tb += UNR) {
+      float cur[UNR][VEC];
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) {
-        float u = bv[i] + w4[0][i] * win[0][i] + w4[1][i] * win[1][i] +
-                  w4[2][i] * win[2][i] + w4[3][i] * cur[i];
-        o[i] = apply_silu ? silu_f32(u) : u;
-        win[0][i] = win[1][i];
-        win[1][i] = win[2][i];
-        win[2][i] = cur[i];
+      for (int r = 0; r < UNR; ++r)
+        Vec<Tin, VEC>::load(x + ((int64_t)b * L + min(tb + r, t1 - 1)) * x_stride + c, cur[r]);
+#pragma unroll
+      for (int r = 0; r < UNR; ++r) {
+        float o[VEC];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          float u = bv[i] + w4[0][i] * win[0][i] + w4[1][i] * win[1][i] +
+                    w4[2][i] * win[2][i] + w4[3][i] * cur[r][i];
+          o[i] = apply_silu ? silu_f32(u) : u;
+          win[0][i] = win[1][i];
+          win[1][i] = win[2][i];
+          win[2][i] = cur[r][i];
+        }
+        if (tb + r < t1) store_vec<Tout, VEC>(out + ((int64_t)b * L + tb + r) * out_stride + c, o);
       }
-      store_vec<Tout, VEC>(out + ((int64_t)b * L + t) * out_stride + c, o);
     }
   }
 
