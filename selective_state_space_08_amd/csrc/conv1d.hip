@@ -7,15 +7,21 @@
 // walks TOK consecutive tokens, keeping the last three inputs in registers,
 // so neighbouring threads read neighbouring 16-byte pieces of one token row
 // (fully coalesced) and the 3-token halo is re-read only once per TOK tokens.
-// The loads of 4 tokens are issued together (0.645 -> 0.578 ms for bf16 in,
-// fp32 out at 4 x 8192 tokens x 10240 channels; 8 together is no faster, and
-// non-temporal output stores make it slower).
+// The loads of 4 tokens are issued together, and large problems take windows
+// of 128 tokens, which spread each thread's tap loads and halo over more
+// outputs (bf16 in, fp32 out at 4 x 8192 tokens x 10240 channels: 0.645 ms
+// with 32-token windows and one load at a time, 0.578 with 4 loads in
+// flight, 0.466 with 128-token windows; 8 loads in flight, 256-token windows
+// or non-temporal output stores are no faster).
 #include "ssd_common.h"
 
 namespace ssd {
 namespace {
 
-constexpr int TOK = 32;       // tokens per thread
+// tokens per thread: TOK_LONG when that still gives every CU a workgroup,
+// else TOK_SHORT (more, shorter windows for small problems)
+constexpr int TOK_SHORT = 32, TOK_LONG = 128;
+constexpr int NUM_CUS = 256;
 constexpr int THREADS = 256;
 
 template <typename T, int VEC> struct Vec;
@@ -81,7 +87,7 @@ __device__ __forceinline__ void load_raw(const Tin* x, int64_t x_stride, const T
   }
 }
 
-template <typename Tin, typename Tout, int VEC>
+template <typename Tin, typename Tout, int VEC, int TOK>
 __global__ __launch_bounds__(THREADS) void causal_conv1d_kernel(
     const Tin* __restrict__ x, int64_t x_stride, const float* __restrict__ w,
     const float* __restrict__ bias, const Tin* __restrict__ hist_in,
@@ -154,11 +160,21 @@ hipError_t launch_typed(const void* x, int64_t x_stride, const float* w, const f
                         int64_t out_stride, int B, int L, int C, int K, int apply_silu,
                         hipStream_t stream) {
   const int nv = C / VEC;
-  dim3 grid((nv + THREADS - 1) / THREADS, L > 0 ? (L + TOK - 1) / TOK : 1, B);
-  hipLaunchKernelGGL((causal_conv1d_kernel<Tin, Tout, VEC>), grid, dim3(THREADS), 0, stream,
-                     static_cast<const Tin*>(x), x_stride, w, bias,
-                     static_cast<const Tin*>(hist_in), static_cast<Tin*>(hist_out), hs,
-                     static_cast<Tout*>(out), out_stride, L, C, K, apply_silu);
+  const int64_t gx = (nv + THREADS - 1) / THREADS;
+  const int64_t long_wgs = gx * ((L + TOK_LONG - 1) / TOK_LONG) * B;
+  if (long_wgs >= NUM_CUS) {
+    dim3 grid((unsigned)gx, (L + TOK_LONG - 1) / TOK_LONG, B);
+    hipLaunchKernelGGL((causal_conv1d_kernel<Tin, Tout, VEC, TOK_LONG>), grid, dim3(THREADS), 0,
+                       stream, static_cast<const Tin*>(x), x_stride, w, bias,
+                       static_cast<const Tin*>(hist_in), static_cast<Tin*>(hist_out), hs,
+                       static_cast<Tout*>(out), out_stride, L, C, K, apply_silu);
+  } else {
+    dim3 grid((unsigned)gx, L > 0 ? (L + TOK_SHORT - 1) / TOK_SHORT : 1, B);
+    hipLaunchKernelGGL((causal_conv1d_kernel<Tin, Tout, VEC, TOK_SHORT>), grid, dim3(THREADS), 0,
+                       stream, static_cast<const Tin*>(x), x_stride, w, bias,
+                       static_cast<const Tin*>(hist_in), static_cast<Tin*>(hist_out), hs,
+                       static_cast<Tout*>(out), out_stride, L, C, K, apply_silu);
+  }
   return hipGetLastError();
 }
 

@@ -39,6 +39,9 @@ def small(B, L, H, G, dtype="bf16", h0=True, seed=1):
     (1, 1, 256, 4, "f32", "f32", True, False),
     (2, 2, 264, 4, "f32", "f32", True, True),       # L < K-1: history reaches into the old one
     (1, 33, 128, 1, "f32", "f32", False, False),
+    # large enough for 128-token windows (a ragged last window, both vector widths)
+    (2, 4200, 8192, 4, "bf16", "f32", True, True),
+    (2, 4200, 8192, 3, "f32", "bf16", True, False),
 ])
 def test_conv_kernel(B, L, C, K, xd, od, hist, bias):
     say("conv B=%d L=%d C=%d K=%d %s->%s" % (B, L, C, K, xd, od))
