@@ -822,22 +822,38 @@ __global__ void conv_bwd_kernel(const void* x, int64_t xs, const void* Bm, int64
     else if (pos < 0 && blk == 0 && dhist != nullptr && pos >= -(K - 1))
       dhist[((int64_t)b * (K - 1) + (K - 1) + pos) * cdim + c] = v;
   };
-  for (int t = t0; t < tend; ++t) {
-    win[0] = win[1]; win[1] = win[2]; win[2] = win[3];
-    win[3] = raw(t);
-    float u = bc;
+  // UNR tokens per step: their raw inputs and output gradients are loaded
+  // together (positions past tend re-read the last one and are not used),
+  // so that each thread keeps 2 UNR loads in flight; t >= t0 >= 0 here
+  constexpr int UNR = 4;
+  for (int tb = t0; tb < tend; tb += UNR) {
+    float rv[UNR], dv[UNR];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) u = fmaf(wp[j], win[j], u);
-    const float d = dpost[((int64_t)b * seqlen + t) * cdim + c] * silu_grad_f32(u);
-    if (t < t1) {
-      gb += d;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) gw[j] = fmaf(d, win[j], gw[j]);
+    for (int r = 0; r < UNR; ++r) {
+      const int t = min(tb + r, tend - 1);
+      rv[r] = to_f32(src[((int64_t)b * seqlen + t) * st + cc]);
+      dv[r] = dpost[((int64_t)b * seqlen + t) * cdim + c];
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = fmaf(wp[j], d, acc[j]);
-    emit(t - 3, acc[0]);  // position t - 3 has all its taps
-    acc[0] = acc[1]; acc[1] = acc[2]; acc[2] = acc[3]; acc[3] = 0.f;
+    for (int r = 0; r < UNR; ++r) {
+      const int t = tb + r;
+      if (t >= tend) break;
+      win[0] = win[1]; win[1] = win[2]; win[2] = win[3];
+      win[3] = rv[r];
+      float u = bc;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) u = fmaf(wp[j], win[j], u);
+      const float d = dv[r] * silu_grad_f32(u);
+      if (t < t1) {
+        gb += d;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) gw[j] = fmaf(d, win[j], gw[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = fmaf(wp[j], d, acc[j]);
+      emit(t - 3, acc[0]);  // position t - 3 has all its taps
+      acc[0] = acc[1]; acc[1] = acc[2]; acc[2] = acc[3]; acc[3] = 0.f;
+    }
   }
   // the positions still open (their later taps lie past the sequence)
   emit(tend - 3, acc[0]);
