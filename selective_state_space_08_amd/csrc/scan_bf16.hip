@@ -383,6 +383,24 @@ __global__ __launch_bounds__(PACK_THREADS) void bc_pack_kernel(ScanArgs a, bf16*
   bf16* pk = pack + ((int64_t)(b * G + g) * nc + c) * PACK;
   constexpr int HALO = CONV ? 3 : 0;
 
+  // bf16 inputs: the raw B and C rows first, so that their loads are in
+  // flight while the taps are read and staged (about 0.5% of the prefill
+  // call); fp32 rows are loaded one tensor at a time, since holding both
+  // would cost the kernel half its occupancy
+  constexpr bool EARLY = sizeof(Tin) == 2;
+  const int tstart = t0 + 8 * rg - HALO;
+  RowLoad<Tin, 8 + HALO> rlm[2];
+  auto load_rows = [&](int m) {
+    const Tin* src = static_cast<const Tin*>(m == 0 ? a.Bm : a.Cm);
+    const int64_t stride = m == 0 ? a.b_stride : a.c_stride;
+    const int hcol = HP + m * GN + g * N + 8 * cv;  // channel in the conv state rows
+    rlm[m].load(a, src, stride, g * N + 8 * cv, hcol, cdim, b, tstart);
+  };
+  if constexpr (EARLY) {
+    load_rows(0);
+    load_rows(1);
+  }
+
   if constexpr (CONV) {
     // taps of the group's B channels (local 0..N-1) and C channels (N..2N-1)
     const int K = a.conv_k;
@@ -396,14 +414,10 @@ __global__ __launch_bounds__(PACK_THREADS) void bc_pack_kernel(ScanArgs a, bf16*
     lds_barrier();
   }
 
-  const int tstart = t0 + 8 * rg - HALO;
 #pragma unroll
   for (int m = 0; m < 2; ++m) {  // m = 0: B, m = 1: C
-    const Tin* src = static_cast<const Tin*>(m == 0 ? a.Bm : a.Cm);
-    const int64_t stride = m == 0 ? a.b_stride : a.c_stride;
-    const int hcol = HP + m * GN + g * N + 8 * cv;  // channel in the conv state rows
-    RowLoad<Tin, 8 + HALO> rl;
-    rl.load(a, src, stride, g * N + 8 * cv, hcol, cdim, b, tstart);
+    if constexpr (!EARLY) load_rows(m);
+    const RowLoad<Tin, 8 + HALO>& rl = rlm[m];
     float v[8][8];
     if constexpr (CONV)
       conv_rows_to<Tin, 8>(a, rl, tstart, sCw, 2 * N, m * N + 8 * cv, 8 * rg, Lc, &v[0][0], 8);
