@@ -155,6 +155,8 @@ int ssd_causal_conv1d_fwd(const void* x, int64_t x_tok_stride, ssd_dtype_t x_dty
   if (batch < 0 || seqlen < 0 || cdim <= 0)
     return fail(SSD_ERR_INVALID_ARG, "conv1d: bad size batch=%d seqlen=%d cdim=%d", batch,
                 seqlen, cdim);
+  if (batch > 65535)  // the batch is the third grid dimension of the launch
+    return fail(SSD_ERR_UNSUPPORTED, "conv1d: batch %d > 65535", batch);
   if (width < 1) return fail(SSD_ERR_INVALID_ARG, "conv1d: width %d < 1", width);
   if (width > 4) return fail(SSD_ERR_UNSUPPORTED, "conv1d: width %d > 4", width);
   if (apply_silu != 0 && apply_silu != 1)
@@ -215,6 +217,8 @@ int ssd_chunk_scan_fwd(const void* x, int64_t x_tok_stride, const void* Bm,
   if (nheads % ngroups != 0)
     return fail(SSD_ERR_INVALID_ARG, "scan: nheads %d not a multiple of ngroups %d", nheads,
                 ngroups);
+  if (batch > 65535)  // the batch is the third grid dimension of the pack and conv launches
+    return fail(SSD_ERR_UNSUPPORTED, "scan: batch %d > 65535", batch);
   if (dt_softplus != 0 && dt_softplus != 1)
     return fail(SSD_ERR_INVALID_ARG, "scan: dt_softplus must be 0 or 1");
   if (headdim != kP || dstate != kN)
@@ -276,6 +280,12 @@ int ssd_chunk_scan_fwd(const void* x, int64_t x_tok_stride, const void* Bm,
   for (int i = 0; i < 5; ++i)
     if (overlap(rfs, ins[i]))
       return fail(SSD_ERR_INVALID_ARG, "scan: final_state overlaps an activation");
+  // the state of (b, h) is read whole before it is written, but by the
+  // workgroup of (b, h) only: final_state may be initial_state itself, and
+  // no other overlap of the two is allowed
+  if (final_state != initial_state && overlap(rfs, ins[5]))
+    return fail(SSD_ERR_INVALID_ARG,
+                "scan: final_state partly overlaps initial_state (only exact aliasing is allowed)");
   // ---- workspace
   const bool mc = math == SSD_MATH_BF16 && rows > 0;
   const int nseg = mc ? plan_segments(batch, seqlen, nheads) : 1;
@@ -495,6 +505,8 @@ int ssd_chunk_scan_bwd(const void* x, int64_t x_tok_stride, const void* Bm,
                 ngroups);
   if (dt_softplus != 0 && dt_softplus != 1)
     return fail(SSD_ERR_INVALID_ARG, "scan_bwd: dt_softplus must be 0 or 1");
+  if (batch > 65535)  // the batch is the third grid dimension of the conv launches
+    return fail(SSD_ERR_UNSUPPORTED, "scan_bwd: batch %d > 65535", batch);
   if (headdim != kP || dstate != kN)
     return fail(SSD_ERR_UNSUPPORTED, "scan_bwd: headdim %d / dstate %d (supported: 64 / 128)",
                 headdim, dstate);

@@ -195,18 +195,21 @@ void gemm_bf16_kernel(GemmArgs g) {
           (__attribute__((address_space(3))) void*)&sW[buf][(32 * wv + 8 * i) * TK], 16, 0, 0);
     }
   };
-  // after the loads of step kt have landed: zero the chunks past K
+  // after this wave's loads of the last step have landed: zero the chunks
+  // past K.  Each lane clears exactly the slots its own direct loads filled
+  // (slot l % 8 of rows 32 wv + 8 i + l / 8, which holds chunk lchunk), so
+  // the wave's own wait for its loads orders every clear after the load it
+  // replaces; a slot filled by another wave is never cleared here.
   const int nk = (g.K + TK - 1) / TK;
   const int kvalid = (g.K - (nk - 1) * TK) / 8;  // valid chunks of the last step
   auto zero_tail = [&](int buf) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    const int kc = tid & 7, srow = tid >> 3;
-    if (kc >= kvalid) {
+    if (lchunk >= kvalid) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = srow + 64 * i;
-        *reinterpret_cast<u32x4*>(&sA[buf][row * TK + 8 * slot(row, kc)]) = zero;
-        *reinterpret_cast<u32x4*>(&sW[buf][row * TK + 8 * slot(row, kc)]) = zero;
+        const int row = 32 * wv + 8 * i + lrow;
+        *reinterpret_cast<u32x4*>(&sA[buf][row * TK + 8 * slot(row, lchunk)]) = zero;
+        *reinterpret_cast<u32x4*>(&sW[buf][row * TK + 8 * slot(row, lchunk)]) = zero;
       }
     }
   };

@@ -998,6 +998,9 @@ hipError_t launch_walkers(const ScanArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((bc_pack_kernel<Tx, XCONV>), dim3(nc, a.ngroups, a.batch),
                      dim3(PACK_THREADS), 0, stream, a,
                      static_cast<bf16*>(const_cast<void*>(a.bc_pack)));
+  // no walker runs on a pack that was never written
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int BH = a.batch * a.nheads;
   if (a.nseg > 1) {
     hipLaunchKernelGGL((scan_bf16_kernel<Tx, Ta, Ty, XCONV, true>), dim3(BH * (a.nseg - 1)),

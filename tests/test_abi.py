@@ -174,6 +174,21 @@ def test_scan_rejects_conv_state_out_on_conv_state_in():
     assert call_scan(a) == INVALID
 
 
+def test_scan_rejects_final_state_partly_on_initial_state():
+    """final_state may be initial_state itself, but any other overlap races:
+    the workgroup of head h + 1 would read initial[h + 1] while the one of h
+    writes final[h] over it."""
+    a = scan_args()
+    a["hT"] = ctypes.c_void_p(a["h0"].value + 64 * 128 * 4)
+    assert call_scan(a) == INVALID
+    assert "initial_state" in ssd.load().ssd_last_error().decode()
+
+
+def test_scan_rejects_batch_beyond_grid():
+    assert call_scan(scan_args(B=65536, L=1)) == UNSUPPORTED
+    assert conv_call(B=65536, L=1) == UNSUPPORTED
+
+
 def test_scan_workspace_required():
     """One long sequence with few heads needs a workspace for the sequence
     split; without it (or with too little) the call fails with SSD_ERR_WORKSPACE."""

@@ -95,6 +95,10 @@ def check_linear(a, w, got, ref, od):
     (513, 520, 192, "f32", "bf16"),     # an odd number of K steps
     (130, 300, 200, "bf16", "f32"),     # three full steps and a partial one
     (1000, 4096, 4096, "f32", "bf16"),  # out_proj-like
+    # K below one step with rows of every wave stored: each wave clears the
+    # tail chunks of the rows it loaded itself
+    (300, 300, 40, "f32", None),
+    (300, 300, 2056, "bf16", "f32"),    # a one-chunk last step after 32 full ones
 ])
 def test_linear(M, N, K, od, res):
     say("linear M=%d N=%d K=%d out=%s res=%s" % (M, N, K, od, res))

@@ -342,7 +342,7 @@ def test_decode_equals_prefill():
     rng = np.random.default_rng(100)
     dims = (4, 3, 2, 5)
     H, P, G, N = dims
-    T, B = 23, 3
+    T, B = 1000, 3
     lp = layer_problem(rng, B, T, *dims)
     y, hT, hout = layer(lp, slice(None), lp["h0"], lp["hist"], dims)
     carry = oracle.DecodeState(lp["h0"], lp["hist"])

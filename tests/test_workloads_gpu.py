@@ -20,7 +20,16 @@ from selective_state_space_08_amd.workloads import WORKLOADS
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
-PROBE_TOL = {"f32": 1e-5, "bf16": 1e-2}
+# SSM-only probes (D = 0, no gate), where the scan's own terms make up all of
+# y.  Relative RMS error: fp32 a few ulps; bf16 about 2.6 unit roundoffs
+# (u = 2^-9): the matrix-core products round each operand once (C, B, the
+# masked C B^T tile, x, the bf16 copy of the state), with independent errors
+# of RMS u / sqrt(3) each, so an element sums about 4 of them, RMS ~2.3e-3;
+# measured 2.3e-3 .. 3.3e-3.  A 1% error in the SSM term fails it.
+PROBE_TOL = {"f32": 1e-5, "bf16": 5e-3}
+# max|e| / RMS(y) of the same probes: y_ssm is heavy-tailed (max |y| ~ 35 RMS)
+# and the error of an element scales with its own terms
+PROBE_MAX = {"f32": 1e-4, "bf16": 0.5}
 PREFILL = ["tiny_f32_b1_l512_h4", "nemotron_h_8b_b4_l8192", "nemotron3_nano_b8_l4096",
            "long_ctx_3b_b1_l131072"]
 NSAMPLE = {"tiny_f32_b1_l512_h4": 4, "nemotron_h_8b_b4_l8192": 12,
@@ -66,9 +75,12 @@ def test_prefill_workload(name):
     # SSM-only probe (D = 0, no gate)
     run(inp, None, bufs, D=False, z=False)
     yr0, _ = oracle_pairs(inp, pairs, D=False, z=False)
-    perr = rel_rms_err(gather_y(bufs["y"], pairs), yr0)
-    say("workload %s: SSM-only probe rel RMS err %.3e" % (name, perr))
+    yg0 = gather_y(bufs["y"], pairs)
+    perr = rel_rms_err(yg0, yr0)
+    pmax = rel_max_err(yg0, yr0)
+    say("workload %s: SSM-only probe rel RMS err %.3e, max|err|/RMS %.3e" % (name, perr, pmax))
     assert perr <= PROBE_TOL[math_mode]
+    assert pmax <= PROBE_MAX[math_mode]
 
 
 def test_prefill_slow_decay_probe():
@@ -84,10 +96,13 @@ def test_prefill_slow_decay_probe():
     run(inp, None, bufs, D=False, z=False)
     pairs = pick_pairs(wl, 6)
     yr, hr = oracle_pairs(inp, pairs, D=False, z=False)
-    err = rel_rms_err(gather_y(bufs["y"], pairs), yr)
+    yg = gather_y(bufs["y"], pairs)
+    err = rel_rms_err(yg, yr)
+    emax = rel_max_err(yg, yr)
     herr = rel_max_err(np.stack([bufs["hT"][b, h].double().cpu().numpy() for b, h in pairs]), hr)
-    say("slow decay: rel RMS err %.3e, final state %.3e" % (err, herr))
+    say("slow decay: rel RMS err %.3e, max|err|/RMS %.3e, final state %.3e" % (err, emax, herr))
     assert err <= PROBE_TOL["bf16"]
+    assert emax <= PROBE_MAX["bf16"]
     assert herr <= TOL["bf16"]
 
 
