@@ -203,6 +203,32 @@ int ssd_state_update_ws(float* state, const void* xbc, ssd_dtype_t xbc_dtype, vo
                         int dstate, void* workspace, size_t workspace_bytes,
                         hipStream_t stream);
 
+/*
+ * ssd_state_update_ws without a workspace argument and without allocating:
+ * for callers that cannot call hipMalloc (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments (minus
+ * the workspace), results, in-place updates and errors as ssd_state_update_ws,
+ * through the same kernels; the post-conv x|B|C goes to a static 16 MiB
+ * device array that the library holds on each device it runs on until the
+ * process ends.
+ *
+ *   Limit: batch * Cdim <= 4194304 (Cdim = H*P + 2*G*N; batch 409 at
+ *   Cdim 10240); larger calls return SSD_ERR_UNSUPPORTED and touch nothing.
+ *   Concurrency: every call on one device shares that device's array (each
+ *   call writes all of the part it reads before reading it, so nothing needs
+ *   clearing); calls that overlap in time on one device, from different
+ *   streams or threads, race on it and must be serialised by the caller.
+ *   The first call on a device looks up the array's device address
+ *   (hipGetSymbolAddress) and keeps it; SSD_ERR_HIP if that fails.
+ */
+int ssd_state_update_noalloc(float* state, const void* xbc, ssd_dtype_t xbc_dtype,
+                             void* conv_state, const float* conv_w, const float* conv_b,
+                             int conv_width, const void* dt, const void* z,
+                             ssd_dtype_t act_dtype, const float* A, const float* D,
+                             const float* dt_bias, int dt_softplus, void* y, ssd_dtype_t y_dtype,
+                             int batch, int nheads, int headdim, int ngroups, int dstate,
+                             hipStream_t stream);
+
 /* Bytes of decode cache per sequence and layer: the fp32 SSM state
  * (4*H*P*N) plus the conv ring ((K-1) * Cdim elements of conv_dtype).
  * This is the fixed-size Mamba cache of "Hybrid Architectures ..." summary,

@@ -470,6 +470,35 @@ int ssd_state_update_ws(float* state, const void* xbc, ssd_dtype_t xbc_dtype, vo
   return e == hipSuccess ? SSD_OK : hip_fail(e, "state_update_ws launch");
 }
 
+int ssd_state_update_noalloc(float* state, const void* xbc, ssd_dtype_t xbc_dtype,
+                             void* conv_state, const float* conv_w, const float* conv_b,
+                             int conv_width, const void* dt, const void* z,
+                             ssd_dtype_t act_dtype, const float* A, const float* D,
+                             const float* dt_bias, int dt_softplus, void* y, ssd_dtype_t y_dtype,
+                             int batch, int nheads, int headdim, int ngroups, int dstate,
+                             hipStream_t stream) {
+  g_last_error.clear();
+  Range ry, ins[5];
+  const int st = check_state_update("state_update_noalloc", state, xbc, xbc_dtype, conv_state,
+                                    conv_w, conv_b, conv_width, dt, z, act_dtype, A, dt_softplus,
+                                    y, y_dtype, batch, nheads, headdim, ngroups, dstate, &ry, ins);
+  if (st != SSD_OK) return st;
+  const int64_t cdim = (int64_t)nheads * kP + 2 * (int64_t)ngroups * kN;
+  if ((int64_t)batch * cdim > kNoAllocScratchFloats)
+    return fail(SSD_ERR_UNSUPPORTED,
+                "state_update_noalloc: batch x channels = %lld exceeds its static scratch of "
+                "%lld floats (16 MiB); use ssd_state_update_ws with a workspace",
+                (long long)((int64_t)batch * cdim), (long long)kNoAllocScratchFloats);
+  if (batch == 0) return SSD_OK;
+  float* post = nullptr;
+  hipError_t e = no_alloc_scratch(&post);
+  if (e != hipSuccess) return hip_fail(e, "state_update_noalloc: scratch address");
+  e = launch_state_update_ws(state, xbc, xbc_dtype, conv_state, conv_w, conv_b,
+                             conv_w ? conv_width : 1, dt, z, act_dtype, A, D, dt_bias,
+                             dt_softplus, y, y_dtype, batch, nheads, ngroups, post, stream);
+  return e == hipSuccess ? SSD_OK : hip_fail(e, "state_update_noalloc launch");
+}
+
 // ------------------------------------------------------------------ backward
 
 size_t ssd_chunk_scan_bwd_workspace_bytes(int batch, int seqlen, int nheads, int headdim,

@@ -106,6 +106,12 @@ hipError_t launch_state_update_ws(float* state, const void* xbc, ssd_dtype_t xbc
                                   int softplus, void* y, ssd_dtype_t y_dtype, int batch,
                                   int nheads, int ngroups, float* post, hipStream_t stream);
 
+// The allocation-free decode step keeps its post-conv x|B|C in a static
+// device array of this many floats (16 MiB per device); no_alloc_scratch
+// gives the current device's address of it.
+constexpr int64_t kNoAllocScratchFloats = (int64_t)(16 << 20) / 4;
+hipError_t no_alloc_scratch(float** out);
+
 // Everything the backward pass needs (validated by the caller).
 struct ScanBwdLaunch {
   const void* x; int64_t x_stride;

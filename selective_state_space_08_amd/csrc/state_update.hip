@@ -25,6 +25,8 @@
 // B = 256, H = 128: 0.355 ms against 0.404 ms per step), and the 40 KiB of
 // post-conv values per sequence are read from L2 by the 32 workgroups that
 // share them instead of being recomputed.
+#include <mutex>
+
 #include "ssd_common.h"
 
 namespace ssd {
@@ -312,6 +314,40 @@ hipError_t pick_y_ws(ssd_dtype_t yd, float* state, const void* xbc, void* ring, 
 }
 
 }  // namespace
+
+// ------------------------------------------------------------ without any allocation
+
+// Scratch of the allocation-free decode step: the post-conv x|B|C of the
+// step (one float per sequence and channel), in a file-scope device array
+// instead of a caller's workspace.  Every device the library runs on holds
+// its own copy, at its own address, until the process ends.  Host code never
+// uses the array's name as an address (on the host it is only a stand-in
+// for the symbol); it uses the device address looked up per device below.
+static __device__ __align__(256) float scratch[kNoAllocScratchFloats];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// The current device's address of the scratch array: looked up once per
+// device, with that device current, on its first call, and kept.
+hipError_t no_alloc_scratch(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_state_update(float* state, const void* xbc, ssd_dtype_t xd, void* ring,
                                const float* conv_w, const float* conv_b, int K, const void* dt,

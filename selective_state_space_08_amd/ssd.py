@@ -35,6 +35,8 @@ SIGNATURES = {
     "ssd_state_update_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "ssd_state_update_ws": (_I, [_V, _V, _I, _V, _V, _V, _I, _V, _V, _I, _V, _V, _V, _I, _V,
                                  _I, _I, _I, _I, _I, _I, _V, _SZ, _V]),
+    "ssd_state_update_noalloc": (_I, [_V, _V, _I, _V, _V, _V, _I, _V, _V, _I, _V, _V, _V, _I,
+                                      _V, _I, _I, _I, _I, _I, _I, _V]),
     "ssd_decode_cache_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "ssd_chunk_scan_bwd_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "ssd_chunk_scan_bwd": (_I, [_V, _I64, _V, _I64, _V, _I64, _I, _V, _V, _I, _V, _V, _I64, _V,
@@ -268,6 +270,22 @@ def ssd_state_update_ws(state, xbc, dt, A, *, ngroups, conv_state=None, conv_w=N
                                    _p(conv_b), K, _p(dt), _p(z), _dt(dt), _p(A), _p(D),
                                    _p(dt_bias), int(bool(dt_softplus)), _p(y), _dt(y), B, H, P,
                                    G, N, _p(workspace), wsz, _stream(state)))
+    return y
+
+
+def ssd_state_update_noalloc(state, xbc, dt, A, *, ngroups, conv_state=None, conv_w=None,
+                             conv_b=None, z=None, D=None, dt_bias=None, dt_softplus=True,
+                             y=None, y_dtype=torch.float32):
+    """The two-kernel decode step with no workspace and no allocation in the
+    library (its scratch is a static device array; batch * Cdim <= 4194304).
+    Pass y to allocate nothing here either."""
+    lib = load()
+    y, B, H, P, G, N, K = _state_update_args(state, xbc, dt, ngroups, conv_state, conv_w,
+                                             conv_b, z, y, y_dtype)
+    _check(lib.ssd_state_update_noalloc(_p(state), _p(xbc), _dt(xbc), _p(conv_state),
+                                        _p(conv_w), _p(conv_b), K, _p(dt), _p(z), _dt(dt), _p(A),
+                                        _p(D), _p(dt_bias), int(bool(dt_softplus)), _p(y), _dt(y),
+                                        B, H, P, G, N, _stream(state)))
     return y
 
 

@@ -1,0 +1,67 @@
+"""ssd_state_update_noalloc against ssd_state_update_ws, through the C ABI.
+
+The allocation-free entry point runs the same two kernels as the workspace
+one, with its post-conv scratch in a static device array: its outputs (y, the
+updated state and the shifted conv ring) must equal the workspace path's byte
+for byte.  Two calls in a row, the second with a smaller batch, check that
+the shared array's leftover contents from the first call do not leak into the
+second.  Sizes beyond the array are refused before anything is touched.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from harness import dev, dev32, params, say
+from selective_state_space_08_amd import ssd, synth
+from selective_state_space_08_amd.workloads import Workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _step(entry, inp, xbc, dt, z, dtype):
+    p = params(inp)
+    st = dev32(inp.state)
+    ring = dev(inp.ring, dtype)
+    B = inp.wl.batch
+    y = torch.empty((B, inp.wl.d_inner), device="cuda")
+    for t in range(xbc.shape[0]):
+        entry(st, dev(xbc[t], dtype), dev(dt[t], dtype), p.A, ngroups=inp.wl.ngroups,
+              conv_state=ring, conv_w=p.conv_w, z=dev(z[t], dtype), D=p.D, dt_bias=p.dt_bias,
+              y=y)
+    torch.cuda.synchronize()
+    return y.cpu(), st.cpu(), ring.cpu()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_no_alloc_equals_workspace_path(dtype):
+    # the first call fills more of the static array than the second reads
+    for B, H, G, seed in ((64, 128, 8, 71), (5, 16, 4, 72)):
+        wl = Workload("na", batch=B, seqlen=1, nheads=H, ngroups=G, dtype=dtype,
+                      decode_steps=3, initial_state=True, seed=seed)
+        inp = synth.make_decode(wl)
+        xbc, z, dt = inp.steps(0, 3)
+        say("no-alloc decode %s B=%d H=%d G=%d" % (dtype, B, H, G))
+        want = _step(ssd.ssd_state_update_ws, inp, xbc, dt, z, dtype)
+        got = _step(ssd.ssd_state_update_noalloc, inp, xbc, dt, z, dtype)
+        for g_, w_ in zip(got, want):
+            assert torch.equal(g_, w_)
+
+
+def test_no_alloc_refuses_beyond_its_scratch():
+    """batch x Cdim above 4194304 floats: SSD_ERR_UNSUPPORTED, nothing run
+    (pointers are never dereferenced; validation precedes every launch)."""
+    lib = ssd.load()
+    H, G = 128, 8
+    cdim = H * 64 + 2 * G * 128
+    B = (1 << 22) // cdim + 1
+    fake = [ctypes.c_void_p((1 << 44) + (i << 36)) for i in range(8)]
+    st = lib.ssd_state_update_noalloc(fake[0], fake[1], 1, fake[2], fake[3], None, 4, fake[4],
+                                      fake[5], 1, fake[6], None, None, 1, fake[7], 0, B, H, 64, G,
+                                      128, None)
+    assert st == -2
+    assert "static scratch" in lib.ssd_last_error().decode()
+    np.testing.assert_equal(lib.ssd_state_update_noalloc(
+        fake[0], fake[1], 1, fake[2], fake[3], None, 4, fake[4], fake[5], 1, fake[6], None, None,
+        1, fake[7], 0, 0, H, 64, G, 128, None), 0)
