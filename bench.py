@@ -6,10 +6,15 @@ One step = one prefill of the Nemotron-H-8B-shaped Mamba-2 layer (batch 4 x
 SiLU(z) gate; bf16 activations, fp32 state and output) through libssd: the
 causal conv, the chunked scan and the gated epilogue.  `value` is prefill
 tokens/s with every input already resident in HBM.  The same run times the
-decode workload (256 sequences x 1000 chained one-token ssd_state_update
-steps, fp32 state) and reports it under "decode", and the pre-norm residual
-block around the layer (RMSNorm, in_proj, the layer, out_proj + residual;
-d_model 4096) under "block", with the MFMA roofline of its projections.
+other prefill workloads (tiny fp32 prefill; the Nemotron-3-Nano layer with
+an initial state; the 131072-token long-context sequence) under "configs",
+each with its own roofline; the decode workload (256 sequences x 1000
+chained one-token steps, fp32 state) through ssd_state_update_ws and
+ssd_state_update under "decode"; the pre-norm residual block around the
+layer (RMSNorm, in_proj, the layer, out_proj + residual; d_model 4096) under
+"block", with the MFMA roofline of its projections; and the backward pass.
+Measured peaks (HBM streaming, back-to-back bf16 MFMAs) come from the
+library's calibration kernels, beside the published ones.
 
 Kernel durations come from HIP events recorded on the stream the kernels are
 launched on (torch's current stream, which the binding passes to libssd).
@@ -50,10 +55,14 @@ def src_hash(*names):
 
 def prefill_alg_bytes_per_token(wl, fused: bool) -> float:
     """Minimum HBM traffic of the layer per token: raw x|B|C, z and dt read once
-    (bf16), y written once (fp32).  The unfused path adds the fp32 conv
-    intermediate's write and re-read."""
-    e, o = 2, 4
+    (in the workload's activation dtype), y written once (fp32), and, where
+    the workload has them, the fp32 initial state read and final state
+    written once per sequence (spread over its tokens).  The unfused path
+    adds the fp32 conv intermediate's write and re-read."""
+    e, o = (4 if wl.dtype == "f32" else 2), 4
     b = e * wl.cdim + e * wl.d_inner + e * wl.nheads + o * wl.d_inner
+    if wl.initial_state:
+        b += 2 * 4 * wl.nheads * wl.headdim * wl.dstate / wl.seqlen
     if not fused:
         b += 2 * 4 * wl.cdim
     return float(b)
@@ -88,7 +97,11 @@ def traffic_record(kernel_key: str, current_hash: str):
     return rec.get("bytes_per_launch")
 
 
-def time_prefill(args, wl, torch, layer, synth, dev, dev32):
+def time_prefill(args, wl, torch, layer, synth, dev, dev32, steps=None, warmup=None,
+                 fused=None):
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
+    math_mode = "f32" if wl.dtype == "f32" else "bf16"
     log("prefill %s: generating inputs" % wl.name)
     t0 = time.time()
     inp = synth.make_prefill(wl)
@@ -103,28 +116,29 @@ def time_prefill(args, wl, torch, layer, synth, dev, dev32):
     h0 = dev32(inp.h0)
     hT = torch.empty((wl.batch, wl.nheads, wl.headdim, wl.dstate), device="cuda")
     y = torch.empty((wl.batch, wl.seqlen, wl.nheads, wl.headdim), device="cuda")
-    fused = not args.unfused
+    fused = (not args.unfused) if fused is None else fused
     conv_out = None if fused else torch.empty((wl.batch, wl.seqlen, wl.cdim), device="cuda")
     need = ssd.ssd_chunk_scan_workspace_bytes(wl.batch, wl.seqlen, wl.nheads,
-                                              ngroups=wl.ngroups, fused_conv=fused)
+                                              ngroups=wl.ngroups, fused_conv=fused,
+                                              math=math_mode)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     del inp
 
     def step():
-        layer.prefill(xbc, dt, z, p, fused=fused, math="bf16", initial_state=h0,
+        layer.prefill(xbc, dt, z, p, fused=fused, math=math_mode, initial_state=h0,
                       final_state=hT, conv_out=conv_out, y=y, workspace=ws)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+          for _ in range(steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         ev[i][0].record(stream)
         step()
         ev[i][1].record(stream)
@@ -133,10 +147,11 @@ def time_prefill(args, wl, torch, layer, synth, dev, dev32):
     t_wall = time.perf_counter() - t_wall
     total_ms = start.elapsed_time(stop)
     per = sorted(a.elapsed_time(b) for a, b in ev)
-    step_ms = total_ms / args.steps
-    log("prefill: %.3f ms/step (events), median step %.3f ms, wall %.3f s" %
-        (step_ms, per[len(per) // 2], t_wall))
-    return dict(step_ms=step_ms, median_ms=per[len(per) // 2], fused=fused,
+    step_ms = total_ms / steps
+    log("prefill %s: %.3f ms/step (events), median step %.3f ms, wall %.3f s" %
+        (wl.name, step_ms, per[len(per) // 2], t_wall))
+    del xbc, dt, z, y, ws, conv_out
+    return dict(step_ms=step_ms, median_ms=per[len(per) // 2], fused=fused, math=math_mode,
                 nseg_workspace=need)
 
 
@@ -166,28 +181,35 @@ def time_decode(args, wl, torch, layer, synth, dev, dev32):
                      dtype=torch.uint8, device="cuda")
     log("decode: inputs resident (%.1f GB)" % ((xbc.numel() + z.numel()) * 2 / 1e9))
 
-    def chain(n):
-        for t in range(n):
-            layer.decode_step(st, xbc[t], dt[t], z[t], ring, p, y=y[t], workspace=ws)
+    def run(fused):
+        """The chain of T steps from the seeded state and ring, through
+        ssd_state_update_ws (fused=False) or ssd_state_update (fused=True)."""
+        for t in range(min(T, 20)):
+            layer.decode_step(st, xbc[t], dt[t], z[t], ring, p, y=y[t], workspace=ws,
+                              fused=fused)
+        torch.cuda.synchronize()
+        st.copy_(st0)
+        ring.copy_(ring0)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(T + 1)]
+        marks[0].record(stream)
+        for t in range(T):
+            layer.decode_step(st, xbc[t], dt[t], z[t], ring, p, y=y[t], workspace=ws,
+                              fused=fused)
+            marks[t + 1].record(stream)
+        torch.cuda.synchronize()
+        total_ms = marks[0].elapsed_time(marks[T])
+        steps = [marks[t].elapsed_time(marks[t + 1]) for t in range(T)]
+        first = sum(steps[:10]) / 10
+        last = sum(steps[-10:]) / 10
+        log("decode (%s): %.3f ms per step; first 10 %.3f ms, last 10 %.3f ms" %
+            ("ssd_state_update" if fused else "ssd_state_update_ws", total_ms / T, first, last))
+        return dict(chain_ms=total_ms, step_ms=total_ms / T, first10_ms=first, last10_ms=last)
 
-    chain(min(T, 20))
-    torch.cuda.synchronize()
-    st.copy_(st0)
-    ring.copy_(ring0)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(T + 1)]
-    marks[0].record(stream)
-    for t in range(T):
-        layer.decode_step(st, xbc[t], dt[t], z[t], ring, p, y=y[t], workspace=ws)
-        marks[t + 1].record(stream)
-    torch.cuda.synchronize()
-    total_ms = marks[0].elapsed_time(marks[T])
-    steps = [marks[t].elapsed_time(marks[t + 1]) for t in range(T)]
-    first = sum(steps[:10]) / 10
-    last = sum(steps[-10:]) / 10
-    log("decode: %.3f ms per step; first 10 %.3f ms, last 10 %.3f ms" % (total_ms / T, first, last))
-    return dict(chain_ms=total_ms, step_ms=total_ms / T, first10_ms=first, last10_ms=last)
+    res = run(False)
+    res["fused"] = run(True)
+    return res
 
 
 def bwd_alg_bytes_per_call(wl) -> float:
@@ -281,54 +303,62 @@ def time_block(args, wl, torch, ssd, synth, dev, dev32):
     return dict(call_ms=call_ms, in_ms=in_ms, out_ms=out_ms)
 
 
-def measure_bf16_gemm_peak(torch, n: int = 8192, reps: int = 10):
-    """The matrix-core rate this GPU reaches on a large square bf16 product
-    through the vendor GEMM (torch.matmul on contiguous 2-D tensors): the
-    measured counterpart of the nominal bf16 MFMA peak.  Measurement only;
-    nothing on the path uses it.  Returns TFLOP/s."""
-    a = torch.randn((n, n), device="cuda").to(torch.bfloat16)
-    b = torch.randn((n, n), device="cuda").to(torch.bfloat16)
-    for _ in range(2):
-        torch.matmul(a, b)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        torch.matmul(a, b)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    del a, b
-    return 2.0 * n ** 3 / (ms / 1e3) / 1e12
-
-
-def calibrate_copy(torch, ssd, reps: int = 3):
-    """A plain copy kernel of known size: ssd_chunk_scan_fwd on an empty
-    sequence copies initial_state to final_state (the library's
-    copy_or_zero_kernel) and does nothing else.  Used for scaling the HBM
-    byte counters, and timed as the measured HBM bandwidth of this GPU.
-    Returns (bytes copied per call, median GB/s of read + write)."""
-    B, H, P, N = 256, 128, 64, 128
-    nbytes = B * H * P * N * 4
-    h0 = torch.randn((B, H, P, N), device="cuda")
-    hT = torch.empty_like(h0)
-    x = torch.empty((B, 0, H, P), dtype=torch.bfloat16, device="cuda")
-    bc = torch.empty((B, 0, 1, N), dtype=torch.bfloat16, device="cuda")
-    dt = torch.empty((B, 0, H), dtype=torch.bfloat16, device="cuda")
-    A = -torch.ones(H, device="cuda")
+def measure_peaks(torch, ssd, nbytes: int = 1 << 30, reps: int = 20):
+    """The rates this GPU reaches, measured with the library's calibration
+    kernels after warm-up: HBM streaming over a buffer of nbytes (four times
+    the last-level cache), in place (read and written back at the same
+    addresses, the decode state's pattern) and as a copy, each as reps passes
+    back to back between two events (as the decode chain is timed); and
+    back-to-back bf16 MFMAs on register operands (8 independent chains per
+    wave, 8 waves per SIMD).  Measurement only.
+    Returns (GB/s of the faster streaming form, its name, TFLOP/s)."""
+    n = nbytes // 4
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
     stream = torch.cuda.current_stream()
-    times = []
-    for _ in range(reps):
+    best = {}
+    for name, dst, src in (("in place", a, a), ("copy", b, a)):
+        for _ in range(3):
+            ssd.ssd_calibrate_stream(dst, src)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        ssd.ssd_chunk_scan_fwd(x, bc, bc, dt, A, initial_state=h0, final_state=hT)
+        for _ in range(reps):
+            ssd.ssd_calibrate_stream(dst, src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        best[name] = 2 * nbytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+        log("stream %s: %.0f GB/s (%d passes back to back, 2 x %d MiB each)" %
+            (name, best[name], reps, nbytes >> 20))
+    del a, b
+    out = torch.empty(2048 * 256, device="cuda")
+    iters = 4096
+    ssd.ssd_calibrate_mfma_bf16(out, iters)
+    times = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        flops = ssd.ssd_calibrate_mfma_bf16(out, iters)
         e1.record(stream)
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1))
-    assert torch.equal(hT, h0)
-    del h0, hT
-    ms = sorted(times)[len(times) // 2]
-    return nbytes, 2 * nbytes / (ms / 1e3) / 1e9
+    tflops = flops / (min(times) / 1e3) / 1e12
+    log("bf16 MFMA loop: %.0f TFLOP/s (best of 5)" % tflops)
+    del out
+    form = max(best, key=best.get)
+    return best[form], form, tflops
+
+
+def calibrate_copy(torch, ssd, nbytes: int = 1 << 30):
+    """A plain copy kernel of known size (the library's calibration stream,
+    dst != src) for scaling the HBM byte counters of a rocprofv3 --pmc run.
+    Returns the bytes read (= bytes written) per call."""
+    a = torch.ones(nbytes // 4, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        ssd.ssd_calibrate_stream(b, a)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    return nbytes
 
 
 def cpu_model():
@@ -378,6 +408,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other prefill workloads (tiny fp32, Nemotron-3-Nano, long context)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the layer's backward pass")
@@ -407,14 +439,11 @@ def main():
         sys.exit(1)
     ssd.load()
     if args.calibrate_copy:
-        nbytes, gbs = calibrate_copy(torch, ssd)
-        print(json.dumps({"calibration": "copy_or_zero_kernel", "bytes_read": nbytes,
-                          "bytes_written": nbytes, "GB/s": gbs}), flush=True)
+        nbytes = calibrate_copy(torch, ssd)
+        print(json.dumps({"calibration": "stream_kernel (copy)", "bytes_read": nbytes,
+                          "bytes_written": nbytes, "calls": 3}), flush=True)
         return
-    _, copy_gbs = calibrate_copy(torch, ssd, reps=5)
-    log("copy kernel: %.0f GB/s (read + write)" % copy_gbs)
-    gemm_tflops = measure_bf16_gemm_peak(torch)
-    log("vendor bf16 GEMM (8192^3): %.0f TFLOP/s" % gemm_tflops)
+    copy_gbs, stream_form, gemm_tflops = measure_peaks(torch, ssd)
     wl = WORKLOADS[PREFILL_MAIN]
     pre = time_prefill(args, wl, torch, layer, synth, dev, dev32)
     tok_s = wl.tokens / (pre["step_ms"] / 1e3)
@@ -422,6 +451,8 @@ def main():
     fpt = prefill_alg_flops_per_token(wl)
     kernel_ms = pre["median_ms"]
     achieved = bpt * wl.tokens / (kernel_ms / 1e3) / 1e9
+    peaks = {"hbm_gbs": copy_gbs, "hbm_form": "stream kernel, " + stream_form,
+             "bf16_mfma_tflops": gemm_tflops, "mfma_form": "MFMA loop on register operands"}
     # The measured unit is one ssd_chunk_scan_fwd call: the B|C pack kernel
     # (conv of B and C once per group, their matrix-core layouts and the
     # chunk's C B^T tiles into the workspace) and then the scan walker;
@@ -464,6 +495,31 @@ def main():
                  "measured_peak_tflops": gemm_tflops,
                  "frac_of_measured": fpt * wl.tokens / (kernel_ms / 1e3) / 1e12 / gemm_tflops},
     }
+    out["measured_peaks"] = peaks
+    if not args.no_configs:
+        out["configs"] = {}
+        for name in [n for n in WORKLOADS if n not in (PREFILL_MAIN, DECODE_MAIN)]:
+            cwl = WORKLOADS[name]
+            r = time_prefill(args, cwl, torch, layer, synth, dev, dev32, fused=True)
+            cb = prefill_alg_bytes_per_token(cwl, True)
+            cf = prefill_alg_flops_per_token(cwl)
+            ms = r["median_ms"]
+            gbs = cb * cwl.tokens / (ms / 1e3) / 1e9
+            tf = cf * cwl.tokens / (ms / 1e3) / 1e12
+            mpeak = BF16_PEAK_TFLOPS if r["math"] == "bf16" else FP32_MFMA_PEAK_TFLOPS
+            out["configs"][name] = {
+                "batch": cwl.batch, "seqlen": cwl.seqlen, "nheads": cwl.nheads,
+                "ngroups": cwl.ngroups, "activations": cwl.dtype, "math": r["math"],
+                "initial_state": cwl.initial_state, "ms_per_call": r["step_ms"],
+                "median_ms": ms, "tokens_per_s": cwl.tokens / (r["step_ms"] / 1e3),
+                "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                             "kernel": "prefill_fused_call", "alg_bytes_per_token": cb,
+                             "tokens_per_launch": cwl.tokens, "launch_ms": ms,
+                             "measured_peak": copy_gbs, "frac_of_measured": gbs / copy_gbs},
+                "mfma": {"alg_flops_per_token": cf, "achieved_tflops": tf, "peak_tflops": mpeak,
+                         "frac": tf / mpeak},
+            }
     if not args.no_decode:
         dwl = WORKLOADS[DECODE_MAIN].with_(decode_steps=args.decode_steps)
         dec = time_decode(args, dwl, torch, layer, synth, dev, dev32)
@@ -482,6 +538,15 @@ def main():
                                       "measured_peak": copy_gbs,
                                       "frac_of_measured": dach / copy_gbs,
                                       "alg_bytes_per_step": dbytes}}
+        fz = dec["fused"]
+        fach = dbytes / (fz["step_ms"] / 1e3) / 1e9
+        out["decode"]["ssd_state_update"] = {
+            "steps_per_s": 1e3 / fz["step_ms"], "ms_per_step": fz["step_ms"],
+            "first10_ms": fz["first10_ms"], "last10_ms": fz["last10_ms"],
+            "roofline": {"bound": "hbm", "achieved": fach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": fach / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "state_update_kernel", "measured_peak": copy_gbs,
+                         "frac_of_measured": fach / copy_gbs, "alg_bytes_per_step": dbytes}}
     if not args.no_block:
         blk = time_block(args, wl, torch, ssd, synth, dev, dev32)
         T, dm, HP, din = wl.tokens, wl.d_model, wl.d_inner, wl.d_in_proj

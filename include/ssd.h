@@ -229,6 +229,24 @@ int ssd_state_update_noalloc(float* state, const void* xbc, ssd_dtype_t xbc_dtyp
                              int batch, int nheads, int headdim, int ngroups, int dstate,
                              hipStream_t stream);
 
+/*
+ * Measurement aids (not part of the layer): what this GPU reaches on plain
+ * streaming and on back-to-back bf16 matrix-core products, for comparing
+ * the layer's kernels with measured rates beside the published peaks.
+ *
+ * ssd_calibrate_stream: one non-temporal pass dst[i] = src[i] over bytes/16
+ *   16-byte words.  dst == src streams the buffer in place (every word read
+ *   and written back at its own address, as the decode step does with its
+ *   state); otherwise a copy (which must not partly overlap).  bytes and both
+ *   pointers 16-byte multiples.  Moves 2 * bytes through HBM.
+ * ssd_calibrate_mfma_bf16: blocks workgroups of 4 waves; each wave issues
+ *   iters * 8 independent-chain 16x16x32 bf16 MFMAs (16384 flops each) on
+ *   register operands and writes one float per lane to out (blocks * 256
+ *   floats).  Flops per call: blocks * 4 * iters * 8 * 16384.
+ */
+int ssd_calibrate_stream(void* dst, const void* src, size_t bytes, hipStream_t stream);
+int ssd_calibrate_mfma_bf16(float* out, int blocks, int iters, hipStream_t stream);
+
 /* Bytes of decode cache per sequence and layer: the fp32 SSM state
  * (4*H*P*N) plus the conv ring ((K-1) * Cdim elements of conv_dtype).
  * This is the fixed-size Mamba cache of "Hybrid Architectures ..." summary,

@@ -135,6 +135,28 @@ const char* ssd_status_string(int status) {
 
 const char* ssd_last_error(void) { return g_last_error.c_str(); }
 
+int ssd_calibrate_stream(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  g_last_error.clear();
+  if (dst == nullptr || src == nullptr)
+    return fail(SSD_ERR_INVALID_ARG, "calibrate_stream: dst or src is NULL");
+  if (bytes % 16 != 0 || !aligned(dst, 16) || !aligned(src, 16))
+    return fail(SSD_ERR_INVALID_ARG, "calibrate_stream: bytes and pointers must be 16-byte multiples");
+  if (dst != src && overlap(dense_range(dst, (int64_t)bytes, 1), dense_range(src, (int64_t)bytes, 1)))
+    return fail(SSD_ERR_INVALID_ARG, "calibrate_stream: dst partly overlaps src");
+  if (bytes / 16 / 512 > (size_t)INT32_MAX)
+    return fail(SSD_ERR_UNSUPPORTED, "calibrate_stream: %zu bytes is too large", bytes);
+  const hipError_t e = launch_stream(dst, src, bytes, 1.0f, stream);
+  return e == hipSuccess ? SSD_OK : hip_fail(e, "calibrate_stream launch");
+}
+
+int ssd_calibrate_mfma_bf16(float* out, int blocks, int iters, hipStream_t stream) {
+  g_last_error.clear();
+  if (out == nullptr || blocks <= 0 || iters <= 0)
+    return fail(SSD_ERR_INVALID_ARG, "calibrate_mfma_bf16: bad argument");
+  const hipError_t e = launch_mfma_loop(out, blocks, iters, stream);
+  return e == hipSuccess ? SSD_OK : hip_fail(e, "calibrate_mfma_bf16 launch");
+}
+
 size_t ssd_decode_cache_bytes(int nheads, int headdim, int ngroups, int dstate, int width,
                               ssd_dtype_t conv_dtype) {
   if (nheads <= 0 || headdim <= 0 || ngroups <= 0 || dstate <= 0 || width < 1 ||

@@ -150,6 +150,12 @@ hipError_t launch_gemm_bf16(const void* a, int64_t lda, const void* w, int64_t l
                             int64_t ldo, ssd_dtype_t out_dtype, int64_t M, int N, int K,
                             hipStream_t stream);
 
+// Measurement aids: one streaming pass dst = a * src over bytes / 16 words
+// (in place when dst == src), and blocks x 4 waves of back-to-back bf16 MFMAs
+// (iters x 8 per wave) writing blocks x 256 floats to out.
+hipError_t launch_stream(void* dst, const void* src, size_t bytes, float a, hipStream_t stream);
+hipError_t launch_mfma_loop(float* out, int blocks, int iters, hipStream_t stream);
+
 // Copies (or zero-fills when src is null) n floats / n elements: used for the
 // state hand-through of empty sequences.  A kernel, not hipMemsetAsync.
 hipError_t launch_copy_or_zero(void* dst, const void* src, size_t bytes, hipStream_t stream);

@@ -47,6 +47,8 @@ SIGNATURES = {
     "ssd_block_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "ssd_block_fwd": (_I, [_V, _I, _V, ctypes.c_float, _V, _V, _V, _I, _V, _V, _V, _I, _V, _V,
                            _V, _V, _V, _V, _I, _I, _I, _I, _I, _I, _I, _I, _V, _SZ, _V]),
+    "ssd_calibrate_stream": (_I, [_V, _V, _SZ, _V]),
+    "ssd_calibrate_mfma_bf16": (_I, [_V, _I, _I, _V]),
     "ssd_status_string": (ctypes.c_char_p, [_I]),
     "ssd_last_error": (ctypes.c_char_p, []),
     "ssd_version": (ctypes.c_char_p, []),
@@ -130,6 +132,26 @@ def _dense(t: Optional[torch.Tensor], shape, name: str, dtype=None):
         raise ValueError("%s must be a contiguous device tensor of shape %s" % (name, tuple(shape)))
     if dtype is not None and t.dtype != dtype:
         raise TypeError("%s must be %s" % (name, dtype))
+
+
+def ssd_calibrate_stream(dst, src):
+    """One non-temporal streaming pass dst = src (in place when dst is src);
+    moves 2 * nbytes through HBM.  Measurement only."""
+    nb = dst.numel() * dst.element_size()
+    if src.numel() * src.element_size() != nb:
+        raise ValueError("ssd_calibrate_stream: dst and src differ in size")
+    _check(load().ssd_calibrate_stream(_p(dst), _p(src), nb, _stream(dst)))
+
+
+MFMA_CAL_FLOPS_PER_WAVE_ITER = 8 * 16 * 16 * 32 * 2
+
+
+def ssd_calibrate_mfma_bf16(out, iters):
+    """Back-to-back bf16 MFMAs on register operands: out.numel() / 256 blocks
+    of 4 waves, iters * 8 products per wave.  Returns the flop count."""
+    blocks = out.numel() // 256
+    _check(load().ssd_calibrate_mfma_bf16(_p(out), blocks, iters, _stream(out)))
+    return blocks * 4 * iters * MFMA_CAL_FLOPS_PER_WAVE_ITER
 
 
 def ssd_version() -> str:
