@@ -245,15 +245,22 @@ struct RowLoad {
       v[i].load(p);
     }
   }
+  // CHECK = false: the caller knows every row lies in the sequence, or feeds
+  // only outputs that are discarded (a chunk that neither starts the
+  // sequence nor is cut short by its end), and the per-element selects are
+  // left out
+  template <bool CHECK = true>
   __device__ __forceinline__ void get(const ScanArgs& a, int tstart, int i, float* out) const {
-    const int tau = tstart + i;
-    // bitwise, not short-circuit: a per-lane test without branches
-    const bool ok = (tau < a.seqlen) &
-                    ((tau >= 0) | ((a.conv_state_in != nullptr) & (tau >= -(a.conv_k - 1))));
     v[i].get(out);
-    if (!ok) {
+    if (CHECK) {
+      const int tau = tstart + i;
+      // bitwise, not short-circuit: a per-lane test without branches
+      const bool ok = (tau < a.seqlen) &
+                      ((tau >= 0) | ((a.conv_state_in != nullptr) & (tau >= -(a.conv_k - 1))));
+      if (!ok) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) out[e] = 0.f;
+        for (int e = 0; e < 8; ++e) out[e] = 0.f;
+      }
     }
   }
 };
@@ -265,7 +272,7 @@ struct RowLoad {
 // in front when the width is below 4), the bias at cw[4 * cws + c]; cl is the
 // local channel of the first of the 8; cws is the stride between taps (the
 // number of channels staged).
-template <typename Tx, int R, typename Td>
+template <typename Tx, int R, typename Td, bool CHECK = true>
 __device__ __forceinline__ void conv_rows_to(const ScanArgs& a, const RowLoad<Tx, R + 3>& rl,
                                              int tstart, const float* cw, int cws, int cl,
                                              int rfirst, int nvalid, Td* dst, int ld) {
@@ -279,14 +286,14 @@ __device__ __forceinline__ void conv_rows_to(const ScanArgs& a, const RowLoad<Tx
     d[4] = hi.x; d[5] = hi.y; d[6] = hi.z; d[7] = hi.w;
   }
   float win[3][8];
-  rl.get(a, tstart, 0, win[0]);
-  rl.get(a, tstart, 1, win[1]);
-  rl.get(a, tstart, 2, win[2]);
+  rl.template get<CHECK>(a, tstart, 0, win[0]);
+  rl.template get<CHECK>(a, tstart, 1, win[1]);
+  rl.template get<CHECK>(a, tstart, 2, win[2]);
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     float cur[8], o[8];
-    rl.get(a, tstart, i + 3, cur);
-    const bool ok = rfirst + i < nvalid;
+    rl.template get<CHECK>(a, tstart, i + 3, cur);
+    const bool ok = !CHECK || rfirst + i < nvalid;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float u = bv[e] + w4[0][e] * win[0][e] + w4[1][e] * win[1][e] +
@@ -302,14 +309,14 @@ __device__ __forceinline__ void conv_rows_to(const ScanArgs& a, const RowLoad<Tx
 }
 
 // Rows as they are (post-conv input), zero for rows >= nvalid.
-template <typename Tx, int R, typename Td>
+template <typename Tx, int R, typename Td, bool CHECK = true>
 __device__ __forceinline__ void copy_rows_to(const ScanArgs& a, const RowLoad<Tx, R>& rl,
                                              int tstart, int rfirst, int nvalid, Td* dst, int ld) {
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     float o[8];
-    rl.get(a, tstart, i, o);
-    if (rfirst + i >= nvalid)
+    rl.template get<CHECK>(a, tstart, i, o);
+    if (CHECK && rfirst + i >= nvalid)
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = 0.f;
     put8(dst + i * ld, o);
@@ -518,14 +525,15 @@ struct StageX {
 
   // the thread's 2 x 8 post-conv values, tmp[8 i + e] = x[2 xr + i][8 xv + e]
   // (zero past the end of the sequence)
+  template <bool CHECK>
   __device__ __forceinline__ void compute(const ScanArgs& a, const float* cw, int t0, int Lc,
                                           float* tmp) const {
     const int tid = threadIdx.x;
     const int xv = tid & 7, xr = tid >> 3;
     if constexpr (XCONV)
-      conv_rows_to<Tx, 2>(a, rx, t0 + 2 * xr - 3, cw, P, 8 * xv, 2 * xr, Lc, tmp, 8);
+      conv_rows_to<Tx, 2, float, CHECK>(a, rx, t0 + 2 * xr - 3, cw, P, 8 * xv, 2 * xr, Lc, tmp, 8);
     else
-      copy_rows_to<Tx, 2>(a, rx, t0 + 2 * xr, 2 * xr, Lc, tmp, 8);
+      copy_rows_to<Tx, 2, float, CHECK>(a, rx, t0 + 2 * xr, 2 * xr, Lc, tmp, 8);
   }
 };
 
@@ -717,7 +725,13 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     if (STATE_ONLY) log_decay += lam_last;
 
     float xt[16];  // xt[8 i + e] = x[2 xr + i][8 xv + e], post-conv fp32
-    sx.compute(a, sCw, t0, Lc, xt);
+    // the selects for rows outside the sequence and tokens past its end only
+    // where they can occur: its first chunk and a last chunk cut short
+    // (a uniform test)
+    if (c == 0 || Lc < Q)
+      sx.template compute<true>(a, sCw, t0, Lc, xt);
+    else
+      sx.template compute<false>(a, sCw, t0, Lc, xt);
     if (OUT) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -790,15 +804,21 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     for (int pt = 0; pt < 4; ++pt) hacc[pt] *= gamma;
 #pragma unroll
     for (int kk = 0; kk < Q / 32; ++kk) {
+      bf16x8 xhi[4], xlo[4];
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
         const int o = prow(16 * pt + l16) * LDT + 32 * kk + 8 * q;
-        const bf16x8 xhi = lds8(sXWh + o);
-        const bf16x8 xlo = lds8(sXWl + o);
-        hacc[pt] = mfma(bth[kk], xhi, hacc[pt]);
-        hacc[pt] = mfma(btl[kk], xhi, hacc[pt]);
-        hacc[pt] = mfma(bth[kk], xlo, hacc[pt]);
+        xhi[pt] = lds8(sXWh + o);
+        xlo[pt] = lds8(sXWl + o);
       }
+      // the four accumulators in turn, so that no product waits for the
+      // one before it
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) hacc[pt] = mfma(bth[kk], xhi[pt], hacc[pt]);
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) hacc[pt] = mfma(btl[kk], xhi[pt], hacc[pt]);
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) hacc[pt] = mfma(bth[kk], xlo[pt], hacc[pt]);
       // keep the operand loads of the next K step below this one's products
       // (hoisting them all at once costs more registers than the wave has)
       __builtin_amdgcn_sched_barrier(0);
