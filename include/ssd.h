@@ -16,7 +16,8 @@
  *    2*N_L*(d_ssm*d_state + N_conv*(2*d_state + d_ssm)) in "Hybrid
  *    Architectures ..." summary, Appendix C.
  *  - Shapes: head_dim P = 64, d_state N = 128, n_groups G, chunk 128
- *    (feasibility study, table 1.4).
+ *    (feasibility study, table 1.4); chunks of 64 and 256 tokens are
+ *    compiled too (the chunk length changes the blocking, not the result).
  *  - The decode state is of fixed size, independent of the position
  *    ("Nemotron-H paper explainer", Transformer-vs-Mamba table: O(1) compute
  *    and memory per token).
@@ -106,9 +107,11 @@ int ssd_causal_conv1d_fwd(const void* x, int64_t x_tok_stride, ssd_dtype_t x_dty
  * passed (the size does not depend on it in this version).  The matrix-core
  * path uses the workspace for B and C of every chunk and group, post-conv, in
  * the bf16 layouts its products read, and for the chunk's causal C B^T tiles
- * in fp32 (132 KiB per sequence, group and 128-token chunk; all of it is
- * formed once per group rather than once per head), and for per-segment
- * states when it splits a long sequence over more workgroups. */
+ * in fp32 (per sequence and group, 58 KiB per 64-token chunk, 132 KiB per
+ * 128-token chunk, 328 KiB per 256-token chunk; all of it is formed once per
+ * group rather than once per head), and for per-segment states when it
+ * splits a long sequence over more workgroups.  0 for a chunk length the
+ * matrix-core path does not support. */
 size_t ssd_chunk_scan_workspace_bytes(int batch, int seqlen, int nheads, int headdim,
                                       int ngroups, int dstate, int chunk,
                                       ssd_math_t math, int fused_conv);
@@ -135,8 +138,8 @@ size_t ssd_chunk_scan_workspace_bytes(int batch, int seqlen, int nheads, int hea
  *       fp32 or NULL.  They may be the same buffer.
  *   y   [B, L, H, P]  y_dtype, token stride y_tok_stride; must not overlap any
  *       input.
- *   Supported: P = 64, N = 128, H % G == 0; chunk 128 for SSD_MATH_BF16 and
- *   chunk in {32, 64, 128, 256} for SSD_MATH_F32; seqlen >= 0 (0 only copies
+ *   Supported: P = 64, N = 128, H % G == 0; chunk in {64, 128, 256} for
+ *   SSD_MATH_BF16 and in {32, 64, 128, 256} for SSD_MATH_F32; seqlen >= 0 (0 only copies
  *   the states); innermost rows 16-byte aligned.
  *   workspace: at least ssd_chunk_scan_workspace_bytes(...) bytes, 256-byte
  *   aligned, overlapping no tensor (NULL allowed when that is 0).

@@ -17,9 +17,10 @@ thread_local std::string g_last_error;
 
 constexpr int kP = 64;
 constexpr int kN = 128;
+// the chunk length the block runs its layer with ("Mamba2(..., chunk_size=128)")
 constexpr int kBf16Chunk = 128;
 // MI355X: 256 compute units; one matrix-core walker fits per CU (its LDS
-// footprint is ~120 KiB of 160 KiB).  The sequence-split plan below is sized
+// footprint is 67 to 115 KiB of 160 KiB, by chunk length).  The sequence-split plan below is sized
 // for this count so that the workspace size is a pure function of the shape.
 constexpr int kWalkerSlots = 256;
 constexpr int kMaxSegments = 64;
@@ -69,9 +70,9 @@ bool overlap(const Range& a, const Range& b) {
 
 // Number of sequence segments for the matrix-core scan: the smallest S that
 // minimises (rounds of walkers over the CU slots) x (chunks per segment).
-int plan_segments(int batch, int seqlen, int nheads) {
-  const int64_t bh = (int64_t)batch * nheads;
-  const int nc = (seqlen + kBf16Chunk - 1) / kBf16Chunk;
+int plan_segments(int batch, int seqlen, int nheads, int chunk) {
+  const int64_t bh = (int64_t)batch * nheads * scan_bf16_walkers_per_head(chunk);
+  const int nc = (seqlen + chunk - 1) / chunk;
   if (bh <= 0 || nc <= 1) return 1;
   int best = 1;
   int64_t best_cost = INT64_MAX;
@@ -96,7 +97,7 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 struct WsLayout {
   size_t seg_state = 0, seg_ld = 0, bc = 0, total = 0;
 };
-WsLayout ws_layout(int batch, int seqlen, int nheads, int ngroups, int nseg) {
+WsLayout ws_layout(int batch, int seqlen, int nheads, int ngroups, int chunk, int nseg) {
   WsLayout w;
   const size_t bh = (size_t)batch * nheads;
   size_t off = 0;
@@ -105,7 +106,7 @@ WsLayout ws_layout(int batch, int seqlen, int nheads, int ngroups, int nseg) {
   w.seg_ld = off;
   if (nseg > 1) off += round_up(bh * nseg * sizeof(float), 256);
   w.bc = off;
-  off += round_up(scan_bf16_pack_bytes(batch, seqlen, ngroups), 256);
+  off += round_up(scan_bf16_pack_bytes(batch, seqlen, ngroups, chunk), 256);
   w.total = off;
   return w;
 }
@@ -209,10 +210,12 @@ int ssd_causal_conv1d_fwd(const void* x, int64_t x_tok_stride, ssd_dtype_t x_dty
 size_t ssd_chunk_scan_workspace_bytes(int batch, int seqlen, int nheads, int headdim,
                                       int ngroups, int dstate, int chunk, ssd_math_t math,
                                       int fused_conv) {
-  (void)headdim; (void)dstate; (void)chunk; (void)fused_conv;
+  (void)headdim; (void)dstate; (void)fused_conv;
   if (batch <= 0 || seqlen <= 0 || nheads <= 0 || ngroups <= 0) return 0;
-  if (math != SSD_MATH_BF16) return 0;
-  return ws_layout(batch, seqlen, nheads, ngroups, plan_segments(batch, seqlen, nheads)).total;
+  if (math != SSD_MATH_BF16 || !scan_bf16_supports_chunk(chunk)) return 0;
+  return ws_layout(batch, seqlen, nheads, ngroups, chunk,
+                   plan_segments(batch, seqlen, nheads, chunk))
+      .total;
 }
 
 int ssd_chunk_scan_fwd(const void* x, int64_t x_tok_stride, const void* Bm,
@@ -246,8 +249,9 @@ int ssd_chunk_scan_fwd(const void* x, int64_t x_tok_stride, const void* Bm,
   if (headdim != kP || dstate != kN)
     return fail(SSD_ERR_UNSUPPORTED, "scan: headdim %d / dstate %d (supported: 64 / 128)",
                 headdim, dstate);
-  if (math == SSD_MATH_BF16 && chunk != kBf16Chunk)
-    return fail(SSD_ERR_UNSUPPORTED, "scan: chunk %d (matrix-core path supports 128)", chunk);
+  if (math == SSD_MATH_BF16 && !scan_bf16_supports_chunk(chunk))
+    return fail(SSD_ERR_UNSUPPORTED, "scan: chunk %d (matrix-core path supports 64/128/256)",
+                chunk);
   if (math == SSD_MATH_F32 && chunk != 32 && chunk != 64 && chunk != 128 && chunk != 256)
     return fail(SSD_ERR_UNSUPPORTED, "scan: chunk %d (fp32 path supports 32/64/128/256)", chunk);
   // ---- conv options
@@ -310,8 +314,8 @@ int ssd_chunk_scan_fwd(const void* x, int64_t x_tok_stride, const void* Bm,
                 "scan: final_state partly overlaps initial_state (only exact aliasing is allowed)");
   // ---- workspace
   const bool mc = math == SSD_MATH_BF16 && rows > 0;
-  const int nseg = mc ? plan_segments(batch, seqlen, nheads) : 1;
-  const WsLayout wl = mc ? ws_layout(batch, seqlen, nheads, ngroups, nseg) : WsLayout{};
+  const int nseg = mc ? plan_segments(batch, seqlen, nheads, chunk) : 1;
+  const WsLayout wl = mc ? ws_layout(batch, seqlen, nheads, ngroups, chunk, nseg) : WsLayout{};
   const size_t ws_need = wl.total;
   if (ws_need > 0) {
     if (workspace == nullptr || workspace_bytes < ws_need)

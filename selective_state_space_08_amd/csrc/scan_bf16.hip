@@ -4,7 +4,8 @@
 // y_t = C_t h_t + D x_t ("Hybrid Architectures for Language Models" summary,
 // section 2 Background) is evaluated in its chunked matrix form (the same
 // section: SSD recasts the state-space computation as matrix multiplies).
-// For a chunk of Q = 128 tokens with cumulative log decay Lam_t:
+// For a chunk of Q tokens (Q = 64, 128 or 256, one instance each) with
+// cumulative log decay Lam_t:
 //   Y      = (C B^T o exp(Lam_t - Lam_s) delta_s [s <= t]) X + diag(exp Lam) C H^T
 //   H_next = exp(Lam_last) H + (X o w)^T B,  w_s = exp(Lam_last - Lam_s) delta_s
 //   out    = (Y + D x) * silu(z)
@@ -23,15 +24,16 @@
 // no conversion work.
 //
 // scan_bf16_kernel ("walker", 8 waves, two per SIMD) owns one (sequence,
-// head) -- or one segment of it, see below -- and walks its chunks in order,
-// carrying the fp32 state H [64 x 128] in MFMA accumulator registers, so no
-// state goes to HBM between chunks.  Wave w owns the 16 output tokens of row
-// tile rt(w) = w < 4 ? w : 11 - w (the two waves of a SIMD together own tiles
-// i and 7 - i, which balances the causal triangle of C B^T) and the 16 state
-// columns n in [16 w, 16 w + 16), held as rows of H^T.  Each wave loads the
-// C rows of its tokens and the B^T rows of its state columns straight into
-// registers; x and the bf16 copy of H, which every wave reads whole, go
-// through LDS.
+// head) -- or one segment of it, see below; at Q = 256 one half of the head's
+// channels -- and walks its chunks in order, carrying its rows of the fp32
+// state H [64 x 128] in MFMA accumulator registers, so no state goes to HBM
+// between chunks.  Wave w owns the 16 state columns n in [16 w, 16 w + 16),
+// held as rows of H^T, and the output tokens of one or two 16-token row
+// tiles, chosen so that the two waves of a SIMD share the causal triangle of
+// C B^T evenly (at Q = 128, tiles w < 4 ? w : 11 - w: a SIMD owns tiles i
+// and 7 - i).  Each wave loads the C rows of its tokens and the B^T rows of
+// its state columns straight into registers; x and the bf16 copy of H, which
+// every wave reads whole, go through LDS.
 //
 // Outputs are produced transposed (Y^T = H C^T + X^T (M)^T, rows p, columns
 // t), so that each lane ends with 4 consecutive channels p of one token: z is
@@ -56,46 +58,92 @@ namespace ssd {
 
 namespace {
 
-constexpr int Q = 128;
 constexpr int P = 64;
 constexpr int N = 128;
 constexpr int THREADS = 512;     // walker: 8 waves
-constexpr int PACK_THREADS = 256;
 constexpr int NXCD = 8;
 constexpr int LDB = N + 8;       // bf16 row stride of [.][n] tiles (272 B)
-constexpr int LDT = Q + 8;       // bf16 row stride of [p][s] tiles (272 B)
-// Row p of a bf16 [p][s] tile is stored at row p + p / 8: with the 272-byte
-// pitch, the 8 rows 8 apart that one staging store writes then fall into
-// distinct LDS banks, and 16 consecutive rows (an MFMA operand read) still do.
+// Row p of a bf16 [p][s] tile is stored at row p + p / 8: with the row
+// pitches below, the 8 rows 8 apart that one staging store writes then fall
+// into distinct LDS banks, and 16 consecutive rows (an MFMA operand read)
+// still do.
 __host__ __device__ constexpr int prow(int p) { return p + (p >> 3); }
-constexpr int PROWS = P + P / 8;
-constexpr int LDX = P + 4;       // fp32 row stride of x [t][p] (272 B)
 
+__host__ __device__ constexpr int tri(int rt) { return rt * (rt + 1) / 2; }
+
+// element offset of M[r][k] in fragment order, for a matrix whose rows have
+// KS steps of K = 32
+template <int KS>
+__host__ __device__ constexpr int frag_off(int r, int k) {
+  return (((r >> 4) * KS + (k >> 5)) * 64 + (r & 15) + 16 * ((k & 31) >> 3)) * 8 + (k & 7);
+}
+
+// The shape of one instance, for the chunk length Q in {64, 128, 256}.
+//
+// A walker owns PW of the head's P = 64 channels: all of them for Q <= 128,
+// half for Q = 256 (two walkers per head), where the [p][s] tiles of a whole
+// head would not fit in the CU's 160 KiB of LDS.  Each wave owns the 16
+// state columns n in [16 w, 16 w + 16) of the walker's rows p, and NIT
+// "items" of output: a 16-token row tile rt and NPJ of the walker's 16-channel
+// tiles.  The two waves of a SIMD (w and w + 4) get row tiles whose causal
+// work adds up to the same amount:
+//   Q =  64: rt = w < 4 ? w : 7 - w, channel tiles {0, 1} (w < 4) or {2, 3}
+//   Q = 128: rt = w < 4 ? w : 11 - w, all four channel tiles
+//   Q = 256: two items, rt = w and rt = 15 - w, both channel tiles
+//
 // One (sequence, group, chunk) of the B|C pack, in bf16 elements.  C and the
 // hi/lo parts of B^T are stored in MFMA fragment order, so that a wave reads
 // the operand of one 16-row tile and one K=32 step as 1 KiB in one piece:
 // fragment (tile i16, step kk) holds, for lane l, the 8 elements
 // M[16 i16 + l % 16][32 kk + 8 (l / 16) + e], e < 8, at
-// ((i16 * 4 + kk) * 64 + l) * 8 + e, with M = C [t][n] or B^T [n][s].
+// ((i16 * KS + kk) * 64 + l) * 8 + e, with M = C [t][n] (KS = N / 32) or
+// B^T [n][s] (KS = Q / 32).
 // The causal 16x16 tiles of B C^T (rows s, columns t, tile (rt, u) with
 // u <= rt holding s in [16 u, 16 u + 16), t in [16 rt, 16 rt + 16)) follow
 // as fp32 in accumulator order: lane l of tile k = rt (rt + 1) / 2 + u holds
 // (B C^T)[16 u + 4 (l / 16) + r][16 rt + l % 16], r < 4, at floats
 // (k * 64 + l) * 4 + r.  They depend on the group only, so they are formed
-// here once instead of once per head.
-constexpr int NTRI = Q / 16 * (Q / 16 + 1) / 2;  // 36 causal tiles
-constexpr int PK_C = 0;            // C  [t][n], fragment order
-constexpr int PK_BTH = Q * N;      // B^T [n][s] hi, fragment order
-constexpr int PK_BTL = 2 * Q * N;  // B^T [n][s] lo, fragment order
-constexpr int PK_CB = 3 * Q * N;   // B C^T causal tiles, fp32 (2 bf16 slots per float)
-constexpr int PACK = 3 * Q * N + 2 * NTRI * 256;
+// there once instead of once per head.
+template <int Q_>
+struct Geo {
+  static constexpr int Q = Q_;
+  static_assert(Q == 64 || Q == 128 || Q == 256, "chunk length");
+  static constexpr int PW = Q == 256 ? 32 : 64;  // channels p per walker
+  static constexpr int NPS = P / PW;             // walkers per head
+  static constexpr int NRT = Q / 16;             // 16-token row tiles per chunk
+  static constexpr int KQ = Q / 32;              // K = 32 steps over the chunk's tokens
+  static constexpr int NPT = PW / 16;            // 16-channel tiles per walker
+  static constexpr int NIT = Q == 256 ? 2 : 1;   // output items per wave
+  static constexpr int NPJ = Q == 64 ? 2 : NPT;  // channel tiles per item
+  static constexpr int LDT = Q + 8;              // bf16 row stride of [p][s] tiles
+  static constexpr int PROWS = PW + PW / 8;
+  static constexpr int LDX = PW + 4;             // fp32 row stride of x [t][p]
+  static constexpr int NTRI = NRT * (NRT + 1) / 2;  // causal tiles
+  static constexpr int PK_C = 0;                 // C  [t][n], fragment order
+  static constexpr int PK_BTH = Q * N;           // B^T [n][s] hi, fragment order
+  static constexpr int PK_BTL = 2 * Q * N;       // B^T [n][s] lo, fragment order
+  static constexpr int PK_CB = 3 * Q * N;        // B C^T causal tiles, fp32
+  static constexpr int PACK = 3 * Q * N + 2 * NTRI * 256;
+  static constexpr int PACK_THREADS = 2 * Q;     // 8 tokens x 8 channels each
+  // x staging: thread (xv = tid % XV, xr = tid / XV) owns channels
+  // [8 xv, 8 xv + 8) of tokens [RX xr, RX xr + RX)
+  static constexpr int XV = PW / 8;
+  static constexpr int RX = Q * PW / (THREADS * 8);
+  static constexpr int DW = Q / 64;              // waves that scan the decay
+  // the B^T rows of a wave are loaded at the top of the chunk when they fit
+  // in registers beside the rest, else step by step in the state product
+  static constexpr bool BT_EARLY = KQ <= 4;
+  // likewise the C B^T tiles of an item: all at once after the staging, or
+  // two per K step of the intra-chunk product
+  static constexpr bool CB_EARLY = NRT <= 8;
 
-__host__ __device__ constexpr int tri(int rt) { return rt * (rt + 1) / 2; }
-
-// element offset of M[r][k] in fragment order (r < 128, k < 128)
-__host__ __device__ constexpr int frag_off(int r, int k) {
-  return (((r >> 4) * 4 + (k >> 5)) * 64 + (r & 15) + 16 * ((k & 31) >> 3)) * 8 + (k & 7);
-}
+  __device__ static int rt_of(int w, int it) {
+    if (Q == 64) return w < 4 ? w : 7 - w;
+    if (Q == 128) return w < 4 ? w : 11 - w;
+    return it == 0 ? w : 15 - w;
+  }
+  __device__ static int pj_base(int w) { return Q == 64 ? 2 * (w >> 2) : 0; }
+};
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -372,13 +420,17 @@ __device__ __forceinline__ void store4(bf16* p, const float* v) {
 
 // ------------------------------------------------------------ B|C pack
 
-// One workgroup per (chunk c, group g, sequence b).  Thread (cv = tid % 16,
-// rg = tid / 16) owns channels [8 cv, 8 cv + 8) and tokens [8 rg, 8 rg + 8)
-// of the chunk for B and for C.  Tokens past the end of the sequence are
-// written as zeros.  With the conv, the workgroup of the last chunk also hands
-// the last K-1 raw B and C rows of the group over to conv_state_out.
-template <typename Tin, bool CONV>
-__global__ __launch_bounds__(PACK_THREADS) void bc_pack_kernel(ScanArgs a, bf16* pack) {
+// One workgroup of 2 Q threads per (chunk c, group g, sequence b).  Thread
+// (cv = tid % 16, rg = tid / 16) owns channels [8 cv, 8 cv + 8) and tokens
+// [8 rg, 8 rg + 8) of the chunk for B and for C.  Tokens past the end of the
+// sequence are written as zeros.  With the conv, the workgroup of the last
+// chunk also hands the last K-1 raw B and C rows of the group over to
+// conv_state_out.
+template <typename Tin, bool CONV, int Q>
+__global__ __launch_bounds__(Geo<Q>::PACK_THREADS) void bc_pack_kernel(ScanArgs a, bf16* pack) {
+  using G_ = Geo<Q>;
+  constexpr int PACK_THREADS = G_::PACK_THREADS, PACK = G_::PACK, NTRI = G_::NTRI;
+  constexpr int KQ = G_::KQ;
   __shared__ __attribute__((aligned(16))) float sCw[CONV ? 5 * 2 * N : 4];
   __shared__ __attribute__((aligned(16))) bf16 sPB[Q * LDB];  // B [s][n] bf16
   __shared__ __attribute__((aligned(16))) bf16 sPC[Q * LDB];  // C [t][n] bf16
@@ -411,13 +463,15 @@ __global__ __launch_bounds__(PACK_THREADS) void bc_pack_kernel(ScanArgs a, bf16*
   if constexpr (CONV) {
     // taps of the group's B channels (local 0..N-1) and C channels (N..2N-1)
     const int K = a.conv_k;
-    const int ch = tid < N ? HP + g * N + tid : HP + GN + g * N + (tid - N);
+    for (int i = tid; i < 2 * N; i += PACK_THREADS) {
+      const int ch = i < N ? HP + g * N + i : HP + GN + g * N + (i - N);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = j - (4 - K);
-      sCw[j * 2 * N + tid] = k >= 0 ? a.conv_w[(int64_t)ch * K + k] : 0.f;
+      for (int j = 0; j < 4; ++j) {
+        const int k = j - (4 - K);
+        sCw[j * 2 * N + i] = k >= 0 ? a.conv_w[(int64_t)ch * K + k] : 0.f;
+      }
+      sCw[4 * 2 * N + i] = a.conv_b ? a.conv_b[ch] : 0.f;
     }
-    sCw[4 * 2 * N + tid] = a.conv_b ? a.conv_b[ch] : 0.f;
     lds_barrier();
   }
 
@@ -439,7 +493,7 @@ __global__ __launch_bounds__(PACK_THREADS) void bc_pack_kernel(ScanArgs a, bf16*
       for (int e = 0; e < 8; ++e) r[e] = (bf16)v[i][e];
       const int t = 8 * rg + i;
       *reinterpret_cast<bf16x8*>((m == 0 ? sPB : sPC) + t * LDB + 8 * cv) = r;
-      if (m == 1) *reinterpret_cast<bf16x8*>(pk + PK_C + frag_off(t, 8 * cv)) = r;
+      if (m == 1) *reinterpret_cast<bf16x8*>(pk + G_::PK_C + frag_off<N / 32>(t, 8 * cv)) = r;
     }
     if (m == 0) {
       // B transposed [n][s], hi and lo
@@ -455,19 +509,20 @@ __global__ __launch_bounds__(PACK_THREADS) void bc_pack_kernel(ScanArgs a, bf16*
         }
         // B^T row n = 8 cv + e, columns s = 8 rg .. 8 rg + 7: 8 consecutive
         // elements in fragment order
-        const int o = frag_off(8 * cv + e, 8 * rg);
-        *reinterpret_cast<bf16x8*>(pk + PK_BTH + o) = hi;
-        *reinterpret_cast<bf16x8*>(pk + PK_BTL + o) = lo;
+        const int o = frag_off<KQ>(8 * cv + e, 8 * rg);
+        *reinterpret_cast<bf16x8*>(pk + G_::PK_BTH + o) = hi;
+        *reinterpret_cast<bf16x8*>(pk + G_::PK_BTL + o) = lo;
       }
     }
   }
 
   // causal tiles of B C^T (rows s, columns t) with fp32 accumulation, in the
-  // accumulator order the walkers use; 9 tiles per wave
+  // accumulator order the walkers use; NTRI / (2 Q / 64) tiles per wave (5,
+  // 9 or 17)
   lds_barrier();
   {
     const int pw = tid >> 6, lane = tid & 63, l16 = lane & 15, q = lane >> 4;
-    float* cbo = reinterpret_cast<float*>(pk + PK_CB);
+    float* cbo = reinterpret_cast<float*>(pk + G_::PK_CB);
     for (int k = pw; k < NTRI; k += PACK_THREADS / 64) {
       int rt = 0;
       while (tri(rt + 1) <= k) ++rt;
@@ -506,48 +561,56 @@ __global__ __launch_bounds__(PACK_THREADS) void bc_pack_kernel(ScanArgs a, bf16*
 
 // ------------------------------------------------------------ x staging
 
-// One chunk's x for the whole workgroup: thread (xv = tid % 8, xr = tid / 8)
-// owns tokens [2 xr, 2 xr + 2) x channels [8 xv, 8 xv + 8) (raw values of
-// type Tx with 3 rows of history in front when XCONV, post-conv otherwise).
-template <typename Tx, bool XCONV>
+// One chunk's x for the whole workgroup: thread (xv = tid % XV,
+// xr = tid / XV) owns tokens [RX xr, RX xr + RX) x channels [8 xv, 8 xv + 8)
+// of the walker's channels from p0 (raw values of type Tx with 3 rows of
+// history in front when XCONV, post-conv otherwise).
+template <typename Tx, bool XCONV, int Q>
 struct StageX {
-  static constexpr int HX = XCONV ? 3 : 0;
-  RowLoad<Tx, 2 + HX> rx;
+  using G_ = Geo<Q>;
+  static constexpr int HX = XCONV ? 3 : 0, RX = G_::RX, XV = G_::XV;
+  RowLoad<Tx, RX + HX> rx;
 
   template <bool HIST>
-  __device__ __forceinline__ void load(const ScanArgs& a, int b, int h, int t0) {
+  __device__ __forceinline__ void load(const ScanArgs& a, int b, int h, int p0, int t0) {
     const int tid = threadIdx.x;
-    const int xv = tid & 7, xr = tid >> 3;
+    const int xv = tid % XV, xr = tid / XV;
     const int cdim = a.nheads * P + 2 * a.ngroups * N;
-    rx.template load<HIST>(a, static_cast<const Tx*>(a.x), a.x_stride, h * P + 8 * xv,
-                           h * P + 8 * xv, cdim, b, t0 + 2 * xr - HX);
+    const int ch = h * P + p0 + 8 * xv;
+    rx.template load<HIST>(a, static_cast<const Tx*>(a.x), a.x_stride, ch, ch, cdim, b,
+                           t0 + RX * xr - HX);
   }
 
-  // the thread's 2 x 8 post-conv values, tmp[8 i + e] = x[2 xr + i][8 xv + e]
+  // the thread's RX x 8 post-conv values, tmp[8 i + e] = x[RX xr + i][8 xv + e]
   // (zero past the end of the sequence)
   template <bool CHECK>
   __device__ __forceinline__ void compute(const ScanArgs& a, const float* cw, int t0, int Lc,
                                           float* tmp) const {
     const int tid = threadIdx.x;
-    const int xv = tid & 7, xr = tid >> 3;
+    const int xv = tid % XV, xr = tid / XV;
     if constexpr (XCONV)
-      conv_rows_to<Tx, 2, float, CHECK>(a, rx, t0 + 2 * xr - 3, cw, P, 8 * xv, 2 * xr, Lc, tmp, 8);
+      conv_rows_to<Tx, RX, float, CHECK>(a, rx, t0 + RX * xr - 3, cw, G_::PW, 8 * xv, RX * xr, Lc,
+                                         tmp, 8);
     else
-      copy_rows_to<Tx, 2, float, CHECK>(a, rx, t0 + 2 * xr, 2 * xr, Lc, tmp, 8);
+      copy_rows_to<Tx, RX, float, CHECK>(a, rx, t0 + RX * xr, RX * xr, Lc, tmp, 8);
   }
 };
 
-// Walker index of this workgroup: (sequence b, head h, segment seg), with
-// the heads of one (b, group, segment) contiguous and dealt to one XCD.
+// Walker index of this workgroup: (sequence b, head h, segment seg, channel
+// slice ps), with the walkers of one (b, group, segment) contiguous and dealt
+// to one XCD.
 struct Walker {
-  int b, h, seg;
+  int b, h, seg, ps;
 };
-__device__ __forceinline__ Walker walker_of(int lin, int total, int H, int G, int nsegs) {
-  // item order: ((b * nsegs + seg) * G + g) * hpg + hh; lin -> item puts
-  // item ranges of length total/8 on one XCD (lin % 8)
+__device__ __forceinline__ Walker walker_of(int lin, int total, int H, int G, int nsegs,
+                                            int nps) {
+  // item order: (((b * nsegs + seg) * G + g) * hpg + hh) * nps + ps; lin ->
+  // item puts item ranges of length total/8 on one XCD (lin % 8)
   const int per = total / NXCD;
   int item = lin;
   if (lin < per * NXCD) item = (lin % NXCD) * per + lin / NXCD;
+  const int ps = item % nps;
+  item /= nps;
   const int hpg = H / G;
   const int hh = item % hpg;
   int rest = item / hpg;
@@ -555,55 +618,59 @@ __device__ __forceinline__ Walker walker_of(int lin, int total, int H, int G, in
   rest /= G;
   const int seg = rest % nsegs;
   const int b = rest / nsegs;
-  return Walker{b, g * hpg + hh, seg};
+  return Walker{b, g * hpg + hh, seg, ps};
 }
 
-template <typename Tx, typename Ta, typename Ty, bool XCONV, bool STATE_ONLY>
+template <typename Tx, typename Ta, typename Ty, bool XCONV, bool STATE_ONLY, int Q>
 __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
+  using G_ = Geo<Q>;
+  constexpr int PW = G_::PW, NRT = G_::NRT, KQ = G_::KQ, NPT = G_::NPT, NIT = G_::NIT;
+  constexpr int NPJ = G_::NPJ, LDT = G_::LDT, PROWS = G_::PROWS, LDX = G_::LDX;
+  constexpr int RX = G_::RX, XV = G_::XV, DW = G_::DW;
   constexpr bool OUT = !STATE_ONLY;
   __shared__ __attribute__((aligned(16))) bf16 sXh[OUT ? PROWS * LDT : 8];  // x hi [p][s]
   __shared__ __attribute__((aligned(16))) bf16 sXWh[PROWS * LDT];            // (x o w) hi
   __shared__ __attribute__((aligned(16))) bf16 sXWl[PROWS * LDT];            // (x o w) lo
   __shared__ __attribute__((aligned(16))) float sX32[OUT ? Q * LDX : 4];  // x [t][p]
-  __shared__ __attribute__((aligned(16))) bf16 sH[OUT ? P * LDB : 8];     // H [p][n]
+  __shared__ __attribute__((aligned(16))) bf16 sH[OUT ? PW * LDB : 8];    // H [p][n]
   // the decay of a chunk, in two buffers (chunk c in buffer c % 2): the next
   // chunk's is computed while the current one is in use
   __shared__ __attribute__((aligned(16))) float sLam[2 * Q];
   __shared__ __attribute__((aligned(16))) float sDel[2 * Q];
   // exp(Lam_r - Lam_s) delta_s, r the last token of s's 16-token tile
   __shared__ __attribute__((aligned(16))) float sE[OUT ? 2 * Q : 4];
-  __shared__ float sRed[2];
-  __shared__ __attribute__((aligned(16))) float sCw[XCONV ? 5 * P : 4];  // x-channel conv
+  __shared__ float sRed[2 * DW];  // each decay wave's total, per buffer
+  __shared__ __attribute__((aligned(16))) float sCw[XCONV ? 5 * PW : 4];  // x-channel conv
 
   const int H = a.nheads, G = a.ngroups, L = a.seqlen;
   // pass 1 (state-only) walks segments 0..nseg-2, pass 2 all segments
   const int nsegs = STATE_ONLY ? a.nseg - 1 : a.nseg;
-  const Walker wk = walker_of(blockIdx.x, gridDim.x, H, G, nsegs);
+  const Walker wk = walker_of(blockIdx.x, gridDim.x, H, G, nsegs, G_::NPS);
   const int b = wk.b, h = wk.h, seg = wk.seg;
+  const int p0 = wk.ps * PW;  // the walker's first channel of the head
   const int bh = b * H + h;
   const int hpg = H / G, g = h / hpg;
   const int HP = H * P, GN = G * N, cdim = HP + 2 * GN;
   const int nc = (L + Q - 1) / Q;
   const int cbeg = seg * a.seg_chunks;
   const int cend = min(nc, cbeg + a.seg_chunks);
-  const bf16* pack = static_cast<const bf16*>(a.bc_pack) + (int64_t)(b * G + g) * nc * PACK;
+  const bf16* pack = static_cast<const bf16*>(a.bc_pack) + (int64_t)(b * G + g) * nc * G_::PACK;
 
   const int tid = threadIdx.x;
   // the wave index is uniform over the wave: held in a scalar register, the
   // branches on it below are scalar branches, not lane masks
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l16 = lane & 15, q = lane >> 4;
-  const int rt = w < 4 ? w : 11 - w;  // output tokens [16 rt, 16 rt + 16)
-  const int tcol = 16 * rt + l16;     // output token of this lane
-  const int xv = tid & 7, xr = tid >> 3;  // x staging: channels 8 xv.., tokens 2 xr..
+  const int pjb = G_::pj_base(w);      // first channel tile of the wave's items
+  const int xv = tid % XV, xr = tid / XV;  // x staging: channels 8 xv.., tokens RX xr..
   const float Ah = a.A[h];
   const float Dh = a.D ? a.D[h] : 0.f;
   const float dtb = a.dt_bias ? a.dt_bias[h] : 0.f;
   const Tx* xg = static_cast<const Tx*>(a.x);
 
   // ---- incoming state.  The state is accumulated transposed, as H^T [n][p]:
-  //      element r of hacc[pt] is (n = 16 w + 4 q + r, p = 16 pt + l16), so
-  //      that each lane holds 4 consecutive n of one row p of H [p][n].
+  //      element r of hacc[pt] is (n = 16 w + 4 q + r, p = p0 + 16 pt + l16),
+  //      so that each lane holds 4 consecutive n of one row p of H [p][n].
   const float* h_in = nullptr;
   if (OUT) {
     if (a.nseg > 1)
@@ -612,43 +679,43 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
       h_in = a.initial_state ? a.initial_state + (int64_t)bh * P * N : nullptr;
   }
   const int hoff = 16 * w + 4 * q;  // the lane's first n in a row of H
-  f32x4 hacc[4];
+  f32x4 hacc[NPT];
 #pragma unroll
-  for (int pt = 0; pt < 4; ++pt) {
+  for (int pt = 0; pt < NPT; ++pt) {
     const int p = 16 * pt + l16;
-    hacc[pt] = h_in ? *reinterpret_cast<const f32x4*>(h_in + p * N + hoff) : f32x4{};
+    hacc[pt] = h_in ? *reinterpret_cast<const f32x4*>(h_in + (p0 + p) * N + hoff) : f32x4{};
     if (OUT) *reinterpret_cast<bf16x4*>(sH + p * LDB + hoff) = to_bf16x4(hacc[pt]);
   }
   float log_decay = 0.f;  // sum of delta*A over the segment (state-only pass)
-  if (XCONV && tid < P) {
-    // the conv of this head's x channels: read at every chunk from LDS (the
+  if (XCONV && tid < PW) {
+    // the conv of this walker's x channels: read at every chunk from LDS (the
     // first read follows the barrier at the top of the chunk loop)
     const int K = a.conv_k;
-    const int64_t ch = (int64_t)h * P + tid;
+    const int64_t ch = (int64_t)h * P + p0 + tid;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int k = j - (4 - K);
-      sCw[j * P + tid] = k >= 0 ? a.conv_w[ch * K + k] : 0.f;
+      sCw[j * PW + tid] = k >= 0 ? a.conv_w[ch * K + k] : 0.f;
     }
-    sCw[4 * P + tid] = a.conv_b ? a.conv_b[ch] : 0.f;
+    sCw[4 * PW + tid] = a.conv_b ? a.conv_b[ch] : 0.f;
   }
 
   // Two barriers per chunk.  After the first: the bf16 copy of the state,
   // the conv of x and its staging, and the split of x o w (the chunk's decay
   // is already in LDS).  After the second: the state product, the read-out,
-  // the intra-chunk product and the epilogue, and then waves 0 and 1 compute
-  // the next chunk's decay.  Chunk c+1's x and dt are loaded as soon as
-  // chunk c is staged, so they are in flight while chunk c is computed.  The
-  // per-wave operands (B^T rows, C rows, C B^T tiles) and z are loaded
+  // the intra-chunk product and the epilogue, and then waves 0 .. DW-1
+  // compute the next chunk's decay.  Chunk c+1's x and dt are loaded as soon
+  // as chunk c is staged, so they are in flight while chunk c is computed.
+  // The per-wave operands (B^T rows, C rows, C B^T tiles) and z are loaded
   // within their own chunk, ahead of their first use.
-  StageX<Tx, XCONV> sx;
+  StageX<Tx, XCONV, Q> sx;
   // the prefetched dt stays in its raw form until it is used, so that no
   // conversion waits for the load while the prefetch is in flight
   Raw1<Ta> dtv;
   // (HIST: whether the chunk may be the first, whose conv reads the history)
   auto prefetch = [&](int cc, auto hist) {
     const int tt0 = cc * Q;
-    sx.template load<decltype(hist)::value>(a, b, h, tt0);
+    sx.template load<decltype(hist)::value>(a, b, h, p0, tt0);
     // every lane loads (threads tid >= Q all re-read the chunk's first token,
     // one cache line, and never use it), so no branch separates these loads
     // from the ones after
@@ -656,7 +723,7 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
              ((int64_t)b * L + min(tt0 + (tid < Q ? tid : 0), L - 1)) * a.dt_stride + h);
   };
   // delta, the cumulative log decay and the tile decays of chunk cc into
-  // buffer cc % 2, by waves 0 and 1 (one token per lane) from the dt in dtv
+  // buffer cc % 2, by waves 0 .. DW-1 (one token per lane) from the dt in dtv
   auto delta_step = [&](int cc) {
     const int Lcc = min(Q, L - cc * Q);
     const int buf = (cc & 1) * Q;
@@ -665,11 +732,11 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     if (tid >= Lcc) d = 0.f;
     sDel[buf + tid] = d;
     // inclusive prefix sum of delta A over the wave's 64 tokens (fixed
-    // order); the second wave's values lack the first wave's total, which
-    // the readers add (lam() below)
+    // order); the values of a later wave lack the totals of the waves before
+    // it, which the readers add (lam() below)
     const float v = wave_prefix_sum(d * Ah);
     sLam[buf + tid] = v;
-    if (tid == 63) sRed[cc & 1] = v;
+    if (lane == 63) sRed[(cc & 1) * DW + w] = v;
     // the tile's last token is in the same wave, so the difference needs
     // no carry; it is <= 0 (the decay only shrinks)
     const float vr = __shfl(v, lane | 15, 64);
@@ -677,30 +744,36 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
   };
   if (cbeg < cend) {
     prefetch(cbeg, std::true_type{});
-    if (w < 2) delta_step(cbeg);  // visible past the first barrier of the loop
+    if (w < DW) delta_step(cbeg);  // visible past the first barrier of the loop
   }
 
   for (int c = cbeg; c < cend; ++c) {
     const int t0 = c * Q;
     const int Lc = min(Q, L - t0);
     const int64_t row0 = (int64_t)b * L + t0;
-    const bf16* pk = pack + (int64_t)c * PACK;
-    // rt, re-read at every chunk through an empty asm statement: the
-    // compiler then evaluates the scalar tests on it where they are used
-    // instead of hoisting them out of the loop as lane masks, which exhausts
-    // the scalar registers
-    int rtc = rt;
-    asm volatile("" : "+s"(rtc));
-
-    // this wave's operands: B^T rows of its state columns (bth/btl, A operand
-    // [i = n][k = s]) now, C rows of its tokens (cf, [k = n][j = t]) and z
-    // after the staging
-    bf16x8 cf[4], bth[4], btl[4];
+    const bf16* pk = pack + (int64_t)c * G_::PACK;
+    // the items' row tiles, re-read at every chunk through an empty asm
+    // statement: the compiler then evaluates the scalar tests on them where
+    // they are used instead of hoisting them out of the loop as lane masks,
+    // which exhausts the scalar registers
+    int rtc[NIT];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const uint32_t o = (((w * 4 + kk) * 64 + lane) * 8) * 2;
-      bth[kk] = ldg8(at_bytes(pk + PK_BTH, o));
-      btl[kk] = ldg8(at_bytes(pk + PK_BTL, o));
+    for (int it = 0; it < NIT; ++it) {
+      rtc[it] = G_::rt_of(w, it);
+      asm volatile("" : "+s"(rtc[it]));
+    }
+
+    // this wave's B^T rows of its state columns (bth/btl, A operand
+    // [i = n][k = s]) now when they fit in registers; C rows of its tokens
+    // (cf, [k = n][j = t]) and z after the staging
+    bf16x8 cf[4], bth[G_::BT_EARLY ? KQ : 1], btl[G_::BT_EARLY ? KQ : 1];
+    auto bt_off = [&](int kk) { return (uint32_t)(((w * KQ + kk) * 64 + lane) * 8) * 2; };
+    if constexpr (G_::BT_EARLY) {
+#pragma unroll
+      for (int kk = 0; kk < KQ; ++kk) {
+        bth[kk] = ldg8(at_bytes(pk + G_::PK_BTH, bt_off(kk)));
+        btl[kk] = ldg8(at_bytes(pk + G_::PK_BTL, bt_off(kk)));
+      }
     }
 
     lds_barrier();  // the previous chunk is done with every LDS buffer
@@ -708,23 +781,33 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
       // the bf16 copy of the state for this chunk's read-out (the previous
       // chunk's read-out of the older state is complete past the barrier)
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt)
+      for (int pt = 0; pt < NPT; ++pt)
         *reinterpret_cast<bf16x4*>(sH + (16 * pt + l16) * LDB + hoff) = to_bf16x4(hacc[pt]);
     }
     // this chunk's decay (computed during the previous chunk, or before the
-    // loop): Lam_s, the cumulative log decay of the chunk up to token s
+    // loop): Lam_s, the cumulative log decay of the chunk up to token s,
+    // is the scanning wave's value plus the totals of the waves before it
+    // (added in a fixed order)
     const float* cLam = sLam + (c & 1) * Q;
     const float* cDel = sDel + (c & 1) * Q;
     const float* cE = sE + (OUT ? (c & 1) * Q : 0);
-    const float carry = sRed[c & 1];
-    auto lam = [&](int s) { return cLam[s] + (s >= 64 ? carry : 0.f); };
+    float pre[DW];  // pre[k]: the carry into the tokens of wave k
+    pre[0] = 0.f;
+#pragma unroll
+    for (int k = 1; k < DW; ++k) pre[k] = pre[k - 1] + sRed[(c & 1) * DW + k - 1];
+    auto carry_at = [&](int s) {
+      if constexpr (DW == 1) return 0.f;
+      else if constexpr (DW == 2) return s >= 64 ? pre[1] : 0.f;
+      else return s >= 128 ? (s >= 192 ? pre[3] : pre[2]) : (s >= 64 ? pre[1] : 0.f);
+    };
+    auto lam = [&](int s) { return cLam[s] + carry_at(s); };
     // the decay to the chunk's last token: token Lc - 1, not Q - 1 -- past
     // the end the increments are 0, but they are summed in another order, so
     // the two can differ by an ulp, which is large when |Lam| is
     const float lam_last = lam(Lc - 1);
     if (STATE_ONLY) log_decay += lam_last;
 
-    float xt[16];  // xt[8 i + e] = x[2 xr + i][8 xv + e], post-conv fp32
+    float xt[8 * RX];  // xt[8 i + e] = x[RX xr + i][8 xv + e], post-conv fp32
     // the selects for rows outside the sequence and tokens past its end only
     // where they can occur: its first chunk and a last chunk cut short
     // (a uniform test)
@@ -734,8 +817,8 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
       sx.template compute<false>(a, sCw, t0, Lc, xt);
     if (OUT) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        float* d = sX32 + (2 * xr + i) * LDX + 8 * xv;
+      for (int i = 0; i < RX; ++i) {
+        float* d = sX32 + (RX * xr + i) * LDX + 8 * xv;
         *reinterpret_cast<float4*>(d) = make_float4(xt[8 * i], xt[8 * i + 1], xt[8 * i + 2],
                                                     xt[8 * i + 3]);
         *reinterpret_cast<float4*>(d + 4) = make_float4(xt[8 * i + 4], xt[8 * i + 5],
@@ -743,30 +826,38 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        bf16x2 v2;
-        v2[0] = (bf16)xt[e];
-        v2[1] = (bf16)xt[8 + e];
-        *reinterpret_cast<bf16x2*>(sXh + prow(8 * xv + e) * LDT + 2 * xr) = v2;
+        bf16* d = sXh + prow(8 * xv + e) * LDT + RX * xr;
+        if constexpr (RX == 2) {
+          bf16x2 v2;
+          v2[0] = (bf16)xt[e];
+          v2[1] = (bf16)xt[8 + e];
+          *reinterpret_cast<bf16x2*>(d) = v2;
+        } else {
+          *d = (bf16)xt[e];
+        }
       }
     }
 
     // ---- (x o w) split into bf16 hi + lo, [p][s], once per workgroup, with
-    //      w_s = exp(Lam_last - Lam_s) delta_s of the thread's two tokens
+    //      w_s = exp(Lam_last - Lam_s) delta_s of the thread's tokens
     {
-      const float w0 = __expf(lam_last - lam(2 * xr)) * cDel[2 * xr];
-      const float w1 = __expf(lam_last - lam(2 * xr + 1)) * cDel[2 * xr + 1];
+      float wt[RX];
+#pragma unroll
+      for (int i = 0; i < RX; ++i)
+        wt[i] = __expf(lam_last - lam(RX * xr + i)) * cDel[RX * xr + i];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        bf16x2 hi, lo;
-        bf16 hh, ll;
-        split1(xt[e] * w0, hh, ll);
-        hi[0] = hh;
-        lo[0] = ll;
-        split1(xt[8 + e] * w1, hh, ll);
-        hi[1] = hh;
-        lo[1] = ll;
-        *reinterpret_cast<bf16x2*>(sXWh + prow(8 * xv + e) * LDT + 2 * xr) = hi;
-        *reinterpret_cast<bf16x2*>(sXWl + prow(8 * xv + e) * LDT + 2 * xr) = lo;
+        bf16 hh[RX], ll[RX];
+#pragma unroll
+        for (int i = 0; i < RX; ++i) split1(xt[8 * i + e] * wt[i], hh[i], ll[i]);
+        const int o = prow(8 * xv + e) * LDT + RX * xr;
+        if constexpr (RX == 2) {
+          *reinterpret_cast<bf16x2*>(sXWh + o) = bf16x2{hh[0], hh[1]};
+          *reinterpret_cast<bf16x2*>(sXWl + o) = bf16x2{ll[0], ll[1]};
+        } else {
+          sXWh[o] = hh[0];
+          sXWl[o] = ll[0];
+        }
       }
     }
 
@@ -774,113 +865,141 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     // chunk (all waves issue theirs at the same time, and they share the
     // CU's load path): the next chunk's x and dt now, the C rows and C B^T
     // tiles after the staging barrier, z after the state product.
-    Raw4<Ta> zr[4];
-    f32x4 cbt[Q / 16];  // B C^T tiles u <= rt of this wave's tokens (u > rt: unused)
+    Raw4<Ta> zr[NPJ];
+    // B C^T tiles u <= rt of the item's tokens (u > rt: unused)
+    f32x4 cbt[G_::CB_EARLY ? NRT : 1];
+    // this lane's part of tile u of row tile rt
+    auto cb_src = [&](int rt, int u) {
+      return at_bytes(reinterpret_cast<const float*>(pk + G_::PK_CB) + (tri(rt) + u) * 256,
+                      (uint32_t)lane * 16);
+    };
+    // C rows of item it's tokens and its C B^T tiles
+    auto load_item = [&](int it) {
+      const int rt = rtc[it];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        cf[kk] = ldg8(at_bytes(pk + G_::PK_C, (uint32_t)(((rt * 4 + kk) * 64 + lane) * 8) * 2));
+      // tiles past rt are not loaded (wave-uniform branches; the loads
+      // after these still retire after them)
+      if constexpr (G_::CB_EARLY) {
+#pragma unroll
+        for (int u = 0; u < NRT; ++u)
+          if (u <= rt) cbt[u] = *reinterpret_cast<const f32x4*>(cb_src(rt, u));
+      }
+    };
     // unconditional (the last chunk re-reads itself), so that no branch
     // separates these loads from the ones after
     // (chunk c + 1 >= 1 reads no history; at the last chunk the loads repeat
     // it and go unused)
     prefetch(min(c + 1, cend - 1), std::false_type{});
     lds_barrier();  // x, its bf16 copy and (x o w) are complete
-    if (OUT) {
-      // C rows of this wave's tokens and its C B^T tiles
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        cf[kk] = ldg8(at_bytes(pk + PK_C, (uint32_t)(((rt * 4 + kk) * 64 + lane) * 8) * 2));
-      const float* cbsrc = at_bytes(reinterpret_cast<const float*>(pk + PK_CB) + tri(rt) * 256,
-                                    (uint32_t)lane * 16);
-      // tiles past rt are not loaded (wave-uniform branches; the loads
-      // after these still retire after them)
-#pragma unroll
-      for (int u = 0; u < Q / 16; ++u)
-        if (u <= rtc) cbt[u] = *reinterpret_cast<const f32x4*>(cbsrc + u * 256);
-    }
+    if (OUT) load_item(0);
     // ---- state: H^T <- exp(Lam_last) H^T + B^T (X o w), operands split
-    //      hi + lo; this wave's rows n of H^T, all 64 columns p.  The read-out below
-    //      still uses the previous state through its bf16 copy in sH, which
-    //      is replaced at the start of the next chunk.
+    //      hi + lo; this wave's rows n of H^T, all the walker's columns p.
+    //      The read-out below still uses the previous state through its
+    //      bf16 copy in sH, which is replaced at the start of the next chunk.
     const float gamma = __expf(lam_last);
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) hacc[pt] *= gamma;
+    for (int pt = 0; pt < NPT; ++pt) hacc[pt] *= gamma;
 #pragma unroll
-    for (int kk = 0; kk < Q / 32; ++kk) {
-      bf16x8 xhi[4], xlo[4];
+    for (int kk = 0; kk < KQ; ++kk) {
+      bf16x8 bh_k, bl_k;
+      if constexpr (G_::BT_EARLY) {
+        bh_k = bth[kk];
+        bl_k = btl[kk];
+      } else {
+        bh_k = ldg8(at_bytes(pk + G_::PK_BTH, bt_off(kk)));
+        bl_k = ldg8(at_bytes(pk + G_::PK_BTL, bt_off(kk)));
+      }
+      bf16x8 xhi[NPT], xlo[NPT];
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
+      for (int pt = 0; pt < NPT; ++pt) {
         const int o = prow(16 * pt + l16) * LDT + 32 * kk + 8 * q;
         xhi[pt] = lds8(sXWh + o);
         xlo[pt] = lds8(sXWl + o);
       }
-      // the four accumulators in turn, so that no product waits for the
-      // one before it
+      // the accumulators in turn, so that no product waits for the one
+      // before it
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) hacc[pt] = mfma(bth[kk], xhi[pt], hacc[pt]);
+      for (int pt = 0; pt < NPT; ++pt) hacc[pt] = mfma(bh_k, xhi[pt], hacc[pt]);
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) hacc[pt] = mfma(btl[kk], xhi[pt], hacc[pt]);
+      for (int pt = 0; pt < NPT; ++pt) hacc[pt] = mfma(bl_k, xhi[pt], hacc[pt]);
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) hacc[pt] = mfma(bth[kk], xlo[pt], hacc[pt]);
+      for (int pt = 0; pt < NPT; ++pt) hacc[pt] = mfma(bh_k, xlo[pt], hacc[pt]);
       // keep the operand loads of the next K step below this one's products
       // (hoisting them all at once costs more registers than the wave has)
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    if (OUT) {
-      // z of token tcol, channels 16 pj + 4 q .. (tokens past the end re-read
-      // the last one and are never stored); without a gate the loads read
-      // the start of the B|C pack instead (at least 128 KiB of global memory;
-      // the values are not used): no branch, and both pointers stay global
-      // so the loads are not flat
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      if (!OUT) break;
+      const int rt = rtc[it];
+      const int tcol = 16 * rt + l16;  // output token of this lane
+      if (it > 0) load_item(it);
+      // z of token tcol, channels p0 + 16 (pjb + pj) + 4 q .. (tokens past the
+      // end re-read the last one and are never stored); without a gate the
+      // loads read the start of the B|C pack instead (at least 58 KiB of
+      // global memory; the values are not used): no branch, and both
+      // pointers stay global so the loads are not flat
       const Ta* zrow = a.z != nullptr
                            ? static_cast<const Ta*>(a.z) +
-                                 (row0 + min(tcol, Lc - 1)) * a.z_stride + h * P + 4 * q
+                                 (row0 + min(tcol, Lc - 1)) * a.z_stride + h * P + p0 +
+                                 16 * pjb + 4 * q
                            : static_cast<const Ta*>(a.bc_pack) + 4 * q;
 #pragma unroll
-      for (int pj = 0; pj < 4; ++pj) zr[pj].load(zrow + 16 * pj);
-    }
-    if (OUT) {
+      for (int pj = 0; pj < NPJ; ++pj) zr[pj].load(zrow + 16 * pj);
+
       // ---- inter-chunk read-out, transposed: Y^T = H C^T scaled by exp(Lam_t);
-      //      element r of yacc[pj] is (p = 16 pj + 4 q + r, t = tcol)
-      f32x4 yacc[4] = {};
+      //      element r of yacc[pj] is (p = p0 + 16 (pjb + pj) + 4 q + r, t = tcol)
+      f32x4 yacc[NPJ] = {};
 #pragma unroll
       for (int kk = 0; kk < N / 32; ++kk)
 #pragma unroll
-        for (int pj = 0; pj < 4; ++pj)
-          yacc[pj] = mfma(lds8(sH + (16 * pj + l16) * LDB + 32 * kk + 8 * q), cf[kk], yacc[pj]);
+        for (int pj = 0; pj < NPJ; ++pj)
+          yacc[pj] = mfma(lds8(sH + (16 * (pjb + pj) + l16) * LDB + 32 * kk + 8 * q), cf[kk],
+                          yacc[pj]);
       const float lam_t = lam(tcol);
       {
         const float e = __expf(lam_t);
 #pragma unroll
-        for (int pj = 0; pj < 4; ++pj) yacc[pj] *= e;
+        for (int pj = 0; pj < NPJ; ++pj) yacc[pj] *= e;
       }
 
       // ---- intra-chunk: Y^T += X^T (C B^T o decay mask)^T over the source
       //      tiles u <= rt, two 16-token tiles per K=32 step
 #pragma unroll
-      for (int u0 = 0; u0 < Q / 16; u0 += 2) {
-        if (u0 > rtc) break;
+      for (int u0 = 0; u0 < NRT; u0 += 2) {
+        if (u0 > rt) break;
         // the step's x operands first, so that their LDS latency is hidden
         // behind the mask arithmetic
-        bf16x8 xf[4];
+        bf16x8 xf[NPJ];
 #pragma unroll
-        for (int pj = 0; pj < 4; ++pj) {
-          const bf16* xp = sXh + prow(16 * pj + l16) * LDT + 16 * u0 + 4 * q;
+        for (int pj = 0; pj < NPJ; ++pj) {
+          const bf16* xp = sXh + prow(16 * (pjb + pj) + l16) * LDT + 16 * u0 + 4 * q;
           const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(xp);
           const bf16x4 x1 = *reinterpret_cast<const bf16x4*>(xp + 16);
           xf[pj] = bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        }
+        f32x4 cbp[2];  // the step's two tiles, when they are loaded step by step
+        if constexpr (!G_::CB_EARLY) {
+#pragma unroll
+          for (int half = 0; half < 2; ++half)
+            if (u0 + half <= rt) cbp[half] = *reinterpret_cast<const f32x4*>(cb_src(rt, u0 + half));
         }
         bf16x8 mf;  // element 4 half + r: M[t = tcol][s = 16 (u0 + half) + 4 q + r]
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int u = u0 + half;
-          if (u > rtc) {  // past the diagonal tile (rt even): a zero K half
+          if (u > rt) {  // past the diagonal tile (rt even): a zero K half
 #pragma unroll
             for (int r = 0; r < 4; ++r) mf[4 * half + r] = (bf16)0.f;
             continue;
           }
-          const f32x4 cb = cbt[u];
+          const f32x4 cb = G_::CB_EARLY ? cbt[u] : cbp[half];
           // cb[r] = (B C^T)[s = 16 u + 4 q + r][t = tcol]
           const int s0 = 16 * u + 4 * q;
-          if (u < rtc) {
+          if (u < rt) {
             // below the diagonal every s precedes every t: the decay
             // exp(Lam_t - Lam_s) factors through the tile's last token r as
             // exp(Lam_t - Lam_r) exp(Lam_r - Lam_s), both factors <= 1
@@ -893,7 +1012,7 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
           } else {
             const float4 l4 = *reinterpret_cast<const float4*>(cLam + s0);
             const float4 d4 = *reinterpret_cast<const float4*>(cDel + s0);
-            const float cs = u >= 4 ? carry : 0.f;  // the 4 tokens share a wave
+            const float cs = carry_at(16 * u);  // the 4 tokens share a wave
             const float ls[4] = {l4.x + cs, l4.y + cs, l4.z + cs, l4.w + cs};
             const float ds[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
@@ -907,18 +1026,19 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
           }
         }
 #pragma unroll
-        for (int pj = 0; pj < 4; ++pj) yacc[pj] = mfma(xf[pj], mf, yacc[pj]);
+        for (int pj = 0; pj < NPJ; ++pj) yacc[pj] = mfma(xf[pj], mf, yacc[pj]);
       }
 
       // ---- epilogue: skip, gate, store 4 consecutive channels per pj
       if (tcol < Lc) {
-        Ty* yrow = static_cast<Ty*>(a.y) + (row0 + tcol) * a.y_stride + h * P + 4 * q;
-        const float* xrow = sX32 + tcol * LDX + 4 * q;
+        Ty* yrow = static_cast<Ty*>(a.y) + (row0 + tcol) * a.y_stride + h * P + p0 + 16 * pjb +
+                   4 * q;
+        const float* xrow = sX32 + tcol * LDX + 16 * pjb + 4 * q;
         // one straight-line copy per case of the (uniform) gate test, so
-        // that the exponentials of all 16 outputs can be in flight together
+        // that the exponentials of all the outputs can be in flight together
         auto emit = [&](auto gated) {
 #pragma unroll
-          for (int pj = 0; pj < 4; ++pj) {
+          for (int pj = 0; pj < NPJ; ++pj) {
             const float4 x4 = *reinterpret_cast<const float4*>(xrow + 16 * pj);
             const float xs[4] = {x4.x, x4.y, x4.z, x4.w};
             float zs[4];
@@ -939,10 +1059,11 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
       }
     }
 
-    // ---- the next chunk's decay, by waves 0 and 1 (the two with the least
-    //      intra-chunk work), into the other buffer: read past the next
-    //      chunk's first barrier, while this chunk's buffer is still in use
-    if (w < 2 && c + 1 < cend) delta_step(c + 1);
+    // ---- the next chunk's decay, by waves 0 .. DW-1 (at Q = 128 the two
+    //      with the least intra-chunk work), into the other buffer: read past
+    //      the next chunk's first barrier, while this chunk's buffer is still
+    //      in use
+    if (w < DW && c + 1 < cend) delta_step(c + 1);
   }
 
   // ---- outgoing state
@@ -953,19 +1074,20 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     h_out = a.final_state ? a.final_state + (int64_t)bh * P * N : nullptr;
   if (h_out != nullptr) {
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt)
-      *reinterpret_cast<f32x4*>(h_out + (16 * pt + l16) * N + hoff) = hacc[pt];
+    for (int pt = 0; pt < NPT; ++pt)
+      *reinterpret_cast<f32x4*>(h_out + (p0 + 16 * pt + l16) * N + hoff) = hacc[pt];
   }
-  if (STATE_ONLY && tid == 0) a.seg_logdecay[(int64_t)bh * a.nseg + seg] = log_decay;
+  // (the channel slices of a head compute the same log decay; the first writes it)
+  if (STATE_ONLY && tid == 0 && p0 == 0) a.seg_logdecay[(int64_t)bh * a.nseg + seg] = log_decay;
 
-  // ---- conv history hand-over of this head's x channels (last segment; the
-  //      B and C channels are handed over by the pack kernel)
+  // ---- conv history hand-over of this walker's x channels (last segment;
+  //      the B and C channels are handed over by the pack kernel)
   if (XCONV && OUT && seg == a.nseg - 1 && a.conv_state_out != nullptr) {
     const int K = a.conv_k;
     Tx* out = static_cast<Tx*>(a.conv_state_out);
     const Tx* hin = static_cast<const Tx*>(a.conv_state_in);
-    for (int i = tid; i < (K - 1) * P; i += THREADS) {
-      const int j = i / P, c = h * P + i % P;
+    for (int i = tid; i < (K - 1) * PW; i += THREADS) {
+      const int j = i / PW, c = h * P + p0 + i % PW;
       const int tau = L - (K - 1) + j;  // < L
       Tx v = from_f32<Tx>(0.f);
       if (tau >= 0)
@@ -1012,48 +1134,67 @@ __global__ __launch_bounds__(COMBINE_THREADS) void combine_segments_kernel(ScanA
   }
 }
 
-template <typename Tx, typename Ta, typename Ty, bool XCONV>
+template <typename Tx, typename Ta, typename Ty, bool XCONV, int Q>
 hipError_t launch_walkers(const ScanArgs& a, hipStream_t stream) {
+  using G_ = Geo<Q>;
   const int nc = (a.seqlen + Q - 1) / Q;
-  hipLaunchKernelGGL((bc_pack_kernel<Tx, XCONV>), dim3(nc, a.ngroups, a.batch),
-                     dim3(PACK_THREADS), 0, stream, a,
+  hipLaunchKernelGGL((bc_pack_kernel<Tx, XCONV, Q>), dim3(nc, a.ngroups, a.batch),
+                     dim3(G_::PACK_THREADS), 0, stream, a,
                      static_cast<bf16*>(const_cast<void*>(a.bc_pack)));
   // no walker runs on a pack that was never written
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int BH = a.batch * a.nheads;
+  const int W = a.batch * a.nheads * G_::NPS;  // walkers per segment
   if (a.nseg > 1) {
-    hipLaunchKernelGGL((scan_bf16_kernel<Tx, Ta, Ty, XCONV, true>), dim3(BH * (a.nseg - 1)),
+    hipLaunchKernelGGL((scan_bf16_kernel<Tx, Ta, Ty, XCONV, true, Q>), dim3(W * (a.nseg - 1)),
                        dim3(THREADS), 0, stream, a);
-    hipLaunchKernelGGL(combine_segments_kernel, dim3(BH, COMBINE_PARTS), dim3(COMBINE_THREADS), 0,
-                       stream, a);
+    hipLaunchKernelGGL(combine_segments_kernel, dim3(a.batch * a.nheads, COMBINE_PARTS),
+                       dim3(COMBINE_THREADS), 0, stream, a);
   }
-  hipLaunchKernelGGL((scan_bf16_kernel<Tx, Ta, Ty, XCONV, false>), dim3(BH * a.nseg),
+  hipLaunchKernelGGL((scan_bf16_kernel<Tx, Ta, Ty, XCONV, false, Q>), dim3(W * a.nseg),
                      dim3(THREADS), 0, stream, a);
   return hipGetLastError();
 }
 
-template <typename Ta, typename Ty>
+template <typename Ta, typename Ty, int Q>
 hipError_t pick_x(const ScanArgs& a, ssd_dtype_t xd, hipStream_t s) {
   if (a.conv_w != nullptr)  // raw x|B|C: conv in the pack kernel and the walker
-    return xd == SSD_BF16 ? launch_walkers<bf16, Ta, Ty, true>(a, s)
-                          : launch_walkers<float, Ta, Ty, true>(a, s);
-  return xd == SSD_BF16 ? launch_walkers<bf16, Ta, Ty, false>(a, s)
-                        : launch_walkers<float, Ta, Ty, false>(a, s);
+    return xd == SSD_BF16 ? launch_walkers<bf16, Ta, Ty, true, Q>(a, s)
+                          : launch_walkers<float, Ta, Ty, true, Q>(a, s);
+  return xd == SSD_BF16 ? launch_walkers<bf16, Ta, Ty, false, Q>(a, s)
+                        : launch_walkers<float, Ta, Ty, false, Q>(a, s);
+}
+
+template <int Q>
+hipError_t pick_types(const ScanArgs& a, ssd_dtype_t xd, ssd_dtype_t ad, ssd_dtype_t yd,
+                      hipStream_t s) {
+  if (ad == SSD_BF16)
+    return yd == SSD_F32 ? pick_x<bf16, float, Q>(a, xd, s) : pick_x<bf16, bf16, Q>(a, xd, s);
+  return yd == SSD_F32 ? pick_x<float, float, Q>(a, xd, s) : pick_x<float, bf16, Q>(a, xd, s);
 }
 
 }  // namespace
 
+bool scan_bf16_supports_chunk(int chunk) { return chunk == 64 || chunk == 128 || chunk == 256; }
+
 hipError_t launch_scan_bf16(const ScanArgs& a, ssd_dtype_t xd, ssd_dtype_t ad, ssd_dtype_t yd,
                             hipStream_t s) {
-  if (ad == SSD_BF16)
-    return yd == SSD_F32 ? pick_x<bf16, float>(a, xd, s) : pick_x<bf16, bf16>(a, xd, s);
-  return yd == SSD_F32 ? pick_x<float, float>(a, xd, s) : pick_x<float, bf16>(a, xd, s);
+  switch (a.chunk) {
+    case 64: return pick_types<64>(a, xd, ad, yd, s);
+    case 128: return pick_types<128>(a, xd, ad, yd, s);
+    case 256: return pick_types<256>(a, xd, ad, yd, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
-size_t scan_bf16_pack_bytes(int batch, int seqlen, int ngroups) {
-  const size_t nc = ((size_t)seqlen + Q - 1) / Q;
-  return (size_t)batch * ngroups * nc * PACK * sizeof(bf16);
+size_t scan_bf16_pack_bytes(int batch, int seqlen, int ngroups, int chunk) {
+  const size_t nc = ((size_t)seqlen + chunk - 1) / chunk;
+  const size_t pack = chunk == 64    ? Geo<64>::PACK
+                      : chunk == 256 ? Geo<256>::PACK
+                                     : Geo<128>::PACK;
+  return (size_t)batch * ngroups * nc * pack * sizeof(bf16);
 }
+
+int scan_bf16_walkers_per_head(int chunk) { return chunk == 256 ? Geo<256>::NPS : 1; }
 
 }  // namespace ssd

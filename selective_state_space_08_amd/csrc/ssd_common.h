@@ -86,11 +86,15 @@ hipError_t launch_causal_conv1d(const void* x, int64_t x_stride, ssd_dtype_t x_d
 hipError_t launch_scan_f32(const ScanArgs& a, ssd_dtype_t xbc_dtype, ssd_dtype_t act_dtype,
                            ssd_dtype_t y_dtype, hipStream_t stream);
 
-// Runs the B|C pack pass and the walkers; a.bc_pack must hold
-// scan_bf16_pack_bytes(batch, seqlen, ngroups) bytes of workspace.
+// Runs the B|C pack pass and the walkers for a.chunk in {64, 128, 256};
+// a.bc_pack must hold scan_bf16_pack_bytes(batch, seqlen, ngroups, chunk)
+// bytes of workspace.
 hipError_t launch_scan_bf16(const ScanArgs& a, ssd_dtype_t xbc_dtype, ssd_dtype_t act_dtype,
                             ssd_dtype_t y_dtype, hipStream_t stream);
-size_t scan_bf16_pack_bytes(int batch, int seqlen, int ngroups);
+bool scan_bf16_supports_chunk(int chunk);
+size_t scan_bf16_pack_bytes(int batch, int seqlen, int ngroups, int chunk);
+// walkers per (sequence, head, segment): the head's channels are split at chunk 256
+int scan_bf16_walkers_per_head(int chunk);
 
 hipError_t launch_state_update(float* state, const void* xbc, ssd_dtype_t xbc_dtype,
                                void* ring, const float* conv_w, const float* conv_b, int K,

@@ -82,6 +82,22 @@ def test_workspace_query():
     assert lib.ssd_chunk_scan_workspace_bytes(0, 128, 8, 64, 8, 128, 128, 1, 0) == 0
 
 
+@pytest.mark.parametrize("Q", [64, 256])
+def test_workspace_query_other_chunks(Q):
+    """The pack per (sequence, group, chunk) for chunk lengths 64 and 256: C
+    and B^T hi/lo for Q tokens in bf16, and the Q/16 (Q/16 + 1) / 2 causal
+    tiles of B C^T in fp32."""
+    lib = ssd.load()
+    ntri = (Q // 16) * (Q // 16 + 1) // 2
+    pack = 3 * Q * 128 * 2 + ntri * 256 * 4
+    assert lib.ssd_chunk_scan_workspace_bytes(4, 8192, 128, 64, 8, 128, Q, 1, 1) == \
+        4 * 8 * (8192 // Q) * pack
+    assert lib.ssd_chunk_scan_workspace_bytes(2, Q + 1, 128, 64, 2, 128, Q, 1, 0) == \
+        2 * 2 * 2 * pack
+    # an unsupported chunk length on the matrix cores needs (and gets) nothing
+    assert lib.ssd_chunk_scan_workspace_bytes(2, 4096, 8, 64, 2, 128, 32, 1, 0) == 0
+
+
 # ------------------------------------------------------------------ validation
 
 class Fake:
@@ -120,6 +136,7 @@ SCAN_CASES = [
     ("dstate 64", dict(N=64), UNSUPPORTED),
     ("H % G", dict(G=3), INVALID),
     ("chunk 100 on matrix cores", dict(Q=100), UNSUPPORTED),
+    ("chunk 32 on matrix cores", dict(Q=32), UNSUPPORTED),
     ("chunk 96 on fp32", dict(Q=96, math=0), UNSUPPORTED),
     ("chunk 0", dict(Q=0), INVALID),
     ("negative seqlen", dict(L=-1), INVALID),
