@@ -324,36 +324,46 @@ template <typename Tx, int R, typename Td, bool CHECK = true>
 __device__ __forceinline__ void conv_rows_to(const ScanArgs& a, const RowLoad<Tx, R + 3>& rl,
                                              int tstart, const float* cw, int cws, int cl,
                                              int rfirst, int nvalid, Td* dst, int ld) {
-  float w4[4][8], bv[8];
+  float o[R][8];
+  // two halves of 4 channels, so that only 20 taps and a window of 12 values
+  // are held at a time (each element's arithmetic is the same either way)
 #pragma unroll
-  for (int j = 0; j < 5; ++j) {
-    const float4 lo = *reinterpret_cast<const float4*>(cw + j * cws + cl);
-    const float4 hi = *reinterpret_cast<const float4*>(cw + j * cws + cl + 4);
-    float* d = j < 4 ? w4[j] : bv;
-    d[0] = lo.x; d[1] = lo.y; d[2] = lo.z; d[3] = lo.w;
-    d[4] = hi.x; d[5] = hi.y; d[6] = hi.z; d[7] = hi.w;
-  }
-  float win[3][8];
-  rl.template get<CHECK>(a, tstart, 0, win[0]);
-  rl.template get<CHECK>(a, tstart, 1, win[1]);
-  rl.template get<CHECK>(a, tstart, 2, win[2]);
+  for (int hf = 0; hf < 2; ++hf) {
+    float w4[4][4], bv[4];
 #pragma unroll
-  for (int i = 0; i < R; ++i) {
-    float cur[8], o[8];
-    rl.template get<CHECK>(a, tstart, i + 3, cur);
-    const bool ok = !CHECK || rfirst + i < nvalid;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float u = bv[e] + w4[0][e] * win[0][e] + w4[1][e] * win[1][e] +
-                      w4[2][e] * win[2][e] + w4[3][e] * cur[e];
-      const float sv = silu_f32(u);  // for every lane, then selected
-      o[e] = ok ? sv : 0.f;
-      win[0][e] = win[1][e];
-      win[1][e] = win[2][e];
-      win[2][e] = cur[e];
+    for (int j = 0; j < 5; ++j) {
+      const float4 t = *reinterpret_cast<const float4*>(cw + j * cws + cl + 4 * hf);
+      float* d = j < 4 ? w4[j] : bv;
+      d[0] = t.x; d[1] = t.y; d[2] = t.z; d[3] = t.w;
     }
-    put8(dst + i * ld, o);
+    float win[3][4];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      float v[8];
+      rl.template get<CHECK>(a, tstart, i, v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) win[i][e] = v[4 * hf + e];
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      float v[8];
+      rl.template get<CHECK>(a, tstart, i + 3, v);
+      const bool ok = !CHECK || rfirst + i < nvalid;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float cur = v[4 * hf + e];
+        const float u = bv[e] + w4[0][e] * win[0][e] + w4[1][e] * win[1][e] +
+                        w4[2][e] * win[2][e] + w4[3][e] * cur;
+        const float sv = silu_f32(u);  // for every lane, then selected
+        o[i][4 * hf + e] = ok ? sv : 0.f;
+        win[0][e] = win[1][e];
+        win[1][e] = win[2][e];
+        win[2][e] = cur;
+      }
+    }
   }
+#pragma unroll
+  for (int i = 0; i < R; ++i) put8(dst + i * ld, o[i]);
 }
 
 // Rows as they are (post-conv input), zero for rows >= nvalid.
@@ -622,12 +632,15 @@ __device__ __forceinline__ Walker walker_of(int lin, int total, int H, int G, in
 }
 
 template <typename Tx, typename Ta, typename Ty, bool XCONV, bool STATE_ONLY, int Q>
-__global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(STATE_ONLY ? 4 : 1))) void scan_bf16_kernel(ScanArgs a) {
   using G_ = Geo<Q>;
   constexpr int PW = G_::PW, NRT = G_::NRT, KQ = G_::KQ, NPT = G_::NPT, NIT = G_::NIT;
   constexpr int NPJ = G_::NPJ, LDT = G_::LDT, PROWS = G_::PROWS, LDX = G_::LDX;
   constexpr int RX = G_::RX, XV = G_::XV, DW = G_::DW;
   constexpr bool OUT = !STATE_ONLY;
+  // (the state-only walker runs four waves per SIMD, in 128 registers, and
+  // loads its B^T rows step by step)
+  constexpr bool BT_EARLY = G_::BT_EARLY && OUT;
   __shared__ __attribute__((aligned(16))) bf16 sXh[OUT ? PROWS * LDT : 8];  // x hi [p][s]
   __shared__ __attribute__((aligned(16))) bf16 sXWh[PROWS * LDT];            // (x o w) hi
   __shared__ __attribute__((aligned(16))) bf16 sXWl[PROWS * LDT];            // (x o w) lo
@@ -766,9 +779,9 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
     // this wave's B^T rows of its state columns (bth/btl, A operand
     // [i = n][k = s]) now when they fit in registers; C rows of its tokens
     // (cf, [k = n][j = t]) and z after the staging
-    bf16x8 cf[4], bth[G_::BT_EARLY ? KQ : 1], btl[G_::BT_EARLY ? KQ : 1];
+    bf16x8 cf[4], bth[BT_EARLY ? KQ : 1], btl[BT_EARLY ? KQ : 1];
     auto bt_off = [&](int kk) { return (uint32_t)(((w * KQ + kk) * 64 + lane) * 8) * 2; };
-    if constexpr (G_::BT_EARLY) {
+    if constexpr (BT_EARLY) {
 #pragma unroll
       for (int kk = 0; kk < KQ; ++kk) {
         bth[kk] = ldg8(at_bytes(pk + G_::PK_BTH, bt_off(kk)));
@@ -904,7 +917,7 @@ __global__ __launch_bounds__(THREADS) void scan_bf16_kernel(ScanArgs a) {
 #pragma unroll
     for (int kk = 0; kk < KQ; ++kk) {
       bf16x8 bh_k, bl_k;
-      if constexpr (G_::BT_EARLY) {
+      if constexpr (BT_EARLY) {
         bh_k = bth[kk];
         bl_k = btl[kk];
       } else {
