@@ -50,9 +50,20 @@ __device__ __forceinline__ void st_stream(float4* p, float4 v) {
   const f32x4 w = {v.x, v.y, v.z, v.w};
   __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(p));
 }
+// base + off bytes, for a wave-uniform base and a per-lane offset below
+// 4 GiB: a scalar base and a 32-bit vector offset instead of a 64-bit
+// address per lane
+template <typename T>
+__device__ __forceinline__ T* at_bytes(T* base, uint32_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off);
+}
+template <typename T>
+__device__ __forceinline__ const T* at_bytes(const T* base, uint32_t off) {
+  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + off);
+}
 
 template <typename Tx, typename Ta, typename Ty>
-__global__ __launch_bounds__(THREADS) void state_update_kernel(
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(8))) void state_update_kernel(
     float* __restrict__ state, const Tx* __restrict__ xbc, Tx* __restrict__ ring,
     const float* __restrict__ conv_w, const float* __restrict__ conv_b, int K,
     const Ta* __restrict__ dt, const Ta* __restrict__ z, const float* __restrict__ A,
@@ -75,9 +86,11 @@ __global__ __launch_bounds__(THREADS) void state_update_kernel(
   // issued first, so they are in flight during it.
   const int h0 = g * hpg;
   float4* st = reinterpret_cast<float4*>(state + ((int64_t)b * H + h0) * P * N);
+  // the thread's byte offset within a head's state, pass j at + j * THREADS * 16
+  const uint32_t toff = (uint32_t)tid * 16;
   float4 cur[PASSES];
 #pragma unroll
-  for (int j = 0; j < PASSES; ++j) cur[j] = ld_stream(st + tid + THREADS * j);
+  for (int j = 0; j < PASSES; ++j) cur[j] = ld_stream(at_bytes(st, toff + j * THREADS * 16));
 
   // Everything per head that the state loop needs is read here, ahead of it:
   // inside the loop the only loads are the state stream, so waiting for one
@@ -115,45 +128,53 @@ __global__ __launch_bounds__(THREADS) void state_update_kernel(
   // thread -> float4 column n4 = tid % 32 (fixed), rows p = tid / 32 + ROWS_PER_PASS j
   const int col = tid & 31;
   const int row0 = tid >> 5;
-  const float4 Bv = reinterpret_cast<const float4*>(sxc + nx)[col];
-  const float4 Cv = reinterpret_cast<const float4*>(sxc + nx + N)[col];
 
 
-  for (int hh = 0; hh < hpg; ++hh) {
+  // one head: update the state in v, store it and the outputs
+  auto head = [&](int hh, float4 (&v)[PASSES]) {
     const int h = h0 + hh;
-    float4 nxt[PASSES];
-    if (hh + 1 < hpg) {
-      const float4* sn = st + (int64_t)(hh + 1) * (P * N / 4);
-#pragma unroll
-      for (int j = 0; j < PASSES; ++j) nxt[j] = ld_stream(sn + tid + THREADS * j);
-    }
     const float delta = sdel[hh];
     const float a = sdec[hh];
     const float Dh = sskip[hh];
+    const float4 Bv = reinterpret_cast<const float4*>(sxc + nx)[col];
+    const float4 Cv = reinterpret_cast<const float4*>(sxc + nx + N)[col];
     float4* sh = st + (int64_t)hh * (P * N / 4);
+    Ty* yh = y + (int64_t)b * HP + (int64_t)h * P;
 #pragma unroll
     for (int j = 0; j < PASSES; ++j) {
       const int p = row0 + ROWS_PER_PASS * j;
       const float xp = sxc[hh * P + p];
       const float dx = delta * xp;
-      float4 s = cur[j];
+      float4 s = v[j];
       s.x = a * s.x + dx * Bv.x;
       s.y = a * s.y + dx * Bv.y;
       s.z = a * s.z + dx * Bv.z;
       s.w = a * s.w + dx * Bv.w;
-      st_stream(sh + tid + THREADS * j, s);
+      st_stream(at_bytes(sh, toff + j * THREADS * 16), s);
       float acc = s.x * Cv.x + s.y * Cv.y + s.z * Cv.z + s.w * Cv.w;
       // sum over the 32 lanes holding row p (fixed butterfly order: deterministic)
 #pragma unroll
       for (int m = 16; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 32);
       if (col == 0) {
         const float yv = (acc + Dh * xp) * sgate[hh * P + p];
-        y[(int64_t)b * HP + h * P + p] = from_f32<Ty>(yv);
+        yh[p] = from_f32<Ty>(yv);
       }
     }
-    if (hh + 1 < hpg) {
+  };
+  auto prefetch = [&](int hh, float4 (&v)[PASSES]) {
+    const float4* sn = st + (int64_t)hh * (P * N / 4);
 #pragma unroll
-      for (int j = 0; j < PASSES; ++j) cur[j] = nxt[j];
+    for (int j = 0; j < PASSES; ++j) v[j] = ld_stream(at_bytes(sn, toff + j * THREADS * 16));
+  };
+  // two register sets in turn: head hh from one while head hh + 1 loads
+  // into the other
+  float4 alt[PASSES];
+  for (int hh = 0; hh < hpg; hh += 2) {
+    if (hh + 1 < hpg) prefetch(hh + 1, alt);
+    head(hh, cur);
+    if (hh + 1 < hpg) {
+      if (hh + 2 < hpg) prefetch(hh + 2, cur);
+      head(hh + 1, alt);
     }
   }
 }
