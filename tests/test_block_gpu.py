@@ -12,7 +12,9 @@ Tolerances (derived from the arithmetic):
                relative RMS error <= 1e-2.  The block rounds three
                intermediates to bf16 (the normed input, the in_proj output and
                the layer output, the matrix cores' operands); with everything
-               else exact those roundings alone give about 2e-2 and 4e-3.
+               else exact those roundings alone give 2.3-3.3e-2 and 4e-3.
+               Against an oracle that makes the same three roundings the
+               block is held to the layer's own 2e-2 and to 1e-3.
   final state  relative RMS error <= 1e-2 and max|e| <= 0.25 RMS(ref): the
                same roundings of the layer's inputs give 3.6e-3 and 0.10 with
                everything else exact (the final state is heavy-tailed: its
@@ -253,6 +255,55 @@ def test_block(B, L, H, G, dm, od, states, inplace):
         w_xbc = bi.in_proj_w[wl.d_inner:wl.d_inner + wl.cdim]
         bound = 2.0 ** -8 * np.abs(cref) + 2.0 ** -8 * oracle.linear(np.abs(u), np.abs(w_xbc))
         assert np.all(np.abs(host(co) - cref) <= bound)
+
+
+def rounded_oracle_block(bi):
+    """The oracle's block with the three bf16 roundings the block makes at
+    its matrix-core interfaces (the normed input, the in_proj output and
+    the layer output), everything else in fp64: the best a block with bf16
+    operands can do.  Those roundings alone already give max|e| of
+    2.3-3.3e-2 RMS(m) against the exact oracle at these shapes (two of them
+    about 2.3-2.6e-2), above the layer's 2e-2."""
+    wl = bi.wl
+    H, G, P, N = wl.nheads, wl.ngroups, 64, 128
+    HP, GN = H * P, G * N
+
+    def rb(a):
+        a = np.array(a, np.float32)
+        synth.round_bf16_(a)
+        return a.astype(np.float64)
+
+    hh = np.asarray(bi.h, np.float64)
+    B, L = hh.shape[0], hh.shape[1]
+    u = rb(oracle.rmsnorm(hh, bi.norm_w, eps=1e-5))
+    zx = rb(oracle.linear(u, bi.in_proj_w))
+    z = zx[..., :HP].reshape(B, L, H, P)
+    y, _, _ = oracle.mamba2_fwd(zx[..., HP:2 * HP + 2 * GN], zx[..., 2 * HP + 2 * GN:], bi.A,
+                                nheads=H, headdim=P, ngroups=G, dstate=N, conv_w=bi.conv_w,
+                                D=bi.D, dt_bias=bi.dt_bias, dt_softplus=True, z=z,
+                                f64_inputs=True)
+    return oracle.linear(rb(y.reshape(B, L, HP)), bi.out_proj_w, residual=hh)
+
+
+@pytest.mark.parametrize("B,L,H,G,dm", [(2, 300, 8, 2, 512), (1, 129, 4, 1, 520)])
+def test_block_matches_rounded_oracle(B, L, H, G, dm):
+    """Against the oracle that rounds the same three interfaces to bf16, the
+    block is within the layer's own bf16 bound (max|e| <= 2e-2 RMS(m)) and
+    within 1e-3 relative RMS (measured: 4-8e-3 and 1.2-1.7e-4): beyond its
+    bf16 operands it adds only the layer's matrix-core error, not another
+    rounding."""
+    say("block vs rounded oracle B=%d L=%d H=%d G=%d d_model=%d" % (B, L, H, G, dm))
+    wl = block_wl(B, L, H, G)
+    bi = synth.make_block(wl, d_model=dm)
+    y, _, _ = run_gpu_block(bi)
+    ref = rounded_oracle_block(bi)
+    got = host(y)
+    mix = ref - np.asarray(bi.h, np.float64)
+    rms = math.sqrt(float(np.mean(mix * mix)))
+    e_max = float(np.max(np.abs(got - ref))) / rms
+    e_rms = rel_rms_err(got - np.asarray(bi.h, np.float64), mix)
+    say("  max|e|/RMS(mix) %.3e  rel RMS %.3e" % (e_max, e_rms))
+    assert e_max <= 2e-2 and e_rms <= 1e-3
 
 
 def test_block_split_carry():
