@@ -283,6 +283,11 @@ int ssd_chunk_scan_fwd(const void* x, int64_t x_tok_stride, const void* Bm,
       (c_tok_stride * (int64_t)xe) % 16 || (y_tok_stride * (int64_t)ye) % 16 ||
       (z != nullptr && (z_tok_stride * (int64_t)ae) % 16))
     return fail(SSD_ERR_INVALID_ARG, "scan: a token stride is not a multiple of 16 bytes");
+  // the matrix-core walker addresses a chunk's rows (up to 256 + 3 of them)
+  // by 32-bit byte offsets from the chunk's first row
+  if (math == SSD_MATH_BF16 && x_tok_stride * (int64_t)xe * 260 >= (INT64_C(1) << 32))
+    return fail(SSD_ERR_UNSUPPORTED, "scan: x token stride %lld too large for the matrix-core path",
+                (long long)x_tok_stride);
   // ---- aliasing: y may not overlap any input; the conv states may not overlap
   const Range ry = tok_range(y, rows, y_tok_stride, HP, ye);
   const int64_t nstate = (int64_t)batch * nheads * kP * kN;

@@ -221,6 +221,14 @@ __device__ __forceinline__ void split1(float v, bf16& hi, bf16& lo) {
   hi = (bf16)v;
   lo = (bf16)(v - (float)hi);
 }
+// the same for two values, the hi pair converted once and read back from
+// its bits
+__device__ __forceinline__ void split2(float v0, float v1, bf16x2& hi, bf16x2& lo) {
+  hi = bf16x2{(bf16)v0, (bf16)v1};
+  const uint32_t hb = __builtin_bit_cast(uint32_t, hi);
+  lo = bf16x2{(bf16)(v0 - __uint_as_float(hb << 16)),
+              (bf16)(v1 - __uint_as_float(hb & 0xffff0000u))};
+}
 
 // 8 raw elements of one token row, kept packed between load and use
 template <typename T> struct Raw8;
@@ -291,6 +299,23 @@ struct RowLoad {
         p = h ? hist + ((int64_t)b * (K - 1) + (K - 1) + tau) * cdim + c0 : p;
       }
       v[i].load(p);
+    }
+  }
+  // The same without the history (positions before the sequence re-read
+  // its first row): a wave-uniform base row rbase, at or below every
+  // clamped row, and 32-bit offsets from it instead of a 64-bit address per
+  // row and lane (the caller checks that Q + 3 rows of the tensor span less
+  // than 4 GiB)
+  __device__ __forceinline__ void load_rows(const ScanArgs& a, const Tx* src, int64_t stride,
+                                            int col, int b, int tstart, int rbase) {
+    const int L = a.seqlen;
+    const Tx* base = src + ((int64_t)b * L + rbase) * stride;
+    const uint32_t sb = (uint32_t)(stride * (int64_t)sizeof(Tx));
+    const uint32_t cb = (uint32_t)(col * (int)sizeof(Tx));
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const uint32_t row = (uint32_t)(min(max(tstart + i, 0), L - 1) - rbase);
+      v[i].load(at_bytes(base, row * sb + cb));
     }
   }
   // CHECK = false: the caller knows every row lies in the sequence, or feeds
@@ -587,8 +612,12 @@ struct StageX {
     const int xv = tid % XV, xr = tid / XV;
     const int cdim = a.nheads * P + 2 * a.ngroups * N;
     const int ch = h * P + p0 + 8 * xv;
-    rx.template load<HIST>(a, static_cast<const Tx*>(a.x), a.x_stride, ch, ch, cdim, b,
-                           t0 + RX * xr - HX);
+    if constexpr (HIST)
+      rx.template load<true>(a, static_cast<const Tx*>(a.x), a.x_stride, ch, ch, cdim, b,
+                             t0 + RX * xr - HX);
+    else  // (the rows before the sequence of a repeated first chunk: row 0)
+      rx.load_rows(a, static_cast<const Tx*>(a.x), a.x_stride, ch, b, t0 + RX * xr - HX,
+                   max(t0 - HX, 0));
   }
 
   // the thread's RX x 8 post-conv values, tmp[8 i + e] = x[RX xr + i][8 xv + e]
@@ -860,16 +889,17 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(STATE_O
         wt[i] = __expf(lam_last - lam(RX * xr + i)) * cDel[RX * xr + i];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        bf16 hh[RX], ll[RX];
-#pragma unroll
-        for (int i = 0; i < RX; ++i) split1(xt[8 * i + e] * wt[i], hh[i], ll[i]);
         const int o = prow(8 * xv + e) * LDT + RX * xr;
         if constexpr (RX == 2) {
-          *reinterpret_cast<bf16x2*>(sXWh + o) = bf16x2{hh[0], hh[1]};
-          *reinterpret_cast<bf16x2*>(sXWl + o) = bf16x2{ll[0], ll[1]};
+          bf16x2 hi, lo;
+          split2(xt[e] * wt[0], xt[8 + e] * wt[1], hi, lo);
+          *reinterpret_cast<bf16x2*>(sXWh + o) = hi;
+          *reinterpret_cast<bf16x2*>(sXWl + o) = lo;
         } else {
-          sXWh[o] = hh[0];
-          sXWl[o] = ll[0];
+          bf16 hh, ll;
+          split1(xt[e] * wt[0], hh, ll);
+          sXWh[o] = hh;
+          sXWl[o] = ll;
         }
       }
     }

@@ -137,6 +137,7 @@ SCAN_CASES = [
     ("H % G", dict(G=3), INVALID),
     ("chunk 100 on matrix cores", dict(Q=100), UNSUPPORTED),
     ("chunk 32 on matrix cores", dict(Q=32), UNSUPPORTED),
+    ("x stride past 32-bit chunk offsets", dict(xs=1 << 23), UNSUPPORTED),
     ("chunk 96 on fp32", dict(Q=96, math=0), UNSUPPORTED),
     ("chunk 0", dict(Q=0), INVALID),
     ("negative seqlen", dict(L=-1), INVALID),
