@@ -348,6 +348,33 @@ def measure_peaks(torch, ssd, nbytes: int = 1 << 30, reps: int = 20):
     return best[form], form, tflops
 
 
+def rebase_measured_hbm(out):
+    """The streaming rate this GPU was seen to reach is at least the fastest
+    HBM-bound rate any timed launch in the run reached: when a kernel's
+    algorithmic rate beats the calibration stream, that rate becomes the
+    measured HBM peak and every HBM roofline's frac_of_measured is taken
+    against it (so none exceeds 1)."""
+    recs = []
+    def walk(o):
+        if isinstance(o, dict):
+            r = o.get("roofline")
+            if isinstance(r, dict) and r.get("unit") == "GB/s":
+                recs.append(r)
+            for v in o.values():
+                walk(v)
+    walk(out)
+    peaks = out["measured_peaks"]
+    best = max(recs, key=lambda r: r["achieved"], default=None)
+    if best is None or best["achieved"] <= peaks["hbm_gbs"]:
+        return
+    peaks["hbm_gbs_stream"] = peaks["hbm_gbs"]
+    peaks["hbm_gbs"] = best["achieved"]
+    peaks["hbm_form"] = "algorithmic rate of %s (above the stream kernel's)" % best["kernel"]
+    for r in recs:
+        r["measured_peak"] = best["achieved"]
+        r["frac_of_measured"] = r["achieved"] / best["achieved"]
+
+
 def calibrate_copy(torch, ssd, nbytes: int = 1 << 30):
     """A plain copy kernel of known size (the library's calibration stream,
     dst != src) for scaling the HBM byte counters of a rocprofv3 --pmc run.
@@ -544,7 +571,9 @@ def main():
             "steps_per_s": 1e3 / fz["step_ms"], "ms_per_step": fz["step_ms"],
             "first10_ms": fz["first10_ms"], "last10_ms": fz["last10_ms"],
             "roofline": {"bound": "hbm", "achieved": fach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": fach / HBM_PEAK_GBS, "traffic": None,
+                         "frac": fach / HBM_PEAK_GBS,
+                         "traffic": traffic_record("decode_fused_state_update",
+                                                   src_hash("state_update.hip", "api.hip")),
                          "kernel": "state_update_kernel", "measured_peak": copy_gbs,
                          "frac_of_measured": fach / copy_gbs, "alg_bytes_per_step": dbytes}}
     if not args.no_block:
@@ -583,6 +612,7 @@ def main():
                          "alg_flops_per_token": fpt_b,
                          "alg_bytes_per_call": bwd_alg_bytes_per_call(wl)},
         }
+    rebase_measured_hbm(out)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
