@@ -551,31 +551,29 @@ def main():
         dwl = WORKLOADS[DECODE_MAIN].with_(decode_steps=args.decode_steps)
         dec = time_decode(args, dwl, torch, layer, synth, dev, dev32)
         dbytes = decode_alg_bytes_per_step(dwl)
-        dach = dbytes / (dec["step_ms"] / 1e3) / 1e9
-        out["decode"] = {"workload": dwl.name, "steps_per_s": 1e3 / dec["step_ms"],
-                         "tokens_per_s": dwl.batch * 1e3 / dec["step_ms"],
-                         "ms_per_step": dec["step_ms"], "first10_ms": dec["first10_ms"],
-                         "last10_ms": dec["last10_ms"],
-                         "roofline": {"bound": "hbm", "achieved": dach, "peak": HBM_PEAK_GBS,
-                                      "unit": "GB/s", "frac": dach / HBM_PEAK_GBS,
-                                      "traffic": traffic_record(
-                                          "decode_state_update",
-                                          src_hash("state_update.hip", "api.hip")),
-                                      "kernel": "conv_step_kernel + state_stream_kernel",
-                                      "measured_peak": copy_gbs,
-                                      "frac_of_measured": dach / copy_gbs,
-                                      "alg_bytes_per_step": dbytes}}
-        fz = dec["fused"]
-        fach = dbytes / (fz["step_ms"] / 1e3) / 1e9
-        out["decode"]["ssd_state_update"] = {
-            "steps_per_s": 1e3 / fz["step_ms"], "ms_per_step": fz["step_ms"],
-            "first10_ms": fz["first10_ms"], "last10_ms": fz["last10_ms"],
-            "roofline": {"bound": "hbm", "achieved": fach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": fach / HBM_PEAK_GBS,
-                         "traffic": traffic_record("decode_fused_state_update",
-                                                   src_hash("state_update.hip", "api.hip")),
-                         "kernel": "state_update_kernel", "measured_peak": copy_gbs,
-                         "frac_of_measured": fach / copy_gbs, "alg_bytes_per_step": dbytes}}
+        fz, wsr = dec["fused"], dec
+
+        def droof(r, key, kernel):
+            ach = dbytes / (r["step_ms"] / 1e3) / 1e9
+            return {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": ach / HBM_PEAK_GBS,
+                    "traffic": traffic_record(key, src_hash("state_update.hip", "api.hip")),
+                    "kernel": kernel, "measured_peak": copy_gbs,
+                    "frac_of_measured": ach / copy_gbs, "alg_bytes_per_step": dbytes}
+        # ssd_state_update (no workspace) is the decode entry point; the
+        # workspace form is timed beside it
+        out["decode"] = {"workload": dwl.name, "entry": "ssd_state_update",
+                         "steps_per_s": 1e3 / fz["step_ms"],
+                         "tokens_per_s": dwl.batch * 1e3 / fz["step_ms"],
+                         "ms_per_step": fz["step_ms"], "first10_ms": fz["first10_ms"],
+                         "last10_ms": fz["last10_ms"],
+                         "roofline": droof(fz, "decode_fused_state_update",
+                                           "state_conv_stream_kernel + ring_shift_bc_kernel")}
+        out["decode"]["ssd_state_update_ws"] = {
+            "steps_per_s": 1e3 / wsr["step_ms"], "ms_per_step": wsr["step_ms"],
+            "first10_ms": wsr["first10_ms"], "last10_ms": wsr["last10_ms"],
+            "roofline": droof(wsr, "decode_state_update",
+                              "conv_step_kernel + state_stream_kernel")}
     if not args.no_block:
         blk = time_block(args, wl, torch, ssd, synth, dev, dev32)
         T, dm, HP, din = wl.tokens, wl.d_model, wl.d_inner, wl.d_in_proj

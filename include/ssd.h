@@ -160,7 +160,11 @@ int ssd_chunk_scan_fwd(const void* x, int64_t x_tok_stride, const void* Bm,
 /*
  * One-token decode step for a batch of sequences: the conv step on the ring of
  * the last K-1 raw inputs, then h <- exp(delta A) h + delta x B^T and
- * y = h C + D x, gated.  The state and the ring are updated in place.
+ * y = h C + D x, gated.  The state and the ring are updated in place.  Two
+ * launches on the stream, no workspace: one workgroup per (sequence, head)
+ * convolves what its head needs from the ring and streams the head's state
+ * once; a second, small launch then shifts the ring columns of B and C,
+ * which every head of a group reads.
  *
  *   state      [B, H, P, N] fp32, in/out
  *   xbc        [B, Cdim] xbc_dtype: the new token's raw x|B|C when conv_w is
@@ -189,9 +193,9 @@ size_t ssd_state_update_workspace_bytes(int batch, int nheads, int headdim, int 
  * and in-place updates, taken in two passes through a caller-provided
  * workspace: the conv step of every channel (writing the post-conv x|B|C to
  * the workspace and shifting the ring), then the state update and readout
- * with many small workgroups, which streams the state through HBM faster.
- * Results agree with ssd_state_update up to the order of the fp32 sum in
- * y = h C (each path's order is fixed, so each is deterministic).
+ * with one workgroup per 16 state rows of a head.  Both entry points take
+ * the same sums in the same fixed order, so their results agree (each is
+ * deterministic).
  *
  *   workspace: at least ssd_state_update_workspace_bytes(...) bytes,
  *   256-byte aligned, overlapping no tensor (may be NULL when batch is 0).

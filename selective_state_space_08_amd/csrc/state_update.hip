@@ -6,25 +6,25 @@
 // Appendix C).
 //
 // HBM-bound: the fp32 state (32 KiB per head) is read and written once per
-// step and is ~98% of the bytes.  Two implementations:
-//
-// state_update_kernel (no workspace): one workgroup owns one (sequence,
-// group): it convolves the group's channels once (x of its H/G heads, B and
-// C of the group), so the ring rows it shifts are touched by no other
-// workgroup, then streams the heads' states with 16-byte coalesced,
-// non-temporal accesses (512 threads, 4 float4 per thread per head),
-// prefetching the next head's state while it updates the current one.
+// step and is ~98% of the bytes.  Short-lived workgroups that each sweep a
+// short contiguous range stream HBM faster on this GPU than a few that walk
+// many heads one after the other.  Two implementations, which differ in
+// where the conv step happens:
 //
 // conv_step_kernel + state_stream_kernel (with a workspace): the conv step
 // and ring shift of every channel first, one thread per (sequence, channel),
 // writing the post-conv x|B|C in fp32 to the workspace; then one workgroup of
 // 256 threads per (sequence, head, block of 16 state rows), two float4 of the
-// state per thread, both loaded before anything else.  Narrow workgroups that
-// each sweep a short contiguous range stream HBM faster on this GPU than a
-// few wide workgroups that walk many heads one after the other (measured at
-// B = 256, H = 128: 0.355 ms against 0.404 ms per step), and the 40 KiB of
-// post-conv values per sequence are read from L2 by the 32 workgroups that
-// share them instead of being recomputed.
+// state per thread, which reads it from there (the 64 workgroups of a
+// sequence and group share B and C through L2).
+//
+// state_conv_stream_kernel + ring_shift_bc_kernel (no workspace): one
+// workgroup of 256 threads per (sequence, head), eight float4 of the state
+// per thread, all loaded after the conv's small inputs.  It convolves what it
+// needs from the unshifted ring itself (the group's B and C, the head's x)
+// and shifts the ring columns of the head's x channels; B and C columns,
+// which every workgroup of the group reads, are shifted by a second small
+// launch.
 #include <mutex>
 
 #include "ssd_common.h"
@@ -34,182 +34,7 @@ namespace {
 
 constexpr int P = 64;
 constexpr int N = 128;
-constexpr int THREADS = 512;
-constexpr int ROWS_PER_PASS = THREADS / (N / 4);  // 16 state rows per pass
-constexpr int PASSES = P / ROWS_PER_PASS;         // 4 float4 per thread per head
-
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-// The state is streamed once per step and not reused: non-temporal loads
-// and stores keep it from displacing other data in the caches.
-__device__ __forceinline__ float4 ld_stream(const float4* p) {
-  const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-  return make_float4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ void st_stream(float4* p, float4 v) {
-  const f32x4 w = {v.x, v.y, v.z, v.w};
-  __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(p));
-}
-// base + off bytes, for a wave-uniform base and a per-lane offset below
-// 4 GiB: a scalar base and a 32-bit vector offset instead of a 64-bit
-// address per lane
-template <typename T>
-__device__ __forceinline__ T* at_bytes(T* base, uint32_t off) {
-  return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off);
-}
-template <typename T>
-__device__ __forceinline__ const T* at_bytes(const T* base, uint32_t off) {
-  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + off);
-}
-
-template <typename Tx, typename Ta, typename Ty>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(8))) void state_update_kernel(
-    float* __restrict__ state, const Tx* __restrict__ xbc, Tx* __restrict__ ring,
-    const float* __restrict__ conv_w, const float* __restrict__ conv_b, int K,
-    const Ta* __restrict__ dt, const Ta* __restrict__ z, const float* __restrict__ A,
-    const float* __restrict__ D, const float* __restrict__ dt_bias, int softplus,
-    Ty* __restrict__ y, int H, int G) {
-  // LDS: post-conv x of the group's heads | B | C, then the gate silu(z) of
-  // the group's heads, then delta, exp(delta A) and D of each head
-  extern __shared__ float sxc[];
-  const int g = blockIdx.x, b = blockIdx.y;
-  const int hpg = H / G;
-  const int HP = H * P, GN = G * N, C = HP + 2 * GN;
-  const int nx = hpg * P, nch = nx + 2 * N;
-  const int tid = threadIdx.x;
-  float* sgate = sxc + nch;
-  float* sdel = sgate + nx;
-  float* sdec = sdel + hpg;
-  float* sskip = sdec + hpg;
-
-  // The first head's state does not depend on the conv step: its loads are
-  // issued first, so they are in flight during it.
-  const int h0 = g * hpg;
-  float4* st = reinterpret_cast<float4*>(state + ((int64_t)b * H + h0) * P * N);
-  // the thread's byte offset within a head's state, pass j at + j * THREADS * 16
-  const uint32_t toff = (uint32_t)tid * 16;
-  float4 cur[PASSES];
-#pragma unroll
-  for (int j = 0; j < PASSES; ++j) cur[j] = ld_stream(at_bytes(st, toff + j * THREADS * 16));
-
-  // Everything per head that the state loop needs is read here, ahead of it:
-  // inside the loop the only loads are the state stream, so waiting for one
-  // head's state never waits behind a small load issued after the prefetch.
-  for (int i = tid; i < nx; i += THREADS)
-    sgate[i] = z != nullptr ? silu_f32(to_f32(z[(int64_t)b * HP + h0 * P + i])) : 1.f;
-  if (tid < hpg) {
-    const int h = h0 + tid;
-    const float delta = make_delta(to_f32(dt[(int64_t)b * H + h]), dt_bias, h, softplus);
-    sdel[tid] = delta;
-    sdec[tid] = __expf(delta * A[h]);
-    sskip[tid] = D ? D[h] : 0.f;
-  }
-
-  // conv step for the group's channels; each channel's ring column is owned
-  // by this workgroup alone
-  for (int i = tid; i < nch; i += THREADS) {
-    const int c = i < nx ? g * nx + i
-                         : (i < nx + N ? HP + g * N + (i - nx) : HP + GN + g * N + (i - nx - N));
-    const Tx raw = xbc[(int64_t)b * C + c];
-    float v = to_f32(raw);
-    if (conv_w != nullptr) {
-      Tx* r = ring + (int64_t)b * (K - 1) * C + c;  // r[k*C]: row k, oldest first
-      float u = conv_b ? conv_b[c] : 0.f;
-      for (int k = 0; k < K - 1; ++k) u += conv_w[(int64_t)c * K + k] * to_f32(r[(int64_t)k * C]);
-      u += conv_w[(int64_t)c * K + K - 1] * v;
-      for (int k = 0; k + 1 < K - 1; ++k) r[(int64_t)k * C] = r[(int64_t)(k + 1) * C];
-      if (K > 1) r[(int64_t)(K - 2) * C] = raw;
-      v = silu_f32(u);
-    }
-    sxc[i] = v;
-  }
-  __syncthreads();
-
-  // thread -> float4 column n4 = tid % 32 (fixed), rows p = tid / 32 + ROWS_PER_PASS j
-  const int col = tid & 31;
-  const int row0 = tid >> 5;
-
-
-  // one head: update the state in v, store it and the outputs
-  auto head = [&](int hh, float4 (&v)[PASSES]) {
-    const int h = h0 + hh;
-    const float delta = sdel[hh];
-    const float a = sdec[hh];
-    const float Dh = sskip[hh];
-    const float4 Bv = reinterpret_cast<const float4*>(sxc + nx)[col];
-    const float4 Cv = reinterpret_cast<const float4*>(sxc + nx + N)[col];
-    float4* sh = st + (int64_t)hh * (P * N / 4);
-    Ty* yh = y + (int64_t)b * HP + (int64_t)h * P;
-#pragma unroll
-    for (int j = 0; j < PASSES; ++j) {
-      const int p = row0 + ROWS_PER_PASS * j;
-      const float xp = sxc[hh * P + p];
-      const float dx = delta * xp;
-      float4 s = v[j];
-      s.x = a * s.x + dx * Bv.x;
-      s.y = a * s.y + dx * Bv.y;
-      s.z = a * s.z + dx * Bv.z;
-      s.w = a * s.w + dx * Bv.w;
-      st_stream(at_bytes(sh, toff + j * THREADS * 16), s);
-      float acc = s.x * Cv.x + s.y * Cv.y + s.z * Cv.z + s.w * Cv.w;
-      // sum over the 32 lanes holding row p (fixed butterfly order: deterministic)
-#pragma unroll
-      for (int m = 16; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 32);
-      if (col == 0) {
-        const float yv = (acc + Dh * xp) * sgate[hh * P + p];
-        yh[p] = from_f32<Ty>(yv);
-      }
-    }
-  };
-  auto prefetch = [&](int hh, float4 (&v)[PASSES]) {
-    const float4* sn = st + (int64_t)hh * (P * N / 4);
-#pragma unroll
-    for (int j = 0; j < PASSES; ++j) v[j] = ld_stream(at_bytes(sn, toff + j * THREADS * 16));
-  };
-  // two register sets in turn: head hh from one while head hh + 1 loads
-  // into the other
-  float4 alt[PASSES];
-  for (int hh = 0; hh < hpg; hh += 2) {
-    if (hh + 1 < hpg) prefetch(hh + 1, alt);
-    head(hh, cur);
-    if (hh + 1 < hpg) {
-      if (hh + 2 < hpg) prefetch(hh + 2, cur);
-      head(hh + 1, alt);
-    }
-  }
-}
-
-template <typename Tx, typename Ta, typename Ty>
-hipError_t launch_typed(float* state, const void* xbc, void* ring, const float* conv_w,
-                        const float* conv_b, int K, const void* dt, const void* z,
-                        const float* A, const float* D, const float* dt_bias, int softplus,
-                        void* y, int B, int H, int G, hipStream_t stream) {
-  const int hpg = H / G;
-  const size_t lds = sizeof(float) * (size_t)(2 * hpg * P + 2 * N + 3 * hpg);
-  if (lds > 64 * 1024) {  // many heads per group: opt in to more than 64 KiB
-    const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&state_update_kernel<Tx, Ta, Ty>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL((state_update_kernel<Tx, Ta, Ty>), dim3(G, B), dim3(THREADS), lds, stream,
-                     state, static_cast<const Tx*>(xbc), static_cast<Tx*>(ring), conv_w, conv_b,
-                     K, static_cast<const Ta*>(dt), static_cast<const Ta*>(z), A, D, dt_bias,
-                     softplus, static_cast<Ty*>(y), H, G);
-  return hipGetLastError();
-}
-
-template <typename Tx, typename Ta>
-hipError_t pick_y(ssd_dtype_t yd, float* state, const void* xbc, void* ring, const float* w,
-                  const float* cb, int K, const void* dt, const void* z, const float* A,
-                  const float* D, const float* dtb, int sp, void* y, int B, int H, int G,
-                  hipStream_t s) {
-  if (yd == SSD_F32)
-    return launch_typed<Tx, Ta, float>(state, xbc, ring, w, cb, K, dt, z, A, D, dtb, sp, y, B, H,
-                                       G, s);
-  return launch_typed<Tx, Ta, bf16>(state, xbc, ring, w, cb, K, dt, z, A, D, dtb, sp, y, B, H, G,
-                                    s);
-}
 
 // ------------------------------------------------------------ with a workspace
 
@@ -306,6 +131,223 @@ __global__ __launch_bounds__(SS_THREADS) void state_stream_kernel(
   }
 }
 
+// ------------------------------------------------------------ without a workspace
+
+// Post-conv value of channel c of sequence b: SiLU(conv_b[c] + sum_k w[c, k]
+// u_k) over the ring's K-1 raw inputs (oldest first) and the new one, summed
+// in the order conv_step_kernel uses; without a conv, the input itself.  With
+// SHIFT the channel's ring column is also shifted by one token (the caller
+// owns that column).
+template <bool SHIFT, typename Tx>
+__device__ __forceinline__ float conv_channel(const Tx* __restrict__ xbc, Tx* __restrict__ ring,
+                                              const float* __restrict__ conv_w,
+                                              const float* __restrict__ conv_b, int K, int64_t b,
+                                              int64_t C, int64_t c) {
+  const Tx raw = xbc[b * C + c];
+  float out = to_f32(raw);
+  if (conv_w == nullptr) return out;
+  float u = conv_b ? conv_b[c] : 0.f;
+  if (K > 1) {
+    Tx* r = ring + b * (K - 1) * C + c;  // r[k*C]: row k, oldest first
+    for (int k = 0; k < K - 1; ++k) u += conv_w[c * K + k] * to_f32(r[(int64_t)k * C]);
+    if (SHIFT) {
+      for (int k = 0; k + 1 < K - 1; ++k) r[(int64_t)k * C] = r[(int64_t)(k + 1) * C];
+      r[(int64_t)(K - 2) * C] = raw;
+    }
+  }
+  u += conv_w[c * K + K - 1] * out;
+  return silu_f32(u);
+}
+
+// delta, exp(delta A) and D of head h into out[0..2]
+__device__ __forceinline__ void sdelta_of(float dtv, const float* __restrict__ dt_bias, int h,
+                                          int softplus, const float* __restrict__ A,
+                                          const float* __restrict__ D, float (&out)[3]) {
+  const float delta = make_delta(dtv, dt_bias, h, softplus);
+  out[0] = delta;
+  out[1] = __expf(delta * A[h]);
+  out[2] = D ? D[h] : 0.f;
+}
+
+// One workgroup per head: every workgroup convolves the group's B and C, so
+// the fewer the workgroups, the less of that (measured at B = 256, H = 128:
+// 0.354 ms per step with the head's 64 rows per workgroup, 0.368 with 32,
+// 0.377 with 16).
+constexpr int CS_JJ = 8;                          // float4 of the state per thread
+constexpr int CS_ROWS = SS_THREADS / (N / 4) * CS_JJ;  // state rows per workgroup: 64
+
+// The raw inputs of one channel's conv step at width 4, loaded together so
+// that they are in flight with the state's loads; summed in the order
+// conv_step_kernel uses.
+template <typename Tx>
+struct Conv4 {
+  float w0, w1, w2, w3, bias, r0, r1, r2, raw;
+  Tx traw, t1, t2;
+  __device__ __forceinline__ void load(const Tx* __restrict__ xbc, const Tx* __restrict__ ring,
+                                       const float* __restrict__ conv_w,
+                                       const float* __restrict__ conv_b, int64_t b, int64_t C,
+                                       int64_t c) {
+    const f32x4 w = *reinterpret_cast<const f32x4*>(conv_w + c * 4);
+    w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
+    bias = conv_b ? conv_b[c] : 0.f;
+    const Tx* r = ring + b * 3 * C + c;
+    const Tx t0 = r[0];
+    t1 = r[C], t2 = r[2 * C];
+    traw = xbc[b * C + c];
+    r0 = to_f32(t0);
+  }
+  __device__ __forceinline__ float value() {
+    r1 = to_f32(t1), r2 = to_f32(t2), raw = to_f32(traw);
+    float u = bias;
+    u += w0 * r0;
+    u += w1 * r1;
+    u += w2 * r2;
+    u += w3 * raw;
+    return silu_f32(u);
+  }
+  // the channel's ring column shifted by one token
+  __device__ __forceinline__ void shift(Tx* __restrict__ ring, int64_t b, int64_t C, int64_t c) {
+    Tx* r = ring + b * 3 * C + c;
+    r[0] = t1, r[C] = t2, r[2 * C] = traw;
+  }
+};
+
+// The decode step with no workspace, first launch.  Workgroup (h, rb) of
+// sequence b owns state rows CS_ROWS rb .. CS_ROWS rb + CS_ROWS - 1 of head h
+// (with CS_ROWS = 64, the whole head): thread t holds columns 4 (t % 32) ..
+// +3 of rows CS_ROWS rb + t / 32 + 8 j.  It takes the conv step of what those
+// rows need straight from the (unshifted) ring: B and C of the head's group
+// (one channel per thread) and x of its rows, into LDS.  The ring columns of
+// those x channels belong to this workgroup alone, so it shifts them;
+// the group's B and C columns are read by every workgroup of the group, so
+// ring_shift_bc_kernel shifts them afterwards.  W4 (conv width 4, the
+// layer's): the conv's inputs are loaded before the state, so that the conv
+// is computed while the state is in flight; otherwise (other widths, no
+// conv) the conv follows the state's loads.  GATED (width 4 only): z is given.
+template <bool W4, bool GATED, typename Tx, typename Ta, typename Ty>
+__global__ __launch_bounds__(SS_THREADS) void state_conv_stream_kernel(
+    float* __restrict__ state, const Tx* __restrict__ xbc, Tx* __restrict__ ring,
+    const float* __restrict__ conv_w, const float* __restrict__ conv_b, int K,
+    const Ta* __restrict__ dt, const Ta* __restrict__ z, const float* __restrict__ A,
+    const float* __restrict__ D, const float* __restrict__ dt_bias, int softplus,
+    Ty* __restrict__ y, int H, int G) {
+  static_assert(2 * N == SS_THREADS, "one thread per B and C channel of a group");
+  __shared__ f32x4 sbc[2 * N / 4];  // post-conv B | C of the group
+  __shared__ float sx[SS_THREADS];  // post-conv x of the workgroup's rows (slots 0 .. CS_ROWS - 1)
+  constexpr int RB = P / CS_ROWS;
+  const int h = blockIdx.x / RB, rb = blockIdx.x - h * RB, b = blockIdx.y;
+  const int g = h / (H / G);
+  const int64_t HP = (int64_t)H * P, GN = (int64_t)G * N, C = HP + 2 * GN;
+  const int tid = threadIdx.x;
+  const int p0 = CS_ROWS * rb + (tid >> 5), n4 = 4 * (tid & 31);
+  const int64_t cbc = HP + (int64_t)g * N + (tid < N ? tid : GN + (tid - N));
+  const int64_t cx = (int64_t)h * P + CS_ROWS * rb + (tid & (CS_ROWS - 1));
+  f32x4* sp = reinterpret_cast<f32x4*>(state + (((int64_t)b * H + h) * P + p0) * N + n4);
+  f32x4 s[CS_JJ];
+  float gate[CS_JJ];
+  float sdel[3];  // delta, exp(delta A), D of the head
+  if constexpr (W4) {
+    // every small load first (dt, z, the conv's inputs; the x channel's by all
+    // threads, so no branch splits them), then the state: waiting for the
+    // small ones then leaves the state in flight
+    const Ta dtv = dt[(int64_t)b * H + h];
+    Ta zr[CS_JJ];
+    if constexpr (GATED) {
+#pragma unroll
+      for (int j = 0; j < CS_JJ; ++j) zr[j] = z[(int64_t)b * HP + (int64_t)h * P + p0 + 8 * j];
+    }
+    Conv4<Tx> vbc, vx;
+    vbc.load(xbc, ring, conv_w, conv_b, b, C, cbc);
+    vx.load(xbc, ring, conv_w, conv_b, b, C, cx);
+#pragma unroll
+    for (int j = 0; j < CS_JJ; ++j) s[j] = __builtin_nontemporal_load(sp + j * 8 * (N / 4));
+    reinterpret_cast<float*>(sbc)[tid] = vbc.value();
+    // every thread keeps its x channel's value (threads 0 .. CS_ROWS - 1
+    // hold the distinct ones), so that the loads above are not moved into
+    // the branch
+    sx[tid] = vx.value();
+    if (tid < CS_ROWS) vx.shift(ring, b, C, cx);
+#pragma unroll
+    for (int j = 0; j < CS_JJ; ++j) gate[j] = GATED ? silu_f32(to_f32(zr[j])) : 1.f;
+    sdelta_of(to_f32(dtv), dt_bias, h, softplus, A, D, sdel);
+  } else {
+#pragma unroll
+    for (int j = 0; j < CS_JJ; ++j) s[j] = __builtin_nontemporal_load(sp + j * 8 * (N / 4));
+    reinterpret_cast<float*>(sbc)[tid] = conv_channel<false>(xbc, ring, conv_w, conv_b, K, b, C, cbc);
+    if (tid < CS_ROWS) sx[tid] = conv_channel<true>(xbc, ring, conv_w, conv_b, K, b, C, cx);
+#pragma unroll
+    for (int j = 0; j < CS_JJ; ++j)
+      gate[j] = z != nullptr ? silu_f32(to_f32(z[(int64_t)b * HP + (int64_t)h * P + p0 + 8 * j])) : 1.f;
+    sdelta_of(to_f32(dt[(int64_t)b * H + h]), dt_bias, h, softplus, A, D, sdel);
+  }
+  const float delta = sdel[0], a = sdel[1], Dh = sdel[2];
+  __syncthreads();
+  const f32x4 Bv = sbc[tid & 31];
+  const f32x4 Cv = sbc[N / 4 + (tid & 31)];
+#pragma unroll
+  for (int j = 0; j < CS_JJ; ++j) {
+    const int p = p0 + 8 * j;
+    const int64_t hp = (int64_t)h * P + p;
+    const float xp = sx[p - CS_ROWS * rb];
+    s[j] = a * s[j] + (delta * xp) * Bv;
+    __builtin_nontemporal_store(s[j], sp + j * 8 * (N / 4));
+    const float acc =
+        half_wave_sum(s[j].x * Cv.x + s[j].y * Cv.y + s[j].z * Cv.z + s[j].w * Cv.w);
+    if ((tid & 31) == 31) y[(int64_t)b * HP + hp] = from_f32<Ty>((acc + Dh * xp) * gate[j]);
+  }
+}
+
+// Second launch: the ring columns of every B and C channel shifted by one
+// token, the new raw input appended.  One thread per (sequence, channel).
+template <typename Tx>
+__global__ __launch_bounds__(CONV_THREADS) void ring_shift_bc_kernel(
+    const Tx* __restrict__ xbc, Tx* __restrict__ ring, int K, int64_t HP, int64_t C,
+    int64_t nbc, int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * CONV_THREADS + threadIdx.x;
+  if (i >= total) return;
+  const int64_t b = i / nbc, c = HP + (i - b * nbc);
+  Tx* r = ring + b * (K - 1) * C + c;
+  for (int k = 0; k + 1 < K - 1; ++k) r[(int64_t)k * C] = r[(int64_t)(k + 1) * C];
+  r[(int64_t)(K - 2) * C] = xbc[b * C + c];
+}
+
+template <typename Tx, typename Ta, typename Ty>
+hipError_t launch_typed(float* state, const void* xbc, void* ring, const float* conv_w,
+                        const float* conv_b, int K, const void* dt, const void* z,
+                        const float* A, const float* D, const float* dt_bias, int softplus,
+                        void* y, int B, int H, int G, hipStream_t stream) {
+  // width 4 with 16-byte aligned taps: the conv's loads go out before the state's
+  const bool w4 = conv_w != nullptr && K == 4 && (reinterpret_cast<uintptr_t>(conv_w) & 15) == 0;
+  auto kern = !w4              ? state_conv_stream_kernel<false, true, Tx, Ta, Ty>
+              : z != nullptr ? state_conv_stream_kernel<true, true, Tx, Ta, Ty>
+                             : state_conv_stream_kernel<true, false, Tx, Ta, Ty>;
+  hipLaunchKernelGGL(kern, dim3(H * (P / CS_ROWS), B), dim3(SS_THREADS), 0, stream, state,
+                     static_cast<const Tx*>(xbc), static_cast<Tx*>(ring), conv_w, conv_b, K,
+                     static_cast<const Ta*>(dt), static_cast<const Ta*>(z), A, D, dt_bias,
+                     softplus, static_cast<Ty*>(y), H, G);
+  if (conv_w != nullptr && K > 1) {
+    const int64_t HP = (int64_t)H * P, nbc = 2 * (int64_t)G * N, C = HP + nbc;
+    const int64_t total = (int64_t)B * nbc;
+    hipLaunchKernelGGL(ring_shift_bc_kernel<Tx>,
+                       dim3((unsigned)((total + CONV_THREADS - 1) / CONV_THREADS)),
+                       dim3(CONV_THREADS), 0, stream, static_cast<const Tx*>(xbc),
+                       static_cast<Tx*>(ring), K, HP, C, nbc, total);
+  }
+  return hipGetLastError();
+}
+
+template <typename Tx, typename Ta>
+hipError_t pick_y(ssd_dtype_t yd, float* state, const void* xbc, void* ring, const float* w,
+                  const float* cb, int K, const void* dt, const void* z, const float* A,
+                  const float* D, const float* dtb, int sp, void* y, int B, int H, int G,
+                  hipStream_t s) {
+  if (yd == SSD_F32)
+    return launch_typed<Tx, Ta, float>(state, xbc, ring, w, cb, K, dt, z, A, D, dtb, sp, y, B, H,
+                                       G, s);
+  return launch_typed<Tx, Ta, bf16>(state, xbc, ring, w, cb, K, dt, z, A, D, dtb, sp, y, B, H, G,
+                                    s);
+}
+
 template <typename Tx, typename Ta, typename Ty>
 hipError_t launch_ws_typed(float* state, const void* xbc, void* ring, const float* conv_w,
                            const float* conv_b, int K, const void* dt, const void* z,
@@ -375,6 +417,7 @@ hipError_t launch_state_update(float* state, const void* xbc, ssd_dtype_t xd, vo
                                const void* z, ssd_dtype_t ad, const float* A, const float* D,
                                const float* dt_bias, int softplus, void* y, ssd_dtype_t yd,
                                int B, int H, int G, hipStream_t s) {
+  if (B == 0) return hipSuccess;
   if (xd == SSD_BF16 && ad == SSD_BF16)
     return pick_y<bf16, bf16>(yd, state, xbc, ring, conv_w, conv_b, K, dt, z, A, D, dt_bias,
                               softplus, y, B, H, G, s);

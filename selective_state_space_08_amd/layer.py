@@ -73,7 +73,7 @@ def decode_step(state, xbc, dt, z, conv_state, p: LayerParams, *, y=None,
     """One token per sequence: state [B,H,P,N] and conv_state [B,K-1,Cdim]
     are updated in place; returns y [B, H*P].  By default the two-kernel step
     through a workspace (allocated per call when not given); fused=True takes
-    the single-kernel step, which needs none."""
+    ssd_state_update, which needs none."""
     if fused:
         return ssd.ssd_state_update(state, xbc, dt, p.A, ngroups=p.ngroups,
                                     conv_state=conv_state, conv_w=p.conv_w, conv_b=p.conv_b,

@@ -258,7 +258,7 @@ def _state_update_args(state, xbc, dt, ngroups, conv_state, conv_w, conv_b, z, y
 def ssd_state_update(state, xbc, dt, A, *, ngroups, conv_state=None, conv_w=None, conv_b=None,
                      z=None, D=None, dt_bias=None, dt_softplus=True, y=None,
                      y_dtype=torch.float32):
-    """One decode step, one fused kernel.  state [B, H, P, N] fp32 (in place),
+    """One decode step, no workspace.  state [B, H, P, N] fp32 (in place),
     xbc [B, Cdim], conv_state [B, K-1, Cdim] (in place), dt [B, H],
     z [B, H*P] -> y [B, H*P]."""
     lib = load()
