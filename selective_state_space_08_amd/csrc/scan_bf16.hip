@@ -455,6 +455,15 @@ __device__ __forceinline__ void store4(bf16* p, const float* v) {
 
 // ------------------------------------------------------------ B|C pack
 
+// Swizzle key of row n of the pack's [n][s] B^T staging tile (Q / 8 blocks
+// of 16 bytes per row): distinct across the rows 8 apart that 16 lanes write
+// at once, and across 16 consecutive rows, which 16 lanes read at once.
+template <int Q>
+__device__ __forceinline__ int bt_key(int n) {
+  return ((n >> 3) ^ ((n & 7) << 1)) & (Q / 8 - 1);
+}
+
+
 // One workgroup of 2 Q threads per (chunk c, group g, sequence b).  Thread
 // (cv = tid % 16, rg = tid / 16) owns channels [8 cv, 8 cv + 8) and tokens
 // [8 rg, 8 rg + 8) of the chunk for B and for C.  Tokens past the end of the
@@ -510,55 +519,39 @@ __global__ __launch_bounds__(Geo<Q>::PACK_THREADS) void bc_pack_kernel(ScanArgs 
     lds_barrier();
   }
 
+  // C first, then B, whose values stay in v for the B^T parts
+  float v[8][8];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {  // m = 0: B, m = 1: C
+  for (int mm = 0; mm < 2; ++mm) {
+    const int m = 1 - mm;  // m = 0: B, m = 1: C
     if constexpr (!EARLY) load_rows(m);
     const RowLoad<Tin, 8 + HALO>& rl = rlm[m];
-    float v[8][8];
     if constexpr (CONV)
       conv_rows_to<Tin, 8>(a, rl, tstart, sCw, 2 * N, m * N + 8 * cv, 8 * rg, Lc, &v[0][0], 8);
     else
       copy_rows_to<Tin, 8>(a, rl, tstart, 8 * rg, Lc, &v[0][0], 8);
-    // bf16 rows [t][n] into LDS for the B C^T tiles, and C in fragment order
-    // (the 8 channels 8 cv .. 8 cv + 7 of a row are 8 consecutive elements)
+    // bf16 rows [t][n] into LDS (the 8 channels 8 cv .. 8 cv + 7 of a row
+    // are 8 consecutive elements)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       bf16x8 r;
 #pragma unroll
       for (int e = 0; e < 8; ++e) r[e] = (bf16)v[i][e];
-      const int t = 8 * rg + i;
-      *reinterpret_cast<bf16x8*>((m == 0 ? sPB : sPC) + t * LDB + 8 * cv) = r;
-      if (m == 1) *reinterpret_cast<bf16x8*>(pk + G_::PK_C + frag_off<N / 32>(t, 8 * cv)) = r;
-    }
-    if (m == 0) {
-      // B transposed [n][s], hi and lo
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        bf16x8 hi, lo;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          bf16 hh, ll;
-          split1(v[i][e], hh, ll);
-          hi[i] = hh;
-          lo[i] = ll;
-        }
-        // B^T row n = 8 cv + e, columns s = 8 rg .. 8 rg + 7: 8 consecutive
-        // elements in fragment order
-        const int o = frag_off<KQ>(8 * cv + e, 8 * rg);
-        *reinterpret_cast<bf16x8*>(pk + G_::PK_BTH + o) = hi;
-        *reinterpret_cast<bf16x8*>(pk + G_::PK_BTL + o) = lo;
-      }
+      *reinterpret_cast<bf16x8*>((m == 0 ? sPB : sPC) + (8 * rg + i) * LDB + 8 * cv) = r;
     }
   }
-
-  // causal tiles of B C^T (rows s, columns t) with fp32 accumulation, in the
-  // accumulator order the walkers use; NTRI / (2 Q / 64) tiles per wave (5,
-  // 9 or 17)
   lds_barrier();
+
+  // Every part of the pack leaves through LDS, so that each wave writes whole
+  // 1 KiB fragments (16 bytes per lane, consecutive lanes consecutive in
+  // memory) rather than 16-byte pieces scattered over many lines.
+  const int pw = tid >> 6, lane = tid & 63, l16 = lane & 15, q = lane >> 4;
+  constexpr int NW = PACK_THREADS / 64;
+  // causal tiles of B C^T (rows s, columns t) with fp32 accumulation, in the
+  // accumulator order the walkers use; NTRI / NW tiles per wave (5, 9 or 17)
   {
-    const int pw = tid >> 6, lane = tid & 63, l16 = lane & 15, q = lane >> 4;
     float* cbo = reinterpret_cast<float*>(pk + G_::PK_CB);
-    for (int k = pw; k < NTRI; k += PACK_THREADS / 64) {
+    for (int k = pw; k < NTRI; k += NW) {
       int rt = 0;
       while (tri(rt + 1) <= k) ++rt;
       const int u = k - tri(rt);
@@ -570,6 +563,48 @@ __global__ __launch_bounds__(Geo<Q>::PACK_THREADS) void bc_pack_kernel(ScanArgs 
         acc = mfma(lds8(brow + 32 * kk), lds8(crow + 32 * kk), acc);
       *reinterpret_cast<f32x4*>(cbo + (k * 64 + lane) * 4) = acc;
     }
+  }
+  // C in fragment order: fragment f = (t tile i16, K step kk) takes lane l's
+  // 8 channels 32 kk + 8 q .. of token 16 i16 + l % 16
+  for (int f = pw; f < (Q / 16) * (N / 32); f += NW) {
+    const int i16 = f / (N / 32), kk = f % (N / 32);
+    *reinterpret_cast<bf16x8*>(pk + G_::PK_C + (f * 64 + lane) * 8) =
+        lds8(sPC + (16 * i16 + l16) * LDB + 32 * kk + 8 * q);
+  }
+  lds_barrier();
+
+  // B^T hi and lo, [n][s], into the two tiles just read: row n holds Q
+  // tokens with no padding, its 16-byte block cb (tokens 8 cb .. 8 cb + 7)
+  // at block cb ^ bt_key(n), which keeps both the writes below (rows 8 apart
+  // across lanes) and the fragment reads after (16 consecutive rows) clear
+  // of bank conflicts
+  static_assert(N * Q <= Q * LDB, "the B^T staging tile fits in the [t][n] tiles");
+  bf16* sBTh = sPB;
+  bf16* sBTl = sPC;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    bf16x8 hi, lo;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      bf16 hh, ll;
+      split1(v[i][e], hh, ll);
+      hi[i] = hh;
+      lo[i] = ll;
+    }
+    const int n = 8 * cv + e;
+    const int o = n * Q + 8 * (rg ^ bt_key<Q>(n));
+    *reinterpret_cast<bf16x8*>(sBTh + o) = hi;
+    *reinterpret_cast<bf16x8*>(sBTl + o) = lo;
+  }
+  lds_barrier();
+  // fragment f = (n tile i16, K step kk): lane l's 8 tokens 32 kk + 8 q .. of
+  // channel 16 i16 + l % 16
+  for (int f = pw; f < 8 * KQ; f += NW) {
+    const int i16 = f / KQ, kk = f % KQ;
+    const int n = 16 * i16 + l16;
+    const int o = n * Q + 8 * ((4 * kk + q) ^ bt_key<Q>(n));
+    *reinterpret_cast<bf16x8*>(pk + G_::PK_BTH + (f * 64 + lane) * 8) = lds8(sBTh + o);
+    *reinterpret_cast<bf16x8*>(pk + G_::PK_BTL + (f * 64 + lane) * 8) = lds8(sBTl + o);
   }
 
   // conv history hand-over of the group's B and C channels
