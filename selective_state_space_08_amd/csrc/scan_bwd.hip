@@ -760,6 +760,9 @@ __global__ void reduce_bc_kernel(const float* __restrict__ dBh, const float* __r
   const int hpg = nheads / ngroups;
   const float* src = isC ? dCh : dBh;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  // (unrolled so that the loads of several heads are in flight together;
+  // the sum is still taken over j in order)
+#pragma unroll 8
   for (int j = 0; j < hpg; ++j) {
     const int h = g * hpg + j;
     const float4 v = *reinterpret_cast<const float4*>(src + (((int64_t)b * nheads + h) * seqlen + t) * BN + n);
@@ -868,11 +871,15 @@ __global__ void conv_bwd_kernel(const void* x, int64_t xs, const void* Bm, int64
 
 // Fixed-order sums: dA, dD, dt_bias over the batch; the conv weights and bias
 // over (b, block).
-__global__ void reduce_params_kernel(const float* __restrict__ part, int batch, int nheads,
-                                     float* dA, float* dD, float* dbias,
-                                     const float* __restrict__ wpart, int nparts, int cdim, int K,
-                                     float* dw, float* db) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+constexpr int RP_CH = 32;      // conv channels per workgroup
+constexpr int RP_GROUPS = 8;   // partial-sum groups per channel
+constexpr int RP_THREADS = RP_CH * RP_GROUPS;
+__global__ __launch_bounds__(RP_THREADS) void reduce_params_kernel(
+    const float* __restrict__ part, int batch, int nheads, float* dA, float* dD, float* dbias,
+    const float* __restrict__ wpart, int nparts, int cdim, int K, float* dw, float* db) {
+  __shared__ float sred[RP_GROUPS][RP_CH][5];
+  const int tid = threadIdx.x;
+  const int i = blockIdx.x * RP_THREADS + tid;
   if (i < nheads) {
     float sa = 0.f, sd = 0.f, sb = 0.f;
     for (int b = 0; b < batch; ++b) {
@@ -883,13 +890,28 @@ __global__ void reduce_params_kernel(const float* __restrict__ part, int batch, 
     if (dD) dD[i] = sd;
     if (dbias) dbias[i] = sb;
   }
-  if (wpart != nullptr && i < cdim) {
+  if (wpart != nullptr) {  // (uniform)
+    // channel c of this workgroup's RP_CH: group grp sums parts grp,
+    // grp + RP_GROUPS, ... in order, then the groups are added in order
+    const int cl = tid % RP_CH, grp = tid / RP_CH;
+    const int c = blockIdx.x * RP_CH + cl;
     float s[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < nparts; ++j)
-      for (int k = 0; k < 5; ++k) s[k] += wpart[((int64_t)j * cdim + i) * 5 + k];
-    if (dw)
-      for (int k = 0; k < K; ++k) dw[i * K + k] = s[k];
-    if (db) db[i] = s[4];
+    if (c < cdim)
+      for (int j = grp; j < nparts; j += RP_GROUPS)
+#pragma unroll
+        for (int k = 0; k < 5; ++k) s[k] += wpart[((int64_t)j * cdim + c) * 5 + k];
+#pragma unroll
+    for (int k = 0; k < 5; ++k) sred[grp][cl][k] = s[k];
+    __syncthreads();
+    if (grp == 0 && c < cdim) {
+      float t[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int gg = 0; gg < RP_GROUPS; ++gg)
+#pragma unroll
+        for (int k = 0; k < 5; ++k) t[k] += sred[gg][cl][k];
+      if (dw)
+        for (int k = 0; k < K; ++k) dw[c * K + k] = t[k];
+      if (db) db[c] = t[4];
+    }
   }
 }
 
@@ -1023,8 +1045,9 @@ hipError_t launch_scan_bwd(const ScanBwdLaunch& l, hipStream_t stream) {
   }
   // 6. parameter sums
   {
-    const int n = l.conv_w ? (cdim > H ? cdim : H) : H;
-    reduce_params_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(
+    const int gh = (H + RP_THREADS - 1) / RP_THREADS;
+    const int gc = l.conv_w ? (cdim + RP_CH - 1) / RP_CH : 0;
+    reduce_params_kernel<<<(unsigned)(gh > gc ? gh : gc), RP_THREADS, 0, stream>>>(
         a.part, B, H, l.dA, l.dD, l.ddt_bias, l.conv_w ? wpart : nullptr, B * nblk, cdim,
         l.conv_k, l.dconv_w, l.dconv_b);
     if ((e = hipGetLastError()) != hipSuccess) return e;
