@@ -124,7 +124,8 @@ struct Geo {
   static constexpr int PK_BTL = 2 * Q * N;       // B^T [n][s] lo, fragment order
   static constexpr int PK_CB = 3 * Q * N;        // B C^T causal tiles, fp32
   static constexpr int PACK = 3 * Q * N + 2 * NTRI * 256;
-  static constexpr int PACK_THREADS = 2 * Q;     // 8 tokens x 8 channels each
+  static constexpr int PACK_TOK = 4;             // pack: tokens per thread
+  static constexpr int PACK_THREADS = 16 * Q / PACK_TOK;  // PACK_TOK tokens x 8 channels each
   // x staging: thread (xv = tid % XV, xr = tid / XV) owns channels
   // [8 xv, 8 xv + 8) of tokens [RX xr, RX xr + RX)
   static constexpr int XV = PW / 8;
@@ -464,9 +465,9 @@ __device__ __forceinline__ int bt_key(int n) {
 }
 
 
-// One workgroup of 2 Q threads per (chunk c, group g, sequence b).  Thread
+// One workgroup of 4 Q threads per (chunk c, group g, sequence b).  Thread
 // (cv = tid % 16, rg = tid / 16) owns channels [8 cv, 8 cv + 8) and tokens
-// [8 rg, 8 rg + 8) of the chunk for B and for C.  Tokens past the end of the
+// [4 rg, 4 rg + 4) of the chunk for B and for C.  Tokens past the end of the
 // sequence are written as zeros.  With the conv, the workgroup of the last
 // chunk also hands the last K-1 raw B and C rows of the group over to
 // conv_state_out.
@@ -474,7 +475,7 @@ template <typename Tin, bool CONV, int Q>
 __global__ __launch_bounds__(Geo<Q>::PACK_THREADS) void bc_pack_kernel(ScanArgs a, bf16* pack) {
   using G_ = Geo<Q>;
   constexpr int PACK_THREADS = G_::PACK_THREADS, PACK = G_::PACK, NTRI = G_::NTRI;
-  constexpr int KQ = G_::KQ;
+  constexpr int KQ = G_::KQ, PT = G_::PACK_TOK;
   __shared__ __attribute__((aligned(16))) float sCw[CONV ? 5 * 2 * N : 4];
   __shared__ __attribute__((aligned(16))) bf16 sPB[Q * LDB];  // B [s][n] bf16
   __shared__ __attribute__((aligned(16))) bf16 sPC[Q * LDB];  // C [t][n] bf16
@@ -491,8 +492,8 @@ __global__ __launch_bounds__(Geo<Q>::PACK_THREADS) void bc_pack_kernel(ScanArgs 
   // call); fp32 rows are loaded one tensor at a time, since holding both
   // would cost the kernel half its occupancy
   constexpr bool EARLY = sizeof(Tin) == 2;
-  const int tstart = t0 + 8 * rg - HALO;
-  RowLoad<Tin, 8 + HALO> rlm[2];
+  const int tstart = t0 + PT * rg - HALO;
+  RowLoad<Tin, PT + HALO> rlm[2];
   auto load_rows = [&](int m) {
     const Tin* src = static_cast<const Tin*>(m == 0 ? a.Bm : a.Cm);
     const int64_t stride = m == 0 ? a.b_stride : a.c_stride;
@@ -520,24 +521,24 @@ __global__ __launch_bounds__(Geo<Q>::PACK_THREADS) void bc_pack_kernel(ScanArgs 
   }
 
   // C first, then B, whose values stay in v for the B^T parts
-  float v[8][8];
+  float v[PT][8];
 #pragma unroll
   for (int mm = 0; mm < 2; ++mm) {
     const int m = 1 - mm;  // m = 0: B, m = 1: C
     if constexpr (!EARLY) load_rows(m);
-    const RowLoad<Tin, 8 + HALO>& rl = rlm[m];
+    const RowLoad<Tin, PT + HALO>& rl = rlm[m];
     if constexpr (CONV)
-      conv_rows_to<Tin, 8>(a, rl, tstart, sCw, 2 * N, m * N + 8 * cv, 8 * rg, Lc, &v[0][0], 8);
+      conv_rows_to<Tin, PT>(a, rl, tstart, sCw, 2 * N, m * N + 8 * cv, PT * rg, Lc, &v[0][0], 8);
     else
-      copy_rows_to<Tin, 8>(a, rl, tstart, 8 * rg, Lc, &v[0][0], 8);
+      copy_rows_to<Tin, PT>(a, rl, tstart, PT * rg, Lc, &v[0][0], 8);
     // bf16 rows [t][n] into LDS (the 8 channels 8 cv .. 8 cv + 7 of a row
     // are 8 consecutive elements)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < PT; ++i) {
       bf16x8 r;
 #pragma unroll
       for (int e = 0; e < 8; ++e) r[e] = (bf16)v[i][e];
-      *reinterpret_cast<bf16x8*>((m == 0 ? sPB : sPC) + (8 * rg + i) * LDB + 8 * cv) = r;
+      *reinterpret_cast<bf16x8*>((m == 0 ? sPB : sPC) + (PT * rg + i) * LDB + 8 * cv) = r;
     }
   }
   lds_barrier();
@@ -581,20 +582,22 @@ __global__ __launch_bounds__(Geo<Q>::PACK_THREADS) void bc_pack_kernel(ScanArgs 
   static_assert(N * Q <= Q * LDB, "the B^T staging tile fits in the [t][n] tiles");
   bf16* sBTh = sPB;
   bf16* sBTl = sPC;
+  static_assert(PT == 4, "B^T staging writes 4 tokens (half a 16-byte block) per row");
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    bf16x8 hi, lo;
+    bf16x4 hi, lo;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < PT; ++i) {
       bf16 hh, ll;
       split1(v[i][e], hh, ll);
       hi[i] = hh;
       lo[i] = ll;
     }
+    // tokens 4 rg .. 4 rg + 3: half (rg % 2) of 16-byte block rg / 2
     const int n = 8 * cv + e;
-    const int o = n * Q + 8 * (rg ^ bt_key<Q>(n));
-    *reinterpret_cast<bf16x8*>(sBTh + o) = hi;
-    *reinterpret_cast<bf16x8*>(sBTl + o) = lo;
+    const int o = n * Q + 8 * ((rg >> 1) ^ bt_key<Q>(n)) + 4 * (rg & 1);
+    *reinterpret_cast<bf16x4*>(sBTh + o) = hi;
+    *reinterpret_cast<bf16x4*>(sBTl + o) = lo;
   }
   lds_barrier();
   // fragment f = (n tile i16, K step kk): lane l's 8 tokens 32 kk + 8 q .. of
