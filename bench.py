@@ -257,6 +257,22 @@ def time_backward(args, wl, torch, ssd, synth, dev, dev32):
     return ms
 
 
+def time_conv(args, wl, torch, ssd, synth, dev, dev32):
+    """The standalone conv (ssd_causal_conv1d_fwd) over the workload's raw
+    x|B|C: bf16 in, the fp32 post-conv values out (the first step of the
+    unfused prefill)."""
+    inp = synth.make_prefill(wl)
+    xbc = dev(inp.xbc, "bf16")
+    cw = dev32(inp.conv_w)
+    del inp
+    out = torch.empty(xbc.shape, device="cuda")
+    ms = events_ms(torch, lambda: ssd.ssd_causal_conv1d_fwd(xbc, cw, out=out), args.steps,
+                   args.warmup)
+    log("conv: %.3f ms per call" % ms)
+    del xbc, out
+    return ms
+
+
 def events_ms(torch, fn, steps: int, warmup: int):
     """Mean duration of fn() over `steps` calls, from HIP events on the stream
     the library launches on (torch's current stream)."""
@@ -440,6 +456,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the layer's backward pass")
+    ap.add_argument("--no-conv", action="store_true",
+                    help="skip the standalone conv timing")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the block around the layer (RMSNorm + projections)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -549,6 +567,18 @@ def main():
                 "mfma": {"alg_flops_per_token": cf, "achieved_tflops": tf, "peak_tflops": mpeak,
                          "frac": tf / mpeak},
             }
+    if not args.no_conv:
+        cms = time_conv(args, wl, torch, ssd, synth, dev, dev32)
+        cbytes = (2.0 + 4.0) * wl.cdim * wl.tokens  # bf16 in, fp32 out, each element once
+        cgbs = cbytes / (cms / 1e3) / 1e9
+        out["conv"] = {
+            "workload": wl.name + " x|B|C (bf16 in, fp32 out)", "ms_per_call": cms,
+            "tokens_per_s": wl.tokens / (cms / 1e3),
+            "roofline": {"bound": "hbm", "achieved": cgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": cgbs / HBM_PEAK_GBS,
+                         "traffic": traffic_record("conv_fwd", src_hash("conv1d.hip", "api.hip")),
+                         "kernel": "causal_conv1d_kernel", "alg_bytes_per_call": cbytes,
+                         "measured_peak": copy_gbs, "frac_of_measured": cgbs / copy_gbs}}
     if not args.no_decode:
         dwl = WORKLOADS[DECODE_MAIN].with_(decode_steps=args.decode_steps)
         dec = time_decode(args, dwl, torch, layer, synth, dev, dev32)
