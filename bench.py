@@ -312,7 +312,10 @@ def time_block(args, wl, torch, ssd, synth, dev, dev32):
     zx = torch.empty((T, wl.d_in_proj), dtype=torch.bfloat16, device="cuda")
     in_ms = events_ms(torch, lambda: ssd.ssd_linear_fwd(u, win, out=zx), steps, warm)
     del zx
-    y = torch.zeros((T, wl.d_inner), dtype=torch.bfloat16, device="cuda")
+    # a seeded random layer output (an all-zero operand would let the matrix
+    # cores run at a lower power and a higher clock than real data does)
+    gen = torch.Generator(device="cuda").manual_seed(wl.seed + 7)
+    y = torch.randn((T, wl.d_inner), generator=gen, device="cuda").to(torch.bfloat16)
     o2 = out.view(T, dm)
     out_ms = events_ms(torch, lambda: ssd.ssd_linear_fwd(y, wout, residual=u, out=o2), steps, warm)
     log("block: %.3f ms per call; in_proj %.3f ms, out_proj %.3f ms" % (call_ms, in_ms, out_ms))
