@@ -29,26 +29,6 @@ __device__ __forceinline__ float ldf(const void* p, int64_t i) {
   return to_f32(static_cast<const T*>(p)[i]);
 }
 
-// Post-conv value of element j (index within its own tensor's row) of token t
-// of sequence b; c is the element's conv channel (row of conv_w).
-template <typename Tx, bool CONV>
-__device__ __forceinline__ float load_post(const ScanArgs& a, const void* base, int64_t stride,
-                                           int b, int t, int j, int c, int cdim) {
-  if (!CONV) return ldf<Tx>(base, ((int64_t)b * a.seqlen + t) * stride + j);
-  const int K = a.conv_k;
-  float u = a.conv_b ? a.conv_b[c] : 0.f;
-  for (int k = 0; k < K; ++k) {
-    const int tau = t - (K - 1) + k;
-    float v = 0.f;
-    if (tau >= 0)
-      v = ldf<Tx>(base, ((int64_t)b * a.seqlen + tau) * stride + j);
-    else if (a.conv_state_in != nullptr)
-      v = ldf<Tx>(a.conv_state_in, ((int64_t)b * (K - 1) + (K - 1) + tau) * cdim + c);
-    u += a.conv_w[(int64_t)c * K + k] * v;
-  }
-  return silu_f32(u);
-}
-
 // Raw conv input at tau (possibly negative) for the hand-over of the history.
 template <typename Tx>
 __device__ __forceinline__ float load_raw(const ScanArgs& a, const void* base, int64_t stride,
@@ -58,6 +38,66 @@ __device__ __forceinline__ float load_raw(const ScanArgs& a, const void* base, i
   if (a.conv_state_in != nullptr && tau >= -(K - 1))
     return ldf<Tx>(a.conv_state_in, ((int64_t)b * (K - 1) + (K - 1) + tau) * cdim + c);
   return 0.f;
+}
+
+// A [TT][NC] tile of post-conv values into LDS (row r at dst + r * ld): the
+// rows are tokens tok0 .. tok0 + TT - 1 of sequence b, the columns elements
+// j0 .. j0 + NC - 1 of the tensor's row (conv channels c0 .. c0 + NC - 1).
+// Rows from nvalid on are zero.  Thread t owns column t % NC and a run of
+// TT / (THREADS / NC) consecutive rows: it issues every raw load of the run
+// (with the conv, the run and its 3-token halo) before any arithmetic, and
+// slides the conv window along the run.  Conv: u = bias + the taps' products
+// added oldest input first (the first tap meets the token K - 1 before the
+// output), then SiLU; before the first token the inputs come from the conv
+// state (oldest row first) or are zero.
+template <typename Tx, bool CONV, int NC>
+__device__ __forceinline__ void fill_tile(const ScanArgs& a, const void* base, int64_t stride,
+                                          int b, int tok0, int nvalid, int j0, int c0, int cdim,
+                                          float* dst, int ld) {
+  constexpr int RPT = TT / (THREADS / NC);
+  const int col = threadIdx.x % NC, r0 = (threadIdx.x / NC) * RPT;
+  const int L = a.seqlen, j = j0 + col, c = c0 + col;
+  constexpr int HALO = CONV ? 3 : 0;
+  float raw[RPT + HALO];
+#pragma unroll
+  for (int i = 0; i < RPT + HALO; ++i) {
+    // (rows past the sequence re-read its last token; their results are zeroed)
+    const int tau = min(max(tok0 + r0 - HALO + i, 0), L - 1);
+    raw[i] = ldf<Tx>(base, ((int64_t)b * L + tau) * stride + j);
+  }
+  if (CONV && tok0 + r0 - HALO < 0) {  // the history before the first token
+    const int K = a.conv_k;
+#pragma unroll
+    for (int i = 0; i < HALO; ++i) {
+      const int tau = tok0 + r0 - HALO + i;
+      if (tau < 0)
+        raw[i] = a.conv_state_in != nullptr && tau >= -(K - 1)
+                     ? ldf<Tx>(a.conv_state_in, ((int64_t)b * (K - 1) + (K - 1) + tau) * cdim + c)
+                     : 0.f;
+    }
+  }
+  float out[RPT];
+  if constexpr (CONV) {
+    // taps right-aligned: tap k of 4 meets the token 3 - k before the output
+    const int K = a.conv_k;
+    float w4[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w4[k] = k >= 4 - K ? a.conv_w[(int64_t)c * K + k - (4 - K)] : 0.f;
+    const float bias = a.conv_b ? a.conv_b[c] : 0.f;
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      float u = bias;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (k >= 4 - K) u += w4[k] * raw[r + k];
+      out[r] = silu_f32(u);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) out[r] = raw[r];
+  }
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) dst[(r0 + r) * ld + col] = r0 + r < nvalid ? out[r] : 0.f;
 }
 
 // In-place inclusive prefix sum of s[0..n), n <= THREADS; fixed order.
@@ -127,12 +167,8 @@ __global__ __launch_bounds__(THREADS) void scan_f32_kernel(ScanArgs a) {
     const float lam_last = sLam[Lc - 1];
 
     for (int tt0 = 0; tt0 < Lc; tt0 += TT) {
-      for (int i = tid; i < TT * N; i += THREADS) {
-        const int r = i / N, n = i % N, t = tt0 + r;
-        sCt[r * LDN + n] = t < Lc ? load_post<Tx, CONV>(a, a.Cm, a.c_stride, b, c0 + t, g * N + n,
-                                                        HP + GN + g * N + n, cdim)
-                                  : 0.f;
-      }
+      fill_tile<Tx, CONV, N>(a, a.Cm, a.c_stride, b, c0 + tt0, Lc - tt0, g * N, HP + GN + g * N,
+                             cdim, sCt, LDN);
       __syncthreads();
       float yacc[TT / 4];
 #pragma unroll
@@ -144,18 +180,10 @@ __global__ __launch_bounds__(THREADS) void scan_f32_kernel(ScanArgs a) {
       }
       for (int st0 = 0; st0 <= tt0; st0 += TT) {
         __syncthreads();
-        for (int i = tid; i < TT * N; i += THREADS) {
-          const int r = i / N, n = i % N, s = st0 + r;
-          sBt[r * LDN + n] = s < Lc ? load_post<Tx, CONV>(a, a.Bm, a.b_stride, b, c0 + s, g * N + n,
-                                                          HP + g * N + n, cdim)
-                                    : 0.f;
-        }
-        for (int i = tid; i < TT * P; i += THREADS) {
-          const int r = i / P, p = i % P, s = st0 + r;
-          sX[r * LDP + p] = s < Lc ? load_post<Tx, CONV>(a, a.x, a.x_stride, b, c0 + s, h * P + p,
-                                                         h * P + p, cdim)
-                                   : 0.f;
-        }
+        fill_tile<Tx, CONV, N>(a, a.Bm, a.b_stride, b, c0 + st0, Lc - st0, g * N, HP + g * N, cdim,
+                               sBt, LDN);
+        fill_tile<Tx, CONV, P>(a, a.x, a.x_stride, b, c0 + st0, Lc - st0, h * P, h * P, cdim, sX,
+                               LDP);
         __syncthreads();
         for (int e = tid; e < TT * TT; e += THREADS) {
           const int r = e / TT, q = e % TT, t = tt0 + r, s = st0 + q;
@@ -180,8 +208,8 @@ __global__ __launch_bounds__(THREADS) void scan_f32_kernel(ScanArgs a) {
       for (int i = 0; i < TT / 4; ++i) {
         const int t = tt0 + tr + 4 * i;
         if (t < Lc) {
-          const float xv =
-              load_post<Tx, CONV>(a, a.x, a.x_stride, b, c0 + t, h * P + yp, h * P + yp, cdim);
+          // sX holds the diagonal source tile, i.e. this output tile's x
+          const float xv = sX[(tr + 4 * i) * LDP + yp];
           float yv = yacc[i] + Dh * xv;
           if (a.z != nullptr)
             yv *= silu_f32(ldf<Ta>(a.z, ((int64_t)b * L + c0 + t) * a.z_stride + h * P + yp));
@@ -199,18 +227,10 @@ __global__ __launch_bounds__(THREADS) void scan_f32_kernel(ScanArgs a) {
     for (int k = 0; k < 32; ++k) hacc[k] = gamma * sH[sp * LDN + sn0 + k];
     for (int st0 = 0; st0 < Lc; st0 += TT) {
       __syncthreads();
-      for (int i = tid; i < TT * N; i += THREADS) {
-        const int r = i / N, n = i % N, s = st0 + r;
-        sBt[r * LDN + n] = s < Lc ? load_post<Tx, CONV>(a, a.Bm, a.b_stride, b, c0 + s, g * N + n,
-                                                        HP + g * N + n, cdim)
-                                  : 0.f;
-      }
-      for (int i = tid; i < TT * P; i += THREADS) {
-        const int r = i / P, p = i % P, s = st0 + r;
-        sX[r * LDP + p] = s < Lc ? load_post<Tx, CONV>(a, a.x, a.x_stride, b, c0 + s, h * P + p,
-                                                       h * P + p, cdim)
-                                 : 0.f;
-      }
+      fill_tile<Tx, CONV, N>(a, a.Bm, a.b_stride, b, c0 + st0, Lc - st0, g * N, HP + g * N, cdim,
+                             sBt, LDN);
+      fill_tile<Tx, CONV, P>(a, a.x, a.x_stride, b, c0 + st0, Lc - st0, h * P, h * P, cdim, sX,
+                             LDP);
       __syncthreads();
       for (int q = 0; q < TT && st0 + q < Lc; ++q) {
         const int s = st0 + q;
