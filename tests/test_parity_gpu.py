@@ -215,6 +215,32 @@ def test_layer_with_conv_history(math_mode, fused):
 
 
 @pytest.mark.parametrize("math_mode", ["f32", "bf16"])
+@pytest.mark.parametrize("K", [1, 2, 3])
+def test_layer_narrow_conv(math_mode, K):
+    """The fused prefill with conv widths below the layer's 4 (the boundary
+    takes 1 to 4): a ragged sequence over several chunks, a nonzero conv
+    history and bias, y and the final state against the oracle, and the conv
+    state out equal to the last K-1 raw rows."""
+    dtype = "f32" if math_mode == "f32" else "bf16"
+    wl = Workload("t", batch=2, seqlen=300, nheads=4, ngroups=2, dtype=dtype, initial_state=True,
+                  seed=40 + K, width=K)
+    inp = synth.make_prefill(wl)
+    hist = synth.raw_history(wl, 41 + K) if K > 1 else None
+    conv_b = (0.01 * np.random.default_rng(K).standard_normal(wl.cdim)).astype(np.float32)
+    say("narrow conv K=%d %s" % (K, math_mode))
+    y, fs, cso = gpu_prefill(inp, fused=True, math_mode=math_mode, conv_state_in=hist,
+                             conv_state_out=K > 1, conv_b=conv_b)
+    pairs = [(b, h) for b in range(2) for h in range(4)]
+    yr, hr = oracle_pairs(inp, pairs, conv_state_in=hist, conv_b=conv_b)
+    assert rel_max_err(gather_y(y, pairs), yr) <= TOL[math_mode]
+    hg = np.stack([fs[b, h].double().cpu().numpy() for b, h in pairs])
+    assert rel_max_err(hg, hr) <= TOL[math_mode]
+    if K > 1:
+        series = np.concatenate([hist, inp.xbc], axis=1)
+        np.testing.assert_array_equal(cso.float().cpu().numpy(), series[:, -(K - 1):])
+
+
+@pytest.mark.parametrize("math_mode", ["f32", "bf16"])
 @pytest.mark.parametrize("L1", [1, 128, 200])
 def test_split_carry(math_mode, L1):
     """[0, L1) then [L1, L) with the SSM state and conv history carried equals
