@@ -46,10 +46,16 @@ def log(msg):
 
 
 def src_hash(*names):
+    """Hash of the named csrc files and the compiler options each is built
+    with: counters taken on other code, or the same code built otherwise, do
+    not match it."""
+    from selective_state_space_08_amd import build as libbuild
+    common = [f for f in libbuild.FLAGS if not f.startswith("-I")]  # (paths differ per machine)
     h = hashlib.sha256()
     for n in names:
         with open(os.path.join(ROOT, "selective_state_space_08_amd", "csrc", n), "rb") as f:
             h.update(f.read())
+        h.update(" ".join(common + libbuild.FILE_FLAGS.get(n, [])).encode())
     return h.hexdigest()[:16]
 
 
