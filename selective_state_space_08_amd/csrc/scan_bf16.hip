@@ -71,6 +71,14 @@ __host__ __device__ constexpr int prow(int p) { return p + (p >> 3); }
 
 __host__ __device__ constexpr int tri(int rt) { return rt * (rt + 1) / 2; }
 
+// Column of token s in the rows of the bf16 x tile read by the intra-chunk
+// product: within each 32-token block, token 16 h + 4 j + r (h < 2, j < 4,
+// r < 4) sits at 8 j + 4 h + r, so that the 8 tokens one lane needs for a
+// K = 32 step (4 of each of two 16-token tiles) are one 16-byte read.
+__host__ __device__ constexpr int xcol(int s) {
+  return (s & ~31) | ((s & 12) << 1) | ((s & 16) >> 2) | (s & 3);
+}
+
 // element offset of M[r][k] in fragment order, for a matrix whose rows have
 // KS steps of K = 32
 template <int KS>
@@ -906,7 +914,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(STATE_O
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        bf16* d = sXh + prow(8 * xv + e) * LDT + RX * xr;
+        bf16* d = sXh + prow(8 * xv + e) * LDT + xcol(RX * xr);
         if constexpr (RX == 2) {
           bf16x2 v2;
           v2[0] = (bf16)xt[e];
@@ -1054,14 +1062,11 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(STATE_O
         if (u0 > rt) break;
         // the step's x operands first, so that their LDS latency is hidden
         // behind the mask arithmetic
+        // (u0 is even: the step's 32 tokens are one block of the x tile)
         bf16x8 xf[NPJ];
 #pragma unroll
-        for (int pj = 0; pj < NPJ; ++pj) {
-          const bf16* xp = sXh + prow(16 * (pjb + pj) + l16) * LDT + 16 * u0 + 4 * q;
-          const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(xp);
-          const bf16x4 x1 = *reinterpret_cast<const bf16x4*>(xp + 16);
-          xf[pj] = bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        }
+        for (int pj = 0; pj < NPJ; ++pj)
+          xf[pj] = lds8(sXh + prow(16 * (pjb + pj) + l16) * LDT + 16 * u0 + 8 * q);
         f32x4 cbp[2];  // the step's two tiles, when they are loaded step by step
         if constexpr (!G_::CB_EARLY) {
 #pragma unroll
