@@ -49,6 +49,23 @@ def test_no_alloc_equals_workspace_path(dtype):
             assert torch.equal(g_, w_)
 
 
+def test_no_alloc_at_its_largest_batch():
+    """The largest call the static array takes: one head in one group (Cdim
+    = 64 + 2 * 128 = 320 channels) at batch 13107, 4194240 of its 4194304
+    floats; one step, byte for byte against the workspace path."""
+    H, G = 1, 1
+    B = (1 << 22) // (H * 64 + 2 * G * 128)
+    wl = Workload("na_max", batch=B, seqlen=1, nheads=H, ngroups=G, dtype="bf16",
+                  decode_steps=1, initial_state=True, seed=73)
+    inp = synth.make_decode(wl)
+    xbc, z, dt = inp.steps(0, 1)
+    say("no-alloc decode at the scratch limit: B=%d H=%d G=%d" % (B, H, G))
+    want = _step(ssd.ssd_state_update_ws, inp, xbc, dt, z, "bf16")
+    got = _step(ssd.ssd_state_update_noalloc, inp, xbc, dt, z, "bf16")
+    for g_, w_ in zip(got, want):
+        assert torch.equal(g_, w_)
+
+
 def test_no_alloc_refuses_beyond_its_scratch():
     """batch x Cdim above 4194304 floats: SSD_ERR_UNSUPPORTED, nothing run
     (pointers are never dereferenced; validation precedes every launch)."""
