@@ -325,6 +325,24 @@ def test_no_decay(math_mode, L):
         assert eh <= TOL[math_mode]
 
 
+@pytest.mark.parametrize("math_mode", ["f32", "bf16"])
+def test_scan_at_largest_batch(math_mode):
+    """The largest batch the scan takes (65535: the grid dimension the B|C
+    pack and the conv spread sequences over), on short sequences (3 tokens,
+    one ragged chunk, conv fused); sampled sequences, the last included,
+    against the oracle, with the final state."""
+    dtype = "f32" if math_mode == "f32" else "bf16"
+    B = 65535
+    inp = small(B, 3, 2, 1, dtype, h0=False, seed=51)
+    say("largest batch %s B=%d" % (math_mode, B))
+    pairs = [(0, 0), (B - 1, 1), (B - 1, 0), (12345, 1), (40000, 0)]
+    y, fs, _ = gpu_prefill(inp, fused=True, math_mode=math_mode)
+    yr, hr = oracle_pairs(inp, pairs)
+    assert rel_max_err(gather_y(y, pairs), yr) <= TOL[math_mode]
+    assert rel_max_err(np.stack([fs[b, h].double().cpu().numpy() for b, h in pairs]), hr) <= \
+        TOL[math_mode]
+
+
 def test_in_place_state_with_segments():
     """initial_state and final_state may be one buffer, also when split."""
     inp = small(1, 128 * 24, 2, 1, "bf16", seed=13)
