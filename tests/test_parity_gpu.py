@@ -20,7 +20,12 @@ from selective_state_space_08_amd.workloads import Workload
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
-PROBE_TOL = {"f32": 1e-5, "bf16": 1e-2}
+# SSM-only probes (D = 0, no gate): relative RMS error.  bf16: about 2.6 unit
+# roundoffs (u = 2^-9) -- the matrix-core products round C, B, the masked
+# C B^T tile, x and the bf16 copy of the state once each, independent errors
+# of RMS u / sqrt(3), about 4 per element, RMS ~2.3e-3 -- so that a 1% error
+# in the SSM term fails.
+PROBE_TOL = {"f32": 1e-5, "bf16": 5e-3}
 
 
 def small(B, L, H, G, dtype="bf16", h0=True, seed=1):
