@@ -20,9 +20,28 @@ constexpr int P = 64;
 constexpr int N = 128;
 constexpr int THREADS = 256;
 constexpr int TT = 32;  // token tile
-constexpr int LDN = N + 1;
+// Row pitches of the LDS tiles: multiples of 4 floats, so that the inner
+// loops read 4 consecutive k as one 16-byte read (sums still taken one k
+// at a time, in order); 132 = 4 mod 32, so that 8 lanes reading 8 rows at
+// one column (one 16-byte read each) fall on distinct banks.  The x tile is
+// read one value per lane (consecutive p in consecutive lanes) and keeps an
+// odd pitch.  At chunk 128 the walker takes under 80 KiB of LDS: two
+// workgroups share a CU.
+constexpr int LDN = N + 4;
+// the C tile is only read a row per wave (or two) at a time: no padding
+constexpr int LDC = N;
 constexpr int LDP = P + 1;
-constexpr int LDT = TT + 1;
+constexpr int LDT = TT;
+
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+// s + a . b over 4 consecutive k, added one k at a time in order
+__device__ __forceinline__ float dot4(float s, float4 a, float4 b) {
+  s += a.x * b.x;
+  s += a.y * b.y;
+  s += a.z * b.z;
+  s += a.w * b.w;
+  return s;
+}
 
 template <typename T>
 __device__ __forceinline__ float ldf(const void* p, int64_t i) {
@@ -123,9 +142,9 @@ __global__ __launch_bounds__(THREADS) void scan_f32_kernel(ScanArgs a) {
   const int Q = a.chunk;
   float* sH = smem;                 // [P][LDN]  state
   float* sLam = sH + P * LDN;       // [Q]       cumulative log decay in the chunk
-  float* sDel = sLam + Q;           // [Q]       delta
-  float* sCt = sDel + Q;            // [TT][LDN] C tile (output rows)
-  float* sBt = sCt + TT * LDN;      // [TT][LDN] B tile (source rows)
+  float* sDel = sLam + Q;           // [Q]       delta; then exp(Lam_last - Lam_s) delta_s
+  float* sCt = sDel + Q;            // [TT][LDC] C tile (output rows)
+  float* sBt = sCt + TT * LDC;      // [TT][LDN] B tile (source rows)
   float* sX = sBt + TT * LDN;       // [TT][LDP] x tile (source rows)
   float* sM = sX + TT * LDP;        // [TT][LDT] masked, decayed C B^T tile
   float* sRed = sM + TT * LDT;      // [4]
@@ -168,16 +187,21 @@ __global__ __launch_bounds__(THREADS) void scan_f32_kernel(ScanArgs a) {
 
     for (int tt0 = 0; tt0 < Lc; tt0 += TT) {
       fill_tile<Tx, CONV, N>(a, a.Cm, a.c_stride, b, c0 + tt0, Lc - tt0, g * N, HP + GN + g * N,
-                             cdim, sCt, LDN);
+                             cdim, sCt, LDC);
       __syncthreads();
+      // the read-out of the thread's TT / 4 rows: each 4 n of the state row
+      // read once for all of them (every row's sum still runs over n in order)
       float yacc[TT / 4];
 #pragma unroll
-      for (int i = 0; i < TT / 4; ++i) {
-        const int r = tr + 4 * i;
-        float s = 0.f;
-        for (int n = 0; n < N; ++n) s += sCt[r * LDN + n] * sH[yp * LDN + n];
-        yacc[i] = expf(sLam[tt0 + r]) * s;
+      for (int i = 0; i < TT / 4; ++i) yacc[i] = 0.f;
+#pragma unroll 2
+      for (int n = 0; n < N; n += 4) {
+        const float4 h4 = ld4(&sH[yp * LDN + n]);
+#pragma unroll
+        for (int i = 0; i < TT / 4; ++i) yacc[i] = dot4(yacc[i], ld4(&sCt[(tr + 4 * i) * LDC + n]), h4);
       }
+#pragma unroll
+      for (int i = 0; i < TT / 4; ++i) yacc[i] *= expf(sLam[tt0 + tr + 4 * i]);
       for (int st0 = 0; st0 <= tt0; st0 += TT) {
         __syncthreads();
         fill_tile<Tx, CONV, N>(a, a.Bm, a.b_stride, b, c0 + st0, Lc - st0, g * N, HP + g * N, cdim,
@@ -185,24 +209,43 @@ __global__ __launch_bounds__(THREADS) void scan_f32_kernel(ScanArgs a) {
         fill_tile<Tx, CONV, P>(a, a.x, a.x_stride, b, c0 + st0, Lc - st0, h * P, h * P, cdim, sX,
                                LDP);
         __syncthreads();
-        for (int e = tid; e < TT * TT; e += THREADS) {
-          const int r = e / TT, q = e % TT, t = tt0 + r, s = st0 + q;
-          float v = 0.f;
-          if (s <= t) {
-            float dot = 0.f;
-            for (int n = 0; n < N; ++n) dot += sCt[r * LDN + n] * sBt[q * LDN + n];
-            v = dot * expf(sLam[t] - sLam[s]) * sDel[s];
+        {
+          // the thread's TT * TT / THREADS elements share their column q: each
+          // 4 n of row q of B read once for all of them
+          constexpr int NE = TT * TT / THREADS;
+          const int q = tid % TT, r0 = tid / TT, s = st0 + q;
+          float dot[NE];
+#pragma unroll
+          for (int k = 0; k < NE; ++k) dot[k] = 0.f;
+#pragma unroll 2
+          for (int n = 0; n < N; n += 4) {
+            const float4 b4 = ld4(&sBt[q * LDN + n]);
+#pragma unroll
+            for (int k = 0; k < NE; ++k)
+              dot[k] = dot4(dot[k], ld4(&sCt[(r0 + k * (THREADS / TT)) * LDC + n]), b4);
           }
-          sM[r * LDT + q] = v;
+#pragma unroll
+          for (int k = 0; k < NE; ++k) {
+            const int r = r0 + k * (THREADS / TT), t = tt0 + r;
+            sM[r * LDT + q] = s <= t ? dot[k] * expf(sLam[t] - sLam[s]) * sDel[s] : 0.f;
+          }
         }
         __syncthreads();
+        // each x value read once for the thread's TT / 4 rows; every row's
+        // sum still runs over q in order
+        float sacc[TT / 4];
 #pragma unroll
-        for (int i = 0; i < TT / 4; ++i) {
-          const int r = tr + 4 * i;
-          float s = 0.f;
-          for (int q = 0; q < TT; ++q) s += sM[r * LDT + q] * sX[q * LDP + yp];
-          yacc[i] += s;
+        for (int i = 0; i < TT / 4; ++i) sacc[i] = 0.f;
+#pragma unroll 2
+        for (int q = 0; q < TT; q += 4) {
+          const float4 x4 = make_float4(sX[q * LDP + yp], sX[(q + 1) * LDP + yp],
+                                        sX[(q + 2) * LDP + yp], sX[(q + 3) * LDP + yp]);
+#pragma unroll
+          for (int i = 0; i < TT / 4; ++i)
+            sacc[i] = dot4(sacc[i], ld4(&sM[(tr + 4 * i) * LDT + q]), x4);
         }
+#pragma unroll
+        for (int i = 0; i < TT / 4; ++i) yacc[i] += sacc[i];
       }
 #pragma unroll
       for (int i = 0; i < TT / 4; ++i) {
@@ -220,11 +263,21 @@ __global__ __launch_bounds__(THREADS) void scan_f32_kernel(ScanArgs a) {
       __syncthreads();
     }
 
-    // state: H <- exp(lam_last) H + sum_s exp(lam_last - lam_s) delta_s x_s B_s^T
+    // state: H <- exp(lam_last) H + sum_s exp(lam_last - lam_s) delta_s x_s B_s^T.
+    // Each token's weight exp(lam_last - lam_s) delta_s once per chunk, in
+    // place of its delta (the output tiles are done with it; read past the
+    // barrier at the top of the tile loop below)
+    for (int t = tid; t < Q; t += THREADS) sDel[t] = expf(lam_last - sLam[t]) * sDel[t];
     float hacc[32];
     const float gamma = expf(lam_last);
 #pragma unroll
-    for (int k = 0; k < 32; ++k) hacc[k] = gamma * sH[sp * LDN + sn0 + k];
+    for (int k = 0; k < 32; k += 4) {
+      const float4 h4 = ld4(&sH[sp * LDN + sn0 + k]);
+      hacc[k] = gamma * h4.x;
+      hacc[k + 1] = gamma * h4.y;
+      hacc[k + 2] = gamma * h4.z;
+      hacc[k + 3] = gamma * h4.w;
+    }
     for (int st0 = 0; st0 < Lc; st0 += TT) {
       __syncthreads();
       fill_tile<Tx, CONV, N>(a, a.Bm, a.b_stride, b, c0 + st0, Lc - st0, g * N, HP + g * N, cdim,
@@ -234,14 +287,22 @@ __global__ __launch_bounds__(THREADS) void scan_f32_kernel(ScanArgs a) {
       __syncthreads();
       for (int q = 0; q < TT && st0 + q < Lc; ++q) {
         const int s = st0 + q;
-        const float ws = expf(lam_last - sLam[s]) * sDel[s] * sX[q * LDP + sp];
+        const float ws = sDel[s] * sX[q * LDP + sp];
 #pragma unroll
-        for (int k = 0; k < 32; ++k) hacc[k] += ws * sBt[q * LDN + sn0 + k];
+        for (int k = 0; k < 32; k += 4) {
+          const float4 b4 = ld4(&sBt[q * LDN + sn0 + k]);
+          hacc[k] += ws * b4.x;
+          hacc[k + 1] += ws * b4.y;
+          hacc[k + 2] += ws * b4.z;
+          hacc[k + 3] += ws * b4.w;
+        }
       }
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 32; ++k) sH[sp * LDN + sn0 + k] = hacc[k];
+    for (int k = 0; k < 32; k += 4)
+      *reinterpret_cast<float4*>(&sH[sp * LDN + sn0 + k]) =
+          make_float4(hacc[k], hacc[k + 1], hacc[k + 2], hacc[k + 3]);
   }
   __syncthreads();
 
@@ -272,7 +333,7 @@ __global__ __launch_bounds__(THREADS) void scan_f32_kernel(ScanArgs a) {
 
 template <typename Tx, typename Ta, typename Ty>
 hipError_t launch_typed(const ScanArgs& a, hipStream_t stream) {
-  const size_t lds = sizeof(float) * ((size_t)P * LDN + 2 * a.chunk + 2 * TT * LDN + TT * LDP +
+  const size_t lds = sizeof(float) * ((size_t)P * LDN + 2 * a.chunk + TT * LDC + TT * LDN + TT * LDP +
                                       TT * LDT + 4);
   const dim3 grid(a.batch * a.nheads);
   if (a.conv_w != nullptr) {
