@@ -18,7 +18,10 @@ namespace {
 
 constexpr int P = 64;
 constexpr int N = 128;
-constexpr int THREADS = 256;
+// Threads per walker: 512 (8 waves) when the walkers do not fill the chip,
+// each alone on its CU; 256 otherwise, so that two share a CU (LDS allows two
+// and 256 threads fit their registers).
+constexpr int NUM_CUS = 256;
 constexpr int TT = 32;  // token tile
 // Row pitches of the LDS tiles: multiples of 4 floats, so that the inner
 // loops read 4 consecutive k as one 16-byte read (sums still taken one k
@@ -63,17 +66,17 @@ __device__ __forceinline__ float load_raw(const ScanArgs& a, const void* base, i
 // rows are tokens tok0 .. tok0 + TT - 1 of sequence b, the columns elements
 // j0 .. j0 + NC - 1 of the tensor's row (conv channels c0 .. c0 + NC - 1).
 // Rows from nvalid on are zero.  Thread t owns column t % NC and a run of
-// TT / (THREADS / NC) consecutive rows: it issues every raw load of the run
+// TT / (NT / NC) consecutive rows: it issues every raw load of the run
 // (with the conv, the run and its 3-token halo) before any arithmetic, and
 // slides the conv window along the run.  Conv: u = bias + the taps' products
 // added oldest input first (the first tap meets the token K - 1 before the
 // output), then SiLU; before the first token the inputs come from the conv
 // state (oldest row first) or are zero.
-template <typename Tx, bool CONV, int NC>
+template <typename Tx, bool CONV, int NC, int NT>
 __device__ __forceinline__ void fill_tile(const ScanArgs& a, const void* base, int64_t stride,
                                           int b, int tok0, int nvalid, int j0, int c0, int cdim,
                                           float* dst, int ld) {
-  constexpr int RPT = TT / (THREADS / NC);
+  constexpr int RPT = TT / (NT / NC);
   const int col = threadIdx.x % NC, r0 = (threadIdx.x / NC) * RPT;
   const int L = a.seqlen, j = j0 + col, c = c0 + col;
   constexpr int HALO = CONV ? 3 : 0;
@@ -119,7 +122,7 @@ __device__ __forceinline__ void fill_tile(const ScanArgs& a, const void* base, i
   for (int r = 0; r < RPT; ++r) dst[(r0 + r) * ld + col] = r0 + r < nvalid ? out[r] : 0.f;
 }
 
-// In-place inclusive prefix sum of s[0..n), n <= THREADS; fixed order.
+// In-place inclusive prefix sum of s[0..n), n <= the block size; fixed order.
 __device__ void block_inclusive_scan(float* s, int n, float* red) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   float v = tid < n ? s[tid] : 0.f;
@@ -136,8 +139,11 @@ __device__ void block_inclusive_scan(float* s, int n, float* red) {
   __syncthreads();
 }
 
-template <typename Tx, typename Ta, typename Ty, bool CONV>
-__global__ __launch_bounds__(THREADS) void scan_f32_kernel(ScanArgs a) {
+template <typename Tx, typename Ta, typename Ty, bool CONV, int NT>
+__global__ __launch_bounds__(NT) void scan_f32_kernel(ScanArgs a) {
+  constexpr int THREADS = NT;
+  constexpr int RG = NT / 64;  // output rows: a wave per row group, RPW rows per thread
+  constexpr int SC = NT / 64;  // state update: SC threads per state row p
   extern __shared__ float smem[];
   const int Q = a.chunk;
   float* sH = smem;                 // [P][LDN]  state
@@ -147,7 +153,7 @@ __global__ __launch_bounds__(THREADS) void scan_f32_kernel(ScanArgs a) {
   float* sBt = sCt + TT * LDC;      // [TT][LDN] B tile (source rows)
   float* sX = sBt + TT * LDN;       // [TT][LDP] x tile (source rows)
   float* sM = sX + TT * LDP;        // [TT][LDT] masked, decayed C B^T tile
-  float* sRed = sM + TT * LDT;      // [4]
+  float* sRed = sM + TT * LDT;      // [NT / 64]
 
   const int H = a.nheads, G = a.ngroups, L = a.seqlen;
   const int b = blockIdx.x / H, h = blockIdx.x % H;
@@ -162,10 +168,12 @@ __global__ __launch_bounds__(THREADS) void scan_f32_kernel(ScanArgs a) {
         a.initial_state ? a.initial_state[((int64_t)b * H + h) * P * N + i] : 0.f;
   }
 
-  // output-tile mapping: column p, rows tr + 4 i
+  // output-tile mapping: column p, rows tr + RG i
+  constexpr int RPW = TT / RG;
   const int yp = tid & 63, tr = tid >> 6;
-  // state-update mapping: row sp, columns sn0 .. sn0 + 31
-  const int sp = tid >> 2, sn0 = (tid & 3) * 32;
+  // state-update mapping: row sp, columns sn0 .. sn0 + SW - 1
+  constexpr int SW = N / SC;
+  const int sp = tid / SC, sn0 = (tid % SC) * SW;
 
   for (int c0 = 0; c0 < L; c0 += Q) {
     const int Lc = min(Q, L - c0);
@@ -186,27 +194,27 @@ __global__ __launch_bounds__(THREADS) void scan_f32_kernel(ScanArgs a) {
     const float lam_last = sLam[Lc - 1];
 
     for (int tt0 = 0; tt0 < Lc; tt0 += TT) {
-      fill_tile<Tx, CONV, N>(a, a.Cm, a.c_stride, b, c0 + tt0, Lc - tt0, g * N, HP + GN + g * N,
+      fill_tile<Tx, CONV, N, NT>(a, a.Cm, a.c_stride, b, c0 + tt0, Lc - tt0, g * N, HP + GN + g * N,
                              cdim, sCt, LDC);
       __syncthreads();
-      // the read-out of the thread's TT / 4 rows: each 4 n of the state row
+      // the read-out of the thread's RPW rows: each 4 n of the state row
       // read once for all of them (every row's sum still runs over n in order)
-      float yacc[TT / 4];
+      float yacc[RPW];
 #pragma unroll
-      for (int i = 0; i < TT / 4; ++i) yacc[i] = 0.f;
+      for (int i = 0; i < RPW; ++i) yacc[i] = 0.f;
 #pragma unroll 2
       for (int n = 0; n < N; n += 4) {
         const float4 h4 = ld4(&sH[yp * LDN + n]);
 #pragma unroll
-        for (int i = 0; i < TT / 4; ++i) yacc[i] = dot4(yacc[i], ld4(&sCt[(tr + 4 * i) * LDC + n]), h4);
+        for (int i = 0; i < RPW; ++i) yacc[i] = dot4(yacc[i], ld4(&sCt[(tr + RG * i) * LDC + n]), h4);
       }
 #pragma unroll
-      for (int i = 0; i < TT / 4; ++i) yacc[i] *= expf(sLam[tt0 + tr + 4 * i]);
+      for (int i = 0; i < RPW; ++i) yacc[i] *= expf(sLam[tt0 + tr + RG * i]);
       for (int st0 = 0; st0 <= tt0; st0 += TT) {
         __syncthreads();
-        fill_tile<Tx, CONV, N>(a, a.Bm, a.b_stride, b, c0 + st0, Lc - st0, g * N, HP + g * N, cdim,
+        fill_tile<Tx, CONV, N, NT>(a, a.Bm, a.b_stride, b, c0 + st0, Lc - st0, g * N, HP + g * N, cdim,
                                sBt, LDN);
-        fill_tile<Tx, CONV, P>(a, a.x, a.x_stride, b, c0 + st0, Lc - st0, h * P, h * P, cdim, sX,
+        fill_tile<Tx, CONV, P, NT>(a, a.x, a.x_stride, b, c0 + st0, Lc - st0, h * P, h * P, cdim, sX,
                                LDP);
         __syncthreads();
         {
@@ -231,28 +239,28 @@ __global__ __launch_bounds__(THREADS) void scan_f32_kernel(ScanArgs a) {
           }
         }
         __syncthreads();
-        // each x value read once for the thread's TT / 4 rows; every row's
+        // each x value read once for the thread's RPW rows; every row's
         // sum still runs over q in order
-        float sacc[TT / 4];
+        float sacc[RPW];
 #pragma unroll
-        for (int i = 0; i < TT / 4; ++i) sacc[i] = 0.f;
+        for (int i = 0; i < RPW; ++i) sacc[i] = 0.f;
 #pragma unroll 2
         for (int q = 0; q < TT; q += 4) {
           const float4 x4 = make_float4(sX[q * LDP + yp], sX[(q + 1) * LDP + yp],
                                         sX[(q + 2) * LDP + yp], sX[(q + 3) * LDP + yp]);
 #pragma unroll
-          for (int i = 0; i < TT / 4; ++i)
-            sacc[i] = dot4(sacc[i], ld4(&sM[(tr + 4 * i) * LDT + q]), x4);
+          for (int i = 0; i < RPW; ++i)
+            sacc[i] = dot4(sacc[i], ld4(&sM[(tr + RG * i) * LDT + q]), x4);
         }
 #pragma unroll
-        for (int i = 0; i < TT / 4; ++i) yacc[i] += sacc[i];
+        for (int i = 0; i < RPW; ++i) yacc[i] += sacc[i];
       }
 #pragma unroll
-      for (int i = 0; i < TT / 4; ++i) {
-        const int t = tt0 + tr + 4 * i;
+      for (int i = 0; i < RPW; ++i) {
+        const int t = tt0 + tr + RG * i;
         if (t < Lc) {
           // sX holds the diagonal source tile, i.e. this output tile's x
-          const float xv = sX[(tr + 4 * i) * LDP + yp];
+          const float xv = sX[(tr + RG * i) * LDP + yp];
           float yv = yacc[i] + Dh * xv;
           if (a.z != nullptr)
             yv *= silu_f32(ldf<Ta>(a.z, ((int64_t)b * L + c0 + t) * a.z_stride + h * P + yp));
@@ -268,10 +276,10 @@ __global__ __launch_bounds__(THREADS) void scan_f32_kernel(ScanArgs a) {
     // place of its delta (the output tiles are done with it; read past the
     // barrier at the top of the tile loop below)
     for (int t = tid; t < Q; t += THREADS) sDel[t] = expf(lam_last - sLam[t]) * sDel[t];
-    float hacc[32];
+    float hacc[SW];
     const float gamma = expf(lam_last);
 #pragma unroll
-    for (int k = 0; k < 32; k += 4) {
+    for (int k = 0; k < SW; k += 4) {
       const float4 h4 = ld4(&sH[sp * LDN + sn0 + k]);
       hacc[k] = gamma * h4.x;
       hacc[k + 1] = gamma * h4.y;
@@ -280,16 +288,16 @@ __global__ __launch_bounds__(THREADS) void scan_f32_kernel(ScanArgs a) {
     }
     for (int st0 = 0; st0 < Lc; st0 += TT) {
       __syncthreads();
-      fill_tile<Tx, CONV, N>(a, a.Bm, a.b_stride, b, c0 + st0, Lc - st0, g * N, HP + g * N, cdim,
+      fill_tile<Tx, CONV, N, NT>(a, a.Bm, a.b_stride, b, c0 + st0, Lc - st0, g * N, HP + g * N, cdim,
                              sBt, LDN);
-      fill_tile<Tx, CONV, P>(a, a.x, a.x_stride, b, c0 + st0, Lc - st0, h * P, h * P, cdim, sX,
+      fill_tile<Tx, CONV, P, NT>(a, a.x, a.x_stride, b, c0 + st0, Lc - st0, h * P, h * P, cdim, sX,
                              LDP);
       __syncthreads();
       for (int q = 0; q < TT && st0 + q < Lc; ++q) {
         const int s = st0 + q;
         const float ws = sDel[s] * sX[q * LDP + sp];
 #pragma unroll
-        for (int k = 0; k < 32; k += 4) {
+        for (int k = 0; k < SW; k += 4) {
           const float4 b4 = ld4(&sBt[q * LDN + sn0 + k]);
           hacc[k] += ws * b4.x;
           hacc[k + 1] += ws * b4.y;
@@ -300,7 +308,7 @@ __global__ __launch_bounds__(THREADS) void scan_f32_kernel(ScanArgs a) {
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 32; k += 4)
+    for (int k = 0; k < SW; k += 4)
       *reinterpret_cast<float4*>(&sH[sp * LDN + sn0 + k]) =
           make_float4(hacc[k], hacc[k + 1], hacc[k + 2], hacc[k + 3]);
   }
@@ -331,21 +339,27 @@ __global__ __launch_bounds__(THREADS) void scan_f32_kernel(ScanArgs a) {
   }
 }
 
-template <typename Tx, typename Ta, typename Ty>
-hipError_t launch_typed(const ScanArgs& a, hipStream_t stream) {
-  const size_t lds = sizeof(float) * ((size_t)P * LDN + 2 * a.chunk + TT * LDC + TT * LDN + TT * LDP +
-                                      TT * LDT + 4);
+template <typename Tx, typename Ta, typename Ty, int NT>
+hipError_t launch_nt(const ScanArgs& a, hipStream_t stream) {
+  const size_t lds = sizeof(float) * ((size_t)P * LDN + 2 * a.chunk + TT * LDC + TT * LDN +
+                                      TT * LDP + TT * LDT + NT / 64);
   const dim3 grid(a.batch * a.nheads);
   if (a.conv_w != nullptr) {
-    auto k = scan_f32_kernel<Tx, Ta, Ty, true>;
+    auto k = scan_f32_kernel<Tx, Ta, Ty, true, NT>;
     (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL(k, grid, dim3(THREADS), lds, stream, a);
+    hipLaunchKernelGGL(k, grid, dim3(NT), lds, stream, a);
   } else {
-    auto k = scan_f32_kernel<Tx, Ta, Ty, false>;
+    auto k = scan_f32_kernel<Tx, Ta, Ty, false, NT>;
     (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL(k, grid, dim3(THREADS), lds, stream, a);
+    hipLaunchKernelGGL(k, grid, dim3(NT), lds, stream, a);
   }
   return hipGetLastError();
+}
+
+template <typename Tx, typename Ta, typename Ty>
+hipError_t launch_typed(const ScanArgs& a, hipStream_t stream) {
+  return (int64_t)a.batch * a.nheads <= NUM_CUS ? launch_nt<Tx, Ta, Ty, 512>(a, stream)
+                                                : launch_nt<Tx, Ta, Ty, 256>(a, stream);
 }
 
 template <typename Tx, typename Ta>
