@@ -3,24 +3,25 @@
 // feasibility study", table 1.4).
 //
 // HBM-bound: each input element is read once and each output written once.
-// A thread owns VEC adjacent channels (16-byte loads: 8 bf16 or 4 fp32) and
-// walks TOK consecutive tokens, keeping the last three inputs in registers,
-// so neighbouring threads read neighbouring 16-byte pieces of one token row
-// (fully coalesced) and the 3-token halo is re-read only once per TOK tokens.
-// The loads of 4 tokens are issued together, and large problems take windows
-// of 128 tokens, which spread each thread's tap loads and halo over more
-// outputs (bf16 in, fp32 out at 4 x 8192 tokens x 10240 channels: 0.645 ms
-// with 32-token windows and one load at a time, 0.578 with 4 loads in
-// flight, 0.466 with 128-token windows; 8 loads in flight, 256-token windows
-// or non-temporal output stores are no faster).
+// A thread owns VEC adjacent channels and walks TOK consecutive tokens,
+// keeping the last three inputs in registers, so neighbouring threads read
+// neighbouring pieces of one token row (fully coalesced) and the 3-token halo
+// is re-read only once per TOK tokens.  VEC is 4 for bf16 in and fp32 out
+// (8-byte loads, one 16-byte store per lane and token: a wave's store is one
+// 1 KiB piece), 8 for bf16 in and out, 4 for fp32 in.  The loads of 4 tokens
+// are issued together, and large problems take windows of 128 or 256 tokens,
+// which spread each thread's tap loads and halo over more outputs (bf16 in,
+// fp32 out at 4 x 8192 tokens x 10240 channels: 0.645 ms with 8 channels,
+// 32-token windows and one load at a time, 0.578 with 4 loads in flight,
+// 0.466 with 128-token windows, 0.417 with 4 channels and 256-token windows;
+// 8 loads in flight or non-temporal output stores were no faster).
 #include "ssd_common.h"
 
 namespace ssd {
 namespace {
 
-// tokens per thread: TOK_LONG when that still gives every CU a workgroup,
-// else TOK_SHORT (more, shorter windows for small problems)
-constexpr int TOK_SHORT = 32, TOK_LONG = 128;
+// tokens per thread (window lengths; the launch picks one, below)
+constexpr int TOK_SHORT = 32, TOK_LONG = 128, TOK_WIDE = 256;
 constexpr int NUM_CUS = 256;
 constexpr int THREADS = 256;
 
@@ -34,6 +35,15 @@ template <> struct Vec<bf16, 8> {
       v[2 * i] = __uint_as_float(w[i] << 16);
       v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
+  }
+};
+template <> struct Vec<bf16, 4> {
+  static __device__ __forceinline__ void load(const bf16* p, float* v) {
+    const uint2 r = *reinterpret_cast<const uint2*>(p);
+    v[0] = __uint_as_float(r.x << 16);
+    v[1] = __uint_as_float(r.x & 0xffff0000u);
+    v[2] = __uint_as_float(r.y << 16);
+    v[3] = __uint_as_float(r.y & 0xffff0000u);
   }
 };
 template <> struct Vec<float, 4> {
@@ -154,28 +164,38 @@ __global__ __launch_bounds__(THREADS) void causal_conv1d_kernel(
   }
 }
 
-template <typename Tin, typename Tout, int VEC>
+template <typename Tin, typename Tout, int VEC, int TL>
+hipError_t launch_tl(const void* x, int64_t x_stride, const float* w, const float* bias,
+                     const void* hist_in, void* hist_out, int64_t hs, void* out,
+                     int64_t out_stride, int B, int L, int C, int K, int apply_silu,
+                     int64_t gx, hipStream_t stream) {
+  dim3 grid((unsigned)gx, L > 0 ? (L + TL - 1) / TL : 1, B);
+  hipLaunchKernelGGL((causal_conv1d_kernel<Tin, Tout, VEC, TL>), grid, dim3(THREADS), 0, stream,
+                     static_cast<const Tin*>(x), x_stride, w, bias,
+                     static_cast<const Tin*>(hist_in), static_cast<Tin*>(hist_out), hs,
+                     static_cast<Tout*>(out), out_stride, L, C, K, apply_silu);
+  return hipGetLastError();
+}
+
+// The window length: TOK_WIDE tokens (WIDE instances only) when that still
+// gives every CU at least 4 workgroups, else TOK_LONG when every CU gets one,
+// else TOK_SHORT.
+template <typename Tin, typename Tout, int VEC, bool WIDE>
 hipError_t launch_typed(const void* x, int64_t x_stride, const float* w, const float* bias,
                         const void* hist_in, void* hist_out, int64_t hs, void* out,
                         int64_t out_stride, int B, int L, int C, int K, int apply_silu,
                         hipStream_t stream) {
   const int nv = C / VEC;
   const int64_t gx = (nv + THREADS - 1) / THREADS;
-  const int64_t long_wgs = gx * ((L + TOK_LONG - 1) / TOK_LONG) * B;
-  if (long_wgs >= NUM_CUS) {
-    dim3 grid((unsigned)gx, (L + TOK_LONG - 1) / TOK_LONG, B);
-    hipLaunchKernelGGL((causal_conv1d_kernel<Tin, Tout, VEC, TOK_LONG>), grid, dim3(THREADS), 0,
-                       stream, static_cast<const Tin*>(x), x_stride, w, bias,
-                       static_cast<const Tin*>(hist_in), static_cast<Tin*>(hist_out), hs,
-                       static_cast<Tout*>(out), out_stride, L, C, K, apply_silu);
-  } else {
-    dim3 grid((unsigned)gx, L > 0 ? (L + TOK_SHORT - 1) / TOK_SHORT : 1, B);
-    hipLaunchKernelGGL((causal_conv1d_kernel<Tin, Tout, VEC, TOK_SHORT>), grid, dim3(THREADS), 0,
-                       stream, static_cast<const Tin*>(x), x_stride, w, bias,
-                       static_cast<const Tin*>(hist_in), static_cast<Tin*>(hist_out), hs,
-                       static_cast<Tout*>(out), out_stride, L, C, K, apply_silu);
-  }
-  return hipGetLastError();
+  auto wgs = [&](int tl) { return gx * ((L + tl - 1) / tl) * B; };
+  if (WIDE && wgs(TOK_WIDE) >= 4 * NUM_CUS)
+    return launch_tl<Tin, Tout, VEC, TOK_WIDE>(x, x_stride, w, bias, hist_in, hist_out, hs, out,
+                                               out_stride, B, L, C, K, apply_silu, gx, stream);
+  if (wgs(TOK_LONG) >= NUM_CUS)
+    return launch_tl<Tin, Tout, VEC, TOK_LONG>(x, x_stride, w, bias, hist_in, hist_out, hs, out,
+                                               out_stride, B, L, C, K, apply_silu, gx, stream);
+  return launch_tl<Tin, Tout, VEC, TOK_SHORT>(x, x_stride, w, bias, hist_in, hist_out, hs, out,
+                                              out_stride, B, L, C, K, apply_silu, gx, stream);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -185,7 +205,11 @@ hipError_t dispatch_vec(const void* x, int64_t x_stride, const float* w, const f
                         const void* hist_in, void* hist_out, int64_t hs, void* out,
                         int64_t out_stride, int B, int L, int C, int K, int apply_silu,
                         hipStream_t stream) {
-  constexpr int V = sizeof(Tin) == 2 ? 8 : 4;
+  // bf16 in and fp32 out: 4 channels per thread, so that each lane's output
+  // row is one 16-byte store and a wave's store is 1 KiB in one piece; its
+  // registers then leave room for 256-token windows
+  constexpr bool BF_TO_F32 = sizeof(Tin) == 2 && sizeof(Tout) == 4;
+  constexpr int V = sizeof(Tin) == 2 ? (BF_TO_F32 ? 4 : 8) : 4;
   const bool vec_ok = C % V == 0 && x_stride % V == 0 && out_stride % V == 0 && hs % V == 0 &&
                       aligned16(x) &&
                       (hist_in == nullptr || aligned16(hist_in)) &&
@@ -193,9 +217,9 @@ hipError_t dispatch_vec(const void* x, int64_t x_stride, const float* w, const f
                       (sizeof(Tout) == 2 ? aligned16(out) && out_stride % 8 == 0
                                          : aligned16(out));
   if (vec_ok)
-    return launch_typed<Tin, Tout, V>(x, x_stride, w, bias, hist_in, hist_out, hs, out,
+    return launch_typed<Tin, Tout, V, BF_TO_F32>(x, x_stride, w, bias, hist_in, hist_out, hs, out,
                                       out_stride, B, L, C, K, apply_silu, stream);
-  return launch_typed<Tin, Tout, 1>(x, x_stride, w, bias, hist_in, hist_out, hs, out,
+  return launch_typed<Tin, Tout, 1, false>(x, x_stride, w, bias, hist_in, hist_out, hs, out,
                                     out_stride, B, L, C, K, apply_silu, stream);
 }
 
