@@ -40,7 +40,9 @@ def small(B, L, H, G, dtype="bf16", h0=True, seed=1):
     (1, 512, 512, 4, "f32", "f32", False, False),
     (2, 300, 1024, 4, "bf16", "f32", True, True),
     (3, 37, 520, 3, "bf16", "bf16", True, False),
-    (2, 45, 260, 4, "bf16", "f32", True, True),     # not a multiple of 8: scalar path
+    (2, 45, 260, 4, "bf16", "f32", True, True),     # 4 channels per thread (bf16 -> fp32)
+    (2, 45, 262, 4, "bf16", "f32", True, True),     # not a multiple of 4: scalar path
+    (1, 70, 260, 3, "bf16", "bf16", True, False),   # not a multiple of 8: scalar path
     (1, 1, 256, 4, "f32", "f32", True, False),
     (2, 2, 264, 4, "f32", "f32", True, True),       # L < K-1: history reaches into the old one
     (1, 33, 128, 1, "f32", "f32", False, False),
