@@ -52,7 +52,7 @@ struct BwdArgs {
   const float* h0; const float* dhT;
   float* states;              // [B, H, nc, P, N]
   float* dpost;               // [B, L, Cdim]: x part written here
-  float* dBh; float* dCh;     // [B, H, L, N]
+  float* dBh; float* dCh;     // [B, L, H, N]: a token's heads side by side
   float* ddt;                 // [B, L, H]
   float* dz;                  // [B, L, H, P] or null
   float* dh0;                 // [B, H, P, N] or null
@@ -671,16 +671,16 @@ __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
             db[k] = mfma4(at[e], bc[e][k], db[k]);
           }
       }
-      float* dcp = a.dCh + (((int64_t)b * H + h) * L + t0) * BN;
-      float* dbp = a.dBh + (((int64_t)b * H + h) * L + t0) * BN;
+      float* dcp = a.dCh + (((int64_t)b * L + t0) * H + h) * BN;
+      float* dbp = a.dBh + (((int64_t)b * L + t0) * H + h) * BN;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * ty + 4 * lq + e;
         if (t < Lc) {
 #pragma unroll
           for (int k = 0; k < 2; ++k) {
-            dcp[t * BN + 16 * (nb + k) + li] = dc[k][e];
-            dbp[t * BN + 16 * (nb + k) + li] = db[k][e];
+            dcp[(int64_t)t * H * BN + 16 * (nb + k) + li] = dc[k][e];
+            dbp[(int64_t)t * H * BN + 16 * (nb + k) + li] = db[k][e];
           }
         }
       }
@@ -743,7 +743,8 @@ __global__ __launch_bounds__(WT) void bwd_chunk_kernel(BwdArgs a) {
 }
 
 // The B and C gradients of a group: the sum of its heads' shares, in head
-// order.  One thread per (b, t, 4 consecutive n of B or C).
+// order.  One thread per (b, t, 4 consecutive n of B or C); the shares of a
+// token's heads are side by side, so a group's are one contiguous piece.
 __global__ void reduce_bc_kernel(const float* __restrict__ dBh, const float* __restrict__ dCh,
                                  float* __restrict__ dpost, int batch, int seqlen, int nheads,
                                  int ngroups, int cdim) {
@@ -752,8 +753,7 @@ __global__ void reduce_bc_kernel(const float* __restrict__ dBh, const float* __r
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= total) return;
   const int k = (int)(i % (2 * GN4));
-  const int64_t bt = i / (2 * GN4);
-  const int b = (int)(bt / seqlen), t = (int)(bt % seqlen);
+  const int64_t bt = i / (2 * GN4);  // b * seqlen + t
   const bool isC = k >= GN4;
   const int gn = (isC ? k - GN4 : k) * 4;
   const int g = gn / BN, n = gn % BN;
@@ -765,7 +765,7 @@ __global__ void reduce_bc_kernel(const float* __restrict__ dBh, const float* __r
 #pragma unroll 8
   for (int j = 0; j < hpg; ++j) {
     const int h = g * hpg + j;
-    const float4 v = *reinterpret_cast<const float4*>(src + (((int64_t)b * nheads + h) * seqlen + t) * BN + n);
+    const float4 v = *reinterpret_cast<const float4*>(src + (bt * nheads + h) * BN + n);
     acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
   }
   const int HP = nheads * BP;
